@@ -1,0 +1,344 @@
+"""Checks that pin the CPU oracle to facts fixed outside itself.
+
+Every check takes the oracle module as its argument, so the same checks run
+against the real oracle (tests/test_oracle_pins.py) and against copies with a
+planted mistake (tests/test_pin_mutations.py), which they must reject.
+
+Sources of the pinned facts (page title, section):
+  Speculative Decoding —— LLM推理优化技术（一）: §2.2 the output law of the
+    accept/resample rule is exactly p; §2.4 E[accept] = 1 - TV(p, q);
+    §3.1 tokens per round (1 - a^(K+1)) / (1 - a).
+  Lookahead Decoding 完全拆解:Jacobi 迭代与 N-gram 池: eq. (5), the expected
+    tokens per step with b disjoint candidates of gamma tokens each.
+  Hand-worked rounds in tests/golden/ (derivations stored beside them).
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+from scipy import special, stats
+
+from golden_io import greedy_case, load, logits_from_probs, sample_case
+from workloads import make_greedy_inputs, verify_uniforms
+
+
+# --------------------------------------------------------------------------- golden
+
+def check_golden_sample(orc) -> None:
+    for case in load("sample_worked.json")["cases"]:
+        c = sample_case(case)
+        res = orc.oracle_sample(c["target"], c["draft"], c["tokens"], c["uniforms"], c["T"])
+        assert np.array_equal(res.tokens, c["expect_tokens"]), (c["name"], res.tokens, c["expect_tokens"])
+        assert np.array_equal(res.n_accepted, c["expect_n"]), (c["name"], res.n_accepted, c["expect_n"])
+
+
+def check_golden_greedy(orc) -> None:
+    for case in load("greedy_worked.json")["cases"]:
+        c = greedy_case(case)
+        res = orc.oracle_greedy(c["logits"], c["cand"])
+        assert np.array_equal(res.tokens, c["expect_tokens"]), (c["name"], res.tokens)
+        assert np.array_equal(res.accept_len, c["expect_len"]), (c["name"], res.accept_len)
+        assert np.array_equal(res.best, c["expect_best"]), (c["name"], res.best)
+
+
+# --------------------------------------------------------------------------- closed forms
+
+def check_softmax_closed_forms(orc) -> None:
+    # equal logits: 1/V
+    for V in (1, 3, 1000):
+        p = orc.softmax64(np.full(V, 2.5), 0.7)
+        assert np.allclose(p, 1.0 / V, rtol=1e-14, atol=0)
+    # one logit a above V-1 zeros: e^(a/T) / (e^(a/T) + V - 1)
+    for a, V, T in ((3.0, 10, 1.0), (-2.0, 7, 0.5), (40.0, 128256, 2.0)):
+        x = np.zeros(V)
+        x[V // 2] = a
+        T64 = float(np.float32(T))
+        expect = math.exp(a / T64) / (math.exp(a / T64) + V - 1)
+        p = orc.softmax64(x, T)
+        assert abs(p[V // 2] - expect) <= 1e-14 * expect
+        assert abs(p[0] - 1.0 / (math.exp(a / T64) + V - 1)) <= 1e-14 * p[0]
+    # -inf entries carry no mass; the rest renormalise
+    p = orc.softmax64(np.array([0.0, -np.inf, 0.0, -np.inf]), 1.0)
+    assert np.array_equal(p, [0.5, 0.0, 0.5, 0.0])
+    # special case that reduces to a library routine: scipy's softmax of x / T,
+    # with T the float32 value the caller passes
+    rng = np.random.default_rng(7)
+    for T in (1.0, 0.7, 0.8, 1.3):
+        x = rng.normal(0, 3, 5000)
+        ref = special.softmax(x / float(np.float32(T)))
+        assert np.allclose(orc.softmax64(x, T), ref, rtol=1e-12, atol=1e-300)
+
+
+def check_acceptance_special_cases(orc) -> None:
+    a = orc.acceptance_probability
+    assert a(0.5, 0.25) == 1.0 and a(0.25, 0.25) == 1.0
+    assert a(0.125, 0.5) == 0.25
+    assert a(0.0, 0.5) == 0.0 and a(0.0, 0.0) == 0.0
+    assert a(0.3, 0.0) == 1.0
+    rng = np.random.default_rng(11)
+    V, K = 50, 3
+    # p == q at every position: every draft is accepted for any r < 1
+    tgt = rng.normal(0, 2, (8, K + 1, V))
+    drf = tgt[:, :K].copy()
+    toks = rng.integers(0, V, (8, K)).astype(np.int32)
+    uni = np.full((8, K + 1, 2), 1.0 - 2.0 ** -24, dtype=np.float32)
+    res = orc.oracle_sample(tgt, drf, toks, uni, 1.0)
+    assert np.all(res.n_accepted == K)
+    assert np.array_equal(res.tokens[:, :K], toks)
+    # one-hot q at x: alpha = p(x). Target uniform on 4 tokens holding x, so p(x) = 1/4.
+    tgt = np.full((2, 2, 8), -np.inf)
+    tgt[:, :, :4] = 0.0
+    drf = np.full((2, 1, 8), -np.inf)
+    drf[:, 0, 2] = 5.0
+    toks = np.array([[2], [2]], dtype=np.int32)
+    uni = np.zeros((2, 2, 2), dtype=np.float32)
+    uni[0, 0, 0] = 0.25 - 2.0 ** -24      # just below alpha: accept
+    uni[1, 0, 0] = 0.25                   # on alpha: reject
+    res = orc.oracle_sample(tgt, drf, toks, uni, 1.0)
+    assert res.n_accepted.tolist() == [1, 0]
+    # one-hot p at y, draft token x != y: alpha = 0 and the residual is all on y
+    tgt = np.full((3, 2, 6), -np.inf)
+    tgt[:, 0, 4] = 1.0
+    tgt[:, 1, :] = 0.0
+    drf = rng.normal(0, 1, (3, 1, 6))
+    toks = np.array([[0], [1], [5]], dtype=np.int32)
+    uni = np.zeros((3, 2, 2), dtype=np.float32)
+    uni[:, 0, 1] = [0.0, 0.5, 1.0 - 2.0 ** -24]
+    res = orc.oracle_sample(tgt, drf, toks, uni, 1.0)
+    assert res.n_accepted.tolist() == [0, 0, 0]
+    assert res.tokens[:, 0].tolist() == [4, 4, 4]
+
+
+def check_inverse_cdf(orc) -> None:
+    # uniform weights on 2^m tokens: C_k = (k+1)/2^m exactly; u = k/2^m selects k
+    for m in (1, 3, 6):
+        n = 2 ** m
+        w = np.full(n, 1.0 / n)
+        for k in range(n):
+            assert orc.inverse_cdf_draw(w, k / n)[0] == k
+            assert orc.inverse_cdf_draw(w, (k + 0.5) / n)[0] == k
+    # zero-mass tokens are never drawn, even when u*Z lands on their boundary
+    w = np.array([0.0, 1.0, 0.0, 1.0, 0.0])
+    assert orc.inverse_cdf_draw(w, 0.0)[0] == 1
+    assert orc.inverse_cdf_draw(w, 0.5)[0] == 3
+    assert orc.inverse_cdf_draw(w, 1.0 - 2.0 ** -24)[0] == 3
+    # unnormalised weights: the draw compares u*Z with the running sums
+    w = np.array([1.0, 2.0, 1.0])
+    assert [orc.inverse_cdf_draw(w, u)[0] for u in (0.0, 0.24, 0.25, 0.74, 0.75)] == [0, 0, 1, 1, 2]
+    k, Z, margin = orc.inverse_cdf_draw(w, 0.3)
+    assert Z == 4.0 and abs(margin - 0.2) < 1e-15
+
+
+# --------------------------------------------------------------------------- exact law on a grid
+
+GRID_PAIRS = [
+    # (p0, q0, p1): dyadic laws; every alpha and every w/Z is a multiple of 1/64
+    (["1/2", "1/4", "1/8", "1/8"], ["1/8", "1/8", "1/4", "1/2"], ["1/16", "3/16", "1/4", "1/2"]),
+    (["1/2", "1/2", "0", "0"], ["0", "0", "3/4", "1/4"], ["1/4", "1/4", "1/4", "1/4"]),
+    (["3/8", "1/8", "1/2", "0"], ["3/8", "1/8", "1/2", "0"], ["0", "0", "1/8", "7/8"]),
+    (["0", "5/16", "1/4", "1/16", "3/8", "0"], ["1/8", "1/16", "1/2", "1/16", "1/8", "1/8"],
+     ["1/2", "0", "0", "0", "0", "1/2"]),
+]
+
+
+def check_exact_law_on_grid(orc, pairs=GRID_PAIRS, grid: int = 64) -> None:
+    """Theorem of Speculative Decoding -- LLM推理优化技术（一） §2.2: the emitted token has law p exactly.
+
+    K = 1. The draft token x runs over q's support with weight q(x) (exact), the
+    accept uniform r and the draw uniform u over the midpoints of a 1/grid mesh.
+    All boundaries are multiples of 1/grid, so each mesh cell lies on one side
+    of each boundary and the mesh integral is exact. Checked exactly in
+    rationals: P(first token = y) = p0(y); P(all accepted) = 1 - TV(p0, q0)
+    (§2.4); P(all accepted, bonus = y) = (1 - TV) p1(y) (§2.3 step 4). The
+    bonus uniform is 1 - u, so a draw that read the wrong position's uniform
+    would show up as a mirrored law.
+    """
+    mids = (np.arange(grid) + 0.5) / grid
+    for p0s, q0s, p1s in pairs:
+        p0 = [Fraction(s) for s in p0s]
+        q0 = [Fraction(s) for s in q0s]
+        p1 = [Fraction(s) for s in p1s]
+        V = len(p0)
+        xs = [x for x in range(V) if q0[x] > 0]
+        rr, uu = np.meshgrid(mids, mids, indexing="ij")
+        rr, uu = rr.ravel(), uu.ravel()
+        cells = rr.size
+        B = len(xs) * cells
+        tgt = np.stack([logits_from_probs(p0s, 1.0), logits_from_probs(p1s, 1.0)])
+        tgt = np.broadcast_to(tgt, (B, 2, V))
+        drf = np.broadcast_to(logits_from_probs(q0s, 1.0), (B, 1, V))
+        toks = np.repeat(np.array(xs, dtype=np.int32), cells)[:, None]
+        uni = np.zeros((B, 2, 2), dtype=np.float64)
+        uni[:, 0, 0] = np.tile(rr, len(xs))
+        uni[:, 0, 1] = np.tile(uu, len(xs))
+        uni[:, 1, 1] = 1.0 - np.tile(uu, len(xs))
+        res = orc.oracle_sample(tgt, drf, toks, uni, 1.0, with_probs=False)
+        first = np.zeros(V, dtype=object)
+        bonus = np.zeros(V, dtype=object)
+        accepted = Fraction(0)
+        for j, x in enumerate(xs):
+            sl = slice(j * cells, (j + 1) * cells)
+            wgt = q0[x] / cells
+            t0 = res.tokens[sl, 0]
+            n = res.n_accepted[sl]
+            assert np.all(n >= 0)
+            for y in range(V):
+                first[y] += wgt * int(np.sum(t0 == y))
+                bonus[y] += wgt * int(np.sum((n == 1) & (res.tokens[sl, 1] == y)))
+            accepted += wgt * int(np.sum(n == 1))
+        tv = sum(abs(a - b) for a, b in zip(p0, q0)) / 2
+        assert list(first) == p0, ("first-token law", list(first), p0)
+        assert accepted == 1 - tv, ("acceptance", accepted, 1 - tv)
+        assert list(bonus) == [(1 - tv) * v for v in p1], ("bonus law", list(bonus))
+
+
+# --------------------------------------------------------------------------- statistics
+
+def _sample_from(q: np.ndarray, rng: np.random.Generator, n: int) -> np.ndarray:
+    return rng.choice(q.shape[-1], size=n, p=q / q.sum()).astype(np.int32)
+
+
+def check_chisquare_law(orc, trials: int = 30000) -> None:
+    """Output law = p (§2.2) by chi-square on non-dyadic laws; p-value >= 1e-3."""
+    rng = np.random.default_rng(2024)
+    for V in (2, 5, 16):
+        lt = rng.normal(0, 1.5, V)
+        ld = rng.normal(0, 1.5, V)
+        if V == 16:                       # disjoint-ish supports: half the target mass where q has none
+            ld[:4] = -np.inf
+        p = special.softmax(lt)
+        q = special.softmax(np.where(np.isinf(ld), -np.inf, ld))
+        toks = _sample_from(q, rng, trials)[:, None]
+        tgt = np.broadcast_to(np.stack([lt, lt]), (trials, 2, V))
+        drf = np.broadcast_to(ld, (trials, 1, V))
+        uni = verify_uniforms(100 + V, 0, trials, 1)
+        res = orc.oracle_sample(tgt, drf, toks, uni, 1.0, with_probs=False)
+        counts = np.bincount(res.tokens[:, 0], minlength=V)
+        pv = stats.chisquare(counts, p * trials).pvalue
+        assert pv >= 1e-3, (V, pv)
+
+
+def _fixed_tv_rows(rng, V: int, K: int, alpha: float):
+    """Logit rows with TV(p_i, q_i) = 1 - alpha at every position: q = (1-e) p + e delta_k."""
+    tgt = np.empty((K + 1, V))
+    drf = np.empty((K, V))
+    qs = []
+    for i in range(K + 1):
+        p = rng.dirichlet(np.ones(V))
+        tgt[i] = np.log(p)
+        if i < K:
+            k = int(np.argmin(p))
+            eps = (1.0 - alpha) / (1.0 - p[k])
+            q = (1.0 - eps) * p
+            q[k] += eps
+            drf[i] = np.log(q)
+            qs.append(q)
+    return tgt, drf, qs
+
+
+def check_acceptance_is_one_minus_tv(orc, trials: int = 20000) -> None:
+    """E[accept at i | position i reached] = 1 - TV(p_i, q_i) (§2.4), within 5 sigma."""
+    rng = np.random.default_rng(99)
+    V, K = 8, 4
+    tgt = rng.normal(0, 1.2, (K + 1, V))
+    drf = tgt[:K] + rng.normal(0, [[0.3], [0.8], [1.5], [3.0]], (K, V))
+    p = special.softmax(tgt[:K], axis=1)
+    q = special.softmax(drf, axis=1)
+    tv = 0.5 * np.abs(p - q).sum(axis=1)
+    toks = np.stack([_sample_from(q[i], rng, trials) for i in range(K)], axis=1)
+    uni = verify_uniforms(5, 0, trials, K)
+    res = orc.oracle_sample(np.broadcast_to(tgt, (trials, K + 1, V)), np.broadcast_to(drf, (trials, K, V)),
+                            toks, uni, 1.0, with_probs=False)
+    n = res.n_accepted
+    for i in range(K):
+        reached = n >= i
+        acc = n[reached] > i
+        m = reached.sum()
+        expect = 1.0 - tv[i]
+        sd = math.sqrt(expect * (1 - expect) / m)
+        assert abs(acc.mean() - expect) <= 5 * sd, (i, acc.mean(), expect, sd)
+
+
+def tokens_per_round(alpha: float, K: int) -> float:
+    """(1 - a^(K+1)) / (1 - a) (Speculative Decoding -- LLM推理优化技术（一） §3.1)."""
+    return (1.0 - alpha ** (K + 1)) / (1.0 - alpha)
+
+
+def check_tokens_per_round(orc, trials: int = 8000) -> None:
+    rng = np.random.default_rng(31)
+    V = 8
+    for K, alpha in ((3, 0.5), (5, 0.8), (7, 0.9)):
+        tgt, drf, qs = _fixed_tv_rows(rng, V, K, alpha)
+        toks = np.stack([_sample_from(qs[i], rng, trials) for i in range(K)], axis=1)
+        uni = verify_uniforms(77 + K, 0, trials, K)
+        res = orc.oracle_sample(np.broadcast_to(tgt, (trials, K + 1, V)), np.broadcast_to(drf, (trials, K, V)),
+                                toks, uni, 1.0, with_probs=False)
+        got = res.n_accepted + 1
+        expect = tokens_per_round(alpha, K)
+        sd = got.std() / math.sqrt(trials)
+        assert abs(got.mean() - expect) <= 5 * sd, (K, alpha, got.mean(), expect, sd)
+
+
+def lookahead_eq5(alpha: float, gamma: int, b: int) -> float:
+    """E(#tokens) = (gamma+1) - sum_{i=1..gamma} (1 - alpha^i)^b (Lookahead Decoding 完全拆解, eq. (5))."""
+    return (gamma + 1) - sum((1.0 - alpha ** i) ** b for i in range(1, gamma + 1))
+
+
+def check_greedy_eq5(orc, B: int = 6000) -> None:
+    """Mean accepted length + 1 over B rows of G disjoint candidates matches eq. (5), within 5 sigma.
+
+    float32 logits (no bf16 ties), so a candidate token matches the argmax with
+    probability alpha = 0.6 + 0.4/V, independently per position and candidate.
+    """
+    G, N, V = 7, 5, 64
+    g = make_greedy_inputs(0, B=B, G=G, N=N, V=V, dtype="f32", seed=3)
+    res = orc.oracle_greedy(g.logits_f32(), g.cand)
+    got = res.accept_len + 1
+    alpha = 0.6 + 0.4 / V
+    expect = lookahead_eq5(alpha, N - 1, G)
+    sd = got.std() / math.sqrt(B)
+    assert abs(got.mean() - expect) <= 5 * sd, (got.mean(), expect, sd)
+    p_full = 1.0 - (1.0 - alpha ** (N - 1)) ** G
+    frac = np.mean(res.accept_len == N - 1)
+    assert abs(frac - p_full) <= 5 * math.sqrt(p_full * (1 - p_full) / B), (frac, p_full)
+
+
+def check_greedy_argmax_brute_force(orc) -> None:
+    """Lowest-index argmax checked against a plain scan on small rows with many ties."""
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        V = int(rng.integers(1, 12))
+        row = rng.integers(-3, 3, V).astype(np.float64)
+        row[rng.random(V) < 0.2] = -np.inf
+        if not np.any(np.isfinite(row)):
+            continue
+        best, best_v = 0, row[0]
+        for v in range(1, V):
+            if row[v] > best_v:
+                best, best_v = v, row[v]
+        assert orc.first_argmax(row) == best
+
+
+def check_faults(orc) -> None:
+    """Fault reading: only consulted rows can fault; a fault gives n = -1 and all tokens -1."""
+    V, K = 6, 2
+    tgt = np.zeros((4, K + 1, V))
+    drf = np.zeros((4, K, V))
+    drf[:, 0, 3:] = -np.inf                 # q0 uniform on {0,1,2}
+    toks = np.array([[4, 0], [0, 0], [0, 0], [0, 0]], dtype=np.int32)
+    uni = np.zeros((4, K + 1, 2), dtype=np.float32)
+    # row 0: x0 = 4 has q0 = 0 and p0 = 1/6 > 0: alpha = 1 -> accepted, x1 fine -> n = 2
+    # row 1: draft row 1 all -inf -> consulted at i = 1 (x0 accepted) -> fault
+    drf[1, 1, :] = -np.inf
+    # row 2: x0 rejected (target mass 0 at x0) -> draft row 1 never consulted -> no fault
+    tgt[2, 0, 0] = -np.inf
+    drf[2, 1, :] = -np.inf
+    # row 3: all accepted, bonus row all -inf -> fault
+    tgt[3, K, :] = -np.inf
+    res = orc.oracle_sample(tgt, drf, toks, uni, 1.0)
+    assert res.n_accepted.tolist() == [2, -1, 0, -1]
+    assert np.all(res.tokens[[1, 3]] == -1)
+    assert res.tokens[0, :2].tolist() == [4, 0] and 0 <= res.tokens[0, 2] < V
+    assert res.tokens[2, 1:].tolist() == [-1, -1] and res.tokens[2, 0] in (1, 2, 3, 4, 5)

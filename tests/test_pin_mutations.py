@@ -1,0 +1,92 @@
+"""Plant plausible mistakes in copies of the oracle; the pins must reject every copy (CPU only).
+
+Each mutation edits the oracle's source text (a dropped term, a wrong sign,
+index or operand, a flipped comparison), loads it as a separate module and runs
+the pin checks until one fails. A mutation that passes every pin would mean
+the pins cannot see that kind of mistake.
+"""
+import importlib.util
+import os
+import sys
+
+import pytest
+
+import pins
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "verify.py")
+
+MUTATIONS = [
+    ("accept compares with <=", "if r < alpha:", "if r <= alpha:"),
+    ("ratio operands swapped", "return p_x / q_x", "return q_x / p_x"),
+    ("no truncation to one", "if p_x >= q_x:\n        return 1.0\n", ""),
+    ("residual sign flipped", "np.maximum(0.0, p_rej - q_rej)", "np.maximum(0.0, q_rej - p_rej)"),
+    ("residual without the clamp", "np.maximum(0.0, p_rej - q_rej)", "(p_rej - q_rej)"),
+    ("bonus from the wrong row", "softmax64(target[b, K], temperature)", "softmax64(target[b, K - 1], temperature)"),
+    ("draw uses the accept uniform", "float(uniforms[b, n, 1])", "float(uniforms[b, n, 0])"),
+    ("draw uses position 0's uniform", "float(uniforms[b, n, 1])", "float(uniforms[b, 0, 1])"),
+    ("draw boundary inclusive", "np.nonzero(c > tau)", "np.nonzero(c >= tau)"),
+    ("softmax not normalised", "return e / np.sum(e)", "return e"),
+    ("temperature multiplies", "/ temperature64(temperature)", "* temperature64(temperature)"),
+    ("temperature ignored", "/ temperature64(temperature)", "/ 1.0"),
+    ("draw not scaled by Z", "tau = float(u) * Z", "tau = float(u)"),
+    ("accepted prefix shifted", "tokens[b, :n] = draft_tokens[b, :n]", "tokens[b, :n] = draft_tokens[b, ::-1][:n]"),
+    ("rejection position off by one", "n = i                              #", "n = min(i + 1, K)                  #"),
+    ("no zero-mass fallback", "if np.sum(w) == 0.0:", "if False:"),
+    ("greedy match test inverted", "cand[b, g, L[g]] == amax[b, g, L[g]]", "cand[b, g, L[g]] != amax[b, g, L[g]]"),
+    ("greedy highest candidate wins ties", "best = int(np.argmax(L))", "best = int(len(L) - 1 - np.argmax(L[::-1]))"),
+    ("greedy extra token from the wrong row", "amax[b, best, Lb]", "amax[b, best, max(Lb - 1, 0)]"),
+    ("greedy argmax highest index on ties",
+     "return int(np.argmax(np.asarray(row, dtype=np.float64)))",
+     "return int(len(row) - 1 - np.argmax(np.asarray(row, dtype=np.float64)[::-1]))"),
+    ("greedy counts one position too many", "while L[g] < N - 1 and", "while L[g] < N and"),
+]
+
+CHECKS = [
+    pins.check_golden_sample,
+    pins.check_golden_greedy,
+    pins.check_softmax_closed_forms,
+    pins.check_acceptance_special_cases,
+    pins.check_inverse_cdf,
+    pins.check_faults,
+    pins.check_greedy_argmax_brute_force,
+    pins.check_exact_law_on_grid,
+    pins.check_acceptance_is_one_minus_tv,
+    pins.check_tokens_per_round,
+]
+
+
+def _mutant(name: str, old: str, new: str):
+    with open(ORACLE_SRC, encoding="utf-8") as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation '{name}' does not apply: text not found"
+    src = src.replace(old, new)
+    modname = "oracle_mutant_" + "".join(ch if ch.isalnum() else "_" for ch in name)
+    spec = importlib.util.spec_from_loader(modname, loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[modname] = mod
+    exec(compile(src, f"<{modname}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_reject_planted_mistake(name, old, new):
+    mod = _mutant(name, old, new)
+    try:
+        for check in CHECKS:
+            try:
+                check(mod)
+            except Exception:
+                return  # caught
+        pytest.fail(f"planted mistake '{name}' passed every pin")
+    finally:
+        sys.modules.pop(mod.__name__, None)
+
+
+def test_unmutated_copy_passes_every_pin():
+    """Control: a copy loaded the same way, with no edit, passes all the checks."""
+    mod = _mutant("control", "import numpy as np", "import numpy as np")
+    try:
+        for check in CHECKS:
+            check(mod)
+    finally:
+        sys.modules.pop(mod.__name__, None)
