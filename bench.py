@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Throughput of the speculative-decoding verify step on one MI355X.
+
+One step = one verify round of the B=64, K=8, V=128256 bf16 workload (T = 1.0):
+both launches of spec_verify_sample (pass 1: row statistics, accept tests and
+the first rejection; pass 2: the residual / bonus draw). Inputs are seeded
+synthetic logits already resident in HBM. The timed steps cycle through
+several copies of the inputs (together more than twice the 256 MB Infinity
+Cache), so each step reads its logits from HBM rather than from the cache.
+Each step is one HIP-graph replay; the timed region is bracketed by HIP events
+on the stream the kernels run on.
+
+Prints ONE JSON line. Also reported: the pass-1 kernel alone (the dominant
+kernel, for the roofline), the greedy verify on its own workload (B=32 G=7 N=5
+V=32000 bf16), and the CPU oracle on a bounded sample of the same round.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, AMD published peak
+CACHE_BYTES = 256 * 2 ** 20  # MI355X Infinity Cache
+METRIC = "verify rounds/s + achieved HBM GB/s (% peak), B=64 K=8 V=128256 bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ["common.hpp", "params.hpp", "sample.hip", "greedy.hip"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--rotate", type=int, default=0, help="input copies (0: enough to exceed 2x the cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-greedy", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch through the Python binding instead of graphs")
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "rejection_sampling_verify_sample_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from rocprofv3 counters, if taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = d.get(kernel)
+    if not ent or ent.get("source_sha") != kernel_source_sha():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+class Timer:
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time(self, fn, n: int) -> float:
+        """Seconds for n calls of fn(i), bracketed by events on the current stream."""
+        t = self.torch
+        t.cuda.synchronize()
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        t.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3
+
+
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import rejection_sampling_verify_sample_amd as rsv
+    from workloads import WORKLOAD_NAMES, make_greedy_inputs, make_sample_inputs
+    from workloads.torch_io import greedy_tensors, sample_tensors
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    timer = Timer(torch)
+
+    # ---------------------------------------------------------------- sampling verify, B=64 K=8 V=128256 bf16
+    t0 = time.time()
+    s = make_sample_inputs(3, 0)
+    B, K, V = s.shape
+    esz = 2
+    base = sample_tensors(s, dev)
+    set_bytes = (base["target"].numel() + base["draft"].numel()) * esz
+    M = args.rotate or max(2, math.ceil(2 * CACHE_BYTES / set_bytes) + 1)
+    log(f"inputs generated in {time.time() - t0:.1f}s; {M} copies of {set_bytes / 1e6:.1f} MB")
+    sets = []
+    for m in range(M):
+        sets.append(dict(target=base["target"].clone(), draft=base["draft"].clone(),
+                         draft_tokens=base["draft_tokens"].clone(), uniforms=base["uniforms"].clone(),
+                         out_tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                         out_n=torch.empty((B,), dtype=torch.int32, device=dev)))
+    del base
+    ws = torch.zeros(rsv.sample_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
+
+    def call(st, phase="both"):
+        rsv.verify_sample(st["target"], st["draft"], st["draft_tokens"], st["uniforms"], s.temperature,
+                          out_tokens=st["out_tokens"], out_num_accepted=st["out_n"], workspace=ws, phase=phase)
+
+    for i in range(3):
+        call(sets[i % M])
+    torch.cuda.synchronize()
+
+    def graphs_for(phase):
+        gs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for st in sets:
+                call(st, phase)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for st in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                call(st, phase)
+            gs.append(g)
+        return gs
+
+    if args.eager:
+        step = lambda i: call(sets[i % M])          # noqa: E731
+        acc = lambda i: call(sets[i % M], "accept")  # noqa: E731
+    else:
+        g_full = graphs_for("both")
+        g_acc = graphs_for("accept")
+        step = lambda i: g_full[i % M].replay()      # noqa: E731
+        acc = lambda i: g_acc[i % M].replay()        # noqa: E731
+
+    timer.time(step, args.warmup)
+    t_step = timer.time(step, args.steps) / args.steps
+    timer.time(acc, max(args.warmup // 4, 10))
+    t_pass1 = timer.time(acc, args.steps) / args.steps
+    # outputs of the last full step of each copy (identical inputs -> identical outputs)
+    for i in range(M):
+        step(i)
+    torch.cuda.synchronize()
+    n_acc = sets[0]["out_n"].cpu().numpy()
+    assert np.all(n_acc >= 0) and np.all(n_acc <= K), "invalid accepted counts"
+    tok = sets[0]["out_tokens"].cpu().numpy()
+    assert np.all((tok[np.arange(B), n_acc] >= 0) & (tok[np.arange(B), n_acc] < V))
+
+    # algorithmic bytes: pass 1 reads the 2K rows of every batch row once; pass 2
+    # rereads target+draft row n after a rejection, or the bonus row once
+    row_bytes = V * esz
+    pass1_bytes = B * 2 * K * row_bytes + B * K * 4 + B * K * 4 * 2 + B * (K + 1) * 4 + B * 4
+    pass2_bytes = int(sum(2 * row_bytes if n < K else row_bytes for n in n_acc)) + B * 8 + B * 4
+    step_bytes = pass1_bytes + pass2_bytes
+    rounds_per_s = 1.0 / t_step
+    step_gbps = step_bytes / t_step / 1e9
+    pass1_gbps = pass1_bytes / t_pass1 / 1e9
+    traffic = measured_traffic("k_sample_pass1")
+    log(f"step {t_step * 1e6:.2f} us ({rounds_per_s:.0f} rounds/s, {step_gbps:.0f} GB/s); "
+        f"pass 1 {t_pass1 * 1e6:.2f} us ({pass1_gbps:.0f} GB/s); mean accepted {n_acc.mean():.3f}")
+    del sets, g_full if not args.eager else None
+
+    # ---------------------------------------------------------------- greedy verify, B=32 G=7 N=5 V=32000 bf16
+    greedy = None
+    if not args.no_greedy:
+        g5 = make_greedy_inputs(0)
+        gb, gg, gn, gv = g5.shape
+        gt = greedy_tensors(g5, dev)
+        gbytes = gt["logits"].numel() * 2
+        M5 = max(2, math.ceil(2 * CACHE_BYTES / gbytes) + 1)
+        gsets = [dict(logits=gt["logits"].clone(), cand=gt["cand"].clone(),
+                      ot=torch.empty((gb, gn), dtype=torch.int32, device=dev),
+                      ol=torch.empty((gb,), dtype=torch.int32, device=dev),
+                      ob=torch.empty((gb,), dtype=torch.int32, device=dev)) for _ in range(M5)]
+        gws = torch.zeros(rsv.greedy_workspace_size(gb, gg, gn, gv), dtype=torch.uint8, device=dev)
+
+        def gcall(st):
+            rsv.verify_greedy(st["logits"], st["cand"], out_tokens=st["ot"], out_accept_len=st["ol"],
+                              out_best=st["ob"], workspace=gws)
+
+        for st in gsets:
+            gcall(st)
+        torch.cuda.synchronize()
+        if args.eager:
+            gstep = lambda i: gcall(gsets[i % M5])   # noqa: E731
+        else:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for st in gsets:
+                    gcall(st)
+            gstep = lambda i: graph.replay()         # noqa: E731
+        reps = max(1, args.steps // M5)
+        timer.time(gstep, max(1, args.warmup // M5))
+        per = (timer.time(gstep, reps) / reps) / (1 if args.eager else M5)
+        gal = gbytes + gb * gg * (gn - 1) * 4 + gb * (gn + 2) * 4
+        greedy = {"workload": WORKLOAD_NAMES[5], "rounds_per_s": round(1.0 / per, 1),
+                  "us_per_round": round(per * 1e6, 3), "achieved_gbps": round(gal / per / 1e9, 1),
+                  "frac_of_hbm_peak": round(gal / per / 1e9 / HBM_PEAK_GBPS, 4), "rotate": M5,
+                  "algorithmic_bytes": gal}
+        log(f"greedy {per * 1e6:.2f} us/round ({gal / per / 1e9:.0f} GB/s)")
+
+    # ---------------------------------------------------------------- CPU oracle on a bounded sample
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        tgt, drf = s.target_f32(), s.draft_f32()
+        rows = 0
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < args.cpu_seconds and rows < 4 * B:
+            b = rows % B
+            oracle.oracle_sample(tgt[b:b + 1], drf[b:b + 1], s.draft_tokens[b:b + 1], s.uniforms[b:b + 1],
+                                 s.temperature, with_probs=False)
+            rows += 1
+        el = time.perf_counter() - t1
+        cpu = {"value": round(rows / el / B, 4), "unit": "verify rounds/s", "cores": 1, "kind": "oracle",
+               "sample": f"{rows} batch rows of the B=64 K=8 V=128256 bf16 round (float64 NumPy, one thread), "
+                         f"{el:.1f} s, scaled to rounds of 64 rows",
+               "host_cpu": cpu_model(), "host_logical_cpus": os.cpu_count()}
+        log(f"cpu oracle {rows} rows in {el:.1f}s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(rounds_per_s, 2),
+        "unit": "verify rounds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[3], "B": B, "K": K, "V": V, "T": s.temperature,
+                   "input_copies": M, "graph": not args.eager},
+        "draft_tokens_per_s": round(B * K * rounds_per_s, 1),
+        "achieved_gbps": round(step_gbps, 1),
+        "frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": step_bytes,
+        "mean_accepted": round(float(n_acc.mean()), 4),
+        "roofline": {"kernel": "k_sample_pass1", "bound": "hbm", "achieved": round(pass1_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(pass1_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": pass1_bytes,
+                     "us_per_launch": round(t_pass1 * 1e6, 3)},
+        "cpu_baseline": cpu,
+        "greedy": greedy,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

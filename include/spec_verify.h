@@ -1,0 +1,183 @@
+/*
+ * spec_verify.h -- C ABI of the speculative-decoding verify library (HIP, gfx950).
+ *
+ * The library implements the verify step of speculative decoding:
+ *   - spec_verify_sample: rejection-sampling verify of K draft tokens per row.
+ *     p_i = softmax(target_i / T), q_i = softmax(draft_i / T), both computed in
+ *     fp32; draft token x_i is accepted iff r_i < min(1, p_i(x_i) / q_i(x_i));
+ *     the walk stops at the first rejection n, where a replacement token is
+ *     drawn from norm(max(0, p_n - q_n)); if all K are accepted, a bonus token
+ *     is drawn from p_K (target row K).
+ *     Sources: "Speculative Decoding —— LLM推理优化技术（一）", §2.1 (acceptance
+ *     probability, residual law), §2.3 (multi-token rule, bonus token), §4 (the
+ *     temperature divides the logits; zero residual mass falls back to p);
+ *     kwkr.cn/news/620797 engineering notes, §3.1 (accept iff r < alpha, reject
+ *     iff r >= alpha; bonus from the target's last position), §3.2 (fp32
+ *     probabilities; truncate alpha to 1 when p >= q), §3.4 (the same
+ *     temperature on both sides).
+ *   - spec_verify_greedy: greedy (temperature 0) verify of G disjoint candidate
+ *     n-grams: the longest prefix matching the target's per-position argmax
+ *     wins and is followed by the argmax after it.
+ *     Source: "Lookahead Decoding 完全拆解:Jacobi 迭代与 N-gram 池,不靠草稿模型的
+ *     投机解码", section "验证分支:输出分布不变性", and eq. (1) (greedy decoding is
+ *     the per-position argmax).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, row-major and
+ *     contiguous, aligned to their element size. The library never allocates
+ *     device memory and keeps no state between calls.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronise the host.
+ *   - Every argument error is detected on the host and returned as a negative
+ *     status BEFORE any HIP call; outputs are then untouched. A launch failure
+ *     returns SPEC_ERR_HIP.
+ *   - Data faults found on the device are reported per row in the outputs
+ *     (see each function), never by the status.
+ *   - Outputs must not overlap inputs or each other.
+ *   - The workspace holds arrival counters that must be zero when a call
+ *     starts; every call leaves them at zero again, at offsets that depend on
+ *     the entry point family and the sizes. Zero the workspace after
+ *     allocation, after a call that failed on the device, and before reusing
+ *     it for other sizes or the other family. Calls that run at the same time
+ *     must use different workspaces; calls of one shape in one stream may
+ *     share one without clearing it in between.
+ *   - Logits are finite or -inf. A +inf or NaN logit gives unspecified values
+ *     for its row (never an out-of-bounds access).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+#define SPEC_MAX_K 64        /* draft positions per row; the first-reject scan is one 64-lane ballot */
+#define SPEC_MAX_V (1 << 30) /* vocabulary entries per row */
+#define SPEC_MAX_ROWS (1 << 24) /* logit rows per call */
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_ERR_NULL = -1,        /* a required pointer is NULL */
+  SPEC_ERR_SHAPE = -2,       /* a size is out of range */
+  SPEC_ERR_TEMPERATURE = -3, /* temperature not finite or not > 0 */
+  SPEC_ERR_DTYPE = -4,       /* unknown spec_dtype */
+  SPEC_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_size query */
+  SPEC_ERR_HIP = -6,         /* a HIP launch failed */
+  SPEC_ERR_ALIGN = -7        /* a pointer is not aligned to its element size */
+} spec_status;
+
+/* Bytes of workspace spec_verify_sample needs for these sizes (0 for invalid sizes). */
+size_t spec_verify_sample_workspace_size(int32_t B, int32_t K, int32_t V);
+
+/*
+ * Rejection-sampling verify of B independent rows.
+ *
+ * target_logits    [B, K+1, V] dtype. Row i (< K) is the target distribution for
+ *                  draft token i (already aligned by the caller: the logits
+ *                  that PREDICT x_i); row K is the bonus row.
+ * draft_logits     [B, K, V] dtype. Row i is the draft distribution x_i was drawn from.
+ * dtype            SPEC_F32 or SPEC_BF16, shared by both logits tensors.
+ * draft_tokens     [B, K] int32.
+ * uniforms         [B, K+1, 2] float, each in [0, 1): [b,i,0] = accept uniform
+ *                  r_i (read for i < K); [b,i,1] = draw uniform u_i (the
+ *                  resample at i < K, the bonus draw at i = K).
+ * B, K, V          0 <= B, 0 <= K <= SPEC_MAX_K, 1 <= V <= SPEC_MAX_V,
+ *                  B*(2K+1) <= SPEC_MAX_ROWS. B = 0 is a no-op. K = 0 draws one
+ *                  token from the bonus row.
+ * temperature      finite, > 0; logits are divided by it on both sides.
+ * out_tokens       [B, K+1] int32: x_0..x_{n-1}, then the drawn token at n, then -1.
+ * out_num_accepted [B] int32: n in [0, K], or -1 for a data fault.
+ * out_probs        NULL or [B, K, 2] float: p_i(x_i), q_i(x_i) in fp32 for every
+ *                  i < K (NaN where x_i is out of range or a row has no finite logit).
+ * workspace        device memory of at least spec_verify_sample_workspace_size bytes.
+ *
+ * Draw rule: token = the smallest k with sum_{v<=k} w_v > u * sum_v w_v, where w
+ * is max(0, p_n - q_n) (or p_K for the bonus draw); if the residual mass is 0,
+ * w = p_n.
+ * Data faults (reported as out_num_accepted[b] = -1 and out_tokens[b,:] = -1):
+ * walking i = 0, 1, ...: x_i outside [0, V), or target row i or draft row i with
+ * no finite logit, at a position the walk reaches; or all K accepted and the
+ * bonus row has no finite logit.
+ */
+spec_status spec_verify_sample(const void* target_logits, const void* draft_logits, int32_t dtype,
+                               const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t K,
+                               int32_t V, float temperature, int32_t* out_tokens,
+                               int32_t* out_num_accepted, float* out_probs, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * The two launches of spec_verify_sample, for callers that schedule or time
+ * them apart. Both take exactly spec_verify_sample's arguments.
+ * spec_verify_sample_accept runs pass 1: it reads target rows 0..K-1 and draft
+ *   rows 0..K-1 once, writes out_num_accepted, out_probs and every out_tokens
+ *   entry except the drawn one, and leaves in the workspace what the draw needs.
+ * spec_verify_sample_draw runs pass 2: it reads only the rows the draw needs
+ *   (target and draft row n after a rejection, or the bonus row) and writes the
+ *   drawn token (and the fault outputs of a bonus row with no finite logit).
+ *   It must follow spec_verify_sample_accept with the same arguments and
+ *   workspace, in stream order. With K = 0 the accept pass does nothing.
+ */
+spec_status spec_verify_sample_accept(const void* target_logits, const void* draft_logits, int32_t dtype,
+                                      const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t K,
+                                      int32_t V, float temperature, int32_t* out_tokens,
+                                      int32_t* out_num_accepted, float* out_probs, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+spec_status spec_verify_sample_draw(const void* target_logits, const void* draft_logits, int32_t dtype,
+                                    const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t K,
+                                    int32_t V, float temperature, int32_t* out_tokens,
+                                    int32_t* out_num_accepted, float* out_probs, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace spec_verify_greedy needs for these sizes (0 for invalid sizes). */
+size_t spec_verify_greedy_workspace_size(int32_t B, int32_t G, int32_t N, int32_t V);
+
+/*
+ * Greedy verify of G disjoint candidates per row (temperature 0 only: argmax
+ * matching under sampling would change the output law, kwkr.cn notes §2).
+ *
+ * target_logits  [B, G, N, V] dtype. Row i of candidate g holds the target's
+ *                logits after the prefix cand[b,g,0..i-1]; row N-1 is the bonus row.
+ * cand_tokens    [B, G, N-1] int32: the candidate n-gram's tokens after the
+ *                (already matched) first token.
+ * B, G, N, V     0 <= B, 1 <= G, 2 <= N <= SPEC_MAX_K + 1, G*N <= 8192,
+ *                1 <= V <= SPEC_MAX_V, B*G*N <= SPEC_MAX_ROWS.
+ * out_tokens     [B, N] int32: cand[b,best,0..L-1], then argmax of row L of
+ *                candidate best, then -1.
+ * out_accept_len [B] int32: L in [0, N-1], or -1 for a data fault.
+ * out_best_cand  [B] int32: the winning candidate, or -1 for a data fault.
+ * Argmax ties go to the lowest vocabulary index; prefix-length ties to the
+ * lowest candidate index. Data faults: a candidate token outside [0, V), or a
+ * row with no finite logit (out_tokens[b,:] = -1).
+ */
+spec_status spec_verify_greedy(const void* target_logits, int32_t dtype, const int32_t* cand_tokens,
+                               int32_t B, int32_t G, int32_t N, int32_t V, int32_t* out_tokens,
+                               int32_t* out_accept_len, int32_t* out_best_cand, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * Fill out [B, K+1, 2] with the verify uniforms of one round from
+ * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+ * as 1, 2, 3", SC'11). Counter for (b, i) = (i, b, round lo32, round hi32);
+ * key = (seed lo32, seed hi32); output word 0 -> [b,i,0], word 1 -> [b,i,1],
+ * each mapped as (w >> 8) * 2^-24.
+ * 0 <= B, 0 <= K <= SPEC_MAX_K, B*(K+1) <= SPEC_MAX_ROWS.
+ */
+spec_status spec_fill_uniforms(uint64_t seed, uint64_t round, int32_t B, int32_t K, float* out, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* spec_status_string(int32_t status);
+
+/* SPEC_ABI_VERSION of the built library. */
+int32_t spec_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,260 @@
+"""ctypes binding of libspecverify.so: argument marshalling only.
+
+Every step of the verify computation runs in the HIP library. This module
+checks tensor devices, dtypes, shapes and contiguity, allocates outputs and a
+per-stream workspace through PyTorch, and passes raw pointers plus the current
+HIP stream. If the library has not been built it raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libspecverify.so")
+
+SPEC_F32 = 0
+SPEC_BF16 = 1
+SPEC_MAX_K = 64
+
+_c_void_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_u64 = ctypes.c_uint64
+_size_t = ctypes.c_size_t
+
+_SIGNATURES = {
+    "spec_abi_version": (_i32, []),
+    "spec_status_string": (ctypes.c_char_p, [_i32]),
+    "spec_verify_sample_workspace_size": (_size_t, [_i32, _i32, _i32]),
+    "spec_verify_sample": (_i32, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                  ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
+                                  _c_void_p]),
+    "spec_verify_sample_accept": None,
+    "spec_verify_sample_draw": None,
+    "spec_verify_greedy_workspace_size": (_size_t, [_i32, _i32, _i32, _i32]),
+    "spec_verify_greedy": (_i32, [_c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
+                                  _c_void_p, _c_void_p, _size_t, _c_void_p]),
+    "spec_fill_uniforms": (_i32, [_u64, _u64, _i32, _i32, _c_void_p, _c_void_p]),
+}
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is not built; run `python -m rejection_sampling_verify_sample_amd.build`"
+                                   " (hipcc, gfx950). There is no fallback path.")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, sig in _SIGNATURES.items():
+                res, args = sig if sig is not None else _SIGNATURES["spec_verify_sample"]
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().spec_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().spec_abi_version())
+
+
+def sample_workspace_size(B: int, K: int, V: int) -> int:
+    return int(lib().spec_verify_sample_workspace_size(B, K, V))
+
+
+def greedy_workspace_size(B: int, G: int, N: int, V: int) -> int:
+    return int(lib().spec_verify_greedy_workspace_size(B, G, N, V))
+
+
+# ------------------------------------------------------------------ tensors and streams
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t: torch.Tensor, name: str, device: torch.device, dtype=None, shape=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(stream, device: torch.device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+_workspaces: dict[tuple[int, int], list] = {}
+_ws_lock = threading.Lock()
+
+
+def workspace_for(device: torch.device, stream_handle: int, nbytes: int, layout_key: tuple) -> torch.Tensor:
+    """A workspace reused by every call on one (device, stream).
+
+    The library leaves its arrival counters at zero after each call, at the
+    offsets of that call's layout; a call with other sizes puts its counters
+    elsewhere. So the buffer is zeroed when it is created and whenever the
+    layout (entry point family and sizes) changes from the previous call.
+    """
+    key = (device.index, stream_handle)
+    with _ws_lock:
+        ent = _workspaces.get(key)
+        if ent is None or ent[0].numel() < nbytes:
+            ent = [torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device), None]
+            _workspaces[key] = ent
+        if ent[1] != layout_key:
+            with torch.cuda.stream(torch.cuda.ExternalStream(stream_handle, device=device)):
+                ent[0].zero_()
+            ent[1] = layout_key
+        return ent[0]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ------------------------------------------------------------------ entry points
+
+@dataclass
+class SampleOutputs:
+    tokens: torch.Tensor        # [B, K+1] int32
+    num_accepted: torch.Tensor  # [B] int32
+    probs: torch.Tensor | None  # [B, K, 2] float32
+
+
+_PHASE_ENTRY = {"both": "spec_verify_sample", "accept": "spec_verify_sample_accept", "draw": "spec_verify_sample_draw"}
+
+
+def verify_sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                  temperature: float, *, out_tokens: torch.Tensor | None = None,
+                  out_num_accepted: torch.Tensor | None = None, out_probs: torch.Tensor | None = None,
+                  want_probs: bool = False, workspace: torch.Tensor | None = None, stream=None,
+                  phase: str = "both") -> SampleOutputs:
+    """spec_verify_sample on torch tensors (layouts as in include/spec_verify.h). Asynchronous on `stream`.
+
+    phase="accept" / "draw" calls the library's pass-1 / pass-2 entry point alone
+    (the draw must follow an accept call with the same arguments and workspace).
+    """
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    _check(target, "target", dev)
+    code = _dtype_code(target)
+    _check(draft, "draft", dev, target.dtype, (B, K, V))
+    _check(draft_tokens, "draft_tokens", dev, torch.int32, (B, K))
+    _check(uniforms, "uniforms", dev, torch.float32, (B, K + 1, 2))
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", dev, torch.int32, (B, K + 1))
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(out_num_accepted, "out_num_accepted", dev, torch.int32, (B,))
+    if out_probs is None and want_probs:
+        out_probs = torch.empty((B, K, 2), dtype=torch.float32, device=dev)
+    if out_probs is not None:
+        _check(out_probs, "out_probs", dev, torch.float32, (B, K, 2))
+    sh = _stream_handle(stream, dev)
+    nbytes = sample_workspace_size(B, K, V)
+    if nbytes == 0 and B > 0:
+        raise SpecVerifyError(-2, "spec_verify_sample_workspace_size")
+    if workspace is None:
+        workspace = workspace_for(dev, sh, nbytes, ("sample", B, K, V))
+    _check(workspace, "workspace", dev, torch.uint8)
+    entry = getattr(lib(), _PHASE_ENTRY[phase])
+    st = entry(_ptr(target), _ptr(draft), code, _ptr(draft_tokens), _ptr(uniforms), B, K, V,
+                                  float(temperature), _ptr(out_tokens), _ptr(out_num_accepted), _ptr(out_probs),
+                                  _ptr(workspace), workspace.numel(), ctypes.c_void_p(sh))
+    if st != 0:
+        raise SpecVerifyError(st, _PHASE_ENTRY[phase])
+    return SampleOutputs(out_tokens, out_num_accepted, out_probs)
+
+
+@dataclass
+class GreedyOutputs:
+    tokens: torch.Tensor      # [B, N] int32
+    accept_len: torch.Tensor  # [B] int32
+    best: torch.Tensor        # [B] int32
+
+
+def verify_greedy(logits: torch.Tensor, cand: torch.Tensor, *, out_tokens: torch.Tensor | None = None,
+                  out_accept_len: torch.Tensor | None = None, out_best: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stream=None) -> GreedyOutputs:
+    """spec_verify_greedy on torch tensors (layouts as in include/spec_verify.h). Asynchronous on `stream`."""
+    if logits.dim() != 4:
+        raise ValueError("logits must be [B, G, N, V]")
+    B, G, N, V = logits.shape
+    dev = logits.device
+    _check(logits, "logits", dev)
+    code = _dtype_code(logits)
+    _check(cand, "cand", dev, torch.int32, (B, G, N - 1))
+    if out_tokens is None:
+        out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if out_accept_len is None:
+        out_accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_best is None:
+        out_best = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", dev, torch.int32, (B, N))
+    _check(out_accept_len, "out_accept_len", dev, torch.int32, (B,))
+    _check(out_best, "out_best", dev, torch.int32, (B,))
+    sh = _stream_handle(stream, dev)
+    nbytes = greedy_workspace_size(B, G, N, V)
+    if nbytes == 0 and B > 0:
+        raise SpecVerifyError(-2, "spec_verify_greedy_workspace_size")
+    if workspace is None:
+        workspace = workspace_for(dev, sh, nbytes, ("greedy", B, G, N, V))
+    _check(workspace, "workspace", dev, torch.uint8)
+    st = lib().spec_verify_greedy(_ptr(logits), code, _ptr(cand), B, G, N, V, _ptr(out_tokens),
+                                  _ptr(out_accept_len), _ptr(out_best), _ptr(workspace), workspace.numel(),
+                                  ctypes.c_void_p(sh))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_verify_greedy")
+    return GreedyOutputs(out_tokens, out_accept_len, out_best)
+
+
+def fill_uniforms(seed: int, rnd: int, B: int, K: int, *, out: torch.Tensor | None = None,
+                  device: torch.device | str | None = None, stream=None) -> torch.Tensor:
+    """spec_fill_uniforms: the verify uniforms [B, K+1, 2] of one round, on the device."""
+    if out is None:
+        dev = torch.device(device if device is not None else "cuda")
+        out = torch.empty((B, K + 1, 2), dtype=torch.float32, device=dev)
+    _check(out, "out", out.device, torch.float32, (B, K + 1, 2))
+    sh = _stream_handle(stream, out.device)
+    st = lib().spec_fill_uniforms(int(seed) & (2 ** 64 - 1), int(rnd) & (2 ** 64 - 1), B, K, _ptr(out),
+                                  ctypes.c_void_p(sh))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_fill_uniforms")
+    return out

@@ -1,0 +1,239 @@
+// C ABI of the verify library: argument checks, workspace layout, launches.
+// Every argument error is found here, on the host, before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+
+#include "../../include/spec_verify.h"
+#include "params.hpp"
+
+#define SPEC_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace sv {
+hipError_t launch_sample(const SampleParams& P, bool bf16, int phases, hipStream_t stream);
+hipError_t launch_greedy(const GreedyParams& P, bool bf16, hipStream_t stream);
+hipError_t launch_philox(uint64_t seed, uint64_t round, int32_t B, int32_t K, float* out, hipStream_t stream);
+}  // namespace sv
+
+namespace {
+
+using sv::GreedyLayout;
+using sv::SampleLayout;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Most segments a row may be split into: bounds the partials the workspace holds.
+int32_t seg_max(int64_t rows, int64_t V) {
+  int64_t s = ceil_div(65536, std::max<int64_t>(rows, 1));
+  s = std::min<int64_t>(s, 64);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, V / 256));
+  return static_cast<int32_t>(std::max<int64_t>(s, 1));
+}
+
+// Segments per row: enough workgroups to fill 256 CUs several times over, but
+// segments of at least `min_seg` elements. SPECVERIFY_S<n> overrides (tuning).
+int32_t seg_choice(int64_t rows, int64_t V, int64_t target_blocks, int64_t min_seg, int32_t smax,
+                   const char* env) {
+  int64_t s = ceil_div(target_blocks, std::max<int64_t>(rows, 1));
+  s = std::min<int64_t>(s, std::max<int64_t>(1, V / min_seg));
+  if (const char* e = std::getenv(env)) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v > 0) s = v;
+  }
+  return static_cast<int32_t>(std::clamp<int64_t>(s, 1, smax));
+}
+
+bool sample_shape_ok(int32_t B, int32_t K, int32_t V) {
+  if (B < 0 || K < 0 || K > SPEC_MAX_K || V < 1 || V > SPEC_MAX_V) return false;
+  return static_cast<int64_t>(B) * (2 * static_cast<int64_t>(K) + 1) <= SPEC_MAX_ROWS;
+}
+
+bool greedy_shape_ok(int32_t B, int32_t G, int32_t N, int32_t V) {
+  if (B < 0 || G < 1 || N < 2 || N > SPEC_MAX_K + 1 || V < 1 || V > SPEC_MAX_V) return false;
+  if (static_cast<int64_t>(G) * N > sv::kMaxGreedyRowsPerBatch) return false;
+  return static_cast<int64_t>(B) * G * N <= SPEC_MAX_ROWS;
+}
+
+SampleLayout sample_layout(int32_t B, int32_t K, int32_t V) {
+  SampleLayout L{};
+  const int64_t rows1 = static_cast<int64_t>(B) * 2 * K;
+  L.S1max = seg_max(rows1, V);
+  L.S2max = seg_max(B, V);
+  L.S1 = seg_choice(rows1, V, 2048, 2048, L.S1max, "SPECVERIFY_S1");
+  L.S2 = seg_choice(B, V, 1024, 2048, L.S2max, "SPECVERIFY_S2");
+  size_t off = 0;
+  const size_t p1 = static_cast<size_t>(rows1) * L.S1max;
+  L.off_p1m = off; off = align256(off + p1 * sizeof(float));
+  L.off_p1s = off; off = align256(off + p1 * sizeof(double));
+  L.off_cnt1 = off; off = align256(off + static_cast<size_t>(B) * sizeof(uint32_t));
+  L.off_info_n = off; off = align256(off + static_cast<size_t>(B) * sizeof(int32_t));
+  L.off_info_R = off; off = align256(off + static_cast<size_t>(B) * 2 * sizeof(float));
+  L.off_info_S = off; off = align256(off + static_cast<size_t>(B) * 2 * sizeof(double));
+  const size_t p2 = static_cast<size_t>(B) * L.S2max;
+  L.off_p2m = off; off = align256(off + p2 * sizeof(float));
+  L.off_p2s = off; off = align256(off + p2 * sizeof(double));
+  L.off_cnt2 = off; off = align256(off + static_cast<size_t>(B) * sizeof(uint32_t));
+  L.total = std::max<size_t>(off, 256);
+  return L;
+}
+
+GreedyLayout greedy_layout(int32_t B, int32_t G, int32_t N, int32_t V) {
+  GreedyLayout L{};
+  const int64_t rows = static_cast<int64_t>(B) * G * N;
+  L.S3max = seg_max(rows, V);
+  L.S3 = seg_choice(rows, V, 2048, 2048, L.S3max, "SPECVERIFY_S3");
+  size_t off = 0;
+  const size_t p3 = static_cast<size_t>(rows) * L.S3max;
+  L.off_p3v = off; off = align256(off + p3 * sizeof(float));
+  L.off_p3i = off; off = align256(off + p3 * sizeof(int32_t));
+  L.off_cnt3 = off; off = align256(off + static_cast<size_t>(B) * sizeof(uint32_t));
+  L.total = std::max<size_t>(off, 256);
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+SPEC_EXPORT int32_t spec_abi_version(void) { return SPEC_ABI_VERSION; }
+
+SPEC_EXPORT const char* spec_status_string(int32_t status) {
+  switch (status) {
+    case SPEC_OK: return "ok";
+    case SPEC_ERR_NULL: return "a required pointer is NULL";
+    case SPEC_ERR_SHAPE: return "a size is out of range";
+    case SPEC_ERR_TEMPERATURE: return "temperature must be finite and > 0";
+    case SPEC_ERR_DTYPE: return "unknown dtype";
+    case SPEC_ERR_WORKSPACE: return "workspace too small";
+    case SPEC_ERR_HIP: return "HIP launch failed";
+    case SPEC_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    default: return "unknown status";
+  }
+}
+
+SPEC_EXPORT size_t spec_verify_sample_workspace_size(int32_t B, int32_t K, int32_t V) {
+  if (!sample_shape_ok(B, K, V)) return 0;
+  return sample_layout(B, K, V).total;
+}
+
+SPEC_EXPORT size_t spec_verify_greedy_workspace_size(int32_t B, int32_t G, int32_t N, int32_t V) {
+  if (!greedy_shape_ok(B, G, N, V)) return 0;
+  return greedy_layout(B, G, N, V).total;
+}
+
+namespace {
+spec_status verify_sample_phases(const void* target_logits, const void* draft_logits, int32_t dtype,
+                                 const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t K,
+                                 int32_t V, float temperature, int32_t* out_tokens, int32_t* out_num_accepted,
+                                 float* out_probs, void* workspace, size_t workspace_bytes, void* stream,
+                                 int phases) {
+  if (!sample_shape_ok(B, K, V)) return SPEC_ERR_SHAPE;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
+  if (!(std::isfinite(temperature) && temperature > 0.f)) return SPEC_ERR_TEMPERATURE;
+  const float c = static_cast<float>(1.4426950408889634074 / static_cast<double>(temperature));
+  if (!std::isfinite(c)) return SPEC_ERR_TEMPERATURE;
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !uniforms || !out_tokens || !out_num_accepted || !workspace) return SPEC_ERR_NULL;
+  if (K > 0 && (!draft_logits || !draft_tokens)) return SPEC_ERR_NULL;
+  const size_t es = dtype == SPEC_BF16 ? 2 : 4;
+  if (!aligned(target_logits, es) || (K > 0 && !aligned(draft_logits, es)) ||
+      (K > 0 && !aligned(draft_tokens, 4)) || !aligned(uniforms, 4) || !aligned(out_tokens, 4) ||
+      !aligned(out_num_accepted, 4) || (out_probs && !aligned(out_probs, 4)) || !aligned(workspace, 8))
+    return SPEC_ERR_ALIGN;
+  const SampleLayout L = sample_layout(B, K, V);
+  if (workspace_bytes < L.total) return SPEC_ERR_WORKSPACE;
+
+  sv::SampleParams P{};
+  P.target = target_logits;
+  P.draft = draft_logits;
+  P.tokens = draft_tokens;
+  P.uniforms = uniforms;
+  P.B = B;
+  P.K = K;
+  P.V = V;
+  P.c = c;
+  P.S1 = L.S1;
+  P.S2 = L.S2;
+  P.out_tokens = out_tokens;
+  P.out_n = out_num_accepted;
+  P.out_probs = out_probs;
+  P.p1_m = at<float>(workspace, L.off_p1m);
+  P.p1_s = at<double>(workspace, L.off_p1s);
+  P.cnt1 = at<uint32_t>(workspace, L.off_cnt1);
+  P.info_n = at<int32_t>(workspace, L.off_info_n);
+  P.info_R = at<float>(workspace, L.off_info_R);
+  P.info_S = at<double>(workspace, L.off_info_S);
+  P.p2_m = at<float>(workspace, L.off_p2m);
+  P.p2_s = at<double>(workspace, L.off_p2s);
+  P.cnt2 = at<uint32_t>(workspace, L.off_cnt2);
+  const hipError_t e = sv::launch_sample(P, dtype == SPEC_BF16, phases, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+}  // namespace
+
+#define SPEC_SAMPLE_ARGS                                                                                     \
+  const void *target_logits, const void *draft_logits, int32_t dtype, const int32_t *draft_tokens,           \
+      const float *uniforms, int32_t B, int32_t K, int32_t V, float temperature, int32_t *out_tokens,        \
+      int32_t *out_num_accepted, float *out_probs, void *workspace, size_t workspace_bytes, void *stream
+#define SPEC_SAMPLE_FWD                                                                                      \
+  target_logits, draft_logits, dtype, draft_tokens, uniforms, B, K, V, temperature, out_tokens,              \
+      out_num_accepted, out_probs, workspace, workspace_bytes, stream
+
+SPEC_EXPORT spec_status spec_verify_sample(SPEC_SAMPLE_ARGS) { return verify_sample_phases(SPEC_SAMPLE_FWD, 3); }
+SPEC_EXPORT spec_status spec_verify_sample_accept(SPEC_SAMPLE_ARGS) {
+  return verify_sample_phases(SPEC_SAMPLE_FWD, 1);
+}
+SPEC_EXPORT spec_status spec_verify_sample_draw(SPEC_SAMPLE_ARGS) { return verify_sample_phases(SPEC_SAMPLE_FWD, 2); }
+
+SPEC_EXPORT spec_status spec_verify_greedy(const void* target_logits, int32_t dtype, const int32_t* cand_tokens,
+                                           int32_t B, int32_t G, int32_t N, int32_t V, int32_t* out_tokens,
+                                           int32_t* out_accept_len, int32_t* out_best_cand, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  if (!greedy_shape_ok(B, G, N, V)) return SPEC_ERR_SHAPE;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !cand_tokens || !out_tokens || !out_accept_len || !out_best_cand || !workspace)
+    return SPEC_ERR_NULL;
+  const size_t es = dtype == SPEC_BF16 ? 2 : 4;
+  if (!aligned(target_logits, es) || !aligned(cand_tokens, 4) || !aligned(out_tokens, 4) ||
+      !aligned(out_accept_len, 4) || !aligned(out_best_cand, 4) || !aligned(workspace, 8))
+    return SPEC_ERR_ALIGN;
+  const GreedyLayout L = greedy_layout(B, G, N, V);
+  if (workspace_bytes < L.total) return SPEC_ERR_WORKSPACE;
+
+  sv::GreedyParams P{};
+  P.logits = target_logits;
+  P.cand = cand_tokens;
+  P.B = B;
+  P.G = G;
+  P.N = N;
+  P.V = V;
+  P.S3 = L.S3;
+  P.out_tokens = out_tokens;
+  P.out_len = out_accept_len;
+  P.out_best = out_best_cand;
+  P.p3_v = at<float>(workspace, L.off_p3v);
+  P.p3_i = at<int32_t>(workspace, L.off_p3i);
+  P.cnt3 = at<uint32_t>(workspace, L.off_cnt3);
+  const hipError_t e = sv::launch_greedy(P, dtype == SPEC_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+SPEC_EXPORT spec_status spec_fill_uniforms(uint64_t seed, uint64_t round, int32_t B, int32_t K, float* out,
+                                           void* stream) {
+  if (B < 0 || K < 0 || K > SPEC_MAX_K || static_cast<int64_t>(B) * (K + 1) > SPEC_MAX_ROWS)
+    return SPEC_ERR_SHAPE;
+  if (B == 0) return SPEC_OK;
+  if (!out) return SPEC_ERR_NULL;
+  if (!aligned(out, 4)) return SPEC_ERR_ALIGN;
+  const hipError_t e = sv::launch_philox(seed, round, B, K, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}

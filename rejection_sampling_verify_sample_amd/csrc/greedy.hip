@@ -1,0 +1,191 @@
+// Greedy (temperature 0) verify of G disjoint candidate n-grams (gfx950).
+//
+// Method ("Lookahead Decoding 完全拆解:Jacobi 迭代与 N-gram 池,不靠草稿模型的投机解码",
+// section "验证分支:输出分布不变性", eq. (1)): the i-th token of a candidate must equal
+// the target's argmax at position i; the longest matched prefix among the
+// candidates wins, followed by the argmax right after it.
+//
+// k_greedy: one workgroup per (logit row, segment) streams its segment with
+// 16-byte loads and keeps the running (maximum, lowest index attaining it) per
+// thread, visiting its elements in increasing index order; a block reduction on
+// (value desc, index asc) gives the segment's first argmax. The last workgroup
+// of batch row b merges the segments in index order, matches every candidate's
+// prefix, and picks the longest (lowest candidate index on ties).
+#include "common.hpp"
+#include "params.hpp"
+
+namespace sv {
+
+struct ArgMax {
+  float v;
+  int64_t i;  // -1: no element seen yet
+  // Elements arrive in increasing index order, so a tie keeps the earlier index.
+  __device__ __forceinline__ void take(float x, int64_t e) {
+    if (i < 0 || x > v) {
+      v = x;
+      i = e;
+    }
+  }
+  template <int VEC>
+  __device__ __forceinline__ void take_vec(const float (&x)[VEC], int64_t base) {
+    float m = x[0];
+#pragma unroll
+    for (int e = 1; e < VEC; ++e) m = fmaxf(m, x[e]);
+    if (i < 0 || m > v) {
+      int first = VEC - 1;
+#pragma unroll
+      for (int e = VEC - 1; e >= 0; --e)
+        if (x[e] == m) first = e;  // lowest e attaining m
+      v = m;
+      i = base + first;
+    }
+  }
+};
+
+// (value desc, index asc) merge of two candidates; i < 0 means empty.
+__device__ __forceinline__ void argmax_merge(float& v, int64_t& i, float v2, int64_t i2) {
+  if (i2 < 0) return;
+  if (i < 0 || v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void argmax_segment(const T* row, int64_t V, int seg, int S, ArgMax& a) {
+  constexpr int VEC = Elem<T>::kVec;
+  const SegRange r = seg_range(row, V, seg, S);
+  if (seg == 0)
+    for (int64_t e = threadIdx.x; e < r.head; e += kBlock) a.take(Elem<T>::get(row, e), e);
+  const T* vb = row + r.head;
+  int64_t v = r.v0 + threadIdx.x;
+  for (; v + kBlock < r.v1; v += 2 * kBlock) {
+    float x0[VEC], x1[VEC];
+    Elem<T>::vec(vb + v * VEC, x0);
+    Elem<T>::vec(vb + (v + kBlock) * VEC, x1);
+    a.take_vec(x0, r.head + v * VEC);
+    a.take_vec(x1, r.head + (v + kBlock) * VEC);
+  }
+  for (; v < r.v1; v += kBlock) {
+    float x0[VEC];
+    Elem<T>::vec(vb + v * VEC, x0);
+    a.take_vec(x0, r.head + v * VEC);
+  }
+  if (seg == S - 1)
+    for (int64_t e = r.head + ((V - r.head) / VEC) * VEC + threadIdx.x; e < V; e += kBlock)
+      a.take(Elem<T>::get(row, e), e);
+}
+
+__device__ __forceinline__ void block_argmax(float& v, int64_t& i) {
+  __shared__ float sh_v[kWaves];
+  __shared__ int64_t sh_i[kWaves];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(v, o, 64);
+    const int64_t i2 = __shfl_xor(i, o, 64);
+    argmax_merge(v, i, v2, i2);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sh_v[threadIdx.x >> 6] = v;
+    sh_i[threadIdx.x >> 6] = i;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kWaves; ++w) argmax_merge(v, i, sh_v[w], sh_i[w]);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_greedy(GreedyParams P) {
+  const int S = P.S3;
+  const int GN = P.G * P.N;
+  const int seg = blockIdx.x % S;
+  const int row = blockIdx.x / S;  // in [0, B*G*N)
+  const int b = row / GN;
+  const T* rp = static_cast<const T*>(P.logits) + static_cast<int64_t>(row) * P.V;
+
+  ArgMax a{-INFINITY, -1};
+  argmax_segment(rp, P.V, seg, S, a);
+  float v = a.v;
+  int64_t i = a.i;
+  block_argmax(v, i);
+  if (threadIdx.x == 0) {
+    // a segment whose maximum is -inf holds no finite logit: report it as empty
+    const bool finite_max = isfinite(v);
+    st_agent(P.p3_v + static_cast<int64_t>(row) * S + seg, v);
+    st_agent(P.p3_i + static_cast<int64_t>(row) * S + seg, finite_max ? static_cast<int32_t>(i) : -1);
+  }
+  if (!arrive_last(P.cnt3 + b, static_cast<uint32_t>(GN * S))) return;
+
+  // ---- epilogue of batch row b
+  extern __shared__ int32_t sh_amax[];  // [G*N] argmax per row of this batch row
+  __shared__ int sh_fault;
+  __shared__ uint32_t sh_key;
+  if (threadIdx.x == 0) {
+    sh_fault = 0;
+    sh_key = 0;
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < GN; r += kBlock) {
+    const int64_t base = (static_cast<int64_t>(b) * GN + r) * S;
+    float bv = -INFINITY;
+    int32_t bi = -1;
+    for (int j = 0; j < S; ++j) {  // segments in index order: strict > keeps the lowest index
+      const int32_t ij = ld_agent(P.p3_i + base + j);
+      const float vj = ld_agent(P.p3_v + base + j);
+      if (ij >= 0 && (bi < 0 || vj > bv)) {
+        bv = vj;
+        bi = ij;
+      }
+    }
+    sh_amax[r] = bi;
+    if (bi < 0) atomicOr(&sh_fault, 1);
+  }
+  __syncthreads();
+  const int N = P.N, G = P.G;
+  const int32_t* cb = P.cand + static_cast<int64_t>(b) * G * (N - 1);
+  for (int g = threadIdx.x; g < G; g += kBlock) {
+    int L = 0;
+    bool run = true;
+    for (int t = 0; t < N - 1; ++t) {
+      const int32_t ct = cb[g * (N - 1) + t];
+      if (ct < 0 || ct >= P.V) atomicOr(&sh_fault, 1);
+      if (run && ct == sh_amax[g * N + t]) ++L;
+      else run = false;
+    }
+    // key: longer prefix first, then lower candidate index
+    atomicMax(&sh_key, (static_cast<uint32_t>(L) << 16) | static_cast<uint32_t>(0xFFFF - g));
+  }
+  __syncthreads();
+  const bool fault = sh_fault != 0;
+  const uint32_t key = sh_key;
+  const int L = static_cast<int>(key >> 16);
+  const int best = 0xFFFF - static_cast<int>(key & 0xFFFF);
+  int32_t* ot = P.out_tokens + static_cast<int64_t>(b) * N;
+  for (int t = threadIdx.x; t < N; t += kBlock) {
+    int32_t tok = -1;
+    if (!fault) {
+      if (t < L) tok = cb[best * (N - 1) + t];
+      else if (t == L) tok = sh_amax[best * N + L];
+    }
+    ot[t] = tok;
+  }
+  if (threadIdx.x == 0) {
+    P.out_len[b] = fault ? -1 : L;
+    P.out_best[b] = fault ? -1 : best;
+  }
+}
+
+template <typename T>
+static hipError_t launch_greedy_t(const GreedyParams& P, hipStream_t stream) {
+  const int64_t g = static_cast<int64_t>(P.B) * P.G * P.N * P.S3;
+  const size_t lds = static_cast<size_t>(P.G) * P.N * sizeof(int32_t);
+  hipLaunchKernelGGL(k_greedy<T>, dim3(static_cast<uint32_t>(g)), dim3(kBlock), lds, stream, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_greedy(const GreedyParams& P, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_greedy_t<bf16_t>(P, stream) : launch_greedy_t<float>(P, stream);
+}
+
+}  // namespace sv

@@ -1,0 +1,116 @@
+"""Compare the HIP path's outputs with the oracle's, under the parity rule.
+
+Rule (task statement of the verify step): accepted counts and token ids
+bit-exact, except rows where a uniform lies within WINDOW of the boundary that
+decided it; softmax probabilities within 1e-5 absolute and 1e-4 relative.
+
+Rows inside the window are not skipped: the GPU's decision there must still be
+valid -- a differing accept decision must be one whose uniform lies within the
+window of alpha, and a differing drawn token must own an interval of the
+oracle's cumulative weights that lies within the window of u*Z. Draw margins are
+in probability mass (the units of max(0, p - q)); see the oracle's doc.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle
+
+WINDOW = 1e-6
+PROB_RTOL = 1e-4
+PROB_ATOL = 1e-5
+
+
+@dataclass
+class ParityReport:
+    rows: int = 0
+    ambiguous: int = 0
+    ambiguous_agree: int = 0
+    mismatches: list = field(default_factory=list)
+
+    def merge(self, other: "ParityReport") -> "ParityReport":
+        self.rows += other.rows
+        self.ambiguous += other.ambiguous
+        self.ambiguous_agree += other.ambiguous_agree
+        self.mismatches += other.mismatches
+        return self
+
+    def summary(self) -> str:
+        return (f"rows={self.rows} ambiguous={self.ambiguous} ({self.ambiguous / max(self.rows, 1):.2e}) "
+                f"agree-in-window={self.ambiguous_agree} mismatches={len(self.mismatches)}")
+
+
+def _draw_weights(tgt_row, drf_row, T, residual: bool):
+    p = oracle.softmax64(tgt_row, T)
+    if not residual:
+        return p
+    w = np.maximum(0.0, p - oracle.softmax64(drf_row, T))
+    return w if np.sum(w) > 0 else p
+
+
+def _interval_distance(w: np.ndarray, u: float, k: int) -> float:
+    """Distance of u*Z from token k's interval [C_{k-1}, C_k) of the cumulative weights."""
+    c = np.cumsum(w)
+    tau = u * c[-1]
+    lo = c[k - 1] if k > 0 else 0.0
+    hi = c[k]
+    if hi <= lo:   # a zero-mass token can never be a valid draw
+        return np.inf
+    if lo <= tau < hi:
+        return 0.0
+    return min(abs(tau - lo), abs(tau - hi))
+
+
+def compare_sample(target, draft, tokens_in, uniforms, T, res: "oracle.SampleResult", gpu_tokens, gpu_n,
+                   gpu_probs=None, window: float = WINDOW) -> ParityReport:
+    """target/draft: float arrays (bf16 widened); gpu_* numpy arrays. Raises AssertionError on a violation."""
+    B, K = tokens_in.shape
+    rep = ParityReport(rows=B)
+    if gpu_probs is not None:
+        op = res.probs
+        both_nan = np.isnan(op) & np.isnan(gpu_probs)
+        finite = np.isfinite(op)
+        assert np.array_equal(np.isnan(op), np.isnan(gpu_probs)), "probability NaN pattern differs"
+        ok = np.isclose(gpu_probs[finite], op[finite], rtol=PROB_RTOL, atol=PROB_ATOL)
+        assert ok.all(), f"probabilities differ beyond tolerance at {np.argwhere(finite)[~ok][:5]}"
+        del both_nan
+    margin = res.min_margin()
+    small_z = np.nan_to_num(res.residual_mass, nan=1.0) < window
+    for b in range(B):
+        on, gn = int(res.n_accepted[b]), int(gpu_n[b])
+        same = on == gn and np.array_equal(res.tokens[b], gpu_tokens[b])
+        amb = margin[b] < window or small_z[b]
+        if not amb:
+            if not same:
+                rep.mismatches.append(b)
+                raise AssertionError(f"row {b}: oracle n={on} tokens={res.tokens[b].tolist()} vs GPU n={gn} "
+                                     f"tokens={gpu_tokens[b].tolist()} (margin {margin[b]:.3e})")
+            continue
+        rep.ambiguous += 1
+        if same:
+            rep.ambiguous_agree += 1
+            continue
+        # validity inside the window
+        assert on >= 0 and gn >= 0, f"row {b}: fault status differs ({on} vs {gn})"
+        if on != gn:
+            i = min(on, gn)
+            assert res.accept_margin[b, i] < window, f"row {b}: accept decision at {i} differs outside the window"
+            assert np.array_equal(res.tokens[b, :i], gpu_tokens[b, :i])
+            continue
+        n = on
+        assert np.array_equal(res.tokens[b, :n], gpu_tokens[b, :n])
+        assert np.all(gpu_tokens[b, n + 1:] == -1)
+        w = _draw_weights(target[b, n], draft[b, n] if n < K else None, T, residual=n < K)
+        d = _interval_distance(w, float(uniforms[b, n, 1]), int(gpu_tokens[b, n]))
+        assert d < window, f"row {b}: GPU token {gpu_tokens[b, n]} is {d:.3e} from u*Z"
+    return rep
+
+
+def compare_greedy(res: "oracle.GreedyResult", gpu_tokens, gpu_len, gpu_best) -> None:
+    bad = np.nonzero((res.accept_len != gpu_len) | (res.best != gpu_best) |
+                     np.any(res.tokens != gpu_tokens, axis=1))[0]
+    assert bad.size == 0, (f"greedy mismatch in rows {bad[:8].tolist()}: oracle {res.tokens[bad[0]].tolist()} "
+                           f"L={res.accept_len[bad[0]]} best={res.best[bad[0]]} vs GPU {gpu_tokens[bad[0]].tolist()} "
+                           f"L={gpu_len[bad[0]]} best={gpu_best[bad[0]]}")

@@ -1,0 +1,139 @@
+"""The C ABI library: loads, exports what include/*.h declares, rejects bad arguments on the host (no GPU).
+
+Argument errors are detected before any HIP call, so these calls run on a
+machine without a GPU. Pointers here are never dereferenced: every call is
+built to fail validation (or to be a B = 0 no-op).
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import rejection_sampling_verify_sample_amd as rsv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6, -7
+P = 0x10000  # aligned, never dereferenced
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h, encoding="utf-8").read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names.update(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(spec_\w+)\s*\(", src, flags=re.M))
+    return sorted(names)
+
+
+def test_library_is_built_and_loads():
+    assert os.path.exists(rsv.LIB_PATH)
+    assert rsv.abi_version() == 1
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 9, names
+    L = ctypes.CDLL(rsv.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/ but not exported"
+
+
+def sample(**kw):
+    a = dict(target=P, draft=P, dtype=1, tokens=P, uniforms=P, B=4, K=3, V=100, T=1.0, out_tokens=P, out_n=P,
+             out_probs=None, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return rsv.lib().spec_verify_sample(a["target"], a["draft"], a["dtype"], a["tokens"], a["uniforms"], a["B"],
+                                        a["K"], a["V"], a["T"], a["out_tokens"], a["out_n"], a["out_probs"],
+                                        a["ws"], a["ws_bytes"], a["stream"])
+
+
+def greedy(**kw):
+    a = dict(logits=P, dtype=1, cand=P, B=2, G=3, N=4, V=100, out_tokens=P, out_len=P, out_best=P, ws=P,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return rsv.lib().spec_verify_greedy(a["logits"], a["dtype"], a["cand"], a["B"], a["G"], a["N"], a["V"],
+                                        a["out_tokens"], a["out_len"], a["out_best"], a["ws"], a["ws_bytes"],
+                                        a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), ERR_SHAPE), (dict(K=-1), ERR_SHAPE), (dict(K=65), ERR_SHAPE), (dict(V=0), ERR_SHAPE),
+    (dict(V=(1 << 30) + 1), ERR_SHAPE), (dict(B=1 << 22, K=8), ERR_SHAPE),
+    (dict(dtype=2), ERR_DTYPE), (dict(dtype=-1), ERR_DTYPE),
+    (dict(T=0.0), ERR_TEMP), (dict(T=-1.0), ERR_TEMP), (dict(T=float("nan")), ERR_TEMP),
+    (dict(T=float("inf")), ERR_TEMP), (dict(T=1e-45), ERR_TEMP),
+    (dict(target=None), ERR_NULL), (dict(draft=None), ERR_NULL), (dict(tokens=None), ERR_NULL),
+    (dict(uniforms=None), ERR_NULL), (dict(out_tokens=None), ERR_NULL), (dict(out_n=None), ERR_NULL),
+    (dict(ws=None), ERR_NULL),
+    (dict(target=P + 1), ERR_ALIGN), (dict(dtype=0, draft=P + 2), ERR_ALIGN), (dict(tokens=P + 2), ERR_ALIGN),
+    (dict(out_probs=P + 1), ERR_ALIGN), (dict(ws=P + 4), ERR_ALIGN),
+    (dict(ws_bytes=16), ERR_WS),
+    (dict(B=0), OK), (dict(B=0, target=None, ws=None), OK),
+])
+def test_sample_argument_checks(kw, expect):
+    assert sample(**kw) == expect
+
+
+@pytest.mark.parametrize("entry", ["spec_verify_sample_accept", "spec_verify_sample_draw"])
+def test_phase_entry_points_check_arguments(entry):
+    fn = getattr(rsv.lib(), entry)
+    assert fn(P, P, 1, P, P, 4, 3, 100, 0.0, P, P, None, P, 1 << 30, None) == ERR_TEMP
+    assert fn(P, P, 1, P, P, 4, 3, 100, 1.0, P, P, None, P, 16, None) == ERR_WS
+    assert fn(P, P, 1, P, P, 4, 99, 100, 1.0, P, P, None, P, 1 << 30, None) == ERR_SHAPE
+
+
+def test_sample_k0_needs_no_draft():
+    # K = 0 draws from the bonus row only: draft pointers may be null; still fails on the workspace size
+    assert sample(K=0, draft=None, tokens=None, ws_bytes=0) == ERR_WS
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), ERR_SHAPE), (dict(G=0), ERR_SHAPE), (dict(N=1), ERR_SHAPE), (dict(N=66), ERR_SHAPE),
+    (dict(G=3000, N=3), ERR_SHAPE), (dict(V=0), ERR_SHAPE),
+    (dict(dtype=3), ERR_DTYPE), (dict(logits=None), ERR_NULL), (dict(cand=None), ERR_NULL),
+    (dict(out_best=None), ERR_NULL), (dict(logits=P + 1), ERR_ALIGN), (dict(cand=P + 1), ERR_ALIGN),
+    (dict(ws_bytes=8), ERR_WS), (dict(B=0), OK),
+])
+def test_greedy_argument_checks(kw, expect):
+    assert greedy(**kw) == expect
+
+
+def test_fill_uniforms_argument_checks():
+    L = rsv.lib()
+    assert L.spec_fill_uniforms(0, 0, -1, 4, P, None) == ERR_SHAPE
+    assert L.spec_fill_uniforms(0, 0, 4, 65, P, None) == ERR_SHAPE
+    assert L.spec_fill_uniforms(0, 0, 4, 4, None, None) == ERR_NULL
+    assert L.spec_fill_uniforms(0, 0, 4, 4, P + 2, None) == ERR_ALIGN
+    assert L.spec_fill_uniforms(0, 0, 0, 4, None, None) == OK
+
+
+def test_workspace_sizes():
+    assert rsv.sample_workspace_size(64, 8, 128256) > 0
+    assert rsv.sample_workspace_size(0, 8, 100) > 0
+    assert rsv.sample_workspace_size(-1, 8, 100) == 0
+    assert rsv.sample_workspace_size(4, 65, 100) == 0
+    assert rsv.greedy_workspace_size(32, 7, 5, 32000) > 0
+    assert rsv.greedy_workspace_size(32, 7, 1, 32000) == 0
+    # the size depends on the shape only (never on a tuning override)
+    os.environ["SPECVERIFY_S1"] = "3"
+    try:
+        assert rsv.sample_workspace_size(64, 8, 128256) == rsv.sample_workspace_size(64, 8, 128256)
+    finally:
+        del os.environ["SPECVERIFY_S1"]
+
+
+def test_status_strings():
+    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN, 99):
+        assert isinstance(rsv.status_string(s), str) and rsv.status_string(s)
+
+
+def test_binding_checks_tensors_before_the_library():
+    import torch
+    t = torch.zeros(2, 3, 8)
+    with pytest.raises((TypeError, ValueError)):
+        rsv.verify_sample(t, torch.zeros(2, 2, 8, dtype=torch.float64), torch.zeros(2, 2, dtype=torch.int32),
+                          torch.zeros(2, 3, 2), 1.0)
+    with pytest.raises((TypeError, ValueError)):
+        rsv.verify_greedy(torch.zeros(1, 2, 3, 8), torch.zeros(1, 2, 3, dtype=torch.int32))
