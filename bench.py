@@ -7,8 +7,9 @@ the first rejection; pass 2: the residual / bonus draw). Inputs are seeded
 synthetic logits already resident in HBM. The timed steps cycle through
 several copies of the inputs (together more than twice the 256 MB Infinity
 Cache), so each step reads its logits from HBM rather than from the cache.
-Each step is one HIP-graph replay; the timed region is bracketed by HIP events
-on the stream the kernels run on.
+Steps are launched from HIP graphs that each hold a run of consecutive steps
+(a graph launch costs about as much as a short kernel); the timed region, exactly
+--steps steps, is bracketed by HIP events on the stream the kernels run on.
 
 Prints ONE JSON line. Also reported: the pass-1 kernel alone (the dominant
 kernel, for the roofline), the greedy verify on its own workload (B=32 G=7 N=5
@@ -45,7 +46,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--rotate", type=int, default=0, help="input copies (0: enough to exceed 2x the cache)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-greedy", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch through the Python binding instead of graphs")
@@ -138,65 +139,107 @@ def main() -> int:
     del base
     ws = torch.zeros(rsv.sample_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
 
-    def call(st, phase="both"):
+    def call(st, phases=rsv.PHASE_ALL):
         rsv.verify_sample(st["target"], st["draft"], st["draft_tokens"], st["uniforms"], s.temperature,
-                          out_tokens=st["out_tokens"], out_num_accepted=st["out_n"], workspace=ws, phase=phase)
+                          out_tokens=st["out_tokens"], out_num_accepted=st["out_n"], workspace=ws, phases=phases)
 
     for i in range(3):
         call(sets[i % M])
     torch.cuda.synchronize()
 
-    def graphs_for(phase):
-        gs = []
+    def stepper(phases):
+        """fn(i) runs step i; graphs hold CHUNK consecutive steps (a graph launch costs ~20 us)."""
+        if args.eager:
+            return lambda i: call(sets[i % M], phases)
+
+        def capture(first, count):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for j in range(count):
+                    call(sets[(first + j) % M], phases)
+            return g
+
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for st in sets:
-                call(st, phase)
+                call(st, phases)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        for st in sets:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                call(st, phase)
-            gs.append(g)
-        return gs
+        chunk = capture(0, CHUNK)
+        return chunk
 
-    if args.eager:
-        step = lambda i: call(sets[i % M])          # noqa: E731
-        acc = lambda i: call(sets[i % M], "accept")  # noqa: E731
-    else:
-        g_full = graphs_for("both")
-        g_acc = graphs_for("accept")
-        step = lambda i: g_full[i % M].replay()      # noqa: E731
-        acc = lambda i: g_acc[i % M].replay()        # noqa: E731
+    def run_steps(graph, n):
+        """Run exactly n steps: whole chunks, then a graph of the remainder."""
+        if args.eager:
+            for i in range(n):
+                graph(i)
+            return
+        q, r = divmod(n, CHUNK)
+        for _ in range(q):
+            graph.replay()
+        if r:
+            tails.setdefault(id(graph), {})
+            tg = tails[id(graph)].get(r)
+            if tg is None:
+                raise RuntimeError("remainder graph not prepared")
+            tg.replay()
 
-    timer.time(step, args.warmup)
-    t_step = timer.time(step, args.steps) / args.steps
-    timer.time(acc, max(args.warmup // 4, 10))
-    t_pass1 = timer.time(acc, args.steps) / args.steps
+    CHUNK = M * max(1, 48 // M)
+    tails: dict = {}
+
+    def prepare(phases, n_list):
+        g = stepper(phases)
+        if not args.eager:
+            for n in n_list:
+                r = n % CHUNK
+                if r and r not in tails.setdefault(id(g), {}):
+                    tg = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(tg):
+                        for j in range(r):
+                            call(sets[j % M], phases)
+                    tails[id(g)][r] = tg
+        return g
+
+    def timed(g, n):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run_steps(g, n)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3
+
+    g_full = prepare(rsv.PHASE_ALL, [args.warmup, args.steps])
+    g_p1 = prepare(rsv.PHASE_ROW_STATS, [args.warmup, args.steps])
+    timed(g_full, args.warmup)
+    t_step = timed(g_full, args.steps) / args.steps
+    timed(g_p1, args.warmup)
+    t_pass1 = timed(g_p1, args.steps) / args.steps
     # outputs of the last full step of each copy (identical inputs -> identical outputs)
-    for i in range(M):
-        step(i)
+    for st in sets:
+        call(st)
     torch.cuda.synchronize()
     n_acc = sets[0]["out_n"].cpu().numpy()
     assert np.all(n_acc >= 0) and np.all(n_acc <= K), "invalid accepted counts"
     tok = sets[0]["out_tokens"].cpu().numpy()
     assert np.all((tok[np.arange(B), n_acc] >= 0) & (tok[np.arange(B), n_acc] < V))
 
-    # algorithmic bytes: pass 1 reads the 2K rows of every batch row once; pass 2
-    # rereads target+draft row n after a rejection, or the bonus row once
+    # algorithmic bytes. Row statistics (pass 1): the 2K logit rows of every batch
+    # row, read once. Pass 2: target + draft row n after a rejection, or the bonus
+    # row. Plus the draft tokens, the uniforms and the outputs.
     row_bytes = V * esz
-    pass1_bytes = B * 2 * K * row_bytes + B * K * 4 + B * K * 4 * 2 + B * (K + 1) * 4 + B * 4
-    pass2_bytes = int(sum(2 * row_bytes if n < K else row_bytes for n in n_acc)) + B * 8 + B * 4
-    step_bytes = pass1_bytes + pass2_bytes
+    pass1_bytes = B * 2 * K * row_bytes
+    pass2_bytes = int(sum(2 * row_bytes if n < K else row_bytes for n in n_acc))
+    small_bytes = B * K * 4 + B * (K + 1) * 2 * 4 + B * (K + 1) * 4 + B * 4
+    step_bytes = pass1_bytes + pass2_bytes + small_bytes
     rounds_per_s = 1.0 / t_step
     step_gbps = step_bytes / t_step / 1e9
     pass1_gbps = pass1_bytes / t_pass1 / 1e9
-    traffic = measured_traffic("k_sample_pass1")
+    traffic = measured_traffic("k_sample_rowstats")
     log(f"step {t_step * 1e6:.2f} us ({rounds_per_s:.0f} rounds/s, {step_gbps:.0f} GB/s); "
         f"pass 1 {t_pass1 * 1e6:.2f} us ({pass1_gbps:.0f} GB/s); mean accepted {n_acc.mean():.3f}")
-    del sets, g_full if not args.eager else None
+    del sets, g_full, g_p1, tails
 
     # ---------------------------------------------------------------- greedy verify, B=32 G=7 N=5 V=32000 bf16
     greedy = None
@@ -219,17 +262,20 @@ def main() -> int:
         for st in gsets:
             gcall(st)
         torch.cuda.synchronize()
+        L5 = M5 * max(1, 48 // M5)
         if args.eager:
             gstep = lambda i: gcall(gsets[i % M5])   # noqa: E731
+            per_call = 1
         else:
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
-                for st in gsets:
-                    gcall(st)
+                for j in range(L5):
+                    gcall(gsets[j % M5])
             gstep = lambda i: graph.replay()         # noqa: E731
-        reps = max(1, args.steps // M5)
-        timer.time(gstep, max(1, args.warmup // M5))
-        per = (timer.time(gstep, reps) / reps) / (1 if args.eager else M5)
+            per_call = L5
+        reps = max(1, args.steps // per_call)
+        timer.time(gstep, max(1, args.warmup // per_call))
+        per = (timer.time(gstep, reps) / reps) / per_call
         gal = gbytes + gb * gg * (gn - 1) * 4 + gb * (gn + 2) * 4
         greedy = {"workload": WORKLOAD_NAMES[5], "rounds_per_s": round(1.0 / per, 1),
                   "us_per_round": round(per * 1e6, 3), "achieved_gbps": round(gal / per / 1e9, 1),
@@ -244,7 +290,7 @@ def main() -> int:
         tgt, drf = s.target_f32(), s.draft_f32()
         rows = 0
         t1 = time.perf_counter()
-        while time.perf_counter() - t1 < args.cpu_seconds and rows < 4 * B:
+        while time.perf_counter() - t1 < args.cpu_seconds:
             b = rows % B
             oracle.oracle_sample(tgt[b:b + 1], drf[b:b + 1], s.draft_tokens[b:b + 1], s.uniforms[b:b + 1],
                                  s.temperature, with_probs=False)
@@ -276,7 +322,7 @@ def main() -> int:
         "frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": step_bytes,
         "mean_accepted": round(float(n_acc.mean()), 4),
-        "roofline": {"kernel": "k_sample_pass1", "bound": "hbm", "achieved": round(pass1_gbps, 1),
+        "roofline": {"kernel": "k_sample_rowstats", "bound": "hbm", "achieved": round(pass1_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(pass1_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": pass1_bytes,
                      "us_per_launch": round(t_pass1 * 1e6, 3)},

@@ -34,13 +34,10 @@
  *   - Data faults found on the device are reported per row in the outputs
  *     (see each function), never by the status.
  *   - Outputs must not overlap inputs or each other.
- *   - The workspace holds arrival counters that must be zero when a call
- *     starts; every call leaves them at zero again, at offsets that depend on
- *     the entry point family and the sizes. Zero the workspace after
- *     allocation, after a call that failed on the device, and before reusing
- *     it for other sizes or the other family. Calls that run at the same time
- *     must use different workspaces; calls of one shape in one stream may
- *     share one without clearing it in between.
+ *   - The workspace carries partial results from one launch of a call to the
+ *     next launch of the same call. It needs no initialisation and keeps
+ *     nothing between calls. Calls that run at the same time must use
+ *     different workspaces; calls in one stream may share one.
  *   - Logits are finite or -inf. A +inf or NaN logit gives unspecified values
  *     for its row (never an out-of-bounds access).
  */
@@ -69,7 +66,8 @@ typedef enum {
   SPEC_ERR_DTYPE = -4,       /* unknown spec_dtype */
   SPEC_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_size query */
   SPEC_ERR_HIP = -6,         /* a HIP launch failed */
-  SPEC_ERR_ALIGN = -7        /* a pointer is not aligned to its element size */
+  SPEC_ERR_ALIGN = -7,       /* a pointer is not aligned to its element size */
+  SPEC_ERR_PHASE = -8        /* phase mask outside 1..15 (spec_verify_sample_phases) */
 } spec_status;
 
 /* Bytes of workspace spec_verify_sample needs for these sizes (0 for invalid sizes). */
@@ -112,27 +110,32 @@ spec_status spec_verify_sample(const void* target_logits, const void* draft_logi
                                size_t workspace_bytes, void* stream);
 
 /*
- * The two launches of spec_verify_sample, for callers that schedule or time
- * them apart. Both take exactly spec_verify_sample's arguments.
- * spec_verify_sample_accept runs pass 1: it reads target rows 0..K-1 and draft
- *   rows 0..K-1 once, writes out_num_accepted, out_probs and every out_tokens
- *   entry except the drawn one, and leaves in the workspace what the draw needs.
- * spec_verify_sample_draw runs pass 2: it reads only the rows the draw needs
- *   (target and draft row n after a rejection, or the bonus row) and writes the
- *   drawn token (and the fault outputs of a bonus row with no finite logit).
- *   It must follow spec_verify_sample_accept with the same arguments and
- *   workspace, in stream order. With K = 0 the accept pass does nothing.
+ * spec_verify_sample as its four launches, for callers that schedule or time
+ * them apart. Same arguments as spec_verify_sample plus a mask of phases,
+ * which run in this order on `stream` (a call with every bit set is
+ * spec_verify_sample):
+ *   SPEC_PHASE_ROW_STATS  pass 1: reads target rows 0..K-1 and draft rows 0..K-1
+ *                         once; leaves per-segment max / sum-exp in the workspace.
+ *   SPEC_PHASE_ACCEPT     accept tests and the first rejection: writes
+ *                         out_num_accepted, out_probs and every out_tokens entry
+ *                         except the drawn one.
+ *   SPEC_PHASE_MASS       pass 2: reads only the row(s) the draw needs (target and
+ *                         draft row n after a rejection, or the bonus row).
+ *   SPEC_PHASE_DRAW       the inverse-CDF search; writes the drawn token (and the
+ *                         fault outputs of a bonus row with no finite logit).
+ * A phase reads what the earlier phases of the same arguments left in the
+ * workspace; running it without them gives unspecified outputs but never an
+ * access outside the arguments' buffers. SPEC_ERR_PHASE for a mask outside 1..15.
  */
-spec_status spec_verify_sample_accept(const void* target_logits, const void* draft_logits, int32_t dtype,
+#define SPEC_PHASE_ROW_STATS 1
+#define SPEC_PHASE_ACCEPT 2
+#define SPEC_PHASE_MASS 4
+#define SPEC_PHASE_DRAW 8
+spec_status spec_verify_sample_phases(const void* target_logits, const void* draft_logits, int32_t dtype,
                                       const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t K,
                                       int32_t V, float temperature, int32_t* out_tokens,
                                       int32_t* out_num_accepted, float* out_probs, void* workspace,
-                                      size_t workspace_bytes, void* stream);
-spec_status spec_verify_sample_draw(const void* target_logits, const void* draft_logits, int32_t dtype,
-                                    const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t K,
-                                    int32_t V, float temperature, int32_t* out_tokens,
-                                    int32_t* out_num_accepted, float* out_probs, void* workspace,
-                                    size_t workspace_bytes, void* stream);
+                                      size_t workspace_bytes, void* stream, int32_t phases);
 
 /* Bytes of workspace spec_verify_greedy needs for these sizes (0 for invalid sizes). */
 size_t spec_verify_greedy_workspace_size(int32_t B, int32_t G, int32_t N, int32_t V);

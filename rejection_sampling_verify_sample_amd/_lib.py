@@ -33,8 +33,9 @@ _SIGNATURES = {
     "spec_verify_sample": (_i32, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                   ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
                                   _c_void_p]),
-    "spec_verify_sample_accept": None,
-    "spec_verify_sample_draw": None,
+    "spec_verify_sample_phases": (_i32, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                         ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
+                                         _c_void_p, _i32]),
     "spec_verify_greedy_workspace_size": (_size_t, [_i32, _i32, _i32, _i32]),
     "spec_verify_greedy": (_i32, [_c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
                                   _c_void_p, _c_void_p, _size_t, _c_void_p]),
@@ -60,8 +61,7 @@ def lib() -> ctypes.CDLL:
                 raise RuntimeError(f"{LIB_PATH} is not built; run `python -m rejection_sampling_verify_sample_amd.build`"
                                    " (hipcc, gfx950). There is no fallback path.")
             L = ctypes.CDLL(LIB_PATH)
-            for name, sig in _SIGNATURES.items():
-                res, args = sig if sig is not None else _SIGNATURES["spec_verify_sample"]
+            for name, (res, args) in _SIGNATURES.items():
                 fn = getattr(L, name)
                 fn.restype = res
                 fn.argtypes = args
@@ -116,29 +116,19 @@ def _stream_handle(stream, device: torch.device) -> int:
     return int(stream.cuda_stream)
 
 
-_workspaces: dict[tuple[int, int], list] = {}
+_workspaces: dict[tuple[int, int], torch.Tensor] = {}
 _ws_lock = threading.Lock()
 
 
-def workspace_for(device: torch.device, stream_handle: int, nbytes: int, layout_key: tuple) -> torch.Tensor:
-    """A workspace reused by every call on one (device, stream).
-
-    The library leaves its arrival counters at zero after each call, at the
-    offsets of that call's layout; a call with other sizes puts its counters
-    elsewhere. So the buffer is zeroed when it is created and whenever the
-    layout (entry point family and sizes) changes from the previous call.
-    """
+def workspace_for(device: torch.device, stream_handle: int, nbytes: int) -> torch.Tensor:
+    """A workspace reused by every call on one (device, stream); it needs no initialisation."""
     key = (device.index, stream_handle)
     with _ws_lock:
-        ent = _workspaces.get(key)
-        if ent is None or ent[0].numel() < nbytes:
-            ent = [torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device), None]
-            _workspaces[key] = ent
-        if ent[1] != layout_key:
-            with torch.cuda.stream(torch.cuda.ExternalStream(stream_handle, device=device)):
-                ent[0].zero_()
-            ent[1] = layout_key
-        return ent[0]
+        ws = _workspaces.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            _workspaces[key] = ws
+        return ws
 
 
 def _ptr(t):
@@ -154,18 +144,19 @@ class SampleOutputs:
     probs: torch.Tensor | None  # [B, K, 2] float32
 
 
-_PHASE_ENTRY = {"both": "spec_verify_sample", "accept": "spec_verify_sample_accept", "draw": "spec_verify_sample_draw"}
+PHASE_ROW_STATS, PHASE_ACCEPT, PHASE_MASS, PHASE_DRAW, PHASE_ALL = 1, 2, 4, 8, 15
 
 
 def verify_sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor, uniforms: torch.Tensor,
                   temperature: float, *, out_tokens: torch.Tensor | None = None,
                   out_num_accepted: torch.Tensor | None = None, out_probs: torch.Tensor | None = None,
                   want_probs: bool = False, workspace: torch.Tensor | None = None, stream=None,
-                  phase: str = "both") -> SampleOutputs:
+                  phases: int = PHASE_ALL) -> SampleOutputs:
     """spec_verify_sample on torch tensors (layouts as in include/spec_verify.h). Asynchronous on `stream`.
 
-    phase="accept" / "draw" calls the library's pass-1 / pass-2 entry point alone
-    (the draw must follow an accept call with the same arguments and workspace).
+    `phases` (a mask of PHASE_*) runs only some of the four launches, through
+    spec_verify_sample_phases; later phases read what earlier ones of the same
+    arguments left in the workspace.
     """
     if target.dim() != 3:
         raise ValueError("target must be [B, K+1, V]")
@@ -192,14 +183,17 @@ def verify_sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch
     if nbytes == 0 and B > 0:
         raise SpecVerifyError(-2, "spec_verify_sample_workspace_size")
     if workspace is None:
-        workspace = workspace_for(dev, sh, nbytes, ("sample", B, K, V))
+        workspace = workspace_for(dev, sh, nbytes)
     _check(workspace, "workspace", dev, torch.uint8)
-    entry = getattr(lib(), _PHASE_ENTRY[phase])
-    st = entry(_ptr(target), _ptr(draft), code, _ptr(draft_tokens), _ptr(uniforms), B, K, V,
-                                  float(temperature), _ptr(out_tokens), _ptr(out_num_accepted), _ptr(out_probs),
-                                  _ptr(workspace), workspace.numel(), ctypes.c_void_p(sh))
+    args = (_ptr(target), _ptr(draft), code, _ptr(draft_tokens), _ptr(uniforms), B, K, V, float(temperature),
+            _ptr(out_tokens), _ptr(out_num_accepted), _ptr(out_probs), _ptr(workspace), workspace.numel(),
+            ctypes.c_void_p(sh))
+    if phases == PHASE_ALL:
+        st, where = lib().spec_verify_sample(*args), "spec_verify_sample"
+    else:
+        st, where = lib().spec_verify_sample_phases(*args, int(phases)), "spec_verify_sample_phases"
     if st != 0:
-        raise SpecVerifyError(st, _PHASE_ENTRY[phase])
+        raise SpecVerifyError(st, where)
     return SampleOutputs(out_tokens, out_num_accepted, out_probs)
 
 
@@ -235,7 +229,7 @@ def verify_greedy(logits: torch.Tensor, cand: torch.Tensor, *, out_tokens: torch
     if nbytes == 0 and B > 0:
         raise SpecVerifyError(-2, "spec_verify_greedy_workspace_size")
     if workspace is None:
-        workspace = workspace_for(dev, sh, nbytes, ("greedy", B, G, N, V))
+        workspace = workspace_for(dev, sh, nbytes)
     _check(workspace, "workspace", dev, torch.uint8)
     st = lib().spec_verify_greedy(_ptr(logits), code, _ptr(cand), B, G, N, V, _ptr(out_tokens),
                                   _ptr(out_accept_len), _ptr(out_best), _ptr(workspace), workspace.numel(),

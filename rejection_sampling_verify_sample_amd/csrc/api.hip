@@ -26,14 +26,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Most segments a row may be split into: bounds the partials the workspace holds.
-int32_t seg_max(int64_t rows, int64_t V) {
+int32_t seg_max(int64_t rows, int64_t V, int64_t cap = 64) {
   int64_t s = ceil_div(65536, std::max<int64_t>(rows, 1));
-  s = std::min<int64_t>(s, 64);
+  s = std::min<int64_t>(s, cap);
   s = std::min<int64_t>(s, std::max<int64_t>(1, V / 256));
   return static_cast<int32_t>(std::max<int64_t>(s, 1));
 }
 
-// Segments per row: enough workgroups to fill 256 CUs several times over, but
+// Segments per row: enough workgroups to fill the 256 CUs (target_blocks), but
 // segments of at least `min_seg` elements. SPECVERIFY_S<n> overrides (tuning).
 int32_t seg_choice(int64_t rows, int64_t V, int64_t target_blocks, int64_t min_seg, int32_t smax,
                    const char* env) {
@@ -61,21 +61,23 @@ SampleLayout sample_layout(int32_t B, int32_t K, int32_t V) {
   SampleLayout L{};
   const int64_t rows1 = static_cast<int64_t>(B) * 2 * K;
   L.S1max = seg_max(rows1, V);
-  L.S2max = seg_max(B, V);
-  L.S1 = seg_choice(rows1, V, 2048, 2048, L.S1max, "SPECVERIFY_S1");
-  L.S2 = seg_choice(B, V, 1024, 2048, L.S2max, "SPECVERIFY_S2");
+  L.S2max = seg_max(B, V, 256);
+  L.S1 = seg_choice(rows1, V, 1024, 8192, L.S1max, "SPECVERIFY_S1");
+  L.S2 = seg_choice(B, V, 1024, 1024, L.S2max, "SPECVERIFY_S2");
   size_t off = 0;
   const size_t p1 = static_cast<size_t>(rows1) * L.S1max;
   L.off_p1m = off; off = align256(off + p1 * sizeof(float));
   L.off_p1s = off; off = align256(off + p1 * sizeof(double));
-  L.off_cnt1 = off; off = align256(off + static_cast<size_t>(B) * sizeof(uint32_t));
+  L.off_p1x = off; off = align256(off + static_cast<size_t>(rows1) * sizeof(float));
   L.off_info_n = off; off = align256(off + static_cast<size_t>(B) * sizeof(int32_t));
   L.off_info_R = off; off = align256(off + static_cast<size_t>(B) * 2 * sizeof(float));
   L.off_info_S = off; off = align256(off + static_cast<size_t>(B) * 2 * sizeof(double));
-  const size_t p2 = static_cast<size_t>(B) * L.S2max;
-  L.off_p2m = off; off = align256(off + p2 * sizeof(float));
-  L.off_p2s = off; off = align256(off + p2 * sizeof(double));
-  L.off_cnt2 = off; off = align256(off + static_cast<size_t>(B) * sizeof(uint32_t));
+  // pass-2 chunks: 64 16-byte vectors each, plus the head and the tail of the row
+  // (at most ceil(V/256) + 2 for fp32 rows, fewer for bf16)
+  L.NCmax = static_cast<int32_t>(ceil_div(V, 256) + 2);
+  const size_t p2 = static_cast<size_t>(B) * L.NCmax;
+  L.off_p2cm = off; off = align256(off + p2 * sizeof(float));
+  L.off_p2cs = off; off = align256(off + p2 * sizeof(double));
   L.total = std::max<size_t>(off, 256);
   return L;
 }
@@ -84,12 +86,11 @@ GreedyLayout greedy_layout(int32_t B, int32_t G, int32_t N, int32_t V) {
   GreedyLayout L{};
   const int64_t rows = static_cast<int64_t>(B) * G * N;
   L.S3max = seg_max(rows, V);
-  L.S3 = seg_choice(rows, V, 2048, 2048, L.S3max, "SPECVERIFY_S3");
+  L.S3 = seg_choice(rows, V, 3072, 8192, L.S3max, "SPECVERIFY_S3");
   size_t off = 0;
   const size_t p3 = static_cast<size_t>(rows) * L.S3max;
   L.off_p3v = off; off = align256(off + p3 * sizeof(float));
   L.off_p3i = off; off = align256(off + p3 * sizeof(int32_t));
-  L.off_cnt3 = off; off = align256(off + static_cast<size_t>(B) * sizeof(uint32_t));
   L.total = std::max<size_t>(off, 256);
   return L;
 }
@@ -115,6 +116,7 @@ SPEC_EXPORT const char* spec_status_string(int32_t status) {
     case SPEC_ERR_WORKSPACE: return "workspace too small";
     case SPEC_ERR_HIP: return "HIP launch failed";
     case SPEC_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case SPEC_ERR_PHASE: return "phase mask outside 1..15";
     default: return "unknown status";
   }
 }
@@ -136,6 +138,7 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
                                  float* out_probs, void* workspace, size_t workspace_bytes, void* stream,
                                  int phases) {
   if (!sample_shape_ok(B, K, V)) return SPEC_ERR_SHAPE;
+  if (phases < 1 || phases > sv::kPhaseAll) return SPEC_ERR_PHASE;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
   if (!(std::isfinite(temperature) && temperature > 0.f)) return SPEC_ERR_TEMPERATURE;
   const float c = static_cast<float>(1.4426950408889634074 / static_cast<double>(temperature));
@@ -167,13 +170,13 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
   P.out_probs = out_probs;
   P.p1_m = at<float>(workspace, L.off_p1m);
   P.p1_s = at<double>(workspace, L.off_p1s);
-  P.cnt1 = at<uint32_t>(workspace, L.off_cnt1);
   P.info_n = at<int32_t>(workspace, L.off_info_n);
   P.info_R = at<float>(workspace, L.off_info_R);
   P.info_S = at<double>(workspace, L.off_info_S);
-  P.p2_m = at<float>(workspace, L.off_p2m);
-  P.p2_s = at<double>(workspace, L.off_p2s);
-  P.cnt2 = at<uint32_t>(workspace, L.off_cnt2);
+  P.NCmax = L.NCmax;
+  P.p1_x = at<float>(workspace, L.off_p1x);
+  P.p2_cm = at<float>(workspace, L.off_p2cm);
+  P.p2_cs = at<double>(workspace, L.off_p2cs);
   const hipError_t e = sv::launch_sample(P, dtype == SPEC_BF16, phases, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
@@ -187,11 +190,12 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
   target_logits, draft_logits, dtype, draft_tokens, uniforms, B, K, V, temperature, out_tokens,              \
       out_num_accepted, out_probs, workspace, workspace_bytes, stream
 
-SPEC_EXPORT spec_status spec_verify_sample(SPEC_SAMPLE_ARGS) { return verify_sample_phases(SPEC_SAMPLE_FWD, 3); }
-SPEC_EXPORT spec_status spec_verify_sample_accept(SPEC_SAMPLE_ARGS) {
-  return verify_sample_phases(SPEC_SAMPLE_FWD, 1);
+SPEC_EXPORT spec_status spec_verify_sample(SPEC_SAMPLE_ARGS) {
+  return verify_sample_phases(SPEC_SAMPLE_FWD, sv::kPhaseAll);
 }
-SPEC_EXPORT spec_status spec_verify_sample_draw(SPEC_SAMPLE_ARGS) { return verify_sample_phases(SPEC_SAMPLE_FWD, 2); }
+SPEC_EXPORT spec_status spec_verify_sample_phases(SPEC_SAMPLE_ARGS, int32_t phases) {
+  return verify_sample_phases(SPEC_SAMPLE_FWD, phases);
+}
 
 SPEC_EXPORT spec_status spec_verify_greedy(const void* target_logits, int32_t dtype, const int32_t* cand_tokens,
                                            int32_t B, int32_t G, int32_t N, int32_t V, int32_t* out_tokens,
@@ -222,7 +226,6 @@ SPEC_EXPORT spec_status spec_verify_greedy(const void* target_logits, int32_t dt
   P.out_best = out_best_cand;
   P.p3_v = at<float>(workspace, L.off_p3v);
   P.p3_i = at<int32_t>(workspace, L.off_p3i);
-  P.cnt3 = at<uint32_t>(workspace, L.off_cnt3);
   const hipError_t e = sv::launch_greedy(P, dtype == SPEC_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

@@ -14,6 +14,14 @@ struct bf16_t {
   uint16_t bits;
 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the nontemporal hint: the streamed logits are read once, so
+// they should not displace cache lines that are reused.
+__device__ __forceinline__ u32x4 load_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // ---------------------------------------------------------------- element access
 
 template <typename T>
@@ -23,9 +31,11 @@ template <>
 struct Elem<float> {
   static constexpr int kVec = 4;  // elements per 16-byte load
   __device__ __forceinline__ static float get(const float* p, size_t i) { return p[i]; }
+  template <bool NT = true>
   __device__ __forceinline__ static void vec(const float* p, float (&x)[4]) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    const u32x4 v = NT ? load_stream(p) : *reinterpret_cast<const u32x4*>(p);
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
   }
 };
 
@@ -35,8 +45,9 @@ struct Elem<bf16_t> {
   __device__ __forceinline__ static float get(const bf16_t* p, size_t i) {
     return __uint_as_float(static_cast<uint32_t>(p[i].bits) << 16);
   }
+  template <bool NT = true>
   __device__ __forceinline__ static void vec(const bf16_t* p, float (&x)[8]) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const u32x4 v = NT ? load_stream(p) : *reinterpret_cast<const u32x4*>(p);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -128,52 +139,5 @@ struct Online {
   }
   __device__ __forceinline__ void add(float x, float c) { s += exp2_hw(fmaf(x, c, -R)); }
 };
-
-// ---------------------------------------------------------------- coherent scratch access
-//
-// Partials written by one workgroup and read by the last-arriving workgroup of
-// a group travel through device memory with agent-scope atomics, so no
-// per-XCD L2 can serve a stale copy.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(double* p, double v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), static_cast<uint64_t>(__double_as_longlong(v)),
-                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(int32_t* p, int32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ double ld_agent(const double* p) {
-  return __longlong_as_double(static_cast<long long>(
-      __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
-}
-__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Arrive at a group counter after this workgroup's partial is stored. Returns
-// true (in every thread) for the last of `expected` arrivals, which also
-// resets the counter to zero for the next call.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected) {
-  __shared__ int s_last;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = (prev == expected - 1);
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = last;
-  }
-  __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
-}
 
 }  // namespace sv

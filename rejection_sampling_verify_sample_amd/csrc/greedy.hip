@@ -5,12 +5,13 @@
 // the target's argmax at position i; the longest matched prefix among the
 // candidates wins, followed by the argmax right after it.
 //
-// k_greedy: one workgroup per (logit row, segment) streams its segment with
+// k_greedy_argmax: one workgroup per (logit row, segment) streams its segment with
 // 16-byte loads and keeps the running (maximum, lowest index attaining it) per
 // thread, visiting its elements in increasing index order; a block reduction on
-// (value desc, index asc) gives the segment's first argmax. The last workgroup
-// of batch row b merges the segments in index order, matches every candidate's
-// prefix, and picks the longest (lowest candidate index on ties).
+// (value desc, index asc) gives the segment's first argmax.
+// k_greedy_select (launched after it, so no cross-workgroup synchronisation):
+// one workgroup per batch row merges the segments in index order, matches every
+// candidate's prefix, and picks the longest (lowest candidate index on ties).
 #include "common.hpp"
 #include "params.hpp"
 
@@ -51,34 +52,38 @@ __device__ __forceinline__ void argmax_merge(float& v, int64_t& i, float v2, int
   }
 }
 
-template <typename T>
+constexpr int kArgBlock = 128;  // threads per argmax workgroup (measured best on gfx950)
+
+template <int BS, typename T, bool NT = true>
 __device__ __forceinline__ void argmax_segment(const T* row, int64_t V, int seg, int S, ArgMax& a) {
   constexpr int VEC = Elem<T>::kVec;
   const SegRange r = seg_range(row, V, seg, S);
   if (seg == 0)
-    for (int64_t e = threadIdx.x; e < r.head; e += kBlock) a.take(Elem<T>::get(row, e), e);
+    for (int64_t e = threadIdx.x; e < r.head; e += BS) a.take(Elem<T>::get(row, e), e);
   const T* vb = row + r.head;
   int64_t v = r.v0 + threadIdx.x;
-  for (; v + kBlock < r.v1; v += 2 * kBlock) {
+  for (; v + BS < r.v1; v += 2 * BS) {
     float x0[VEC], x1[VEC];
-    Elem<T>::vec(vb + v * VEC, x0);
-    Elem<T>::vec(vb + (v + kBlock) * VEC, x1);
+    Elem<T>::template vec<NT>(vb + v * VEC, x0);
+    Elem<T>::template vec<NT>(vb + (v + BS) * VEC, x1);
     a.take_vec(x0, r.head + v * VEC);
-    a.take_vec(x1, r.head + (v + kBlock) * VEC);
+    a.take_vec(x1, r.head + (v + BS) * VEC);
   }
-  for (; v < r.v1; v += kBlock) {
+  for (; v < r.v1; v += BS) {
     float x0[VEC];
-    Elem<T>::vec(vb + v * VEC, x0);
+    Elem<T>::template vec<NT>(vb + v * VEC, x0);
     a.take_vec(x0, r.head + v * VEC);
   }
   if (seg == S - 1)
-    for (int64_t e = r.head + ((V - r.head) / VEC) * VEC + threadIdx.x; e < V; e += kBlock)
+    for (int64_t e = r.head + ((V - r.head) / VEC) * VEC + threadIdx.x; e < V; e += BS)
       a.take(Elem<T>::get(row, e), e);
 }
 
+template <int BS>
 __device__ __forceinline__ void block_argmax(float& v, int64_t& i) {
-  __shared__ float sh_v[kWaves];
-  __shared__ int64_t sh_i[kWaves];
+  constexpr int W = BS / 64;
+  __shared__ float sh_v[W];
+  __shared__ int64_t sh_i[W];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float v2 = __shfl_xor(v, o, 64);
@@ -91,33 +96,41 @@ __device__ __forceinline__ void block_argmax(float& v, int64_t& i) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < kWaves; ++w) argmax_merge(v, i, sh_v[w], sh_i[w]);
+    for (int w = 1; w < W; ++w) argmax_merge(v, i, sh_v[w], sh_i[w]);
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_greedy(GreedyParams P) {
+template <typename T, int BS, bool NT>
+__device__ __forceinline__ void greedy_argmax_task(const GreedyParams& P, const int64_t task) {
   const int S = P.S3;
-  const int GN = P.G * P.N;
-  const int seg = blockIdx.x % S;
-  const int row = blockIdx.x / S;  // in [0, B*G*N)
-  const int b = row / GN;
+  const int seg = static_cast<int>(task % S);
+  const int row = static_cast<int>(task / S);  // in [0, B*G*N)
   const T* rp = static_cast<const T*>(P.logits) + static_cast<int64_t>(row) * P.V;
-
   ArgMax a{-INFINITY, -1};
-  argmax_segment(rp, P.V, seg, S, a);
+  argmax_segment<BS, T, NT>(rp, P.V, seg, S, a);
   float v = a.v;
   int64_t i = a.i;
-  block_argmax(v, i);
+  block_argmax<BS>(v, i);
   if (threadIdx.x == 0) {
     // a segment whose maximum is -inf holds no finite logit: report it as empty
-    const bool finite_max = isfinite(v);
-    st_agent(P.p3_v + static_cast<int64_t>(row) * S + seg, v);
-    st_agent(P.p3_i + static_cast<int64_t>(row) * S + seg, finite_max ? static_cast<int32_t>(i) : -1);
+    P.p3_v[static_cast<int64_t>(row) * S + seg] = v;
+    P.p3_i[static_cast<int64_t>(row) * S + seg] = isfinite(v) ? static_cast<int32_t>(i) : -1;
   }
-  if (!arrive_last(P.cnt3 + b, static_cast<uint32_t>(GN * S))) return;
+}
 
-  // ---- epilogue of batch row b
+template <typename T, int BS = kArgBlock, bool NT = true>
+__global__ __launch_bounds__(BS) void k_greedy_argmax(GreedyParams P) {
+  const int64_t ntask = static_cast<int64_t>(P.B) * P.G * P.N * P.S3;
+  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
+    greedy_argmax_task<T, BS, NT>(P, task);
+    __syncthreads();  // shared memory is reused by the next task
+  }
+}
+
+__device__ __forceinline__ void greedy_select_task(const GreedyParams& P, const int64_t task) {
+  const int S = P.S3, N = P.N, G = P.G;
+  const int GN = G * N;
+  const int b = static_cast<int>(task);
   extern __shared__ int32_t sh_amax[];  // [G*N] argmax per row of this batch row
   __shared__ int sh_fault;
   __shared__ uint32_t sh_key;
@@ -131,8 +144,8 @@ __global__ __launch_bounds__(kBlock) void k_greedy(GreedyParams P) {
     float bv = -INFINITY;
     int32_t bi = -1;
     for (int j = 0; j < S; ++j) {  // segments in index order: strict > keeps the lowest index
-      const int32_t ij = ld_agent(P.p3_i + base + j);
-      const float vj = ld_agent(P.p3_v + base + j);
+      const int32_t ij = P.p3_i[base + j];
+      const float vj = P.p3_v[base + j];
       if (ij >= 0 && (bi < 0 || vj > bv)) {
         bv = vj;
         bi = ij;
@@ -142,7 +155,6 @@ __global__ __launch_bounds__(kBlock) void k_greedy(GreedyParams P) {
     if (bi < 0) atomicOr(&sh_fault, 1);
   }
   __syncthreads();
-  const int N = P.N, G = P.G;
   const int32_t* cb = P.cand + static_cast<int64_t>(b) * G * (N - 1);
   for (int g = threadIdx.x; g < G; g += kBlock) {
     int L = 0;
@@ -176,11 +188,24 @@ __global__ __launch_bounds__(kBlock) void k_greedy(GreedyParams P) {
   }
 }
 
+__global__ __launch_bounds__(kBlock) void k_greedy_select(GreedyParams P) {
+  const int64_t ntask = P.B;
+  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
+    greedy_select_task(P, task);
+    __syncthreads();  // shared memory is reused by the next task
+  }
+}
+
+constexpr int64_t kMaxGrid = 1 << 20;  // workgroups per launch; kernels loop over their tasks
+
+inline dim3 grid_for(int64_t tasks) { return dim3(static_cast<uint32_t>(tasks < kMaxGrid ? tasks : kMaxGrid)); }
+
 template <typename T>
 static hipError_t launch_greedy_t(const GreedyParams& P, hipStream_t stream) {
   const int64_t g = static_cast<int64_t>(P.B) * P.G * P.N * P.S3;
+  hipLaunchKernelGGL((k_greedy_argmax<T>), grid_for(g), dim3(kArgBlock), 0, stream, P);
   const size_t lds = static_cast<size_t>(P.G) * P.N * sizeof(int32_t);
-  hipLaunchKernelGGL(k_greedy<T>, dim3(static_cast<uint32_t>(g)), dim3(kBlock), lds, stream, P);
+  hipLaunchKernelGGL(k_greedy_select, grid_for(P.B), dim3(kBlock), lds, stream, P);
   return hipGetLastError();
 }
 

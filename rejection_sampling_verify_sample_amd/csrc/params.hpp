@@ -15,25 +15,35 @@ struct SampleParams {
   const float* uniforms;   // [B, K+1, 2]
   int32_t B, K, V;
   float c;                 // log2(e) / T, rounded to fp32
-  int32_t S1, S2;          // segments per row in pass 1 / pass 2
+  int32_t S1, S2;          // segments per row in pass 1 / workgroups per batch row in pass 2
   int32_t* out_tokens;     // [B, K+1]
   int32_t* out_n;          // [B]
   float* out_probs;        // [B, K, 2] or null
-  // workspace
-  float* p1_m;             // [B*2K*S1] segment maxima
+  // workspace (written by one kernel, read by a later one: no counters, no clearing)
+  int32_t NCmax;           // chunk slots per batch row in p2_cm / p2_cs
+  float* p1_m;             // [B*2K*S1] segment maxima (row statistics)
   double* p1_s;            // [B*2K*S1] segment sums against fl(m*c)
-  uint32_t* cnt1;          // [B] pass-1 arrivals
-  int32_t* info_n;         // [B] first rejection n, K when all accepted, -1 on a fault
+  float* p1_x;             // [B*2K] logit of the draft token in each row (NaN if the token is out of range)
+  int32_t* info_n;         // [B] first rejection n, K when all accepted, -1 on a fault (accept decisions)
   float* info_R;           // [B, 2] reference exponents of target row n, draft row n
   double* info_S;          // [B, 2] softmax denominators of those rows
-  float* p2_m;             // [B*S2]
-  double* p2_s;            // [B*S2]
-  uint32_t* cnt2;          // [B] pass-2 arrivals
+  float* p2_cm;            // [B*NCmax] per-chunk maximum (bonus draw)
+  double* p2_cs;           // [B*NCmax] per-chunk mass (residual, or bonus mass against fl(max*c))
+};
+
+// Kernels of the sampling verify, in stream order.
+enum SamplePhase : int {
+  kPhaseRowStats = 1,  // pass 1: online max / sum-exp of target and draft rows 0..K-1
+  kPhaseAccept = 2,    // accept tests, first rejection, accepted prefix
+  kPhaseMass = 4,      // pass 2: residual / bonus mass per segment of the row(s) the draw needs
+  kPhaseDraw = 8,      // inverse-CDF search inside the chosen segment
+  kPhaseAll = 15
 };
 
 struct SampleLayout {
   int32_t S1, S2, S1max, S2max;
-  size_t off_p1m, off_p1s, off_cnt1, off_info_n, off_info_R, off_info_S, off_p2m, off_p2s, off_cnt2, total;
+  int32_t NCmax;
+  size_t off_p1m, off_p1s, off_p1x, off_info_n, off_info_R, off_info_S, off_p2cm, off_p2cs, total;
 };
 
 // ---------------------------------------------------------------- greedy verify
@@ -48,12 +58,11 @@ struct GreedyParams {
   int32_t* out_best;       // [B]
   float* p3_v;             // [B*G*N*S3] segment maxima
   int32_t* p3_i;           // [B*G*N*S3] lowest index attaining them (-1 if none finite)
-  uint32_t* cnt3;          // [B]
 };
 
 struct GreedyLayout {
   int32_t S3, S3max;
-  size_t off_p3v, off_p3i, off_cnt3, total;
+  size_t off_p3v, off_p3i, total;
 };
 
 constexpr int32_t kMaxGreedyRowsPerBatch = 8192;  // G*N: argmaxes of one batch row held in LDS

@@ -14,7 +14,7 @@ import pytest
 import rejection_sampling_verify_sample_amd as rsv
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6, -7
+OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN, ERR_PHASE = 0, -1, -2, -3, -4, -5, -6, -7, -8
 P = 0x10000  # aligned, never dereferenced
 
 
@@ -34,7 +34,7 @@ def test_library_is_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 8, names
     L = ctypes.CDLL(rsv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
@@ -76,12 +76,20 @@ def test_sample_argument_checks(kw, expect):
     assert sample(**kw) == expect
 
 
-@pytest.mark.parametrize("entry", ["spec_verify_sample_accept", "spec_verify_sample_draw"])
-def test_phase_entry_points_check_arguments(entry):
-    fn = getattr(rsv.lib(), entry)
-    assert fn(P, P, 1, P, P, 4, 3, 100, 0.0, P, P, None, P, 1 << 30, None) == ERR_TEMP
-    assert fn(P, P, 1, P, P, 4, 3, 100, 1.0, P, P, None, P, 16, None) == ERR_WS
-    assert fn(P, P, 1, P, P, 4, 99, 100, 1.0, P, P, None, P, 1 << 30, None) == ERR_SHAPE
+def test_phase_entry_point_checks_arguments():
+    fn = rsv.lib().spec_verify_sample_phases
+    args = [P, P, 1, P, P, 4, 3, 100, 1.0, P, P, None, P, 1 << 30, None]
+    for bad in (0, 16, -1):
+        assert fn(*args, bad) == ERR_PHASE
+    a = list(args)
+    a[8] = 0.0
+    assert fn(*a, 1) == ERR_TEMP
+    a = list(args)
+    a[13] = 16
+    assert fn(*a, 4) == ERR_WS
+    a = list(args)
+    a[6] = 99
+    assert fn(*a, 2) == ERR_SHAPE
 
 
 def test_sample_k0_needs_no_draft():
@@ -125,7 +133,7 @@ def test_workspace_sizes():
 
 
 def test_status_strings():
-    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN, 99):
+    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN, ERR_PHASE, 99):
         assert isinstance(rsv.status_string(s), str) and rsv.status_string(s)
 
 
