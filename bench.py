@@ -50,7 +50,40 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-greedy", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch through the Python binding instead of graphs")
+    ap.add_argument("--counters", action="store_true",
+                    help="short run for rocprofv3 --pmc: a 256 MiB copy (calibration), then 3 eager verify rounds "
+                         "and 3 greedy rounds; prints nothing else")
     return ap.parse_args()
+
+
+def counters_run() -> int:
+    """A few dispatches of each kernel for hardware-counter collection (no timing)."""
+    import torch
+
+    import rejection_sampling_verify_sample_amd as rsv
+    from workloads import make_greedy_inputs, make_sample_inputs
+    from workloads.torch_io import greedy_tensors, sample_tensors
+
+    dev = torch.device("cuda:0")
+    n = 256 * 2 ** 20
+    src = torch.full((n // 4,), 1.5, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)  # calibration: reads and writes exactly n bytes
+    torch.cuda.synchronize()
+    del src, dst
+    s = make_sample_inputs(3, 0)
+    t = sample_tensors(s, dev)
+    for _ in range(3):
+        rsv.verify_sample(t["target"], t["draft"], t["draft_tokens"], t["uniforms"], t["temperature"])
+    torch.cuda.synchronize()
+    del t
+    g = greedy_tensors(make_greedy_inputs(0), dev)
+    for _ in range(3):
+        rsv.verify_greedy(g["logits"], g["cand"])
+    torch.cuda.synchronize()
+    print("counters run done", file=sys.stderr)
+    return 0
 
 
 def kernel_source_sha() -> str:
@@ -104,6 +137,8 @@ class Timer:
 
 def main() -> int:
     args = parse_args()
+    if args.counters:
+        return counters_run()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
