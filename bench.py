@@ -53,6 +53,9 @@ def parse_args():
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB copy (calibration), then 3 eager verify rounds "
                          "and 3 greedy rounds; prints nothing else")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from the counter_collection.csv files of two "
+                         "rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of --counters; no GPU needed")
     return ap.parse_args()
 
 
@@ -83,6 +86,58 @@ def counters_run() -> int:
         rsv.verify_greedy(g["logits"], g["cand"])
     torch.cuda.synchronize()
     print("counters run done", file=sys.stderr)
+    return 0
+
+
+TRAFFIC_KERNELS = ["k_sample_rowstats", "k_sample_mass", "k_sample_draw", "k_greedy_argmax", "k_greedy_select"]
+CALIBRATION_KERNEL = "__amd_rocclr_copyBuffer"
+CALIBRATION_KIB = 256 * 1024
+
+
+def _counter_means(path: str, counter: str) -> dict:
+    """Mean counter value (KiB) per kernel family over its dispatches in one rocprofv3 CSV."""
+    import csv
+    acc = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            key = next((k for k in TRAFFIC_KERNELS + [CALIBRATION_KERNEL] if k in name), None)
+            if key is None:
+                continue
+            acc.setdefault(key, []).append(float(row["Counter_Value"]))
+    if CALIBRATION_KERNEL in acc:
+        # the calibration copies come first; later copy dispatches are the small host-to-device input uploads
+        acc[CALIBRATION_KERNEL] = acc[CALIBRATION_KERNEL][:3]
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def ingest_counters(fetch_csv: str, write_csv: str) -> int:
+    """Scale the two counters by what they read for a copy of known size and store bytes per launch."""
+    fetch, write = _counter_means(fetch_csv, "FETCH_SIZE"), _counter_means(write_csv, "WRITE_SIZE")
+    if CALIBRATION_KERNEL not in fetch or CALIBRATION_KERNEL not in write:
+        log("no calibration copy in the counter files")
+        return 1
+    fs = round(CALIBRATION_KIB / fetch[CALIBRATION_KERNEL], 5)
+    ws = round(CALIBRATION_KIB / write[CALIBRATION_KERNEL], 5)
+    sha = kernel_source_sha()
+    out = {
+        "about": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over "
+                 "the dispatches of bench.py --counters), scaled by the factors a 256 MiB device copy gives "
+                 "(copy bytes / counter bytes). source_sha: the kernel sources the counters were taken on "
+                 "(bench.py reports null once they change).",
+        "fetch_scale": fs, "write_scale": ws,
+        "workloads": {"k_sample_*": "B=64 K=8 V=128256 bf16", "k_greedy_*": "B=32 G=7 N=5 V=32000 bf16"},
+    }
+    for k in TRAFFIC_KERNELS:
+        if k in fetch and k in write:
+            out[k] = {"source_sha": sha, "fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
+                      "bytes_per_launch": round(1024 * (fetch[k] * fs + write[k] * ws))}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
     return 0
 
 
@@ -139,6 +194,8 @@ def main() -> int:
     args = parse_args()
     if args.counters:
         return counters_run()
+    if args.ingest_counters:
+        return ingest_counters(*args.ingest_counters)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)

@@ -477,7 +477,7 @@ __device__ __forceinline__ void wave_scalar_chunk_mass(const SampleParams& P, co
 // computed by one wave: the loads of all of them are issued before any is
 // reduced, so a wave keeps CU (or 2*CU) 16-byte loads per lane in flight. Lane 0
 // stores (chunk max, chunk mass).
-constexpr int kChunksPerWave = 4;
+constexpr int kChunksPerWave = 1;
 
 template <typename T>
 __device__ __forceinline__ void wave_vector_chunks_mass(const SampleParams& P, const T* tr, const T* dr,

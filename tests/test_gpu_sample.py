@@ -93,6 +93,19 @@ def test_parity_with_oracle(cfg, kw, rounds):
     save_report(f"cfg{cfg} {kw}", rep)
 
 
+@pytest.mark.parametrize("cfg,kw", [
+    (2, dict(B=3000, V=4000)),
+    (3, dict(B=1500, K=6, V=6000)),
+    (4, dict(B=2000, V=3001)),
+    (1, dict(B=2500, V=2000, dtype="bf16")),
+], ids=lambda x: str(x))
+def test_parity_many_rows(cfg, kw):
+    """Thousands of rows of each value law: outside the window every row is bit-exact."""
+    rep = check_inputs(make_sample_inputs(cfg, 7, **kw))
+    save_report(f"cfg{cfg} many {kw}", rep)
+    assert rep.rows == kw["B"]
+
+
 @pytest.mark.parametrize("cfg", [3, 4])
 def test_parity_full_size(cfg):
     """The full workload in the bench's launch configuration, every row compared."""
