@@ -241,3 +241,173 @@ def oracle_greedy(logits: np.ndarray, cand: np.ndarray) -> GreedyResult:
         acc_len[b] = Lb
         best_out[b] = best
     return GreedyResult(tokens, acc_len, best_out, amax)
+
+
+# --------------------------------------------------------------------------- top-k / top-p consistent verify
+#
+# [KW] §3.4: the temperature rescales both sides before p and q are formed; a
+# top-p (or top-k) truncation must use the same threshold on the draft and the
+# target side, and the correction is drawn only inside the truncated set.
+# Readings where the notes are silent (listed with their reasons in the design
+# notes of the repository):
+#   * top-k then top-p, each on the row's tempered law, top-p on the law left
+#     by top-k and renormalised (the order of the usual sampling pipeline);
+#   * top-k (0 < k < V) keeps every entry with fewer than k entries strictly
+#     above it, so all ties of the k-th largest logit stay; k <= 0 or k >= V
+#     turns it off;
+#   * top-p (p < 1) keeps an entry when the mass of kept entries with a strictly
+#     larger logit is below p, and always keeps the entries of the row's largest
+#     logit (so p <= 0 keeps only those); p >= 1 or NaN turns it off; p is the
+#     float32 value the caller passes;
+#   * p', q' are the kept probabilities renormalised; the verify then runs on
+#     p', q' unchanged (a draft token outside the draft's kept set has q' = 0, so
+#     alpha = 1 when p' > 0);
+#   * a row with no finite logit keeps nothing.
+
+def top_p64(top_p: float) -> float:
+    """The top-p the verify step uses: the float32 value, widened to float64."""
+    return float(np.float32(top_p))
+
+
+@dataclass
+class KeepResult:
+    keep: np.ndarray   # [V] bool: the entries the row keeps
+    margin: float      # |p - mass| of the top-p decisions at the cut, in the top-k law's probability; +inf if no top-p cut
+
+
+def filter_keep(logits: np.ndarray, temperature: float, top_k: int, top_p: float) -> KeepResult:
+    """Entries a logit row keeps under top-k, then top-p on the renormalised top-k law ([KW] §3.4)."""
+    x = np.asarray(logits, dtype=np.float64)
+    V = x.shape[-1]
+    if not np.any(np.isfinite(x)):
+        return KeepResult(np.zeros(V, dtype=bool), np.inf)
+    keep = np.ones(V, dtype=bool)
+    k = int(top_k)
+    if 0 < k < V:
+        kth = np.sort(x)[V - k]            # the k-th largest logit, counting repeats
+        keep = x >= kth
+    p = top_p64(top_p)
+    margin = np.inf
+    if p < 1.0:                            # False for NaN: no top-p
+        z = x / temperature64(temperature)
+        e = np.where(keep, np.exp(z - np.max(z)), 0.0)
+        Z = float(np.sum(e))
+        order = np.argsort(-x, kind="stable")
+        xs, es = x[order], e[order]
+        csum = np.cumsum(es)
+        # first position of each entry's group of equal logits in the descending order
+        start = np.searchsorted(-xs, -xs, side="left")
+        above = np.where(start > 0, csum[np.maximum(start - 1, 0)], 0.0)   # mass strictly above
+        top = xs == xs[0]
+        kept_s = keep[order] & (top | (above < p * Z))
+        J = int(np.sum(kept_s))            # the kept entries form a prefix of the order
+        m_in = np.inf if top[J - 1] else p * Z - above[J - 1]
+        m_out = np.inf
+        if J < V and keep[order][J]:       # the first entry dropped by top-p rather than by top-k
+            m_out = above[J] - p * Z
+        margin = min(m_in, m_out) / Z
+        keep = np.zeros(V, dtype=bool)
+        keep[order] = kept_s
+    return KeepResult(keep, margin)
+
+
+def filtered_softmax64(logits: np.ndarray, temperature: float, keep: np.ndarray) -> np.ndarray:
+    """softmax(logits / T) restricted to `keep` and renormalised over it."""
+    z = np.asarray(logits, dtype=np.float64) / temperature64(temperature)
+    e = np.where(keep, np.exp(z - np.max(z)), 0.0)
+    return e / np.sum(e)
+
+
+@dataclass
+class FilteredResult(SampleResult):
+    kept: np.ndarray = None           # [B, 2K+1] kept entries: target rows 0..K, then draft rows 0..K-1
+    filter_margin: np.ndarray = None  # [B, 2K+1] top-p margin of each row (+inf without a top-p cut)
+    consulted: np.ndarray = None      # [B, 2K+1] bool: the walk read this row's law
+
+    def min_margin(self) -> np.ndarray:
+        fm = np.where(self.consulted, self.filter_margin, np.inf).min(axis=1, initial=np.inf)
+        return np.minimum(SampleResult.min_margin(self), fm)
+
+
+def oracle_sample_filtered(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray, uniforms: np.ndarray,
+                           temperature: float, top_k: np.ndarray, top_p: np.ndarray, *,
+                           with_probs: bool = True) -> FilteredResult:
+    """Rejection-sampling verify on top-k / top-p filtered laws p', q' ([KW] §3.4, [SD] §2.1-2.3).
+
+    Shapes as in oracle_sample; top_k [B] int and top_p [B] float hold the
+    filter of each batch row, applied alike to its target and draft rows.
+    """
+    target = np.asarray(target)
+    draft = np.asarray(draft)
+    B, K, V = draft.shape
+    assert target.shape == (B, K + 1, V) and draft_tokens.shape == (B, K) and uniforms.shape == (B, K + 1, 2)
+    top_k = np.asarray(top_k).reshape(B)
+    top_p = np.asarray(top_p).reshape(B)
+    tokens = np.full((B, K + 1), -1, dtype=np.int32)
+    n_acc = np.zeros(B, dtype=np.int32)
+    probs = np.full((B, K, 2), np.nan)
+    acc_margin = np.full((B, K), np.inf)
+    draw_margin = np.full(B, np.inf)
+    zmass = np.full(B, np.nan)
+    fallback = np.zeros(B, dtype=bool)
+    kept = np.zeros((B, 2 * K + 1), dtype=np.int64)
+    fmargin = np.full((B, 2 * K + 1), np.inf)
+    consulted = np.zeros((B, 2 * K + 1), dtype=bool)
+
+    for b in range(B):
+        rows = [target[b, i] for i in range(K + 1)] + [draft[b, i] for i in range(K)]
+        keeps = [filter_keep(r, temperature, int(top_k[b]), float(top_p[b])) for r in rows]
+        for j, kr in enumerate(keeps):
+            kept[b, j] = int(np.sum(kr.keep))
+            fmargin[b, j] = kr.margin
+
+        def law(j):
+            return filtered_softmax64(rows[j], temperature, keeps[j].keep)
+
+        if with_probs:
+            for i in range(K):
+                x = int(draft_tokens[b, i])
+                if 0 <= x < V and row_is_valid(rows[i]) and row_is_valid(rows[K + 1 + i]):
+                    probs[b, i] = (float(law(i)[x]), float(law(K + 1 + i)[x]))
+        fault = False
+        n = K
+        p_rej = q_rej = None
+        for i in range(K):
+            x = int(draft_tokens[b, i])
+            if not (0 <= x < V) or not row_is_valid(rows[i]) or not row_is_valid(rows[K + 1 + i]):
+                fault = True
+                break
+            consulted[b, i] = consulted[b, K + 1 + i] = True
+            p = law(i)
+            q = law(K + 1 + i)
+            alpha = acceptance_probability(float(p[x]), float(q[x]))
+            r = float(uniforms[b, i, 0])
+            acc_margin[b, i] = abs(r - alpha)
+            if r < alpha:
+                continue
+            n = i
+            p_rej, q_rej = p, q
+            break
+        if not fault and n == K and not row_is_valid(rows[K]):
+            fault = True
+        if fault:
+            n_acc[b] = -1
+            acc_margin[b] = np.inf
+            consulted[b] = False
+            continue
+        if n < K:
+            w = np.maximum(0.0, p_rej - q_rej)   # residual of the filtered laws: inside p's kept set
+            if np.sum(w) == 0.0:
+                w = p_rej
+                fallback[b] = True
+        else:
+            consulted[b, K] = True
+            w = law(K)                           # bonus from the filtered last row
+        k, Z, margin = inverse_cdf_draw(w, float(uniforms[b, n, 1]))
+        tokens[b, :n] = draft_tokens[b, :n]
+        tokens[b, n] = k
+        n_acc[b] = n
+        draw_margin[b] = margin
+        zmass[b] = Z
+    return FilteredResult(tokens, n_acc, probs, acc_margin, draw_margin, zmass, fallback,
+                          kept=kept, filter_margin=fmargin, consulted=consulted)

@@ -46,3 +46,11 @@ def greedy_case(case: dict) -> dict:
     return dict(logits=logits, cand=cand, expect_tokens=np.array([case["tokens"]], dtype=np.int32),
                 expect_len=np.array([case["accept_len"]], dtype=np.int32),
                 expect_best=np.array([case["best"]], dtype=np.int32), name=case["name"])
+
+
+def filtered_case(case: dict) -> dict:
+    c = sample_case(case)
+    c["top_k"] = np.array([int(case["top_k"])], dtype=np.int32)
+    c["top_p"] = np.array([float(case["top_p"])], dtype=np.float32)
+    c["expect_kept"] = np.array([case["kept"]], dtype=np.int64)
+    return c

@@ -10,6 +10,8 @@ Sources of the pinned facts (page title, section):
     §3.1 tokens per round (1 - a^(K+1)) / (1 - a).
   Lookahead Decoding 完全拆解:Jacobi 迭代与 N-gram 池: eq. (5), the expected
     tokens per step with b disjoint candidates of gamma tokens each.
+  kwkr.cn/news/620797 notes §3.4: top-k / top-p must truncate the draft and
+    the target side alike, and the correction is drawn inside the kept set.
   Hand-worked rounds in tests/golden/ (derivations stored beside them).
 """
 from __future__ import annotations
@@ -20,7 +22,7 @@ from fractions import Fraction
 import numpy as np
 from scipy import special, stats
 
-from golden_io import greedy_case, load, logits_from_probs, sample_case
+from golden_io import filtered_case, greedy_case, load, logits_from_probs, sample_case
 from workloads import make_greedy_inputs, verify_uniforms
 
 
@@ -342,3 +344,211 @@ def check_faults(orc) -> None:
     assert np.all(res.tokens[[1, 3]] == -1)
     assert res.tokens[0, :2].tolist() == [4, 0] and 0 <= res.tokens[0, 2] < V
     assert res.tokens[2, 1:].tolist() == [-1, -1] and res.tokens[2, 0] in (1, 2, 3, 4, 5)
+
+
+# --------------------------------------------------------------------------- top-k / top-p filtering
+
+def check_golden_filtered(orc) -> None:
+    for case in load("filtered_worked.json")["cases"]:
+        c = filtered_case(case)
+        res = orc.oracle_sample_filtered(c["target"], c["draft"], c["tokens"], c["uniforms"], c["T"],
+                                         c["top_k"], c["top_p"])
+        assert np.array_equal(res.tokens, c["expect_tokens"]), (c["name"], res.tokens)
+        assert np.array_equal(res.n_accepted, c["expect_n"]), (c["name"], res.n_accepted)
+        assert np.array_equal(res.kept, c["expect_kept"]), (c["name"], res.kept)
+
+
+def _rank_keep(x: np.ndarray, k: int) -> np.ndarray:
+    """Brute force: keep v iff fewer than k entries are strictly larger."""
+    return np.array([np.sum(x > x[v]) < k for v in range(x.size)])
+
+
+def check_filter_top_k_by_rank(orc) -> None:
+    """top-k against a counting brute force on small rows full of ties and -inf."""
+    rng = np.random.default_rng(17)
+    for _ in range(400):
+        V = int(rng.integers(1, 14))
+        x = rng.integers(-3, 4, V).astype(np.float64)
+        x[rng.random(V) < 0.15] = -np.inf
+        k = int(rng.integers(-1, V + 2))
+        kr = orc.filter_keep(x, 1.0, k, 1.0)
+        if not np.any(np.isfinite(x)):
+            assert not kr.keep.any()
+            continue
+        expect = _rank_keep(x, k) if 0 < k < V else np.ones(V, dtype=bool)
+        assert np.array_equal(kr.keep, expect), (x, k, kr.keep)
+        assert kr.margin == np.inf
+        if 0 < k < V and np.unique(x).size == V:
+            assert kr.keep.sum() == k        # distinct values: exactly k
+
+
+def check_filter_top_p_nucleus(orc) -> None:
+    """top-p against the nucleus definition in exact rationals.
+
+    Laws are small integer weights w (zero weight = -inf logit), taken at
+    temperature 1 and 1/2 (logits T ln w, so the tempered law is w itself).
+    The nucleus: among the thresholds t (distinct kept values, high to low) the
+    first whose set {w >= t} reaches mass >= p of the top-k set; the row's
+    largest group is kept whatever p is. Cases closer than 1e-9 to a boundary
+    are skipped (the oracle is float64).
+    """
+    rng = np.random.default_rng(23)
+    checked = 0
+    for _ in range(600):
+        V = int(rng.integers(1, 10))
+        w = rng.integers(0, 6, V)
+        if w.max() == 0:
+            continue
+        T = float(rng.choice([1.0, 0.5]))
+        x = np.array([T * math.log(v) if v > 0 else -math.inf for v in w])
+        k = int(rng.integers(0, V + 1))
+        p = float(np.float32(rng.choice([0.0, 0.1, 0.3, 0.5, 0.7, 0.9, 0.95, rng.random()])))
+        topk = _rank_keep(x, k) if 0 < k < V else np.ones(V, dtype=bool)
+        ws = [Fraction(int(v)) if topk[i] else Fraction(0) for i, v in enumerate(w)]
+        Z = sum(ws)
+        P = Fraction(p)
+        vals = sorted({int(w[i]) for i in range(V) if topk[i]}, reverse=True)
+        chosen = vals[0]
+        near = False
+        for t in vals:
+            mass = sum(ws[i] for i in range(V) if topk[i] and w[i] >= t) / Z
+            if abs(mass - P) < Fraction(1, 10 ** 9):
+                near = True
+            chosen = t
+            if mass >= P:
+                break
+        if near:
+            continue
+        expect = np.array([bool(topk[i]) and int(w[i]) >= chosen for i in range(V)])
+        kr = orc.filter_keep(x, T, k, p)
+        assert np.array_equal(kr.keep, expect), (w.tolist(), T, k, p, kr.keep, expect)
+        checked += 1
+    assert checked > 300
+
+
+def check_filter_special_cases(orc) -> None:
+    rng = np.random.default_rng(29)
+    for _ in range(100):
+        V = int(rng.integers(2, 40))
+        x = np.round(rng.normal(0, 2, V), 1)
+        x[rng.random(V) < 0.1] = -np.inf
+        if not np.any(np.isfinite(x)):
+            continue
+        top = x == np.max(x)
+        T = float(rng.choice([0.5, 1.0, 1.7]))
+        # k = 1 and p -> 0 both keep exactly the entries of the largest logit
+        assert np.array_equal(orc.filter_keep(x, T, 1, 1.0).keep, top)
+        assert np.array_equal(orc.filter_keep(x, T, 0, 1e-30).keep, top)
+        assert np.array_equal(orc.filter_keep(x, T, 0, 0.0).keep, top)
+        # off: k <= 0 or k >= V, p >= 1 or NaN
+        for k, p in ((0, 1.0), (V, 1.0), (-3, 2.0), (V + 5, float("nan"))):
+            assert orc.filter_keep(x, T, k, p).keep.all()
+        # nested: smaller k or smaller p keeps a subset
+        prev = np.ones(V, dtype=bool)
+        for k in range(V, 0, -1):
+            cur = orc.filter_keep(x, T, k, 1.0).keep
+            assert np.all(cur <= prev)
+            prev = cur
+        prev = np.ones(V, dtype=bool)
+        for p in (0.99, 0.9, 0.7, 0.5, 0.2, 0.01):
+            cur = orc.filter_keep(x, T, 0, p).keep
+            assert np.all(cur <= prev) and cur[top].all()
+            prev = cur
+        # top-p never keeps an entry without mass
+        assert not np.any(orc.filter_keep(x, T, 0, 0.999).keep & np.isneginf(x))
+        # the kept mass of a top-p cut reaches p; without its lowest kept group it does not
+        kr = orc.filter_keep(x, T, 0, 0.8)
+        pz = special.softmax(np.where(np.isneginf(x), -np.inf, x / T))
+        low = x == np.min(x[kr.keep])
+        assert pz[kr.keep].sum() >= 0.8 - 1e-12 or kr.keep.all()
+        assert pz[kr.keep & ~low].sum() < 0.8 + 1e-12
+    assert not orc.filter_keep(np.full(5, -np.inf), 1.0, 2, 0.5).keep.any()
+    # temperature matters to top-p, not to top-k: a cut that moves with T
+    x = np.log(np.array([4.0, 2.0, 2.0, 1.0, 1.0]))
+    assert orc.filter_keep(x, 1.0, 0, 0.7).keep.tolist() == [True, True, True, False, False]
+    assert orc.filter_keep(x, 0.5, 0, 0.7).keep.tolist() == [True, True, True, False, False]
+    assert orc.filter_keep(x, 0.25, 0, 0.7).keep.tolist() == [True, False, False, False, False]
+    assert orc.filter_keep(x, 0.25, 3, 1.0).keep.tolist() == [True, True, True, False, False]
+
+
+def check_filters_off_match_plain(orc) -> None:
+    """With both filters off the filtered verify is the plain verify, output for output."""
+    rng = np.random.default_rng(31)
+    B, K, V = 40, 3, 30
+    tgt = rng.normal(0, 2, (B, K + 1, V))
+    drf = tgt[:, :K] + rng.normal(0, 1, (B, K, V))
+    tgt[rng.random(tgt.shape) < 0.05] = -np.inf
+    toks = rng.integers(0, V, (B, K)).astype(np.int32)
+    uni = verify_uniforms(9, 0, B, K)
+    plain = orc.oracle_sample(tgt, drf, toks, uni, 0.8)
+    for k, p in ((0, 1.0), (V, 1.5)):
+        f = orc.oracle_sample_filtered(tgt, drf, toks, uni, 0.8, np.full(B, k), np.full(B, p, dtype=np.float32))
+        assert np.array_equal(f.tokens, plain.tokens) and np.array_equal(f.n_accepted, plain.n_accepted)
+        assert np.allclose(f.probs, plain.probs, rtol=1e-12, atol=0, equal_nan=True)
+        assert np.all(f.kept == V)
+
+
+FILTER_GRID_CASES = [
+    # (T, top_k, top_p, target row 0, draft row 0, bonus row; then the filtered laws p'0, q'0, p'1 by hand)
+    (1.0, 0, 0.7, ["2/5", "1/5", "1/5", "1/10", "1/10", "0"], ["1/5", "0", "1/5", "2/5", "1/10", "1/10"],
+     ["1/10", "1/10", "2/5", "1/5", "1/5", "0"],
+     ["1/2", "1/4", "1/4", "0", "0", "0"], ["1/4", "0", "1/4", "1/2", "0", "0"], ["0", "0", "1/2", "1/4", "1/4", "0"]),
+    (0.5, 2, 1.0, ["1/4", "1/8", "1/8", "1/4", "1/8", "1/8"], ["3/8", "3/8", "1/8", "1/16", "1/16", "0"],
+     ["1/8", "1/8", "1/8", "1/8", "1/4", "1/4"],
+     ["1/2", "0", "0", "1/2", "0", "0"], ["1/2", "1/2", "0", "0", "0", "0"], ["0", "0", "0", "0", "1/2", "1/2"]),
+    (1.0, 3, 0.6, ["1/2", "1/8", "1/4", "1/16", "1/16", "0"], ["1/4", "1/4", "1/4", "1/8", "1/8", "0"],
+     ["1/8", "1/8", "1/8", "1/8", "1/4", "1/4"],
+     ["2/3", "0", "1/3", "0", "0", "0"], ["1/3", "1/3", "1/3", "0", "0", "0"],
+     ["1/8", "1/8", "1/8", "1/8", "1/4", "1/4"]),
+    (0.8, 0, 0.45, ["1/2", "1/4", "1/4", "0"], ["1/8", "1/8", "1/4", "1/2"], ["1/4", "1/4", "1/4", "1/4"],
+     ["1", "0", "0", "0"], ["0", "0", "0", "1"], ["1/4", "1/4", "1/4", "1/4"]),
+]
+
+
+def check_filtered_exact_law(orc, grid: int = 48) -> None:
+    """The theorem of §2.2 on the filtered laws: the emitted token has law p' exactly.
+
+    As check_exact_law_on_grid, with K = 1 and a filter on every row; the draft
+    token runs over q'0's support with weight q'0(x) (the draft samples its own
+    filtered law). The filtered laws are worked out by hand from the unfiltered
+    ones (comments in FILTER_GRID_CASES), not by the oracle: P(first = y) =
+    p'0(y), P(accepted) = 1 - TV(p'0, q'0), P(accepted, bonus = y) = (1 - TV) p'1(y).
+    Every boundary is a multiple of 1/48, so the mesh integral is exact.
+    """
+    mids = (np.arange(grid) + 0.5) / grid
+    for T, k, p, t0s, d0s, t1s, e0s, eq0s, e1s in FILTER_GRID_CASES:
+        pf0 = [Fraction(s) for s in e0s]
+        qf0 = [Fraction(s) for s in eq0s]
+        pf1 = [Fraction(s) for s in e1s]
+        V = len(pf0)
+        xs = [x for x in range(V) if qf0[x] > 0]
+        rr, uu = np.meshgrid(mids, mids, indexing="ij")
+        rr, uu = rr.ravel(), uu.ravel()
+        cells = rr.size
+        B = len(xs) * cells
+        tgt = np.broadcast_to(np.stack([logits_from_probs(t0s, T), logits_from_probs(t1s, T)]), (B, 2, V))
+        drf = np.broadcast_to(logits_from_probs(d0s, T), (B, 1, V))
+        toks = np.repeat(np.array(xs, dtype=np.int32), cells)[:, None]
+        uni = np.zeros((B, 2, 2), dtype=np.float64)
+        uni[:, 0, 0] = np.tile(rr, len(xs))
+        uni[:, 0, 1] = np.tile(uu, len(xs))
+        uni[:, 1, 1] = 1.0 - np.tile(uu, len(xs))
+        res = orc.oracle_sample_filtered(tgt, drf, toks, uni, T, np.full(B, k), np.full(B, p, dtype=np.float32),
+                                         with_probs=False)
+        first = [Fraction(0)] * V
+        bonus = [Fraction(0)] * V
+        accepted = Fraction(0)
+        for j, x in enumerate(xs):
+            sl = slice(j * cells, (j + 1) * cells)
+            wgt = qf0[x] / cells
+            t0 = res.tokens[sl, 0]
+            n = res.n_accepted[sl]
+            assert np.all(n >= 0)
+            for y in range(V):
+                first[y] += wgt * int(np.sum(t0 == y))
+                bonus[y] += wgt * int(np.sum((n == 1) & (res.tokens[sl, 1] == y)))
+            accepted += wgt * int(np.sum(n == 1))
+        tv = sum(abs(a - b) for a, b in zip(pf0, qf0)) / 2
+        assert first == pf0, ("filtered first-token law", T, k, p, first, pf0)
+        assert accepted == 1 - tv, ("filtered acceptance", accepted, 1 - tv)
+        assert bonus == [(1 - tv) * v for v in pf1], ("filtered bonus law", bonus)

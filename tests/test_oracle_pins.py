@@ -49,3 +49,27 @@ def test_greedy_argmax_brute_force():
 
 def test_fault_reading():
     pins.check_faults(oracle)
+
+
+def test_golden_filtered_rounds():
+    pins.check_golden_filtered(oracle)
+
+
+def test_filter_top_k_by_rank():
+    pins.check_filter_top_k_by_rank(oracle)
+
+
+def test_filter_top_p_nucleus_in_rationals():
+    pins.check_filter_top_p_nucleus(oracle)
+
+
+def test_filter_special_cases():
+    pins.check_filter_special_cases(oracle)
+
+
+def test_filters_off_match_plain_verify():
+    pins.check_filters_off_match_plain(oracle)
+
+
+def test_filtered_output_law_exact_on_a_grid():
+    pins.check_filtered_exact_law(oracle)

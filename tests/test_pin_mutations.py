@@ -39,6 +39,27 @@ MUTATIONS = [
      "return int(np.argmax(np.asarray(row, dtype=np.float64)))",
      "return int(len(row) - 1 - np.argmax(np.asarray(row, dtype=np.float64)[::-1]))"),
     ("greedy counts one position too many", "while L[g] < N - 1 and", "while L[g] < N and"),
+    ("top-k drops the ties of the k-th value", "keep = x >= kth", "keep = x > kth"),
+    ("top-k threshold off by one", "kth = np.sort(x)[V - k]", "kth = np.sort(x)[max(V - k - 1, 0)]"),
+    ("top-p counts the entry's own group", "above = np.where(start > 0, csum[np.maximum(start - 1, 0)], 0.0)",
+     "above = csum"),
+    ("top-p ignores the temperature", "z = x / temperature64(temperature)\n        e = np.where(keep",
+     "z = x\n        e = np.where(keep"),
+    ("top-p over the whole row, not the top-k set",
+     "e = np.where(keep, np.exp(z - np.max(z)), 0.0)\n        Z", "e = np.exp(z - np.max(z))\n        Z"),
+    ("top-p without the largest group", "kept_s = keep[order] & (top | (above < p * Z))",
+     "kept_s = keep[order] & (above < p * Z)"),
+    ("filtered law renormalised over the whole row",
+     "e = np.where(keep, np.exp(z - np.max(z)), 0.0)\n    return e / np.sum(e)",
+     "e = np.exp(z - np.max(z))\n    return np.where(keep, e, 0.0) / np.sum(e)"),
+    ("draft rows not filtered",
+     "keeps = [filter_keep(r, temperature, int(top_k[b]), float(top_p[b])) for r in rows]",
+     "keeps = [filter_keep(r, temperature, int(top_k[b]) if j <= K else 0, float(top_p[b]) if j <= K else 1.0)"
+     " for j, r in enumerate(rows)]"),
+    ("bonus row not filtered",
+     "keeps = [filter_keep(r, temperature, int(top_k[b]), float(top_p[b])) for r in rows]",
+     "keeps = [filter_keep(r, temperature, int(top_k[b]) if j != K else 0, float(top_p[b]) if j != K else 1.0)"
+     " for j, r in enumerate(rows)]"),
 ]
 
 CHECKS = [
@@ -52,6 +73,12 @@ CHECKS = [
     pins.check_exact_law_on_grid,
     pins.check_acceptance_is_one_minus_tv,
     pins.check_tokens_per_round,
+    pins.check_golden_filtered,
+    pins.check_filter_top_k_by_rank,
+    pins.check_filter_top_p_nucleus,
+    pins.check_filter_special_cases,
+    pins.check_filters_off_match_plain,
+    pins.check_filtered_exact_law,
 ]
 
 

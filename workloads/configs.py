@@ -247,3 +247,24 @@ def make_greedy_inputs(rnd: int = 0, *, B: int | None = None, G: int | None = No
     cand = np.where(hit, placed, rand_tok).astype(np.int32)
     return GreedyInputs(logits, dt, cand, name=f"cfg5 B={B} G={G} N={N} V={V} {dt} round={rnd}",
                         meta={"placed_max": pos.reshape(B, G, N)})
+
+
+FILTER_TOP_K = (0, 1, 2, 5, 20, 50, 200, 1000)
+FILTER_TOP_P = (1.0, 0.99, 0.95, 0.9, 0.8, 0.5, 0.2)
+
+
+def make_filter_params(B: int, seed: int = 0, *, top_k: int | None = None, top_p: float | None = None,
+                       V: int | None = None):
+    """Per-batch-row top-k / top-p parameters: (top_k [B] int32, top_p [B] float32).
+
+    With top_k / top_p given, every row gets that value. Otherwise each row
+    draws k from FILTER_TOP_K (plus V - 1 and V when V is given, so the
+    boundary of the off range is exercised) and p from FILTER_TOP_P,
+    independently: some rows use neither filter, some one, some both.
+    """
+    rng = _rng(seed, 77, B)
+    ks = list(FILTER_TOP_K) + ([V - 1, V] if V is not None else [])
+    k = np.full(B, top_k, dtype=np.int32) if top_k is not None else rng.choice(ks, size=B).astype(np.int32)
+    p = (np.full(B, top_p, dtype=np.float32) if top_p is not None
+         else rng.choice(FILTER_TOP_P, size=B).astype(np.float32))
+    return k, p
