@@ -12,8 +12,10 @@ Steps are launched from HIP graphs that each hold a run of consecutive steps
 --steps steps, is bracketed by HIP events on the stream the kernels run on.
 
 Prints ONE JSON line. Also reported: the pass-1 kernel alone (the dominant
-kernel, for the roofline), the greedy verify on its own workload (B=32 G=7 N=5
-V=32000 bf16), and the CPU oracle on a bounded sample of the same round.
+kernel, for the roofline), the same round verified on top-k 50 / top-p 0.9
+filtered laws (spec_verify_sample_filtered), the greedy verify on its own
+workload (B=32 G=7 N=5 V=32000 bf16), and the CPU oracle on a bounded sample of
+the same round.
 """
 from __future__ import annotations
 
@@ -33,7 +35,7 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, AMD published peak
 CACHE_BYTES = 256 * 2 ** 20  # MI355X Infinity Cache
 METRIC = "verify rounds/s + achieved HBM GB/s (% peak), B=64 K=8 V=128256 bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["common.hpp", "params.hpp", "sample.hip", "greedy.hip"]
+KERNEL_SOURCES = ["common.hpp", "params.hpp", "sample.hip", "filter.hip", "greedy.hip"]
 
 
 def log(msg: str) -> None:
@@ -49,6 +51,7 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-greedy", action="store_true")
+    ap.add_argument("--no-filtered", action="store_true", help="skip the top-k / top-p filtered leg")
     ap.add_argument("--eager", action="store_true", help="launch through the Python binding instead of graphs")
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB copy (calibration), then 3 eager verify rounds "
@@ -173,6 +176,73 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+CHUNK_STEPS = 48   # verify steps per HIP graph (a graph launch costs about as much as a short kernel)
+FILTER_K, FILTER_P = 50, 0.9
+
+
+class GraphSteps:
+    """Runs verify steps step_fn(i, phases) from HIP graphs holding a run of consecutive steps.
+
+    Steps cycle over the M input copies; a graph holds a whole number of cycles
+    (about CHUNK_STEPS steps), and a remainder graph makes any count exact.
+    """
+
+    def __init__(self, torch, step_fn, M: int, eager: bool):
+        self.torch, self.step_fn, self.M, self.eager = torch, step_fn, M, eager
+        self.chunk = M * max(1, CHUNK_STEPS // M)
+        self.graphs: dict = {}
+
+    def _capture(self, phases, count):
+        g = self.torch.cuda.CUDAGraph()
+        with self.torch.cuda.graph(g):
+            for j in range(count):
+                self.step_fn(j, phases)
+        return g
+
+    def prepare(self, phases, n_list) -> None:
+        if self.eager:
+            return
+        t = self.torch
+        if phases not in self.graphs:
+            side = t.cuda.Stream()
+            side.wait_stream(t.cuda.current_stream())
+            with t.cuda.stream(side):
+                for j in range(self.M):
+                    self.step_fn(j, phases)
+            t.cuda.current_stream().wait_stream(side)
+            t.cuda.synchronize()
+            self.graphs[phases] = (self._capture(phases, self.chunk), {})
+        tails = self.graphs[phases][1]
+        for n in n_list:
+            r = n % self.chunk
+            if r and r not in tails:
+                tails[r] = self._capture(phases, r)
+
+    def run(self, phases, n: int) -> None:
+        """Exactly n steps: whole graphs, then the remainder graph."""
+        if self.eager:
+            for i in range(n):
+                self.step_fn(i, phases)
+            return
+        g, tails = self.graphs[phases]
+        q, r = divmod(n, self.chunk)
+        for _ in range(q):
+            g.replay()
+        if r:
+            tails[r].replay()
+
+    def timed(self, phases, n: int) -> float:
+        """Seconds for n steps, between HIP events on the stream the graphs run on."""
+        t = self.torch
+        t.cuda.synchronize()
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        self.run(phases, n)
+        b.record()
+        t.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3
+
+
 class Timer:
     def __init__(self, torch):
         self.torch = torch
@@ -238,76 +308,14 @@ def main() -> int:
     for i in range(3):
         call(sets[i % M])
     torch.cuda.synchronize()
-
-    def stepper(phases):
-        """fn(i) runs step i; graphs hold CHUNK consecutive steps (a graph launch costs ~20 us)."""
-        if args.eager:
-            return lambda i: call(sets[i % M], phases)
-
-        def capture(first, count):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for j in range(count):
-                    call(sets[(first + j) % M], phases)
-            return g
-
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for st in sets:
-                call(st, phases)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        chunk = capture(0, CHUNK)
-        return chunk
-
-    def run_steps(graph, n):
-        """Run exactly n steps: whole chunks, then a graph of the remainder."""
-        if args.eager:
-            for i in range(n):
-                graph(i)
-            return
-        q, r = divmod(n, CHUNK)
-        for _ in range(q):
-            graph.replay()
-        if r:
-            tails.setdefault(id(graph), {})
-            tg = tails[id(graph)].get(r)
-            if tg is None:
-                raise RuntimeError("remainder graph not prepared")
-            tg.replay()
-
-    CHUNK = M * max(1, 48 // M)
-    tails: dict = {}
-
-    def prepare(phases, n_list):
-        g = stepper(phases)
-        if not args.eager:
-            for n in n_list:
-                r = n % CHUNK
-                if r and r not in tails.setdefault(id(g), {}):
-                    tg = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(tg):
-                        for j in range(r):
-                            call(sets[j % M], phases)
-                    tails[id(g)][r] = tg
-        return g
-
-    def timed(g, n):
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        run_steps(g, n)
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / 1e3
-
-    g_full = prepare(rsv.PHASE_ALL, [args.warmup, args.steps])
-    g_p1 = prepare(rsv.PHASE_ROW_STATS, [args.warmup, args.steps])
-    timed(g_full, args.warmup)
-    t_step = timed(g_full, args.steps) / args.steps
-    timed(g_p1, args.warmup)
-    t_pass1 = timed(g_p1, args.steps) / args.steps
+    steps = GraphSteps(torch, lambda i, ph: call(sets[i % M], ph), M, args.eager)
+    n_list = [args.warmup, args.steps]
+    steps.prepare(rsv.PHASE_ALL, n_list)
+    steps.prepare(rsv.PHASE_ROW_STATS, n_list)
+    steps.timed(rsv.PHASE_ALL, args.warmup)
+    t_step = steps.timed(rsv.PHASE_ALL, args.steps) / args.steps
+    steps.timed(rsv.PHASE_ROW_STATS, args.warmup)
+    t_pass1 = steps.timed(rsv.PHASE_ROW_STATS, args.steps) / args.steps
     # outputs of the last full step of each copy (identical inputs -> identical outputs)
     for st in sets:
         call(st)
@@ -331,7 +339,53 @@ def main() -> int:
     traffic = measured_traffic("k_sample_rowstats")
     log(f"step {t_step * 1e6:.2f} us ({rounds_per_s:.0f} rounds/s, {step_gbps:.0f} GB/s); "
         f"pass 1 {t_pass1 * 1e6:.2f} us ({pass1_gbps:.0f} GB/s); mean accepted {n_acc.mean():.3f}")
-    del sets, g_full, g_p1, tails
+    del steps
+
+    # ---------------------------------------------------------------- the same round, top-k 50 / top-p 0.9 filtered
+    filtered = None
+    if not args.no_filtered:
+        from workloads import make_filter_params
+        fk, fp = make_filter_params(B, top_k=FILTER_K, top_p=FILTER_P)
+        topk = torch.from_numpy(fk).to(dev)
+        topp = torch.from_numpy(fp).to(dev)
+        fws = torch.zeros(rsv.sample_filtered_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
+        kept = torch.empty((B, 2 * K + 1), dtype=torch.int32, device=dev)
+
+        def fcall(st, phases=rsv.PHASE_ALL):
+            rsv.verify_sample_filtered(st["target"], st["draft"], st["draft_tokens"], st["uniforms"], s.temperature,
+                                       topk, topp, out_tokens=st["out_tokens"], out_num_accepted=st["out_n"],
+                                       out_kept=kept, workspace=fws, phases=phases)
+
+        for st in sets:
+            fcall(st)
+        torch.cuda.synchronize()
+        fsteps = GraphSteps(torch, lambda i, ph: fcall(sets[i % M], ph), M, args.eager)
+        fn = max(CHUNK_STEPS, args.steps // 4)
+        fsteps.prepare(rsv.PHASE_ALL, [fn])
+        fsteps.prepare(rsv.PHASE_ROW_STATS, [fn])
+        fsteps.timed(rsv.PHASE_ALL, fn)
+        tf_step = fsteps.timed(rsv.PHASE_ALL, fn) / fn
+        fsteps.timed(rsv.PHASE_ROW_STATS, fn)
+        tf_filter = fsteps.timed(rsv.PHASE_ROW_STATS, fn) / fn
+        fcall(sets[0])
+        torch.cuda.synchronize()
+        fn_acc = sets[0]["out_n"].cpu().numpy()
+        assert np.all(fn_acc >= 0) and np.all(fn_acc <= K), "invalid accepted counts (filtered)"
+        rows = B * (2 * K + 1)
+        one_read = rows * row_bytes
+        passes = 4  # bf16 with both filters: the maximum, then two radix digits of top-k, then two of top-p
+        filtered = {"workload": f"{WORKLOAD_NAMES[3]}; top-k {FILTER_K} and top-p {FILTER_P} on every row",
+                    "rounds_per_s": round(1.0 / tf_step, 1), "us_per_round": round(tf_step * 1e6, 3),
+                    "filter_kernel_us": round(tf_filter * 1e6, 3), "rows_filtered": rows,
+                    "one_read_bytes": one_read, "filter_gbps_one_read": round(one_read / tf_filter / 1e9, 1),
+                    "filter_passes_per_row": passes,
+                    "filter_gbps_as_read": round(passes * one_read / tf_filter / 1e9, 1),
+                    "mean_kept": round(float(kept.float().mean().item()), 2),
+                    "mean_accepted": round(float(fn_acc.mean()), 4)}
+        log(f"filtered step {tf_step * 1e6:.2f} us; filter kernel {tf_filter * 1e6:.2f} us "
+            f"({one_read / tf_filter / 1e9:.0f} GB/s on one read of {rows} rows)")
+        del fsteps
+    del sets
 
     # ---------------------------------------------------------------- greedy verify, B=32 G=7 N=5 V=32000 bf16
     greedy = None
@@ -420,6 +474,7 @@ def main() -> int:
                      "us_per_launch": round(t_pass1 * 1e6, 3)},
         "cpu_baseline": cpu,
         "greedy": greedy,
+        "filtered": filtered,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -67,8 +67,11 @@ typedef enum {
   SPEC_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_size query */
   SPEC_ERR_HIP = -6,         /* a HIP launch failed */
   SPEC_ERR_ALIGN = -7,       /* a pointer is not aligned to its element size */
-  SPEC_ERR_PHASE = -8        /* phase mask outside 1..15 (spec_verify_sample_phases) */
+  SPEC_ERR_PHASE = -8,       /* phase mask outside 1..15 (spec_verify_sample_phases) */
+  SPEC_ERR_FILTER_V = -9     /* V > SPEC_MAX_FILTER_V (spec_verify_sample_filtered) */
 } spec_status;
+
+#define SPEC_MAX_FILTER_V (1 << 24) /* vocabulary entries per row of the filtered verify */
 
 /* Bytes of workspace spec_verify_sample needs for these sizes (0 for invalid sizes). */
 size_t spec_verify_sample_workspace_size(int32_t B, int32_t K, int32_t V);
@@ -92,7 +95,8 @@ size_t spec_verify_sample_workspace_size(int32_t B, int32_t K, int32_t V);
  * out_tokens       [B, K+1] int32: x_0..x_{n-1}, then the drawn token at n, then -1.
  * out_num_accepted [B] int32: n in [0, K], or -1 for a data fault.
  * out_probs        NULL or [B, K, 2] float: p_i(x_i), q_i(x_i) in fp32 for every
- *                  i < K (NaN where x_i is out of range or a row has no finite logit).
+ *                  i < K (NaN where x_i is out of range; p_i (q_i) is NaN when target
+ *                  (draft) row i has no finite logit).
  * workspace        device memory of at least spec_verify_sample_workspace_size bytes.
  *
  * Draw rule: token = the smallest k with sum_{v<=k} w_v > u * sum_v w_v, where w
@@ -136,6 +140,56 @@ spec_status spec_verify_sample_phases(const void* target_logits, const void* dra
                                       int32_t V, float temperature, int32_t* out_tokens,
                                       int32_t* out_num_accepted, float* out_probs, void* workspace,
                                       size_t workspace_bytes, void* stream, int32_t phases);
+
+/* Bytes of workspace spec_verify_sample_filtered needs for these sizes (0 for invalid sizes). */
+size_t spec_verify_sample_filtered_workspace_size(int32_t B, int32_t K, int32_t V);
+
+/*
+ * Rejection-sampling verify on top-k / top-p filtered laws.
+ * Source: kwkr.cn/news/620797 engineering notes, §3.4: the temperature is
+ * applied to both sides before p and q are formed; a top-k or top-p truncation
+ * must use the same parameter on the draft and the target side, and the
+ * correction is drawn only inside the truncated set.
+ *
+ * Arguments as spec_verify_sample, plus:
+ * top_k     NULL or [B] int32 device array: the k of batch row b, applied to its
+ *           target rows 0..K and draft rows 0..K-1 alike. A row keeps every
+ *           entry that has fewer than k entries with a strictly larger logit (all
+ *           ties of the k-th largest logit stay). k <= 0 or k >= V: no top-k.
+ * top_p     NULL or [B] float device array: then, on the law left by top-k and
+ *           renormalised, a row keeps an entry when the kept entries with a
+ *           strictly larger logit hold mass < p, and always keeps the entries of
+ *           its largest logit (so p <= 0 keeps only those). p >= 1 or NaN: no top-p.
+ * out_kept  NULL or [B, 2K+1] int32: the number of entries each row keeps, target
+ *           rows 0..K first, then draft rows 0..K-1 (0 for a row with no finite logit).
+ * V         at most SPEC_MAX_FILTER_V (SPEC_ERR_FILTER_V otherwise): kept masses
+ *           are summed exactly in 64-bit fixed point, 2^-40 per unit of mass.
+ * The verify then runs on p' and q', the kept probabilities renormalised: a draft
+ * token outside its draft row's kept set has q' = 0 (accepted when p' > 0); the
+ * residual max(0, p'_n - q'_n), its zero-mass fallback p'_n and the bonus law p'_K
+ * all lie inside the target row's kept set. out_probs holds p'_i(x_i), q'_i(x_i).
+ * Unlike spec_verify_sample, every row is read (the bonus row too), several
+ * times: one pass for its maximum and one per radix digit of each active
+ * filter (bf16: 2 digits, fp32: 3).
+ */
+spec_status spec_verify_sample_filtered(const void* target_logits, const void* draft_logits, int32_t dtype,
+                                        const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t K,
+                                        int32_t V, float temperature, int32_t* out_tokens,
+                                        int32_t* out_num_accepted, float* out_probs, void* workspace,
+                                        size_t workspace_bytes, void* stream, const int32_t* top_k,
+                                        const float* top_p, int32_t* out_kept);
+
+/*
+ * spec_verify_sample_filtered as its phases (the bits of spec_verify_sample_phases,
+ * run in order); SPEC_PHASE_ROW_STATS is the filter pass over all 2K+1 rows of
+ * every batch row.
+ */
+spec_status spec_verify_sample_filtered_phases(const void* target_logits, const void* draft_logits, int32_t dtype,
+                                               const int32_t* draft_tokens, const float* uniforms, int32_t B,
+                                               int32_t K, int32_t V, float temperature, int32_t* out_tokens,
+                                               int32_t* out_num_accepted, float* out_probs, void* workspace,
+                                               size_t workspace_bytes, void* stream, const int32_t* top_k,
+                                               const float* top_p, int32_t* out_kept, int32_t phases);
 
 /* Bytes of workspace spec_verify_greedy needs for these sizes (0 for invalid sizes). */
 size_t spec_verify_greedy_workspace_size(int32_t B, int32_t G, int32_t N, int32_t V);

@@ -109,7 +109,7 @@ def inverse_cdf_draw(w: np.ndarray, u: float) -> tuple[int, float, float]:
 class SampleResult:
     tokens: np.ndarray          # [B, K+1] int32; first n+1 valid, rest -1
     n_accepted: np.ndarray      # [B] int32; -1 marks a data fault
-    probs: np.ndarray           # [B, K, 2] float64: p_i(x_i), q_i(x_i) (nan where undefined)
+    probs: np.ndarray           # [B, K, 2] float64: p_i(x_i), q_i(x_i) (nan where undefined, each by its own row)
     accept_margin: np.ndarray   # [B, K] |r_i - alpha_i| for evaluated tests, +inf otherwise
     draw_margin: np.ndarray     # [B] margin of the resample / bonus draw (+inf on a fault)
     residual_mass: np.ndarray   # [B] Z of the draw (1 for a bonus draw; nan on a fault)
@@ -121,11 +121,13 @@ class SampleResult:
 
 
 def token_probs(target_row: np.ndarray, draft_row: np.ndarray, x: int, temperature: float) -> tuple[float, float]:
-    """(p(x), q(x)) for one position; nan when a row is invalid or x is out of range."""
+    """(p(x), q(x)) for one position; each is nan when x is out of range or its own row has no finite logit."""
     V = target_row.shape[-1]
-    if not (0 <= x < V) or not row_is_valid(target_row) or not row_is_valid(draft_row):
+    if not (0 <= x < V):
         return float("nan"), float("nan")
-    return float(softmax64(target_row, temperature)[x]), float(softmax64(draft_row, temperature)[x])
+    p = float(softmax64(target_row, temperature)[x]) if row_is_valid(target_row) else float("nan")
+    q = float(softmax64(draft_row, temperature)[x]) if row_is_valid(draft_row) else float("nan")
+    return p, q
 
 
 def oracle_sample(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray,
@@ -367,8 +369,10 @@ def oracle_sample_filtered(target: np.ndarray, draft: np.ndarray, draft_tokens: 
         if with_probs:
             for i in range(K):
                 x = int(draft_tokens[b, i])
-                if 0 <= x < V and row_is_valid(rows[i]) and row_is_valid(rows[K + 1 + i]):
-                    probs[b, i] = (float(law(i)[x]), float(law(K + 1 + i)[x]))
+                if 0 <= x < V:
+                    for side, j in ((0, i), (1, K + 1 + i)):
+                        if row_is_valid(rows[j]):
+                            probs[b, i, side] = float(law(j)[x])
         fault = False
         n = K
         p_rej = q_rej = None

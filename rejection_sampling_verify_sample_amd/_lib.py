@@ -36,6 +36,14 @@ _SIGNATURES = {
     "spec_verify_sample_phases": (_i32, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                          ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
                                          _c_void_p, _i32]),
+    "spec_verify_sample_filtered_workspace_size": (_size_t, [_i32, _i32, _i32]),
+    "spec_verify_sample_filtered": (_i32, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                           ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
+                                           _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "spec_verify_sample_filtered_phases": (_i32, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32,
+                                                  _i32, ctypes.c_float, _c_void_p, _c_void_p, _c_void_p,
+                                                  _c_void_p, _size_t, _c_void_p, _c_void_p, _c_void_p,
+                                                  _c_void_p, _i32]),
     "spec_verify_greedy_workspace_size": (_size_t, [_i32, _i32, _i32, _i32]),
     "spec_verify_greedy": (_i32, [_c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
                                   _c_void_p, _c_void_p, _size_t, _c_void_p]),
@@ -79,6 +87,10 @@ def abi_version() -> int:
 
 def sample_workspace_size(B: int, K: int, V: int) -> int:
     return int(lib().spec_verify_sample_workspace_size(B, K, V))
+
+
+def sample_filtered_workspace_size(B: int, K: int, V: int) -> int:
+    return int(lib().spec_verify_sample_filtered_workspace_size(B, K, V))
 
 
 def greedy_workspace_size(B: int, G: int, N: int, V: int) -> int:
@@ -142,6 +154,7 @@ class SampleOutputs:
     tokens: torch.Tensor        # [B, K+1] int32
     num_accepted: torch.Tensor  # [B] int32
     probs: torch.Tensor | None  # [B, K, 2] float32
+    kept: torch.Tensor | None = None  # [B, 2K+1] int32 (filtered verify only)
 
 
 PHASE_ROW_STATS, PHASE_ACCEPT, PHASE_MASS, PHASE_DRAW, PHASE_ALL = 1, 2, 4, 8, 15
@@ -158,6 +171,28 @@ def verify_sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch
     spec_verify_sample_phases; later phases read what earlier ones of the same
     arguments left in the workspace.
     """
+    return _verify_sample(target, draft, draft_tokens, uniforms, temperature, out_tokens, out_num_accepted,
+                          out_probs, want_probs, workspace, stream, phases, None)
+
+
+def verify_sample_filtered(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                           uniforms: torch.Tensor, temperature: float, top_k: torch.Tensor | None,
+                           top_p: torch.Tensor | None, *, out_tokens: torch.Tensor | None = None,
+                           out_num_accepted: torch.Tensor | None = None, out_probs: torch.Tensor | None = None,
+                           want_probs: bool = False, out_kept: torch.Tensor | None = None, want_kept: bool = False,
+                           workspace: torch.Tensor | None = None, stream=None,
+                           phases: int = PHASE_ALL) -> SampleOutputs:
+    """spec_verify_sample_filtered: the verify on top-k / top-p filtered laws.
+
+    top_k [B] int32 and top_p [B] float32 (device tensors, either may be None)
+    hold the filter of each batch row; out_kept [B, 2K+1] the kept counts.
+    """
+    return _verify_sample(target, draft, draft_tokens, uniforms, temperature, out_tokens, out_num_accepted,
+                          out_probs, want_probs, workspace, stream, phases, (top_k, top_p, out_kept, want_kept))
+
+
+def _verify_sample(target, draft, draft_tokens, uniforms, temperature, out_tokens, out_num_accepted, out_probs,
+                   want_probs, workspace, stream, phases, filt) -> SampleOutputs:
     if target.dim() != 3:
         raise ValueError("target must be [B, K+1, V]")
     B, K1, V = target.shape
@@ -178,23 +213,41 @@ def verify_sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch
         out_probs = torch.empty((B, K, 2), dtype=torch.float32, device=dev)
     if out_probs is not None:
         _check(out_probs, "out_probs", dev, torch.float32, (B, K, 2))
+    out_kept = None
+    if filt is not None:
+        top_k, top_p, out_kept, want_kept = filt
+        if top_k is not None:
+            _check(top_k, "top_k", dev, torch.int32, (B,))
+        if top_p is not None:
+            _check(top_p, "top_p", dev, torch.float32, (B,))
+        if out_kept is None and want_kept:
+            out_kept = torch.empty((B, 2 * K + 1), dtype=torch.int32, device=dev)
+        if out_kept is not None:
+            _check(out_kept, "out_kept", dev, torch.int32, (B, 2 * K + 1))
     sh = _stream_handle(stream, dev)
-    nbytes = sample_workspace_size(B, K, V)
+    nbytes = sample_workspace_size(B, K, V) if filt is None else sample_filtered_workspace_size(B, K, V)
     if nbytes == 0 and B > 0:
-        raise SpecVerifyError(-2, "spec_verify_sample_workspace_size")
+        raise SpecVerifyError(-9 if filt is not None and V > (1 << 24) else -2, "workspace size query")
     if workspace is None:
         workspace = workspace_for(dev, sh, nbytes)
     _check(workspace, "workspace", dev, torch.uint8)
     args = (_ptr(target), _ptr(draft), code, _ptr(draft_tokens), _ptr(uniforms), B, K, V, float(temperature),
             _ptr(out_tokens), _ptr(out_num_accepted), _ptr(out_probs), _ptr(workspace), workspace.numel(),
             ctypes.c_void_p(sh))
-    if phases == PHASE_ALL:
+    if filt is not None:
+        fargs = (_ptr(filt[0]), _ptr(filt[1]), _ptr(out_kept))
+        if phases == PHASE_ALL:
+            st, where = lib().spec_verify_sample_filtered(*args, *fargs), "spec_verify_sample_filtered"
+        else:
+            st, where = (lib().spec_verify_sample_filtered_phases(*args, *fargs, int(phases)),
+                         "spec_verify_sample_filtered_phases")
+    elif phases == PHASE_ALL:
         st, where = lib().spec_verify_sample(*args), "spec_verify_sample"
     else:
         st, where = lib().spec_verify_sample_phases(*args, int(phases)), "spec_verify_sample_phases"
     if st != 0:
         raise SpecVerifyError(st, where)
-    return SampleOutputs(out_tokens, out_num_accepted, out_probs)
+    return SampleOutputs(out_tokens, out_num_accepted, out_probs, out_kept)
 
 
 @dataclass

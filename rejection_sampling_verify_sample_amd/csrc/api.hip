@@ -12,7 +12,7 @@
 #define SPEC_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace sv {
-hipError_t launch_sample(const SampleParams& P, bool bf16, int phases, hipStream_t stream);
+hipError_t launch_sample(const SampleParams& P, bool bf16, bool filtered, int phases, hipStream_t stream);
 hipError_t launch_greedy(const GreedyParams& P, bool bf16, hipStream_t stream);
 hipError_t launch_philox(uint64_t seed, uint64_t round, int32_t B, int32_t K, float* out, hipStream_t stream);
 }  // namespace sv
@@ -78,6 +78,12 @@ SampleLayout sample_layout(int32_t B, int32_t K, int32_t V) {
   const size_t p2 = static_cast<size_t>(B) * L.NCmax;
   L.off_p2cm = off; off = align256(off + p2 * sizeof(float));
   L.off_p2cs = off; off = align256(off + p2 * sizeof(double));
+  // filtered entry point: one (reference, kept mass, threshold) per logit row
+  const size_t rows = static_cast<size_t>(B) * (2 * static_cast<size_t>(K) + 1);
+  L.off_fR = off; off = align256(off + rows * sizeof(float));
+  L.off_fS = off; off = align256(off + rows * sizeof(double));
+  L.off_fthr = off; off = align256(off + rows * sizeof(uint32_t));
+  L.off_infoT = off; off = align256(off + static_cast<size_t>(B) * 2 * sizeof(uint32_t));
   L.total = std::max<size_t>(off, 256);
   return L;
 }
@@ -117,12 +123,18 @@ SPEC_EXPORT const char* spec_status_string(int32_t status) {
     case SPEC_ERR_HIP: return "HIP launch failed";
     case SPEC_ERR_ALIGN: return "a pointer is not aligned to its element size";
     case SPEC_ERR_PHASE: return "phase mask outside 1..15";
+    case SPEC_ERR_FILTER_V: return "vocabulary too large for the filtered verify";
     default: return "unknown status";
   }
 }
 
 SPEC_EXPORT size_t spec_verify_sample_workspace_size(int32_t B, int32_t K, int32_t V) {
   if (!sample_shape_ok(B, K, V)) return 0;
+  return sample_layout(B, K, V).total;
+}
+
+SPEC_EXPORT size_t spec_verify_sample_filtered_workspace_size(int32_t B, int32_t K, int32_t V) {
+  if (!sample_shape_ok(B, K, V) || V > sv::kMaxFilterV) return 0;
   return sample_layout(B, K, V).total;
 }
 
@@ -136,8 +148,10 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
                                  const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t K,
                                  int32_t V, float temperature, int32_t* out_tokens, int32_t* out_num_accepted,
                                  float* out_probs, void* workspace, size_t workspace_bytes, void* stream,
-                                 int phases) {
+                                 int phases, bool filtered = false, const int32_t* top_k = nullptr,
+                                 const float* top_p = nullptr, int32_t* out_kept = nullptr) {
   if (!sample_shape_ok(B, K, V)) return SPEC_ERR_SHAPE;
+  if (filtered && V > sv::kMaxFilterV) return SPEC_ERR_FILTER_V;
   if (phases < 1 || phases > sv::kPhaseAll) return SPEC_ERR_PHASE;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
   if (!(std::isfinite(temperature) && temperature > 0.f)) return SPEC_ERR_TEMPERATURE;
@@ -150,6 +164,8 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
   if (!aligned(target_logits, es) || (K > 0 && !aligned(draft_logits, es)) ||
       (K > 0 && !aligned(draft_tokens, 4)) || !aligned(uniforms, 4) || !aligned(out_tokens, 4) ||
       !aligned(out_num_accepted, 4) || (out_probs && !aligned(out_probs, 4)) || !aligned(workspace, 8))
+    return SPEC_ERR_ALIGN;
+  if ((top_k && !aligned(top_k, 4)) || (top_p && !aligned(top_p, 4)) || (out_kept && !aligned(out_kept, 4)))
     return SPEC_ERR_ALIGN;
   const SampleLayout L = sample_layout(B, K, V);
   if (workspace_bytes < L.total) return SPEC_ERR_WORKSPACE;
@@ -177,7 +193,17 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
   P.p1_x = at<float>(workspace, L.off_p1x);
   P.p2_cm = at<float>(workspace, L.off_p2cm);
   P.p2_cs = at<double>(workspace, L.off_p2cs);
-  const hipError_t e = sv::launch_sample(P, dtype == SPEC_BF16, phases, static_cast<hipStream_t>(stream));
+  if (filtered) {
+    P.top_k = top_k;
+    P.top_p = top_p;
+    P.out_kept = out_kept;
+    P.f_R = at<float>(workspace, L.off_fR);
+    P.f_S = at<double>(workspace, L.off_fS);
+    P.f_thr = at<uint32_t>(workspace, L.off_fthr);
+    P.info_T = at<uint32_t>(workspace, L.off_infoT);
+  }
+  const hipError_t e =
+      sv::launch_sample(P, dtype == SPEC_BF16, filtered, phases, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 }  // namespace
@@ -195,6 +221,14 @@ SPEC_EXPORT spec_status spec_verify_sample(SPEC_SAMPLE_ARGS) {
 }
 SPEC_EXPORT spec_status spec_verify_sample_phases(SPEC_SAMPLE_ARGS, int32_t phases) {
   return verify_sample_phases(SPEC_SAMPLE_FWD, phases);
+}
+
+#define SPEC_FILTER_ARGS const int32_t *top_k, const float *top_p, int32_t *out_kept
+SPEC_EXPORT spec_status spec_verify_sample_filtered(SPEC_SAMPLE_ARGS, SPEC_FILTER_ARGS) {
+  return verify_sample_phases(SPEC_SAMPLE_FWD, sv::kPhaseAll, true, top_k, top_p, out_kept);
+}
+SPEC_EXPORT spec_status spec_verify_sample_filtered_phases(SPEC_SAMPLE_ARGS, SPEC_FILTER_ARGS, int32_t phases) {
+  return verify_sample_phases(SPEC_SAMPLE_FWD, phases, true, top_k, top_p, out_kept);
 }
 
 SPEC_EXPORT spec_status spec_verify_greedy(const void* target_logits, int32_t dtype, const int32_t* cand_tokens,

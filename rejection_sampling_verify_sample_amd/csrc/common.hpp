@@ -93,6 +93,15 @@ __device__ __forceinline__ SegRange seg_range(const T* row, int64_t V, int seg, 
 // 2^t on the hardware exponential unit (v_exp_f32; 2^-inf = 0).
 __device__ __forceinline__ float exp2_hw(float t) { return __builtin_amdgcn_exp2f(t); }
 
+// Order key of a logit: keys compare as unsigned integers exactly as the logits
+// compare as floats (-0 takes the key of +0, so equal values have equal keys;
+// -inf has the smallest key of any non-NaN value).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // ---------------------------------------------------------------- wave / block reductions
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -139,5 +148,35 @@ struct Online {
   }
   __device__ __forceinline__ void add(float x, float c) { s += exp2_hw(fmaf(x, c, -R)); }
 };
+
+// Combine the per-thread online states of a block. Result valid in thread 0:
+// m = block maximum, s = sum against fl(m * c). Each thread rescales its own
+// partial to the block reference in fp32 (exactly as a raise does); the sums
+// across lanes and waves are fp64.
+template <int BS>
+__device__ __forceinline__ void block_online(const Online& o, float c, float& m_out, double& s_out) {
+  constexpr int W = BS / 64;
+  __shared__ float sh_m[W];
+  __shared__ double sh_s[W];
+  const int w = threadIdx.x >> 6;
+  const float mw = wave_max(o.m);
+  if ((threadIdx.x & 63) == 0) sh_m[w] = mw;
+  __syncthreads();
+  float M = sh_m[0];
+#pragma unroll
+  for (int i = 1; i < W; ++i) M = fmaxf(M, sh_m[i]);
+  const float RM = M * c;
+  const float sl = (o.s > 0.f) ? o.s * exp2_hw(o.R - RM) : 0.f;
+  const double sw = wave_sum(static_cast<double>(sl));
+  if ((threadIdx.x & 63) == 0) sh_s[w] = sw;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) s += sh_s[i];
+    m_out = M;
+    s_out = s;
+  }
+}
 
 }  // namespace sv

@@ -29,6 +29,14 @@ struct SampleParams {
   double* info_S;          // [B, 2] softmax denominators of those rows
   float* p2_cm;            // [B*NCmax] per-chunk maximum (bonus draw)
   double* p2_cs;           // [B*NCmax] per-chunk mass (residual, or bonus mass against fl(max*c))
+  // top-k / top-p filtering (filtered entry point only; null / 0 otherwise)
+  const int32_t* top_k;    // [B] or null: k of each batch row (off unless 0 < k < V)
+  const float* top_p;      // [B] or null: p of each batch row (off unless p < 1)
+  int32_t* out_kept;       // [B, 2K+1] or null: kept entries of target rows 0..K, then draft rows 0..K-1
+  float* f_R;              // [B*(2K+1)] reference exponent of each row's masses (same row order as out_kept)
+  double* f_S;             // [B*(2K+1)] kept mass against f_R (0: the row has no finite logit)
+  uint32_t* f_thr;         // [B*(2K+1)] a row keeps the entries whose order key is >= this
+  uint32_t* info_T;        // [B, 2] thresholds of the rows the draw reads
 };
 
 // Kernels of the sampling verify, in stream order.
@@ -43,8 +51,14 @@ enum SamplePhase : int {
 struct SampleLayout {
   int32_t S1, S2, S1max, S2max;
   int32_t NCmax;
-  size_t off_p1m, off_p1s, off_p1x, off_info_n, off_info_R, off_info_S, off_p2cm, off_p2cs, total;
+  size_t off_p1m, off_p1s, off_p1x, off_info_n, off_info_R, off_info_S, off_p2cm, off_p2cs;
+  size_t off_fR, off_fS, off_fthr, off_infoT;  // filtered entry point only
+  size_t total;
 };
+
+// Filtered verify: masses are summed in fixed point, round(m * 2^40) per entry with
+// m <= 1, in 64-bit integers, so a row may hold at most 2^24 entries.
+constexpr int64_t kMaxFilterV = int64_t(1) << 24;
 
 // ---------------------------------------------------------------- greedy verify
 

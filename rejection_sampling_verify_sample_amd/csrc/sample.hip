@@ -26,6 +26,8 @@
 //                      chunk where u*Z falls, and one wave rereads that chunk (1 KB,
 //                      cache-hot) and finds the token with a lane prefix sum.
 // k_sample_accept runs the decisions alone, for callers that run the phases apart.
+#include <type_traits>
+
 #include "common.hpp"
 #include "params.hpp"
 
@@ -85,36 +87,6 @@ __device__ __forceinline__ void online_segment(const T* row, int64_t V, int seg,
     o.s += a;
   }
   if (seg == S - 1) online_scalar<BS>(row, r.head + ((V - r.head) / VEC) * VEC, V, c, o);
-}
-
-// Combine the per-thread online states of a block. Result valid in thread 0:
-// m = block maximum, s = sum against fl(m * c). Each thread rescales its own
-// partial to the block reference in fp32 (exactly as a raise does); the sums
-// across lanes and waves are fp64.
-template <int BS>
-__device__ __forceinline__ void block_online(const Online& o, float c, float& m_out, double& s_out) {
-  constexpr int W = BS / 64;
-  __shared__ float sh_m[W];
-  __shared__ double sh_s[W];
-  const int w = threadIdx.x >> 6;
-  const float mw = wave_max(o.m);
-  if ((threadIdx.x & 63) == 0) sh_m[w] = mw;
-  __syncthreads();
-  float M = sh_m[0];
-#pragma unroll
-  for (int i = 1; i < W; ++i) M = fmaxf(M, sh_m[i]);
-  const float RM = M * c;
-  const float sl = (o.s > 0.f) ? o.s * exp2_hw(o.R - RM) : 0.f;
-  const double sw = wave_sum(static_cast<double>(sl));
-  if ((threadIdx.x & 63) == 0) sh_s[w] = sw;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double s = 0.0;
-#pragma unroll
-    for (int i = 0; i < W; ++i) s += sh_s[i];
-    m_out = M;
-    s_out = s;
-  }
 }
 
 // Merge segment partials (m_j, s_j) of one row, in segment order.
@@ -270,24 +242,48 @@ struct Decision {
   float R[2 * 64];
   double S[2 * 64];
   float prob[2 * 64];
+  uint32_t T[2 * 64];  // key thresholds of the filtered rows
   int n, fault;
 };
 
+// Row j (< K: target row j, else draft row j - K) of batch row b in the filtered
+// row order: target rows 0..K, then draft rows 0..K-1.
+__device__ __forceinline__ int64_t filt_row(const SampleParams& P, int b, int j) {
+  return static_cast<int64_t>(b) * (2 * P.K + 1) + (j < P.K ? j : j + 1);
+}
+
+// FILT: the rows' laws are the top-k / top-p filtered ones, described by the
+// filter kernel's (reference, kept mass, key threshold) per row.
+template <bool FILT>
 __device__ __forceinline__ void decide_block(const SampleParams& P, const int b, const bool write, Decision& d) {
   const int K = P.K, S = P.S1;
   const int tid = threadIdx.x;
   if (tid < 2 * K) {
-    float M;
-    double Ssum;
     const int64_t r = static_cast<int64_t>(b) * 2 * K + tid;
-    merge_partials(P.p1_m + r * S, P.p1_s + r * S, S, P.c, M, Ssum);
-    const float R = M * P.c;
     const float xl = P.p1_x[r];
-    d.R[tid] = R;
-    d.S[tid] = Ssum;
-    const bool ok = isfinite(M) && Ssum > 0.0 && isfinite(Ssum) && !isnan(xl);
-    // p_i(x_i) (tid < K) or q_i(x_i) (tid >= K); NaN marks a row that cannot be used
-    d.prob[tid] = ok ? exp2_hw(fmaf(xl, P.c, -R)) / static_cast<float>(Ssum) : __builtin_nanf("");
+    if constexpr (FILT) {
+      const int64_t fr = filt_row(P, b, tid);
+      const float R = P.f_R[fr];
+      const double Ssum = P.f_S[fr];
+      const uint32_t thr = P.f_thr[fr];
+      d.R[tid] = R;
+      d.S[tid] = Ssum;
+      d.T[tid] = thr;
+      const bool ok = Ssum > 0.0 && isfinite(Ssum) && !isnan(xl);
+      // p'_i(x_i) or q'_i(x_i): 0 outside the row's kept set
+      d.prob[tid] = !ok ? __builtin_nanf("")
+                        : (order_key(xl) >= thr ? exp2_hw(fmaf(xl, P.c, -R)) / static_cast<float>(Ssum) : 0.f);
+    } else {
+      float M;
+      double Ssum;
+      merge_partials(P.p1_m + r * S, P.p1_s + r * S, S, P.c, M, Ssum);
+      const float R = M * P.c;
+      d.R[tid] = R;
+      d.S[tid] = Ssum;
+      const bool ok = isfinite(M) && Ssum > 0.0 && isfinite(Ssum) && !isnan(xl);
+      // p_i(x_i) (tid < K) or q_i(x_i) (tid >= K); NaN marks a row that cannot be used
+      d.prob[tid] = ok ? exp2_hw(fmaf(xl, P.c, -R)) / static_cast<float>(Ssum) : __builtin_nanf("");
+    }
   }
   __syncthreads();
   if (tid < 64) {
@@ -334,16 +330,29 @@ __device__ __forceinline__ void decide_block(const SampleParams& P, const int b,
       P.info_R[2 * b + 1] = d.R[K + n];
       P.info_S[2 * b] = d.S[n];
       P.info_S[2 * b + 1] = d.S[K + n];
+      if constexpr (FILT) {
+        P.info_T[2 * b] = d.T[n];
+        P.info_T[2 * b + 1] = d.T[K + n];
+      }
+    } else if (FILT && !fault) {  // the bonus draw from the filtered last row: no draft side
+      const int64_t fr = static_cast<int64_t>(b) * (2 * K + 1) + K;
+      P.info_R[2 * b] = P.f_R[fr];
+      P.info_R[2 * b + 1] = 0.f;
+      P.info_S[2 * b] = P.f_S[fr];
+      P.info_S[2 * b + 1] = 0.0;
+      P.info_T[2 * b] = P.f_thr[fr];
+      P.info_T[2 * b + 1] = 0xFFFFFFFFu;
     }
   }
 }
 
 constexpr int kAcceptBlock = 128;  // one thread per logit row (2K <= 128)
 
+template <bool FILT>
 __global__ __launch_bounds__(kAcceptBlock) void k_sample_accept(SampleParams P) {
   __shared__ Decision d;
   for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) {
-    decide_block(P, static_cast<int>(task), true, d);
+    decide_block<FILT>(P, static_cast<int>(task), true, d);
     __syncthreads();
   }
 }
@@ -357,6 +366,21 @@ struct Residual {
     const float pt = exp2_hw(fmaf(xt, c, -Rt)) * it;
     const float pq = exp2_hw(fmaf(xq, c, -Rq)) * iq;
     return fmaxf(pt - pq, 0.f);
+  }
+  __device__ __forceinline__ float target(float xt) const { return exp2_hw(fmaf(xt, c, -Rt)) * it; }
+};
+
+// The same on the filtered laws: an entry outside a row's kept set (order key
+// below the row's threshold) has weight 0 on that side.
+struct ResidualF {
+  float c, Rt, Rq, it, iq;
+  uint32_t kt, kq;
+  __device__ __forceinline__ float target(float xt) const {
+    return order_key(xt) >= kt ? exp2_hw(fmaf(xt, c, -Rt)) * it : 0.f;
+  }
+  __device__ __forceinline__ float operator()(float xt, float xq) const {
+    const float pq = order_key(xq) >= kq ? exp2_hw(fmaf(xq, c, -Rq)) * iq : 0.f;
+    return fmaxf(target(xt) - pq, 0.f);
   }
 };
 
@@ -413,12 +437,29 @@ __device__ __forceinline__ Residual residual_of(const SampleParams& P, int b) {
   return r;
 }
 
+__device__ __forceinline__ float inv_or_zero(double s) { return s > 0.0 ? static_cast<float>(1.0 / s) : 0.f; }
+
+__device__ __forceinline__ ResidualF residual_of_f(const SampleParams& P, int b) {
+  ResidualF r;
+  r.c = P.c;
+  r.Rt = P.info_R[2 * b];
+  r.Rq = P.info_R[2 * b + 1];
+  r.it = inv_or_zero(P.info_S[2 * b]);
+  r.iq = inv_or_zero(P.info_S[2 * b + 1]);
+  r.kt = P.info_T[2 * b];
+  r.kq = P.info_T[2 * b + 1];
+  return r;
+}
+
+template <bool FILT>
+using ResOf = typename std::conditional<FILT, ResidualF, Residual>::type;
+
 // Draw weights of vector chunk c for this lane: the VEC weights of the lane's
 // vector (zeros past the row), for the residual (two rows) or the bonus row
 // (against the reference R).
-template <typename T>
+template <typename T, typename Res>
 __device__ __forceinline__ void chunk_lane_weights(const T* tr, const T* dr, bool paired, const Chunks& ch, int c,
-                                                   bool bonus, const Residual& res, float cscale, float R,
+                                                   bool bonus, const Res& res, float cscale, float R,
                                                    float (&w)[Elem<T>::kVec]) {
   constexpr int VEC = Elem<T>::kVec;
   const int lane = threadIdx.x & 63;
@@ -449,9 +490,9 @@ __device__ __forceinline__ void chunk_lane_weights(const T* tr, const T* dr, boo
 // The mass of scalar chunk c (the head or the tail, fewer than VEC elements),
 // computed by one wave; lane 0 stores (chunk max, chunk mass). Bonus chunks are
 // summed against fl(chunk max * c); residual chunks store max -inf.
-template <typename T>
+template <typename T, typename Res>
 __device__ __forceinline__ void wave_scalar_chunk_mass(const SampleParams& P, const T* tr, const T* dr,
-                                                       const Chunks& ch, int c, bool bonus, const Residual& res,
+                                                       const Chunks& ch, int c, bool bonus, const Res& res,
                                                        float* cm, double* cs) {
   const int lane = threadIdx.x & 63;
   int64_t lo, hi;
@@ -479,10 +520,10 @@ __device__ __forceinline__ void wave_scalar_chunk_mass(const SampleParams& P, co
 // stores (chunk max, chunk mass).
 constexpr int kChunksPerWave = 1;
 
-template <typename T>
+template <typename T, typename Res>
 __device__ __forceinline__ void wave_vector_chunks_mass(const SampleParams& P, const T* tr, const T* dr,
                                                         bool paired, const Chunks& ch, int c, int cstride, int cend,
-                                                        bool bonus, const Residual& res, float* cm, double* cs) {
+                                                        bool bonus, const Res& res, float* cm, double* cs) {
   constexpr int VEC = Elem<T>::kVec;
   constexpr int CU = kChunksPerWave;
   const int lane = threadIdx.x & 63;
@@ -537,34 +578,53 @@ __device__ __forceinline__ void wave_vector_chunks_mass(const SampleParams& P, c
 // Pass 2 over the chunks of segment `seg`. With FUSE_ACCEPT the workgroup first
 // takes the accept decisions of its batch row itself (segment 0 also writes them
 // out), so no separate accept launch precedes it.
-template <typename T, bool FUSE_ACCEPT>
+// FILT: the filtered laws; the bonus draw is then a residual with no draft side
+// (its weights are the kept target masses), so no chunk maxima are needed.
+template <typename T, bool FUSE_ACCEPT, bool FILT>
 __device__ __forceinline__ void sample_mass_task(const SampleParams& P, const int64_t task) {
   const int K = P.K, S = P.S2;
   const int seg = static_cast<int>(task % S);
   const int b = static_cast<int>(task / S);
   __shared__ Decision d;
-  Residual res{};
+  ResOf<FILT> res{};
   int n;
   if (FUSE_ACCEPT) {
-    decide_block(P, b, seg == 0, d);  // with K = 0: n = 0, the bonus draw
+    decide_block<FILT>(P, b, seg == 0, d);  // with K = 0: n = 0, the bonus draw
     n = d.n;
     if (d.fault) return;
     if (n < K) {
       res.c = P.c;
       res.Rt = d.R[n];
       res.Rq = d.R[K + n];
-      res.it = static_cast<float>(1.0 / d.S[n]);
-      res.iq = static_cast<float>(1.0 / d.S[K + n]);
+      if constexpr (FILT) {
+        res.it = inv_or_zero(d.S[n]);
+        res.iq = inv_or_zero(d.S[K + n]);
+        res.kt = d.T[n];
+        res.kq = d.T[K + n];
+      } else {
+        res.it = static_cast<float>(1.0 / d.S[n]);
+        res.iq = static_cast<float>(1.0 / d.S[K + n]);
+      }
+    } else if constexpr (FILT) {
+      const int64_t fr = static_cast<int64_t>(b) * (2 * K + 1) + K;
+      res.c = P.c;
+      res.Rt = P.f_R[fr];
+      res.it = inv_or_zero(P.f_S[fr]);
+      res.kt = P.f_thr[fr];
+      res.Rq = 0.f;
+      res.iq = 0.f;
+      res.kq = 0xFFFFFFFFu;
     }
   } else {
     if (!draw_row(P, b, n)) return;  // fault: nothing to draw
-    if (n < K) res = residual_of(P, b);
+    if constexpr (FILT) res = residual_of_f(P, b);
+    else if (n < K) res = residual_of(P, b);
   }
-  const bool bonus = (n == K);
+  const bool bonus = !FILT && (n == K);
   const T* tr = target_row<T>(P, b, n);
-  const T* dr = bonus ? tr : draft_row<T>(P, b, n);
+  const T* dr = (n == K) ? tr : draft_row<T>(P, b, n);
   const Chunks ch = chunks_of(tr, P.V);
-  const bool paired = bonus || head_elems(dr, P.V) == ch.h;
+  const bool paired = (n == K) || head_elems(dr, P.V) == ch.h;
   float* cm = P.p2_cm + static_cast<int64_t>(b) * P.NCmax;
   double* cs = P.p2_cs + static_cast<int64_t>(b) * P.NCmax;
   // vector chunks [c0, c1) of this segment; segment 0 adds the head, the last one the tail
@@ -578,11 +638,11 @@ __device__ __forceinline__ void sample_mass_task(const SampleParams& P, const in
     wave_vector_chunks_mass<T>(P, tr, dr, paired, ch, c, W, c1, bonus, res, cm, cs);
 }
 
-template <typename T, bool FUSE_ACCEPT>
+template <typename T, bool FUSE_ACCEPT, bool FILT>
 __global__ __launch_bounds__(kBlock) void k_sample_mass(SampleParams P) {
   const int64_t ntask = static_cast<int64_t>(P.B) * P.S2;
   for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
-    sample_mass_task<T, FUSE_ACCEPT>(P, task);
+    sample_mass_task<T, FUSE_ACCEPT, FILT>(P, task);
     __syncthreads();  // shared memory is reused by the next task
   }
 }
@@ -640,7 +700,7 @@ __device__ int64_t block_search(int64_t lo, int64_t hi, double tau, const W& w) 
   return lp >= 0 ? lp : lo;
 }
 
-template <typename T>
+template <typename T, bool FILT>
 __device__ __forceinline__ void sample_draw_task(const SampleParams& P, const int64_t task) {
   constexpr int VEC = Elem<T>::kVec;
   const int K = P.K;
@@ -648,9 +708,10 @@ __device__ __forceinline__ void sample_draw_task(const SampleParams& P, const in
   const int tid = threadIdx.x;
   int n;
   if (!draw_row(P, b, n)) return;  // the accept pass already wrote the fault outputs
-  const bool bonus = (n == K);
+  const bool is_bonus = (n == K);
+  const bool bonus = !FILT && is_bonus;  // chunk masses against chunk maxima (unfiltered bonus only)
   const T* tr = target_row<T>(P, b, n);
-  const T* dr = bonus ? tr : draft_row<T>(P, b, n);
+  const T* dr = is_bonus ? tr : draft_row<T>(P, b, n);
   const Chunks ch = chunks_of(tr, P.V);
   const int NC = ch.count();
   const float* cm = P.p2_cm + static_cast<int64_t>(b) * P.NCmax;
@@ -691,7 +752,8 @@ __device__ __forceinline__ void sample_draw_task(const SampleParams& P, const in
   // 0: search a chunk; 1: zero residual mass -> draw from p_n; 2: bonus row fault
   int mode = 0;
   if (bonus && !(isfinite(M) && Z > 0.0 && isfinite(Z))) mode = 2;
-  else if (!bonus && !(Z > 0.0 && isfinite(Z))) mode = 1;
+  else if (FILT && is_bonus && !(Z > 0.0 && isfinite(Z))) mode = 2;
+  else if (!is_bonus && !(Z > 0.0 && isfinite(Z))) mode = 1;
   int32_t* ot = P.out_tokens + static_cast<int64_t>(b) * (K + 1);
   if (mode == 2) {
     for (int i = tid; i <= K; i += kBlock) ot[i] = -1;
@@ -699,10 +761,11 @@ __device__ __forceinline__ void sample_draw_task(const SampleParams& P, const in
     return;
   }
   if (mode == 1) {
-    // zero residual mass: draw from p_n over the whole row
-    const Residual res = residual_of(P, b);
-    const float c = P.c, Rt = res.Rt, it = res.it;
-    auto pw = [&](int64_t e) { return exp2_hw(fmaf(Elem<T>::get(tr, e), c, -Rt)) * it; };
+    // zero residual mass: draw from p_n (p'_n when filtered) over the whole row
+    ResOf<FILT> res;
+    if constexpr (FILT) res = residual_of_f(P, b);
+    else res = residual_of(P, b);
+    auto pw = [&](int64_t e) { return res.target(Elem<T>::get(tr, e)); };
     float a = 0.f;
     for (int64_t e = tid; e < P.V; e += kBlock) a += pw(e);
     const double Zp = block_sum<kBlock>(static_cast<double>(a));
@@ -750,7 +813,9 @@ __device__ __forceinline__ void sample_draw_task(const SampleParams& P, const in
     tau *= exp2(RM - static_cast<double>(R));  // into the chunk's own reference
   }
   if (tid >= 64) return;  // one wave searches the chunk
-  const Residual res = bonus ? Residual{} : residual_of(P, b);
+  ResOf<FILT> res{};
+  if constexpr (FILT) res = residual_of_f(P, b);
+  else if (!bonus) res = residual_of(P, b);
   int64_t k;
   if (jstar == 0 || jstar == ch.nvc + 1) {
     int64_t lo, hi;
@@ -767,7 +832,7 @@ __device__ __forceinline__ void sample_draw_task(const SampleParams& P, const in
     }
     k = kf >= 0 ? kf : (kl >= 0 ? kl : lo);
   } else {
-    const bool paired = bonus || head_elems(dr, P.V) == ch.h;
+    const bool paired = is_bonus || head_elems(dr, P.V) == ch.h;
     float w[VEC];
     chunk_lane_weights<T>(tr, dr, paired, ch, jstar, bonus, res, P.c, R, w);
     float ls = 0.f;
@@ -808,10 +873,10 @@ __device__ __forceinline__ void sample_draw_task(const SampleParams& P, const in
   ot[n] = static_cast<int32_t>(k);
 }
 
-template <typename T>
+template <typename T, bool FILT>
 __global__ __launch_bounds__(kBlock) void k_sample_draw(SampleParams P) {
   for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) {
-    sample_draw_task<T>(P, task);
+    sample_draw_task<T, FILT>(P, task);
     __syncthreads();  // shared memory is reused by the next task
   }
 }
@@ -824,27 +889,38 @@ constexpr int64_t kMaxGrid = 1 << 20;
 
 inline dim3 grid_for(int64_t tasks) { return dim3(static_cast<uint32_t>(tasks < kMaxGrid ? tasks : kMaxGrid)); }
 
-template <typename T>
+hipError_t launch_filter_rows(const SampleParams& P, bool bf16, hipStream_t stream);
+
+// FILT: the row-statistics phase is the filter kernel (all 2K+1 rows of each batch row).
+template <typename T, bool FILT>
 static hipError_t launch_sample_t(const SampleParams& P, int phases, hipStream_t stream) {
-  if ((phases & kPhaseRowStats) && P.K > 0) {
-    const int64_t g = static_cast<int64_t>(P.B) * 2 * P.K * P.S1;
-    hipLaunchKernelGGL(k_sample_rowstats<T>, grid_for(g), dim3(kRowBlock), 0, stream, P);
+  if (phases & kPhaseRowStats) {
+    if (FILT) {
+      const hipError_t e = launch_filter_rows(P, sizeof(T) == 2, stream);
+      if (e != hipSuccess) return e;
+    } else if (P.K > 0) {
+      const int64_t g = static_cast<int64_t>(P.B) * 2 * P.K * P.S1;
+      hipLaunchKernelGGL(k_sample_rowstats<T>, grid_for(g), dim3(kRowBlock), 0, stream, P);
+    }
   }
   const int64_t gm = static_cast<int64_t>(P.B) * P.S2;
   if ((phases & kPhaseAccept) && (phases & kPhaseMass)) {
-    hipLaunchKernelGGL((k_sample_mass<T, true>), grid_for(gm), dim3(kBlock), 0, stream, P);
+    hipLaunchKernelGGL((k_sample_mass<T, true, FILT>), grid_for(gm), dim3(kBlock), 0, stream, P);
   } else if (phases & kPhaseAccept) {
-    hipLaunchKernelGGL(k_sample_accept, grid_for(P.B), dim3(kAcceptBlock), 0, stream, P);
+    hipLaunchKernelGGL(k_sample_accept<FILT>, grid_for(P.B), dim3(kAcceptBlock), 0, stream, P);
   } else if (phases & kPhaseMass) {
-    hipLaunchKernelGGL((k_sample_mass<T, false>), grid_for(gm), dim3(kBlock), 0, stream, P);
+    hipLaunchKernelGGL((k_sample_mass<T, false, FILT>), grid_for(gm), dim3(kBlock), 0, stream, P);
   }
-  if (phases & kPhaseDraw) hipLaunchKernelGGL(k_sample_draw<T>, grid_for(P.B), dim3(kBlock), 0, stream, P);
+  if (phases & kPhaseDraw)
+    hipLaunchKernelGGL((k_sample_draw<T, FILT>), grid_for(P.B), dim3(kBlock), 0, stream, P);
   return hipGetLastError();
 }
 
-// phases: a mask of SamplePhase bits, run in order.
-hipError_t launch_sample(const SampleParams& P, bool bf16, int phases, hipStream_t stream) {
-  return bf16 ? launch_sample_t<bf16_t>(P, phases, stream) : launch_sample_t<float>(P, phases, stream);
+// phases: a mask of SamplePhase bits, run in order; filtered: the top-k / top-p verify.
+hipError_t launch_sample(const SampleParams& P, bool bf16, bool filtered, int phases, hipStream_t stream) {
+  if (filtered)
+    return bf16 ? launch_sample_t<bf16_t, true>(P, phases, stream) : launch_sample_t<float, true>(P, phases, stream);
+  return bf16 ? launch_sample_t<bf16_t, false>(P, phases, stream) : launch_sample_t<float, false>(P, phases, stream);
 }
 
 }  // namespace sv

@@ -114,3 +114,88 @@ def compare_greedy(res: "oracle.GreedyResult", gpu_tokens, gpu_len, gpu_best) ->
     assert bad.size == 0, (f"greedy mismatch in rows {bad[:8].tolist()}: oracle {res.tokens[bad[0]].tolist()} "
                            f"L={res.accept_len[bad[0]]} best={res.best[bad[0]]} vs GPU {gpu_tokens[bad[0]].tolist()} "
                            f"L={gpu_len[bad[0]]} best={gpu_best[bad[0]]}")
+
+
+# --------------------------------------------------------------------------- filtered verify
+
+def kept_count_candidates(row: np.ndarray, kept: int) -> set:
+    """Kept counts a threshold one value group above or below the oracle's would give."""
+    x = np.asarray(row, dtype=np.float64)
+    vals, counts = np.unique(x, return_counts=True)
+    ge = np.cumsum(counts[::-1])            # entries >= each distinct value, high to low
+    hits = np.nonzero(ge == kept)[0]
+    if hits.size == 0:
+        return {kept}
+    j = int(hits[0])
+    return {int(ge[i]) for i in (j - 1, j, j + 1) if 0 <= i < ge.size}
+
+
+def _filtered_draw_weights(target_b, draft_b, T, k, p, n, K):
+    def law(row):
+        return oracle.filtered_softmax64(row, T, oracle.filter_keep(row, T, k, p).keep)
+    pt = law(target_b[n])
+    if n == K:
+        return pt
+    w = np.maximum(0.0, pt - law(draft_b[n]))
+    return w if np.sum(w) > 0 else pt
+
+
+def compare_filtered(target, draft, tokens_in, uniforms, T, top_k, top_p, res: "oracle.FilteredResult", gpu_tokens,
+                     gpu_n, gpu_probs=None, gpu_kept=None, window: float = WINDOW) -> ParityReport:
+    """The parity rule on the filtered verify, plus the kept counts of every row.
+
+    Kept counts are integers: bit-exact wherever the row's top-p cut is outside
+    the window (top-k alone involves no rounding at all); inside it, the GPU's
+    count must belong to a threshold one value group away from the oracle's.
+    Probabilities are compared where both rows' cuts are outside the window.
+    Rows whose walk consulted a cut inside the window are checked for validity
+    (prefix of the draft tokens, token in range) only.
+    """
+    B, K = tokens_in.shape
+    rep = ParityReport(rows=B)
+    fm = res.filter_margin
+    if gpu_kept is not None:
+        for b in range(B):
+            for j in range(2 * K + 1):
+                row = target[b, j] if j <= K else draft[b, j - K - 1]
+                if fm[b, j] >= window:
+                    assert gpu_kept[b, j] == res.kept[b, j], (
+                        f"kept count of row ({b},{j}): oracle {res.kept[b, j]} vs GPU {gpu_kept[b, j]} "
+                        f"(k={top_k[b]} p={top_p[b]} margin {fm[b, j]:.2e})")
+                else:
+                    assert int(gpu_kept[b, j]) in kept_count_candidates(row, int(res.kept[b, j])), (b, j)
+    if gpu_probs is not None:
+        op = res.probs
+        assert np.array_equal(np.isnan(op), np.isnan(gpu_probs)), "probability NaN pattern differs"
+        sure = (fm[:, :K] >= window) & (fm[:, K + 1:] >= window)
+        sel = np.isfinite(op) & sure[:, :, None]
+        ok = np.isclose(gpu_probs[sel], op[sel], rtol=PROB_RTOL, atol=PROB_ATOL)
+        assert ok.all(), f"filtered probabilities differ beyond tolerance at {np.argwhere(sel)[~ok][:5]}"
+    margin = res.min_margin()
+    small_z = np.nan_to_num(res.residual_mass, nan=1.0) < window
+    cut_amb = np.where(res.consulted, fm < window, False).any(axis=1)
+    for b in range(B):
+        on, gn = int(res.n_accepted[b]), int(gpu_n[b])
+        same = on == gn and np.array_equal(res.tokens[b], gpu_tokens[b])
+        if not (margin[b] < window or small_z[b]):
+            assert same, (f"row {b}: oracle n={on} tokens={res.tokens[b].tolist()} vs GPU n={gn} "
+                          f"tokens={gpu_tokens[b].tolist()} (k={top_k[b]} p={top_p[b]}, margin {margin[b]:.3e})")
+            continue
+        rep.ambiguous += 1
+        if same:
+            rep.ambiguous_agree += 1
+            continue
+        assert on >= 0 and gn >= 0, f"row {b}: fault status differs ({on} vs {gn})"
+        i = min(on, gn)
+        assert np.array_equal(res.tokens[b, :i], gpu_tokens[b, :i])
+        assert 0 <= gpu_tokens[b, gn] < target.shape[-1] and np.all(gpu_tokens[b, gn + 1:] == -1)
+        if cut_amb[b]:
+            continue
+        if on != gn:
+            assert res.accept_margin[b, i] < window, f"row {b}: accept decision at {i} differs outside the window"
+            continue
+        n = on
+        w = _filtered_draw_weights(target[b], draft[b], T, int(top_k[b]), float(top_p[b]), n, K)
+        d = _interval_distance(w, float(uniforms[b, n, 1]), int(gpu_tokens[b, n]))
+        assert d < window, f"row {b}: GPU token {gpu_tokens[b, n]} is {d:.3e} from u*Z"
+    return rep

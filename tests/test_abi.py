@@ -15,6 +15,7 @@ import rejection_sampling_verify_sample_amd as rsv
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN, ERR_PHASE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+ERR_FILTER_V = -9
 P = 0x10000  # aligned, never dereferenced
 
 
@@ -34,7 +35,7 @@ def test_library_is_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 11, names
     L = ctypes.CDLL(rsv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
@@ -92,6 +93,38 @@ def test_phase_entry_point_checks_arguments():
     assert fn(*a, 2) == ERR_SHAPE
 
 
+def filtered(**kw):
+    a = dict(target=P, draft=P, dtype=1, tokens=P, uniforms=P, B=4, K=3, V=100, T=1.0, out_tokens=P, out_n=P,
+             out_probs=None, ws=P, ws_bytes=1 << 30, stream=None, top_k=P, top_p=P, out_kept=P)
+    a.update(kw)
+    return rsv.lib().spec_verify_sample_filtered(a["target"], a["draft"], a["dtype"], a["tokens"], a["uniforms"],
+                                                 a["B"], a["K"], a["V"], a["T"], a["out_tokens"], a["out_n"],
+                                                 a["out_probs"], a["ws"], a["ws_bytes"], a["stream"], a["top_k"],
+                                                 a["top_p"], a["out_kept"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(V=(1 << 24) + 1), ERR_FILTER_V), (dict(V=(1 << 30) + 1), ERR_SHAPE), (dict(K=65), ERR_SHAPE),
+    (dict(T=0.0), ERR_TEMP), (dict(dtype=2), ERR_DTYPE), (dict(target=None), ERR_NULL),
+    (dict(top_k=P + 2), ERR_ALIGN), (dict(top_p=P + 1), ERR_ALIGN), (dict(out_kept=P + 2), ERR_ALIGN),
+    (dict(ws_bytes=16), ERR_WS), (dict(B=0), OK),
+    # the filters and the kept counts are optional: with every check passed, only the workspace fails
+    (dict(top_k=None, top_p=None, out_kept=None, ws_bytes=16), ERR_WS),
+])
+def test_filtered_argument_checks(kw, expect):
+    assert filtered(**kw) == expect
+
+
+def test_filtered_phases_checks_arguments():
+    fn = rsv.lib().spec_verify_sample_filtered_phases
+    args = [P, P, 1, P, P, 4, 3, 100, 1.0, P, P, None, P, 1 << 30, None, P, P, None]
+    for bad in (0, 16):
+        assert fn(*args, bad) == ERR_PHASE
+    a = list(args)
+    a[7] = (1 << 24) + 1
+    assert fn(*a, 1) == ERR_FILTER_V
+
+
 def test_sample_k0_needs_no_draft():
     # K = 0 draws from the bonus row only: draft pointers may be null; still fails on the workspace size
     assert sample(K=0, draft=None, tokens=None, ws_bytes=0) == ERR_WS
@@ -122,6 +155,8 @@ def test_workspace_sizes():
     assert rsv.sample_workspace_size(0, 8, 100) > 0
     assert rsv.sample_workspace_size(-1, 8, 100) == 0
     assert rsv.sample_workspace_size(4, 65, 100) == 0
+    assert rsv.sample_filtered_workspace_size(64, 8, 128256) > 0
+    assert rsv.sample_filtered_workspace_size(4, 2, (1 << 24) + 1) == 0
     assert rsv.greedy_workspace_size(32, 7, 5, 32000) > 0
     assert rsv.greedy_workspace_size(32, 7, 1, 32000) == 0
     # the size depends on the shape only (never on a tuning override)
@@ -133,7 +168,7 @@ def test_workspace_sizes():
 
 
 def test_status_strings():
-    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN, ERR_PHASE, 99):
+    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN, ERR_PHASE, ERR_FILTER_V, 99):
         assert isinstance(rsv.status_string(s), str) and rsv.status_string(s)
 
 

@@ -1,0 +1,185 @@
+"""HIP top-k / top-p filtered verify vs the CPU oracle (needs an MI355X).
+
+Inputs are the seeded synthetic workloads (workloads/) with per-batch-row filter
+parameters (make_filter_params: a mix of k in {0,1,2,5,20,50,200,1000,V-1,V}
+and p in {1,0.99,0.95,0.9,0.8,0.5,0.2}); the oracle receives the same arrays.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rejection_sampling_verify_sample_amd as rsv
+from golden_io import filtered_case, load
+from parity import ParityReport, compare_filtered
+from workloads import make_filter_params, make_sample_inputs
+from workloads.torch_io import sample_tensors
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+DEV = "cuda:0"
+REPORT_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+
+
+def log(msg):
+    print(f"[gpu-filtered] {msg}", flush=True)
+
+
+def run_gpu(t, k, p, want_probs=True):
+    kt = None if k is None else torch.from_numpy(np.asarray(k, dtype=np.int32)).to(DEV)
+    pt = None if p is None else torch.from_numpy(np.asarray(p, dtype=np.float32)).to(DEV)
+    out = rsv.verify_sample_filtered(t["target"], t["draft"], t["draft_tokens"], t["uniforms"], t["temperature"],
+                                     kt, pt, want_probs=want_probs, want_kept=True)
+    torch.cuda.synchronize()
+    return (out.tokens.cpu().numpy(), out.num_accepted.cpu().numpy(),
+            out.probs.cpu().numpy() if want_probs else None, out.kept.cpu().numpy())
+
+
+def check(s, k, p, name="") -> ParityReport:
+    log(f"case {s.name} {name}")
+    tok, n, probs, kept = run_gpu(sample_tensors(s, DEV), k, p)
+    tgt, drf = s.target_f32(), s.draft_f32()
+    B = s.shape[0]
+    kk = np.zeros(B, dtype=np.int32) if k is None else np.asarray(k)
+    pp = np.ones(B, dtype=np.float32) if p is None else np.asarray(p)
+    res = oracle.oracle_sample_filtered(tgt, drf, s.draft_tokens, s.uniforms, s.temperature, kk, pp)
+    rep = compare_filtered(tgt, drf, s.draft_tokens, s.uniforms, s.temperature, kk, pp, res, tok, n, probs, kept)
+    log(f"  {rep.summary()}")
+    return rep
+
+
+def save_report(name, rep: ParityReport):
+    os.makedirs(REPORT_DIR, exist_ok=True)
+    with open(os.path.join(REPORT_DIR, "parity_report.jsonl"), "a") as f:
+        f.write(json.dumps({"case": "filtered " + name, "rows": rep.rows, "ambiguous": rep.ambiguous,
+                            "ambiguous_agree": rep.ambiguous_agree}) + "\n")
+
+
+# ------------------------------------------------------------------ hand-worked rounds
+
+@pytest.mark.parametrize("case", load("filtered_worked.json")["cases"], ids=lambda c: c["name"])
+def test_golden_filtered_on_gpu(case):
+    c = filtered_case(case)
+    log(f"golden {c['name']}")
+    t = dict(target=torch.from_numpy(c["target"].astype(np.float32)).to(DEV),
+             draft=torch.from_numpy(c["draft"].astype(np.float32)).to(DEV),
+             draft_tokens=torch.from_numpy(c["tokens"]).to(DEV),
+             uniforms=torch.from_numpy(c["uniforms"]).to(DEV), temperature=c["T"])
+    tok, n, probs, kept = run_gpu(t, c["top_k"], c["top_p"])
+    assert tok.tolist() == c["expect_tokens"].tolist()
+    assert n.tolist() == c["expect_n"].tolist()
+    assert kept.tolist() == c["expect_kept"].tolist()
+    res = oracle.oracle_sample_filtered(c["target"], c["draft"], c["tokens"], c["uniforms"], c["T"], c["top_k"],
+                                        c["top_p"])
+    assert np.allclose(probs, res.probs, rtol=1e-4, atol=1e-5, equal_nan=True), (probs, res.probs)
+
+
+# ------------------------------------------------------------------ workloads with mixed filters
+
+CASES = [
+    (1, dict(B=6, V=5000)),
+    (2, dict()),                          # full size: B=8 K=5 V=32000 bf16 T=0.7
+    (3, dict(B=6, V=20001)),              # bf16, odd V: every 16-byte phase
+    (4, dict(B=8, V=40003)),              # fp32 peaked and flat rows, three radix digits
+    (3, dict(B=5, K=0, V=1000)),          # K = 0: the bonus row only
+    (2, dict(B=3, K=64, V=3000)),         # the largest K
+    (1, dict(B=4, K=2, V=7)),             # V smaller than a vector
+]
+
+
+@pytest.mark.parametrize("cfg,kw", CASES, ids=lambda x: str(x))
+def test_filtered_parity_mixed(cfg, kw):
+    rep = ParityReport()
+    for rnd in range(2):
+        s = make_sample_inputs(cfg, rnd, **kw)
+        B, _, V = s.shape
+        k, p = make_filter_params(B, seed=rnd, V=V)
+        rep.merge(check(s, k, p))
+    save_report(f"cfg{cfg} {kw}", rep)
+
+
+def test_filtered_parity_full_size_k50_p09():
+    """The full B=64 K=8 V=128256 bf16 round with top-k 50, top-p 0.9 on every row, all rows compared."""
+    s = make_sample_inputs(3, 0)
+    k, p = make_filter_params(64, top_k=50, top_p=0.9)
+    rep = check(s, k, p, "k50 p0.9")
+    save_report("cfg3 full k50 p0.9", rep)
+
+
+@pytest.mark.parametrize("k,p", [(None, None), (0, 1.0), (1, 1.0), (0, 1e-30), (0, float("nan")), (2000, 0.999),
+                                 (7, 0.3), (0, 0.95)], ids=lambda x: str(x))
+def test_filter_settings(k, p):
+    s = make_sample_inputs(1, 3, B=6, V=2000)
+    B = 6
+    kk = None if k is None else np.full(B, k, dtype=np.int32)
+    pp = None if p is None else np.full(B, p, dtype=np.float32)
+    check(s, kk, pp, f"k={k} p={p}")
+
+
+# ------------------------------------------------------------------ exact keys, ties and masks
+
+def _f32_tensors(tgt, drf, toks, uni, T=1.0):
+    return dict(target=torch.from_numpy(np.ascontiguousarray(tgt, dtype=np.float32)).to(DEV),
+                draft=torch.from_numpy(np.ascontiguousarray(drf, dtype=np.float32)).to(DEV),
+                draft_tokens=torch.from_numpy(np.asarray(toks, dtype=np.int32)).to(DEV),
+                uniforms=torch.from_numpy(np.asarray(uni, dtype=np.float32)).to(DEV), temperature=T)
+
+
+def test_top_k_resolves_adjacent_float_keys():
+    """fp32 logits one ulp apart (all three radix digits matter) and bf16-style ties: top-k counts exact."""
+    log("adjacent keys")
+    rng = np.random.default_rng(3)
+    B, K, V = 6, 1, 4099
+    base = np.float32(1.5)
+    vals = [base]
+    for _ in range(V - 1):
+        vals.append(np.nextafter(vals[-1], np.float32(2), dtype=np.float32))
+    vals = np.array(vals, dtype=np.float32)
+    tgt = np.empty((B, K + 1, V), dtype=np.float32)
+    for b in range(B):
+        for j in range(K + 1):
+            tgt[b, j] = rng.permutation(vals)
+    tgt[1] = np.round(tgt[1] * 4) / 4          # many ties
+    tgt[2, :, : V // 2] = -np.inf              # masked half
+    drf = tgt[:, :K].copy()
+    toks = rng.integers(0, V, (B, K))
+    uni = np.full((B, K + 1, 2), 0.5, dtype=np.float32)
+    ks = np.array([1, 37, 4098, 1000, 3000, 2], dtype=np.int32)
+    tok, n, _, kept = run_gpu(_f32_tensors(tgt, drf, toks, uni), ks, None, want_probs=False)
+    res = oracle.oracle_sample_filtered(tgt, drf, toks, uni, 1.0, ks, np.ones(B, dtype=np.float32))
+    assert np.array_equal(kept, res.kept), (kept, res.kept)
+    assert np.array_equal(n, res.n_accepted)
+
+
+def test_faults_and_empty_rows_filtered():
+    log("faults")
+    V, K = 300, 2
+    rng = np.random.default_rng(4)
+    tgt = rng.normal(0, 1, (4, K + 1, V))
+    drf = tgt[:, :K] + rng.normal(0, 0.3, (4, K, V))
+    toks = np.array([[3, 4], [V, 0], [1, 2], [5, 6]], dtype=np.int32)
+    uni = np.zeros((4, K + 1, 2), dtype=np.float32)
+    drf[2, 1, :] = -np.inf                   # consulted (r = 0 accepts at 0 when alpha > 0) -> fault, or not
+    tgt[3, K, :] = -np.inf
+    drf[3] = tgt[3, :K]
+    t = _f32_tensors(tgt, drf, toks, uni)
+    k = np.array([5, 5, 0, 0], dtype=np.int32)
+    p = np.array([1.0, 0.9, 0.9, 0.5], dtype=np.float32)
+    tok, n, probs, kept = run_gpu(t, k, p)
+    res = oracle.oracle_sample_filtered(tgt, drf, toks, uni, 1.0, k, p)
+    compare_filtered(tgt, drf, toks, uni, 1.0, k, p, res, tok, n, probs, kept)
+    assert kept[3, K] == 0 and kept[2, K + 2] == 0
+
+
+def test_filtered_is_deterministic():
+    log("determinism")
+    s = make_sample_inputs(4, 1, B=6, V=30000)
+    k, p = make_filter_params(6, seed=5, V=30000)
+    t = sample_tensors(s, DEV)
+    a = run_gpu(t, k, p)
+    b = run_gpu(t, k, p)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y, equal_nan=True) if x.dtype.kind == "f" else np.array_equal(x, y)

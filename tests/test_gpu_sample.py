@@ -184,6 +184,10 @@ def test_faults_and_masked_vocab():
     assert np.array_equal(out.tokens.cpu().numpy(), res.tokens)
     assert np.all(out.tokens.cpu().numpy()[1:5] == -1)
     assert 0 <= res.tokens[5, 0] < 250
+    probs = out.probs.cpu().numpy()
+    assert np.array_equal(np.isnan(probs), np.isnan(res.probs))   # each side NaN only by its own row
+    fin = np.isfinite(res.probs)
+    assert np.allclose(probs[fin], res.probs[fin], rtol=1e-4, atol=1e-5)
 
 
 def test_zero_residual_falls_back_to_p():
