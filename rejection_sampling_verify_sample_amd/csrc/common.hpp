@@ -31,6 +31,10 @@ template <>
 struct Elem<float> {
   static constexpr int kVec = 4;  // elements per 16-byte load
   __device__ __forceinline__ static float get(const float* p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static void unpack(const u32x4& v, float (&x)[4]) {
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+  }
   template <bool NT = true>
   __device__ __forceinline__ static void vec(const float* p, float (&x)[4]) {
     const u32x4 v = NT ? load_stream(p) : *reinterpret_cast<const u32x4*>(p);
@@ -44,6 +48,14 @@ struct Elem<bf16_t> {
   static constexpr int kVec = 8;
   __device__ __forceinline__ static float get(const bf16_t* p, size_t i) {
     return __uint_as_float(static_cast<uint32_t>(p[i].bits) << 16);
+  }
+  __device__ __forceinline__ static void unpack(const u32x4& v, float (&x)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(w[j] << 16);
+      x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
   }
   template <bool NT = true>
   __device__ __forceinline__ static void vec(const bf16_t* p, float (&x)[8]) {
@@ -120,6 +132,88 @@ __device__ __forceinline__ float wave_sumf(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
+}
+
+// ---------------------------------------------------------------- DPP wave scans
+//
+// Inclusive scans across the 64 lanes of a wave with gfx9 DPP moves (row_shr
+// 1/2/4/8 inside each row of 16 lanes, then row_bcast 15 and 31 across rows):
+// six dependent register moves instead of LDS-routed shuffles. Every lane of the
+// wave must be active. Lanes outside a move's source range receive the identity.
+namespace dpp {
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118, kBcast15 = 0x142, kBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t mov(uint32_t v, uint32_t identity) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(identity), static_cast<int>(v), CTRL,
+                                                           ROW_MASK, 0xf, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float movf(float v, float identity) {
+  return __uint_as_float(mov<CTRL, ROW_MASK>(__float_as_uint(v), __float_as_uint(identity)));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double movd(double v) {  // identity +0.0
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = mov<CTRL, ROW_MASK>(static_cast<uint32_t>(u), 0u);
+  const uint32_t hi = mov<CTRL, ROW_MASK>(static_cast<uint32_t>(u >> 32), 0u);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+}  // namespace dpp
+
+// Inclusive prefix sum over the lanes of a wave (lane order), fp64.
+__device__ __forceinline__ double wave_scan_add(double v) {
+  v += dpp::movd<dpp::kShr1, 0xf>(v);
+  v += dpp::movd<dpp::kShr2, 0xf>(v);
+  v += dpp::movd<dpp::kShr4, 0xf>(v);
+  v += dpp::movd<dpp::kShr8, 0xf>(v);
+  v += dpp::movd<dpp::kBcast15, 0xa>(v);
+  v += dpp::movd<dpp::kBcast31, 0xc>(v);
+  return v;
+}
+
+// Inclusive prefix sum over the lanes of a wave, fp32.
+__device__ __forceinline__ float wave_scan_addf(float v) {
+  v += dpp::movf<dpp::kShr1, 0xf>(v, 0.f);
+  v += dpp::movf<dpp::kShr2, 0xf>(v, 0.f);
+  v += dpp::movf<dpp::kShr4, 0xf>(v, 0.f);
+  v += dpp::movf<dpp::kShr8, 0xf>(v, 0.f);
+  v += dpp::movf<dpp::kBcast15, 0xa>(v, 0.f);
+  v += dpp::movf<dpp::kBcast31, 0xc>(v, 0.f);
+  return v;
+}
+
+// Inclusive prefix maximum over the lanes of a wave, fp32 (lane 63 holds the maximum).
+__device__ __forceinline__ float wave_scan_maxf(float v) {
+  v = fmaxf(v, dpp::movf<dpp::kShr1, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp::movf<dpp::kShr2, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp::movf<dpp::kShr4, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp::movf<dpp::kShr8, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp::movf<dpp::kBcast15, 0xa>(v, -INFINITY));
+  v = fmaxf(v, dpp::movf<dpp::kBcast31, 0xc>(v, -INFINITY));
+  return v;
+}
+
+// Value of lane `l` (uniform across the wave) in every lane.
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(__float_as_uint(v)), l)));
+}
+__device__ __forceinline__ int lane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ double lane_d(double v, int l) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u)), l));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u >> 32)), l));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Lowest lane whose predicate holds (64 if none); highest such lane (-1 if none).
+__device__ __forceinline__ int first_lane(bool pred) {
+  const uint64_t m = __ballot(pred);
+  return m ? __ffsll(static_cast<unsigned long long>(m)) - 1 : 64;
+}
+__device__ __forceinline__ int last_lane(bool pred) {
+  const uint64_t m = __ballot(pred);
+  return m ? 63 - __clzll(static_cast<long long>(m)) : -1;
 }
 
 // ---------------------------------------------------------------- online softmax state

@@ -14,20 +14,24 @@
 //                      wave shuffle and an LDS step combine the block. Segment 0 also
 //                      fetches the logit of the row's draft token. The bonus row is not
 //                      read here: it is needed only when all K drafts are accepted.
-//   k_sample_mass      one workgroup per (b, segment). It first takes the accept
-//                      decisions of batch row b (merging the row statistics, alpha_i,
-//                      and the first rejection from one 64-lane ballot); segment 0
-//                      writes them out. Then it reads only the row(s) the draw needs --
-//                      target and draft row n after a rejection, or the bonus row K --
-//                      and records the draw mass of every chunk of 64 vectors (one wave
-//                      load): max(0, p - q) summed, or for the bonus row the chunk's
-//                      maximum and its softmax sum against that maximum.
-//   k_sample_draw      one workgroup per b: scans the chunk masses in fp64, picks the
-//                      chunk where u*Z falls, and one wave rereads that chunk (1 KB,
-//                      cache-hot) and finds the token with a lane prefix sum.
+//   k_sample_mass      one workgroup per (b, segment). Each wave first takes the accept
+//                      decisions of batch row b itself, with no barrier (merging the row
+//                      statistics, alpha_i, and the first rejection from one 64-lane
+//                      ballot); wave 0 of segment 0 writes them out. Then it reads only
+//                      the row(s) the draw needs -- target and draft row n after a
+//                      rejection, or the bonus row K -- and records the draw mass of every
+//                      chunk of 64 vectors (one wave load): max(0, p - q) summed, or for
+//                      the bonus row the chunk's maximum and its softmax sum against it.
+//   k_sample_draw      one wave per b: an fp64 DPP lane scan of the chunk masses picks the
+//                      chunk where u*Z falls; the wave rereads that chunk (one 16-byte
+//                      vector per lane and row) and a second lane scan finds the token.
+// These short kernels are latency-bound: each dependent step (a memory round, an
+// LDS round trip, a barrier) shows in the round time, so the decision and the draw
+// keep to registers, DPP moves and ballots.
 // k_sample_accept runs the decisions alone, for callers that run the phases apart.
 #include <type_traits>
 
+#include "../../include/spec_verify.h"
 #include "common.hpp"
 #include "params.hpp"
 
@@ -35,8 +39,15 @@ namespace sv {
 
 // ---------------------------------------------------------------- online softmax over a segment
 
-constexpr int kRowBlock = 128;  // threads per row-statistics workgroup (measured best on gfx950)
-constexpr int kUnroll = 4;      // 16-byte vectors in flight per thread per step
+// Launch geometry, chosen by measured sweeps on gfx950 (the macros exist for such sweeps).
+#ifndef SV_ROW_BLOCK
+#define SV_ROW_BLOCK 128
+#endif
+#ifndef SV_ROW_UNROLL
+#define SV_ROW_UNROLL 4
+#endif
+constexpr int kRowBlock = SV_ROW_BLOCK;  // threads per row-statistics workgroup
+constexpr int kUnroll = SV_ROW_UNROLL;   // 16-byte vectors in flight per thread per step
 
 template <int BS, typename T>
 __device__ __forceinline__ void online_scalar(const T* row, int64_t lo, int64_t hi, float c, Online& o) {
@@ -94,11 +105,13 @@ __device__ __forceinline__ void merge_partials(const float* pm, const double* ps
                                                double& Ssum) {
   M = -INFINITY;
   for (int j = 0; j < S; ++j) M = fmaxf(M, pm[j]);
-  const double RM = static_cast<double>(M * c);
+  const float RMf = M * c;
+  const double RM = static_cast<double>(RMf);
   Ssum = 0.0;
   for (int j = 0; j < S; ++j) {
     const double sj = ps[j];
-    if (sj > 0.0) Ssum += sj * exp2(static_cast<double>(pm[j] * c) - RM);
+    const float Rj = pm[j] * c;
+    if (sj > 0.0) Ssum += (Rj == RMf) ? sj : sj * exp2(static_cast<double>(Rj) - RM);
   }
 }
 
@@ -232,18 +245,24 @@ __global__ __launch_bounds__(kRowBlock) void k_sample_rowstats(SampleParams P) {
 
 // ---------------------------------------------------------------- accept tests and first rejection
 
-// Accept decisions of batch row b, computed by a whole workgroup (blockDim.x >= 64
-// and >= 2K). One round of independent loads: the row statistics, the draft
-// tokens' logits (fetched in pass 1), the tokens and the accept uniforms. Every
-// thread returns with d.n (K when all K are accepted) and d.fault; the statistics
-// of the 2K rows stay in d. With `write`, the workgroup also writes the accepted
-// prefix, out_num_accepted, out_probs and the draw descriptor.
-struct Decision {
-  float R[2 * 64];
-  double S[2 * 64];
-  float prob[2 * 64];
-  uint32_t T[2 * 64];  // key thresholds of the filtered rows
-  int n, fault;
+// Accept decisions of batch row b, taken by one wave with no barrier; every lane
+// returns the same n and fault. One round of independent loads: the row
+// statistics, the draft tokens' logits (fetched in pass 1), the tokens and the
+// accept uniforms. Lane l holds logit rows j = l and j = l + 64 (j < 2K; row j < K
+// is target row j, else draft row j - K). With `write`, the wave also writes the
+// accepted prefix, out_num_accepted, out_probs and the draw descriptor.
+struct WaveDecision {
+  int n;          // first rejection, K when all K are accepted (wave-uniform)
+  bool fault;     // wave-uniform
+  float R[2];     // per lane: reference exponents of the lane's two rows
+  double S[2];    // softmax denominators (filtered rows: kept masses)
+  uint32_t T[2];  // key thresholds of the filtered rows
+  // values of logit row j (wave-uniform j < 2K)
+  __device__ __forceinline__ float rowR(int j) const { return lane_f(j >= 64 ? R[1] : R[0], j & 63); }
+  __device__ __forceinline__ double rowS(int j) const { return lane_d(j >= 64 ? S[1] : S[0], j & 63); }
+  __device__ __forceinline__ uint32_t rowT(int j) const {
+    return static_cast<uint32_t>(lane_i(static_cast<int>(j >= 64 ? T[1] : T[0]), j & 63));
+  }
 };
 
 // Row j (< K: target row j, else draft row j - K) of batch row b in the filtered
@@ -255,84 +274,110 @@ __device__ __forceinline__ int64_t filt_row(const SampleParams& P, int b, int j)
 // FILT: the rows' laws are the top-k / top-p filtered ones, described by the
 // filter kernel's (reference, kept mass, key threshold) per row.
 template <bool FILT>
-__device__ __forceinline__ void decide_block(const SampleParams& P, const int b, const bool write, Decision& d) {
+__device__ __forceinline__ void decide_wave(const SampleParams& P, const int b, const bool write, WaveDecision& d) {
   const int K = P.K, S = P.S1;
-  const int tid = threadIdx.x;
-  if (tid < 2 * K) {
-    const int64_t r = static_cast<int64_t>(b) * 2 * K + tid;
-    const float xl = P.p1_x[r];
-    if constexpr (FILT) {
-      const int64_t fr = filt_row(P, b, tid);
-      const float R = P.f_R[fr];
-      const double Ssum = P.f_S[fr];
-      const uint32_t thr = P.f_thr[fr];
-      d.R[tid] = R;
-      d.S[tid] = Ssum;
-      d.T[tid] = thr;
-      const bool ok = Ssum > 0.0 && isfinite(Ssum) && !isnan(xl);
-      // p'_i(x_i) or q'_i(x_i): 0 outside the row's kept set
-      d.prob[tid] = !ok ? __builtin_nanf("")
-                        : (order_key(xl) >= thr ? exp2_hw(fmaf(xl, P.c, -R)) / static_cast<float>(Ssum) : 0.f);
-    } else {
-      float M;
-      double Ssum;
-      merge_partials(P.p1_m + r * S, P.p1_s + r * S, S, P.c, M, Ssum);
-      const float R = M * P.c;
-      d.R[tid] = R;
-      d.S[tid] = Ssum;
-      const bool ok = isfinite(M) && Ssum > 0.0 && isfinite(Ssum) && !isnan(xl);
-      // p_i(x_i) (tid < K) or q_i(x_i) (tid >= K); NaN marks a row that cannot be used
-      d.prob[tid] = ok ? exp2_hw(fmaf(xl, P.c, -R)) / static_cast<float>(Ssum) : __builtin_nanf("");
-    }
+  const int lane = threadIdx.x & 63;
+  // the draft token and accept uniform of position `lane`, fetched with the row statistics
+  int x = 0;
+  float r_acc = 0.f;
+  if (lane < K) {
+    x = P.tokens[static_cast<int64_t>(b) * K + lane];
+    r_acc = P.uniforms[(static_cast<int64_t>(b) * (K + 1) + lane) * 2];
   }
-  __syncthreads();
-  if (tid < 64) {
-    bool stop = false, fault = false;
-    if (tid < K) {
-      const int x = P.tokens[static_cast<int64_t>(b) * K + tid];
-      const float p = d.prob[tid], q = d.prob[K + tid];
-      if (x >= 0 && x < P.V && !isnan(p) && !isnan(q)) {
-        // alpha = min(1, p/q), truncated to 1 without dividing when p >= q; 0 when p = 0
-        const float alpha = (p == 0.f) ? 0.f : ((p >= q) ? 1.f : p / q);
-        const float r = P.uniforms[(static_cast<int64_t>(b) * (K + 1) + tid) * 2];
-        stop = !(r < alpha);
+  float prob[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = lane + 64 * h;
+    prob[h] = __builtin_nanf("");
+    d.R[h] = 0.f;
+    d.S[h] = 0.0;
+    d.T[h] = 0u;
+    if (j < 2 * K) {
+      const int64_t r = static_cast<int64_t>(b) * 2 * K + j;
+      const float xl = P.p1_x[r];
+      if constexpr (FILT) {
+        const int64_t fr = filt_row(P, b, j);
+        const float R = P.f_R[fr];
+        const double Ssum = P.f_S[fr];
+        const uint32_t thr = P.f_thr[fr];
+        d.R[h] = R;
+        d.S[h] = Ssum;
+        d.T[h] = thr;
+        const bool ok = Ssum > 0.0 && isfinite(Ssum) && !isnan(xl);
+        // p'_i(x_i) or q'_i(x_i): 0 outside the row's kept set
+        prob[h] = !ok ? __builtin_nanf("")
+                      : (order_key(xl) >= thr ? exp2_hw(fmaf(xl, P.c, -R)) / static_cast<float>(Ssum) : 0.f);
       } else {
-        stop = true;
-        fault = true;
+        float M;
+        double Ssum;
+        merge_partials(P.p1_m + r * S, P.p1_s + r * S, S, P.c, M, Ssum);
+        const float R = M * P.c;
+        d.R[h] = R;
+        d.S[h] = Ssum;
+        const bool ok = isfinite(M) && Ssum > 0.0 && isfinite(Ssum) && !isnan(xl);
+        // p_i(x_i) (j < K) or q_i(x_i) (j >= K); NaN marks a row that cannot be used
+        prob[h] = ok ? exp2_hw(fmaf(xl, P.c, -R)) / static_cast<float>(Ssum) : __builtin_nanf("");
       }
-      if (write && P.out_probs) {
-        P.out_probs[(static_cast<int64_t>(b) * K + tid) * 2] = p;
-        P.out_probs[(static_cast<int64_t>(b) * K + tid) * 2 + 1] = q;
-      }
-    }
-    const uint64_t stops = __ballot(stop);
-    const uint64_t faults = __ballot(fault);
-    if (tid == 0) {
-      const int n = stops ? (__ffsll(static_cast<unsigned long long>(stops)) - 1) : K;
-      d.n = n;
-      d.fault = (n < K) && ((faults >> n) & 1ull);
     }
   }
-  __syncthreads();
+  // position i = lane: p_i(x_i) is the lane's first row, q_i(x_i) is row K + i
+  const int jq = K + lane;
+  const float q0 = __shfl(prob[0], jq & 63, 64);
+  const float q1 = __shfl(prob[1], jq & 63, 64);
+  const float p = prob[0];
+  const float q = (jq < 64) ? q0 : q1;
+  bool stop = false, flt = false;
+  if (lane < K) {
+    if (x >= 0 && x < P.V && !isnan(p) && !isnan(q)) {
+      // alpha = min(1, p/q), truncated to 1 without dividing when p >= q; 0 when p = 0
+      const float alpha = (p == 0.f) ? 0.f : ((p >= q) ? 1.f : p / q);
+      stop = !(r_acc < alpha);
+    } else {
+      stop = true;
+      flt = true;
+    }
+  }
+  const uint64_t stops = __ballot(stop);
+  const uint64_t faults = __ballot(flt);
+  const int n = stops ? (__ffsll(static_cast<unsigned long long>(stops)) - 1) : K;
+  const bool fault = (n < K) && ((faults >> n) & 1ull);
+  d.n = n;
+  d.fault = fault;
   if (!write) return;
-  const int n = d.n;
-  const bool fault = d.fault != 0;
   int32_t* ot = P.out_tokens + static_cast<int64_t>(b) * (K + 1);
-  for (int i = tid; i <= K; i += blockDim.x) {
+  for (int i = lane; i <= K; i += 64) {
     if (fault || i > n) ot[i] = -1;
-    else if (i < n) ot[i] = P.tokens[static_cast<int64_t>(b) * K + i];
+    else if (i < n) ot[i] = x;  // i < n <= K <= 64, so i is this lane's position
   }
-  if (tid == 0) {
+  if (P.out_probs && lane < K) {
+    P.out_probs[(static_cast<int64_t>(b) * K + lane) * 2] = p;
+    P.out_probs[(static_cast<int64_t>(b) * K + lane) * 2 + 1] = q;
+  }
+  // the draw descriptor: references and denominators of the rows the draw reads
+  float R0 = 0.f, R1 = 0.f;
+  double S0 = 0.0, S1 = 0.0;
+  uint32_t T0 = 0u, T1 = 0u;
+  if (!fault && n < K) {
+    R0 = d.rowR(n);
+    R1 = d.rowR(K + n);
+    S0 = d.rowS(n);
+    S1 = d.rowS(K + n);
+    if constexpr (FILT) {
+      T0 = d.rowT(n);
+      T1 = d.rowT(K + n);
+    }
+  }
+  if (lane == 0) {
     P.out_n[b] = fault ? -1 : n;
     P.info_n[b] = fault ? -1 : n;
     if (!fault && n < K) {
-      P.info_R[2 * b] = d.R[n];
-      P.info_R[2 * b + 1] = d.R[K + n];
-      P.info_S[2 * b] = d.S[n];
-      P.info_S[2 * b + 1] = d.S[K + n];
+      P.info_R[2 * b] = R0;
+      P.info_R[2 * b + 1] = R1;
+      P.info_S[2 * b] = S0;
+      P.info_S[2 * b + 1] = S1;
       if constexpr (FILT) {
-        P.info_T[2 * b] = d.T[n];
-        P.info_T[2 * b + 1] = d.T[K + n];
+        P.info_T[2 * b] = T0;
+        P.info_T[2 * b + 1] = T1;
       }
     } else if (FILT && !fault) {  // the bonus draw from the filtered last row: no draft side
       const int64_t fr = static_cast<int64_t>(b) * (2 * K + 1) + K;
@@ -346,14 +391,13 @@ __device__ __forceinline__ void decide_block(const SampleParams& P, const int b,
   }
 }
 
-constexpr int kAcceptBlock = 128;  // one thread per logit row (2K <= 128)
+constexpr int kAcceptBlock = 64;  // one wave per batch row
 
 template <bool FILT>
 __global__ __launch_bounds__(kAcceptBlock) void k_sample_accept(SampleParams P) {
-  __shared__ Decision d;
   for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) {
-    decide_block<FILT>(P, static_cast<int>(task), true, d);
-    __syncthreads();
+    WaveDecision d;
+    decide_wave<FILT>(P, static_cast<int>(task), true, d);
   }
 }
 
@@ -518,7 +562,10 @@ __device__ __forceinline__ void wave_scalar_chunk_mass(const SampleParams& P, co
 // computed by one wave: the loads of all of them are issued before any is
 // reduced, so a wave keeps CU (or 2*CU) 16-byte loads per lane in flight. Lane 0
 // stores (chunk max, chunk mass).
-constexpr int kChunksPerWave = 1;
+#ifndef SV_CHUNKS_PER_WAVE
+#define SV_CHUNKS_PER_WAVE 1
+#endif
+constexpr int kChunksPerWave = SV_CHUNKS_PER_WAVE;
 
 template <typename T, typename Res>
 __device__ __forceinline__ void wave_vector_chunks_mass(const SampleParams& P, const T* tr, const T* dr,
@@ -527,48 +574,56 @@ __device__ __forceinline__ void wave_vector_chunks_mass(const SampleParams& P, c
   constexpr int VEC = Elem<T>::kVec;
   constexpr int CU = kChunksPerWave;
   const int lane = threadIdx.x & 63;
-  float xt[CU][VEC], xq[CU][VEC];
+  // raw 16-byte vectors: every load of the CU chunks is issued before any is unpacked
+  u32x4 rt[CU], rq[CU];
+  const u32x4 none = {0u, 0u, 0u, 0u};  // placeholder for a vector that is not read (never unpacked as data)
 #pragma unroll
   for (int u = 0; u < CU; ++u) {
     const int cu = c + u * cstride;
     const int64_t vi = static_cast<int64_t>(cu - 1) * kChunkVecs + lane;
     const bool in = (cu < cend) && vi < ch.nvec;
-    if (in) {
-      Elem<T>::vec(tr + ch.h + vi * VEC, xt[u]);
-      if (!bonus) {
-        if (paired) {
-          Elem<T>::vec(dr + ch.h + vi * VEC, xq[u]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) xq[u][e] = Elem<T>::get(dr, ch.h + vi * VEC + e);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) xt[u][e] = xq[u][e] = -INFINITY;  // zero weight either way
-    }
+    rt[u] = in ? load_stream(tr + ch.h + vi * VEC) : none;
+    rq[u] = (in && !bonus && paired) ? load_stream(dr + ch.h + vi * VEC) : none;
   }
 #pragma unroll
   for (int u = 0; u < CU; ++u) {
     const int cu = c + u * cstride;
     if (cu >= cend) break;
+    const int64_t vi = static_cast<int64_t>(cu - 1) * kChunkVecs + lane;
+    const bool in = vi < ch.nvec;
+    float xt[VEC], xq[VEC];
+    Elem<T>::unpack(rt[u], xt);
+    if (!in) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) xt[e] = -INFINITY;  // zero weight either way
+    }
     float mx = -INFINITY, a = 0.f;
     if (bonus) {
-      float lm = xt[u][0];
+      float lm = xt[0];
 #pragma unroll
-      for (int e = 1; e < VEC; ++e) lm = fmaxf(lm, xt[u][e]);
-      mx = wave_max(lm);
+      for (int e = 1; e < VEC; ++e) lm = fmaxf(lm, xt[e]);
+      mx = lane_f(wave_scan_maxf(lm), 63);
       if (mx > -INFINITY) {  // a chunk with no finite logit carries no mass
         const float R = mx * P.c;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) a += exp2_hw(fmaf(xt[u][e], P.c, -R));
+        for (int e = 0; e < VEC; ++e) a += exp2_hw(fmaf(xt[e], P.c, -R));
       }
     } else {
+      if (paired) {
+        Elem<T>::unpack(rq[u], xq);
+      } else if (in) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) a += res(xt[u][e], xq[u][e]);
+        for (int e = 0; e < VEC; ++e) xq[e] = Elem<T>::get(dr, ch.h + vi * VEC + e);
+      }
+      if (!in) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) xq[e] = -INFINITY;
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) a += res(xt[e], xq[e]);
     }
-    const float sum = wave_sumf(a);
-    if (lane == 0) {
+    const float sum = wave_scan_addf(a);  // lane 63 holds the chunk's total
+    if (lane == 63) {
       cm[cu] = mx;
       cs[cu] = sum;
     }
@@ -585,25 +640,27 @@ __device__ __forceinline__ void sample_mass_task(const SampleParams& P, const in
   const int K = P.K, S = P.S2;
   const int seg = static_cast<int>(task % S);
   const int b = static_cast<int>(task / S);
-  __shared__ Decision d;
+  const int wave = threadIdx.x >> 6;
   ResOf<FILT> res{};
   int n;
   if (FUSE_ACCEPT) {
-    decide_block<FILT>(P, b, seg == 0, d);  // with K = 0: n = 0, the bonus draw
+    // every wave takes the decisions itself (no barrier); wave 0 of segment 0 writes them out
+    WaveDecision d;
+    decide_wave<FILT>(P, b, seg == 0 && wave == 0, d);  // with K = 0: n = 0, the bonus draw
     n = d.n;
     if (d.fault) return;
     if (n < K) {
       res.c = P.c;
-      res.Rt = d.R[n];
-      res.Rq = d.R[K + n];
+      res.Rt = d.rowR(n);
+      res.Rq = d.rowR(K + n);
       if constexpr (FILT) {
-        res.it = inv_or_zero(d.S[n]);
-        res.iq = inv_or_zero(d.S[K + n]);
-        res.kt = d.T[n];
-        res.kq = d.T[K + n];
+        res.it = inv_or_zero(d.rowS(n));
+        res.iq = inv_or_zero(d.rowS(K + n));
+        res.kt = d.rowT(n);
+        res.kq = d.rowT(K + n);
       } else {
-        res.it = static_cast<float>(1.0 / d.S[n]);
-        res.iq = static_cast<float>(1.0 / d.S[K + n]);
+        res.it = static_cast<float>(1.0 / d.rowS(n));
+        res.iq = static_cast<float>(1.0 / d.rowS(K + n));
       }
     } else if constexpr (FILT) {
       const int64_t fr = static_cast<int64_t>(b) * (2 * K + 1) + K;
@@ -630,7 +687,6 @@ __device__ __forceinline__ void sample_mass_task(const SampleParams& P, const in
   // vector chunks [c0, c1) of this segment; segment 0 adds the head, the last one the tail
   const int c0 = 1 + static_cast<int>(static_cast<int64_t>(ch.nvc) * seg / S);
   const int c1 = 1 + static_cast<int>(static_cast<int64_t>(ch.nvc) * (seg + 1) / S);
-  const int wave = threadIdx.x >> 6;
   constexpr int W = kBlock / 64;
   if (seg == 0 && wave == 0) wave_scalar_chunk_mass<T>(P, tr, dr, ch, 0, bonus, res, cm, cs);
   if (seg == S - 1 && wave == W - 1) wave_scalar_chunk_mass<T>(P, tr, dr, ch, ch.nvc + 1, bonus, res, cm, cs);
@@ -641,10 +697,7 @@ __device__ __forceinline__ void sample_mass_task(const SampleParams& P, const in
 template <typename T, bool FUSE_ACCEPT, bool FILT>
 __global__ __launch_bounds__(kBlock) void k_sample_mass(SampleParams P) {
   const int64_t ntask = static_cast<int64_t>(P.B) * P.S2;
-  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
-    sample_mass_task<T, FUSE_ACCEPT, FILT>(P, task);
-    __syncthreads();  // shared memory is reused by the next task
-  }
+  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) sample_mass_task<T, FUSE_ACCEPT, FILT>(P, task);
 }
 
 // ---------------------------------------------------------------- pass 2: the draw
@@ -657,12 +710,12 @@ __global__ __launch_bounds__(kBlock) void k_sample_mass(SampleParams P) {
 // zero-residual fallback, which draws from p_n over the whole row.
 constexpr int kSearchE = 8;
 
-template <typename W>
+template <int BS, typename W>
 __device__ int64_t block_search(int64_t lo, int64_t hi, double tau, const W& w) {
   __shared__ int64_t sh_k;
   double base = 0.0;
   int64_t last_pos = -1;
-  for (int64_t c0 = lo; c0 < hi; c0 += static_cast<int64_t>(kBlock) * kSearchE) {
+  for (int64_t c0 = lo; c0 < hi; c0 += static_cast<int64_t>(BS) * kSearchE) {
     const int64_t e0 = c0 + static_cast<int64_t>(threadIdx.x) * kSearchE;
     float wv[kSearchE];
     float ts = 0.f;
@@ -674,10 +727,10 @@ __device__ int64_t block_search(int64_t lo, int64_t hi, double tau, const W& w) 
       if (wv[k] > 0.f) last_pos = e;
     }
     double total;
-    const double incl = block_inclusive_scan<kBlock>(static_cast<double>(ts), total);
+    const double incl = block_inclusive_scan<BS>(static_cast<double>(ts), total);
     if (base + total > tau) {
       const double excl = incl - static_cast<double>(ts);
-      const int t = block_first<kBlock>(base + incl > tau);
+      const int t = block_first<BS>(base + incl > tau);
       if (static_cast<int>(threadIdx.x) == t) {
         int64_t k_found = -1, k_lastpos = -1;
         float run = 0.f;
@@ -696,131 +749,206 @@ __device__ int64_t block_search(int64_t lo, int64_t hi, double tau, const W& w) 
     }
     base += total;
   }
-  const int64_t lp = block_max_i64<kBlock>(last_pos);
+  const int64_t lp = block_max_i64<BS>(last_pos);
   return lp >= 0 ? lp : lo;
 }
 
+constexpr int kDrawBlock = 64;      // one wave per batch row
+constexpr int kDrawRegChunks = 10;  // chunk masses a lane keeps in registers (enough for V up to 163840)
+
+// The inverse-CDF draw of batch row b, by one wave with no barrier on its usual path:
+// one round of loads (descriptor, uniforms, this lane's run of chunk masses), an
+// fp64 lane scan of the chunk masses picks the chunk where u*Z falls, and one
+// reload of that chunk (one 16-byte vector per lane and row) with a second lane
+// scan picks the token.
 template <typename T, bool FILT>
-__device__ __forceinline__ void sample_draw_task(const SampleParams& P, const int64_t task) {
+__device__ __forceinline__ void sample_draw_task(const SampleParams& P, const int b) {
   constexpr int VEC = Elem<T>::kVec;
   const int K = P.K;
-  const int b = static_cast<int>(task);
-  const int tid = threadIdx.x;
-  int n;
-  if (!draw_row(P, b, n)) return;  // the accept pass already wrote the fault outputs
+  const int lane = threadIdx.x & 63;
+  const float* cm = P.p2_cm + static_cast<int64_t>(b) * P.NCmax;
+  const double* cs = P.p2_cs + static_cast<int64_t>(b) * P.NCmax;
+  // One round of loads that do not depend on the row the draw reads. Chunk
+  // geometry depends only on the 16-byte phase of the row, which every row of
+  // batch row b shares when a row is a whole number of 16-byte vectors;
+  // otherwise the masses are read again once the row is known.
+  const int n_raw = (K == 0) ? 0 : P.info_n[b];
+  const float u_lane = P.uniforms[(static_cast<int64_t>(b) * (K + 1) + min(lane, K)) * 2 + 1];
+  const float dR0 = P.info_R[2 * b], dR1 = P.info_R[2 * b + 1];
+  const double dS0 = P.info_S[2 * b], dS1 = P.info_S[2 * b + 1];
+  uint32_t dT0 = 0u, dT1 = 0u;
+  if constexpr (FILT) {
+    dT0 = P.info_T[2 * b];
+    dT1 = P.info_T[2 * b + 1];
+  }
+  const int NC0 = chunks_of(target_row<T>(P, b, 0), P.V).count();
+  const int per0 = (NC0 + 63) / 64;
+  const int j00 = min(lane * per0, NC0);
+  const int j01 = min(j00 + per0, NC0);
+  float cmr[kDrawRegChunks];
+  double csr[kDrawRegChunks];
+#pragma unroll
+  for (int i = 0; i < kDrawRegChunks; ++i) {
+    const bool in = j00 + i < j01;
+    cmr[i] = in ? cm[j00 + i] : -INFINITY;
+    csr[i] = in ? cs[j00 + i] : 0.0;
+  }
+  const int n = __builtin_amdgcn_readfirstlane(n_raw);
+  if (n < 0 || n > K) return;  // the accept pass already wrote the fault outputs
+  const float u = (n < 64) ? lane_f(u_lane, n) : P.uniforms[(static_cast<int64_t>(b) * (K + 1) + n) * 2 + 1];
   const bool is_bonus = (n == K);
   const bool bonus = !FILT && is_bonus;  // chunk masses against chunk maxima (unfiltered bonus only)
   const T* tr = target_row<T>(P, b, n);
   const T* dr = is_bonus ? tr : draft_row<T>(P, b, n);
   const Chunks ch = chunks_of(tr, P.V);
   const int NC = ch.count();
-  const float* cm = P.p2_cm + static_cast<int64_t>(b) * P.NCmax;
-  const double* cs = P.p2_cs + static_cast<int64_t>(b) * P.NCmax;
-  const float u = P.uniforms[(static_cast<int64_t>(b) * (K + 1) + n) * 2 + 1];
-  __shared__ float sh_max[kWaves];
-  __shared__ int sh_chunk;
-  __shared__ double sh_tau;
-  // each thread owns a contiguous run of chunks
-  const int per = (NC + kBlock - 1) / kBlock;
-  const int j0 = min(tid * per, NC);
+  // each lane owns a contiguous run of chunks [j0, j1)
+  const int per = (NC + 63) / 64;
+  const int j0 = min(lane * per, NC);
   const int j1 = min(j0 + per, NC);
-  float M = 0.f;
+  // `cached`: the run is the one loaded above and fits the registers (wave-uniform)
+  const bool cached = (NC == NC0) && (per <= kDrawRegChunks);
+  float RMf = 0.f;
   if (bonus) {
     float lm = -INFINITY;
-    for (int j = j0; j < j1; ++j) lm = fmaxf(lm, cm[j]);
-    lm = wave_max(lm);
-    if ((tid & 63) == 0) sh_max[tid >> 6] = lm;
-    __syncthreads();
-    M = sh_max[0];
-    for (int i = 1; i < kWaves; ++i) M = fmaxf(M, sh_max[i]);
+    if (cached) {
+#pragma unroll
+      for (int i = 0; i < kDrawRegChunks; ++i) lm = fmaxf(lm, cmr[i]);
+    } else {
+      for (int j = j0; j < j1; ++j) lm = fmaxf(lm, cm[j]);
+    }
+    const float M = lane_f(wave_scan_maxf(lm), 63);
+    RMf = M * P.c;
+    if (!isfinite(M)) {  // the bonus row has no finite logit
+      int32_t* ot = P.out_tokens + static_cast<int64_t>(b) * (K + 1);
+      for (int i = lane; i <= K; i += 64) ot[i] = -1;
+      if (lane == 0) P.out_n[b] = -1;
+      return;
+    }
   }
-  const double RM = static_cast<double>(M * P.c);
-  auto mass = [&](int j) -> double {
-    const double s = cs[j];
-    if (!bonus) return s;
-    return s > 0.0 ? s * exp2(static_cast<double>(cm[j] * P.c) - RM) : 0.0;
+  // Bonus chunks are rescaled from their own reference fl(max_j * c) to the row's:
+  // the exponent difference is exact in fp64, 2^d comes from the hardware unit.
+  auto factor = [&](float cmj) -> float {
+    return exp2_hw(static_cast<float>(static_cast<double>(cmj * P.c) - static_cast<double>(RMf)));
+  };
+  auto mass_of = [&](float cmj, double csj) -> double {
+    if (!bonus) return csj;
+    return csj > 0.0 ? csj * static_cast<double>(factor(cmj)) : 0.0;
   };
   double mine = 0.0;
   int last_pos = -1;
-  for (int j = j0; j < j1; ++j) {
-    const double mj = mass(j);
-    mine += mj;
-    if (mj > 0.0) last_pos = j;
+  float cm_last = 0.f;
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < kDrawRegChunks; ++i) {
+      const double mj = mass_of(cmr[i], csr[i]);  // 0 past the run
+      mine += mj;
+      if (mj > 0.0) {
+        last_pos = j0 + i;
+        cm_last = cmr[i];
+      }
+    }
+  } else {
+    for (int j = j0; j < j1; ++j) {
+      const double mj = mass_of(cm[j], cs[j]);
+      mine += mj;
+      if (mj > 0.0) last_pos = j;
+    }
   }
-  double Z;
-  const double incl = block_inclusive_scan<kBlock>(mine, Z);  // chunk order, fp64
-  // 0: search a chunk; 1: zero residual mass -> draw from p_n; 2: bonus row fault
-  int mode = 0;
-  if (bonus && !(isfinite(M) && Z > 0.0 && isfinite(Z))) mode = 2;
-  else if (FILT && is_bonus && !(Z > 0.0 && isfinite(Z))) mode = 2;
-  else if (!is_bonus && !(Z > 0.0 && isfinite(Z))) mode = 1;
+  const double incl = wave_scan_add(mine);  // chunk order, fp64
+  const double Z = lane_d(incl, 63);
   int32_t* ot = P.out_tokens + static_cast<int64_t>(b) * (K + 1);
-  if (mode == 2) {
-    for (int i = tid; i <= K; i += kBlock) ot[i] = -1;
-    if (tid == 0) P.out_n[b] = -1;
+  if (is_bonus && !(Z > 0.0 && isfinite(Z))) {  // a bonus row with no mass: fault
+    for (int i = lane; i <= K; i += 64) ot[i] = -1;
+    if (lane == 0) P.out_n[b] = -1;
     return;
   }
-  if (mode == 1) {
+  ResOf<FILT> res{};
+  res.c = P.c;
+  res.Rt = dR0;
+  res.Rq = dR1;
+  if constexpr (FILT) {
+    res.it = inv_or_zero(dS0);
+    res.iq = inv_or_zero(dS1);
+    res.kt = dT0;
+    res.kq = dT1;
+  } else if (!is_bonus) {
+    res.it = static_cast<float>(1.0 / dS0);
+    res.iq = static_cast<float>(1.0 / dS1);
+  }
+  if (!is_bonus && !(Z > 0.0 && isfinite(Z))) {
     // zero residual mass: draw from p_n (p'_n when filtered) over the whole row
-    ResOf<FILT> res;
-    if constexpr (FILT) res = residual_of_f(P, b);
-    else res = residual_of(P, b);
     auto pw = [&](int64_t e) { return res.target(Elem<T>::get(tr, e)); };
     float a = 0.f;
-    for (int64_t e = tid; e < P.V; e += kBlock) a += pw(e);
-    const double Zp = block_sum<kBlock>(static_cast<double>(a));
-    const int64_t k = block_search(0, P.V, static_cast<double>(u) * Zp, pw);
-    if (tid == 0) ot[n] = static_cast<int32_t>(k);
+    for (int64_t e = lane; e < P.V; e += kDrawBlock) a += pw(e);
+    const double Zp = block_sum<kDrawBlock>(static_cast<double>(a));
+    const int64_t k = block_search<kDrawBlock>(0, P.V, static_cast<double>(u) * Zp, pw);
+    if (lane == 0) ot[n] = static_cast<int32_t>(k);
     return;
   }
-  // the chunk where u*Z falls
+  // the chunk where u*Z falls: the first lane whose inclusive mass passes it
   const double target = static_cast<double>(u) * Z;
-  const int t = block_first<kBlock>(incl > target);
-  if (t < kBlock) {
-    if (tid == t) {
-      double run = incl - mine;
-      int jstar = -1;
-      double tau = 0.0;
+  const int t = first_lane(incl > target);
+  int jstar;
+  double tau;
+  float cmx;
+  if (t < 64) {
+    // every lane walks its own run; lane t's result is the one used
+    double run = incl - mine;
+    int js = -1;
+    double ta = 0.0;
+    float cx = 0.f;
+    if (cached) {
+#pragma unroll
+      for (int i = 0; i < kDrawRegChunks; ++i) {
+        if (js < 0 && j0 + i < j1) {
+          const double mj = mass_of(cmr[i], csr[i]);
+          if (run + mj > target) {
+            js = j0 + i;
+            ta = target - run;
+            cx = cmr[i];
+          } else {
+            run += mj;
+          }
+        }
+      }
+    } else if (lane == t) {
       for (int j = j0; j < j1; ++j) {
-        const double mj = mass(j);
+        const double mj = mass_of(cm[j], cs[j]);
         if (run + mj > target) {
-          jstar = j;
-          tau = target - run;
+          js = j;
+          ta = target - run;
+          cx = cm[j];
           break;
         }
         run += mj;
       }
-      if (jstar < 0) {  // rounding inside this thread's run: its last chunk with mass
-        jstar = last_pos >= 0 ? last_pos : j0;
-        tau = INFINITY;
-      }
-      sh_chunk = jstar;
-      sh_tau = tau;
     }
+    if (js < 0 && lane == t) {  // rounding inside the run: its last chunk with mass
+      js = last_pos >= 0 ? last_pos : j0;
+      ta = INFINITY;
+      cx = cached ? cm_last : cm[min(max(js, 0), NC - 1)];
+    }
+    jstar = lane_i(js, t);
+    tau = lane_d(ta, t);
+    cmx = lane_f(cx, t);
   } else {  // rounding put u*Z at the very end: the last chunk holding mass
-    const int64_t jl = block_max_i64<kBlock>(last_pos);
-    if (tid == 0) {
-      sh_chunk = jl >= 0 ? static_cast<int>(jl) : 0;
-      sh_tau = INFINITY;
-    }
+    const int lw = last_lane(last_pos >= 0);
+    jstar = lw >= 0 ? lane_i(last_pos, lw) : 0;
+    tau = INFINITY;
+    cmx = (lw >= 0 && cached) ? lane_f(cm_last, lw) : cm[min(max(jstar, 0), NC - 1)];
   }
-  __syncthreads();
-  const int jstar = min(max(sh_chunk, 0), NC - 1);
-  double tau = sh_tau;
+  jstar = min(max(jstar, 0), NC - 1);
   float R = 0.f;
   if (bonus) {
-    R = cm[jstar] * P.c;
-    tau *= exp2(RM - static_cast<double>(R));  // into the chunk's own reference
+    R = cmx * P.c;
+    tau = tau / static_cast<double>(factor(cmx));  // into the chunk's own reference
   }
-  if (tid >= 64) return;  // one wave searches the chunk
-  ResOf<FILT> res{};
-  if constexpr (FILT) res = residual_of_f(P, b);
-  else if (!bonus) res = residual_of(P, b);
   int64_t k;
   if (jstar == 0 || jstar == ch.nvc + 1) {
     int64_t lo, hi;
     scalar_chunk_range<T>(ch, jstar, P.V, lo, hi);
-    if (tid != 0) return;
+    if (lane != 0) return;
     float run = 0.f;
     int64_t kf = -1, kl = -1;
     for (int64_t e = lo; e < hi; ++e) {
@@ -836,48 +964,41 @@ __device__ __forceinline__ void sample_draw_task(const SampleParams& P, const in
     float w[VEC];
     chunk_lane_weights<T>(tr, dr, paired, ch, jstar, bonus, res, P.c, R, w);
     float ls = 0.f;
+    int kl = -1;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) ls += w[e];
-    const double lincl = wave_inclusive_scan(static_cast<double>(ls));
-    const uint64_t hit = __ballot(lincl > tau);
+    for (int e = 0; e < VEC; ++e) {
+      ls += w[e];
+      if (w[e] > 0.f) kl = e;
+    }
+    const double lincl = wave_scan_add(static_cast<double>(ls));
+    const int hl = first_lane(lincl > tau);
     const int64_t base_e = ch.h + static_cast<int64_t>(jstar - 1) * kChunkVecs * VEC;
-    if (hit) {
-      const int lane = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-      if (tid != lane) return;
+    if (hl < 64) {
+      if (lane != hl) return;
       const double excl = lincl - static_cast<double>(ls);
       float run = 0.f;
-      int kk = -1, kl = -1;
+      int kk = -1;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         run += w[e];
-        if (w[e] > 0.f) kl = e;
         if (kk < 0 && excl + static_cast<double>(run) > tau) kk = e;
       }
       k = base_e + static_cast<int64_t>(lane) * VEC + (kk >= 0 ? kk : (kl >= 0 ? kl : 0));
     } else {
       // rounding left no crossing: the last element of the chunk with weight > 0
-      int kl = -1;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        if (w[e] > 0.f) kl = e;
-      int64_t best = kl >= 0 ? base_e + static_cast<int64_t>(tid) * VEC + kl : -1;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const int64_t y = __shfl_xor(best, o, 64);
-        best = y > best ? y : best;
-      }
-      if (tid != 0) return;
-      k = best >= 0 ? best : base_e;
+      const int lw = last_lane(kl >= 0);
+      if (lane != 0) return;
+      k = lw >= 0 ? base_e + static_cast<int64_t>(lw) * VEC + lane_i(kl, lw) : base_e;
     }
   }
   ot[n] = static_cast<int32_t>(k);
 }
 
 template <typename T, bool FILT>
-__global__ __launch_bounds__(kBlock) void k_sample_draw(SampleParams P) {
+__global__ __launch_bounds__(kDrawBlock) void k_sample_draw(SampleParams P) {
   for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) {
-    sample_draw_task<T, FILT>(P, task);
-    __syncthreads();  // shared memory is reused by the next task
+    sample_draw_task<T, FILT>(P, static_cast<int>(task));
+    __syncthreads();  // the zero-residual search's shared memory is reused by the next task
   }
 }
 
@@ -912,7 +1033,7 @@ static hipError_t launch_sample_t(const SampleParams& P, int phases, hipStream_t
     hipLaunchKernelGGL((k_sample_mass<T, false, FILT>), grid_for(gm), dim3(kBlock), 0, stream, P);
   }
   if (phases & kPhaseDraw)
-    hipLaunchKernelGGL((k_sample_draw<T, FILT>), grid_for(P.B), dim3(kBlock), 0, stream, P);
+    hipLaunchKernelGGL((k_sample_draw<T, FILT>), grid_for(P.B), dim3(kDrawBlock), 0, stream, P);
   return hipGetLastError();
 }
 
