@@ -560,10 +560,11 @@ __device__ __forceinline__ void wave_scalar_chunk_mass(const SampleParams& P, co
 
 // The masses of vector chunks c, c + cstride, ..., (CU of them, below cend),
 // computed by one wave: the loads of all of them are issued before any is
-// reduced, so a wave keeps CU (or 2*CU) 16-byte loads per lane in flight. Lane 0
-// stores (chunk max, chunk mass).
+// reduced (kept as raw 16-byte vectors, so 2*CU loads per lane cost 8*CU
+// registers), and lane 63 stores (chunk max, chunk mass). Four chunks per wave
+// measured best on gfx950 (one round of loads per wave at the 64 x 128k shape).
 #ifndef SV_CHUNKS_PER_WAVE
-#define SV_CHUNKS_PER_WAVE 1
+#define SV_CHUNKS_PER_WAVE 4
 #endif
 constexpr int kChunksPerWave = SV_CHUNKS_PER_WAVE;
 
@@ -635,20 +636,27 @@ __device__ __forceinline__ void wave_vector_chunks_mass(const SampleParams& P, c
 // out), so no separate accept launch precedes it.
 // FILT: the filtered laws; the bonus draw is then a residual with no draft side
 // (its weights are the kept target masses), so no chunk maxima are needed.
-template <typename T, bool FUSE_ACCEPT, bool FILT>
-__device__ __forceinline__ void sample_mass_task(const SampleParams& P, const int64_t task) {
-  const int K = P.K, S = P.S2;
-  const int seg = static_cast<int>(task % S);
-  const int b = static_cast<int>(task / S);
+template <bool FILT>
+struct MassTask {
+  bool run;          // false: a fault, nothing was streamed and nothing is drawn
+  int n;             // the draw's position (K: the bonus draw)
+  ResOf<FILT> res;   // the draw weights (residual, or the filtered bonus row)
+};
+
+template <typename T, bool FUSE_ACCEPT, bool FILT, int BS = kBlock>
+__device__ __forceinline__ MassTask<FILT> sample_mass_task(const SampleParams& P, const int b, const int seg,
+                                                           const int S) {
+  const int K = P.K;
   const int wave = threadIdx.x >> 6;
-  ResOf<FILT> res{};
+  MassTask<FILT> mt{false, 0, {}};
+  ResOf<FILT>& res = mt.res;
   int n;
   if (FUSE_ACCEPT) {
     // every wave takes the decisions itself (no barrier); wave 0 of segment 0 writes them out
     WaveDecision d;
     decide_wave<FILT>(P, b, seg == 0 && wave == 0, d);  // with K = 0: n = 0, the bonus draw
     n = d.n;
-    if (d.fault) return;
+    if (d.fault) return mt;
     if (n < K) {
       res.c = P.c;
       res.Rt = d.rowR(n);
@@ -673,10 +681,12 @@ __device__ __forceinline__ void sample_mass_task(const SampleParams& P, const in
       res.kq = 0xFFFFFFFFu;
     }
   } else {
-    if (!draw_row(P, b, n)) return;  // fault: nothing to draw
+    if (!draw_row(P, b, n)) return mt;  // fault: nothing to draw
     if constexpr (FILT) res = residual_of_f(P, b);
     else if (n < K) res = residual_of(P, b);
   }
+  mt.run = true;
+  mt.n = n;
   const bool bonus = !FILT && (n == K);
   const T* tr = target_row<T>(P, b, n);
   const T* dr = (n == K) ? tr : draft_row<T>(P, b, n);
@@ -687,17 +697,19 @@ __device__ __forceinline__ void sample_mass_task(const SampleParams& P, const in
   // vector chunks [c0, c1) of this segment; segment 0 adds the head, the last one the tail
   const int c0 = 1 + static_cast<int>(static_cast<int64_t>(ch.nvc) * seg / S);
   const int c1 = 1 + static_cast<int>(static_cast<int64_t>(ch.nvc) * (seg + 1) / S);
-  constexpr int W = kBlock / 64;
+  constexpr int W = BS / 64;
   if (seg == 0 && wave == 0) wave_scalar_chunk_mass<T>(P, tr, dr, ch, 0, bonus, res, cm, cs);
   if (seg == S - 1 && wave == W - 1) wave_scalar_chunk_mass<T>(P, tr, dr, ch, ch.nvc + 1, bonus, res, cm, cs);
   for (int c = c0 + wave; c < c1; c += W * kChunksPerWave)
     wave_vector_chunks_mass<T>(P, tr, dr, paired, ch, c, W, c1, bonus, res, cm, cs);
+  return mt;
 }
 
 template <typename T, bool FUSE_ACCEPT, bool FILT>
 __global__ __launch_bounds__(kBlock) void k_sample_mass(SampleParams P) {
   const int64_t ntask = static_cast<int64_t>(P.B) * P.S2;
-  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) sample_mass_task<T, FUSE_ACCEPT, FILT>(P, task);
+  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x)
+    sample_mass_task<T, FUSE_ACCEPT, FILT>(P, static_cast<int>(task / P.S2), static_cast<int>(task % P.S2), P.S2);
 }
 
 // ---------------------------------------------------------------- pass 2: the draw
@@ -753,49 +765,101 @@ __device__ int64_t block_search(int64_t lo, int64_t hi, double tau, const W& w) 
   return lp >= 0 ? lp : lo;
 }
 
+// block_search for one wave, with no barrier: the smallest k in [lo, hi) with
+// (sum of w over [lo, k]) > tau; chunk and lane offsets fp64, the run inside a
+// lane fp32; the last element with w > 0 (lo if none) when rounding leaves no crossing.
+__device__ __forceinline__ int64_t wave_max_i64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int64_t y = __shfl_xor(v, o, 64);
+    v = y > v ? y : v;
+  }
+  return v;
+}
+
+template <typename W>
+__device__ int64_t wave_search(int64_t lo, int64_t hi, double tau, const W& w) {
+  const int lane = threadIdx.x & 63;
+  double base = 0.0;
+  int64_t last_pos = -1;
+  for (int64_t c0 = lo; c0 < hi; c0 += 64 * kSearchE) {
+    const int64_t e0 = c0 + static_cast<int64_t>(lane) * kSearchE;
+    float wv[kSearchE];
+    float ts = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSearchE; ++k) {
+      const int64_t e = e0 + k;
+      wv[k] = (e < hi) ? w(e) : 0.f;
+      ts += wv[k];
+      if (wv[k] > 0.f) last_pos = e;
+    }
+    const double incl = wave_scan_add(static_cast<double>(ts));
+    const double total = lane_d(incl, 63);
+    if (base + total > tau) {
+      const int t = first_lane(base + incl > tau);
+      const double excl = incl - static_cast<double>(ts);
+      int64_t k_found = -1, k_lastpos = -1;
+      float run = 0.f;
+#pragma unroll
+      for (int k = 0; k < kSearchE; ++k) {
+        run += wv[k];
+        if (wv[k] > 0.f) k_lastpos = e0 + k;
+        if (k_found < 0 && base + excl + static_cast<double>(run) > tau) k_found = e0 + k;
+      }
+      const int64_t mine = (k_found >= 0) ? k_found : (k_lastpos >= 0 ? k_lastpos : e0);
+      return __shfl(mine, t < 64 ? t : 63, 64);
+    }
+    base += total;
+  }
+  const int64_t lp = wave_max_i64(last_pos);
+  return lp >= 0 ? lp : lo;
+}
+
 constexpr int kDrawBlock = 64;      // one wave per batch row
 constexpr int kDrawRegChunks = 10;  // chunk masses a lane keeps in registers (enough for V up to 163840)
 
-// The inverse-CDF draw of batch row b, by one wave with no barrier on its usual path:
-// one round of loads (descriptor, uniforms, this lane's run of chunk masses), an
-// fp64 lane scan of the chunk masses picks the chunk where u*Z falls, and one
-// reload of that chunk (one 16-byte vector per lane and row) with a second lane
-// scan picks the token.
+// A lane's contiguous run of the chunk masses of one batch row, held in registers
+// by the draw (lane l owns chunks [l*per, l*per + per), per = ceil(NC / 64)).
+struct DrawMasses {
+  int NC;  // chunk count the runs were laid out for
+  float cm[kDrawRegChunks];
+  double cs[kDrawRegChunks];
+};
+
+__device__ __forceinline__ void load_draw_masses(const SampleParams& P, const int b, const int NC, DrawMasses& dm) {
+  const int lane = threadIdx.x & 63;
+  const float* cm = P.p2_cm + static_cast<int64_t>(b) * P.NCmax;
+  const double* cs = P.p2_cs + static_cast<int64_t>(b) * P.NCmax;
+  const int per = (NC + 63) / 64;
+  const int j0 = min(lane * per, NC);
+  const int j1 = min(j0 + per, NC);
+  dm.NC = NC;
+#pragma unroll
+  for (int i = 0; i < kDrawRegChunks; ++i) {
+    const bool in = j0 + i < j1;
+    dm.cm[i] = in ? cm[j0 + i] : -INFINITY;
+    dm.cs[i] = in ? cs[j0 + i] : 0.0;
+  }
+}
+
+// The inverse-CDF draw of batch row b at position n (K: the bonus draw), by one
+// wave with no barrier on its usual path: an fp64 lane scan of the chunk masses
+// picks the chunk where u*Z falls, one reload of that chunk (one 16-byte vector
+// per lane and row) and a second lane scan pick the token. `res` holds the draw
+// weights (unused by the unfiltered bonus draw); `dm` the lanes' runs of chunk
+// masses when they were laid out for this row's chunk count (else they are read
+// again from the workspace).
 template <typename T, bool FILT>
-__device__ __forceinline__ void sample_draw_task(const SampleParams& P, const int b) {
+__device__ __forceinline__ void draw_core(const SampleParams& P, const int b, const int n, const float u,
+                                          const ResOf<FILT>& res, const DrawMasses& dm) {
   constexpr int VEC = Elem<T>::kVec;
   const int K = P.K;
   const int lane = threadIdx.x & 63;
   const float* cm = P.p2_cm + static_cast<int64_t>(b) * P.NCmax;
   const double* cs = P.p2_cs + static_cast<int64_t>(b) * P.NCmax;
-  // One round of loads that do not depend on the row the draw reads. Chunk
-  // geometry depends only on the 16-byte phase of the row, which every row of
-  // batch row b shares when a row is a whole number of 16-byte vectors;
-  // otherwise the masses are read again once the row is known.
-  const int n_raw = (K == 0) ? 0 : P.info_n[b];
-  const float u_lane = P.uniforms[(static_cast<int64_t>(b) * (K + 1) + min(lane, K)) * 2 + 1];
-  const float dR0 = P.info_R[2 * b], dR1 = P.info_R[2 * b + 1];
-  const double dS0 = P.info_S[2 * b], dS1 = P.info_S[2 * b + 1];
-  uint32_t dT0 = 0u, dT1 = 0u;
-  if constexpr (FILT) {
-    dT0 = P.info_T[2 * b];
-    dT1 = P.info_T[2 * b + 1];
-  }
-  const int NC0 = chunks_of(target_row<T>(P, b, 0), P.V).count();
-  const int per0 = (NC0 + 63) / 64;
-  const int j00 = min(lane * per0, NC0);
-  const int j01 = min(j00 + per0, NC0);
-  float cmr[kDrawRegChunks];
-  double csr[kDrawRegChunks];
-#pragma unroll
-  for (int i = 0; i < kDrawRegChunks; ++i) {
-    const bool in = j00 + i < j01;
-    cmr[i] = in ? cm[j00 + i] : -INFINITY;
-    csr[i] = in ? cs[j00 + i] : 0.0;
-  }
-  const int n = __builtin_amdgcn_readfirstlane(n_raw);
-  if (n < 0 || n > K) return;  // the accept pass already wrote the fault outputs
-  const float u = (n < 64) ? lane_f(u_lane, n) : P.uniforms[(static_cast<int64_t>(b) * (K + 1) + n) * 2 + 1];
+  const float (&cmr)[kDrawRegChunks] = dm.cm;
+  const double (&csr)[kDrawRegChunks] = dm.cs;
+  const int NC0 = dm.NC;
   const bool is_bonus = (n == K);
   const bool bonus = !FILT && is_bonus;  // chunk masses against chunk maxima (unfiltered bonus only)
   const T* tr = target_row<T>(P, b, n);
@@ -863,26 +927,13 @@ __device__ __forceinline__ void sample_draw_task(const SampleParams& P, const in
     if (lane == 0) P.out_n[b] = -1;
     return;
   }
-  ResOf<FILT> res{};
-  res.c = P.c;
-  res.Rt = dR0;
-  res.Rq = dR1;
-  if constexpr (FILT) {
-    res.it = inv_or_zero(dS0);
-    res.iq = inv_or_zero(dS1);
-    res.kt = dT0;
-    res.kq = dT1;
-  } else if (!is_bonus) {
-    res.it = static_cast<float>(1.0 / dS0);
-    res.iq = static_cast<float>(1.0 / dS1);
-  }
   if (!is_bonus && !(Z > 0.0 && isfinite(Z))) {
     // zero residual mass: draw from p_n (p'_n when filtered) over the whole row
     auto pw = [&](int64_t e) { return res.target(Elem<T>::get(tr, e)); };
     float a = 0.f;
-    for (int64_t e = lane; e < P.V; e += kDrawBlock) a += pw(e);
-    const double Zp = block_sum<kDrawBlock>(static_cast<double>(a));
-    const int64_t k = block_search<kDrawBlock>(0, P.V, static_cast<double>(u) * Zp, pw);
+    for (int64_t e = lane; e < P.V; e += 64) a += pw(e);
+    const double Zp = lane_d(wave_scan_add(static_cast<double>(a)), 63);
+    const int64_t k = wave_search(0, P.V, static_cast<double>(u) * Zp, pw);
     if (lane == 0) ot[n] = static_cast<int32_t>(k);
     return;
   }
@@ -994,12 +1045,48 @@ __device__ __forceinline__ void sample_draw_task(const SampleParams& P, const in
   ot[n] = static_cast<int32_t>(k);
 }
 
+// The draw as its own kernel: one round of loads that do not depend on the row
+// the draw reads (the descriptor, every draw uniform, and the lane's run of chunk
+// masses). Chunk geometry depends only on the 16-byte phase of the row, which
+// every row of batch row b shares when a row is a whole number of 16-byte
+// vectors; otherwise draw_core reads the masses again once the row is known.
+template <typename T, bool FILT>
+__device__ __forceinline__ void sample_draw_task(const SampleParams& P, const int b) {
+  const int K = P.K;
+  const int lane = threadIdx.x & 63;
+  const int n_raw = (K == 0) ? 0 : P.info_n[b];
+  const float u_lane = P.uniforms[(static_cast<int64_t>(b) * (K + 1) + min(lane, K)) * 2 + 1];
+  const float dR0 = P.info_R[2 * b], dR1 = P.info_R[2 * b + 1];
+  const double dS0 = P.info_S[2 * b], dS1 = P.info_S[2 * b + 1];
+  uint32_t dT0 = 0u, dT1 = 0u;
+  if constexpr (FILT) {
+    dT0 = P.info_T[2 * b];
+    dT1 = P.info_T[2 * b + 1];
+  }
+  DrawMasses dm;
+  load_draw_masses(P, b, chunks_of(target_row<T>(P, b, 0), P.V).count(), dm);
+  const int n = __builtin_amdgcn_readfirstlane(n_raw);
+  if (n < 0 || n > K) return;  // the accept pass already wrote the fault outputs
+  const float u = (n < 64) ? lane_f(u_lane, n) : P.uniforms[(static_cast<int64_t>(b) * (K + 1) + n) * 2 + 1];
+  ResOf<FILT> res{};
+  res.c = P.c;
+  res.Rt = dR0;
+  res.Rq = dR1;
+  if constexpr (FILT) {
+    res.it = inv_or_zero(dS0);
+    res.iq = inv_or_zero(dS1);
+    res.kt = dT0;
+    res.kq = dT1;
+  } else if (n < K) {
+    res.it = static_cast<float>(1.0 / dS0);
+    res.iq = static_cast<float>(1.0 / dS1);
+  }
+  draw_core<T, FILT>(P, b, n, u, res, dm);
+}
+
 template <typename T, bool FILT>
 __global__ __launch_bounds__(kDrawBlock) void k_sample_draw(SampleParams P) {
-  for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) {
-    sample_draw_task<T, FILT>(P, static_cast<int>(task));
-    __syncthreads();  // the zero-residual search's shared memory is reused by the next task
-  }
+  for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) sample_draw_task<T, FILT>(P, static_cast<int>(task));
 }
 
 // ---------------------------------------------------------------- launch
