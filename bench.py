@@ -12,8 +12,10 @@ Steps are launched from HIP graphs that each hold a run of consecutive steps
 --steps steps, is bracketed by HIP events on the stream the kernels run on.
 
 Prints ONE JSON line. Also reported: the pass-1 kernel alone (the dominant
-kernel, for the roofline), the same round verified on top-k 50 / top-p 0.9
-filtered laws (spec_verify_sample_filtered), the greedy verify on its own
+kernel, for the roofline), the same round with early exit (pass 1 in stages,
+spec_verify_sample_staged, which must give the same outputs), the same round
+verified on top-k 50 / top-p 0.9 filtered laws (spec_verify_sample_filtered),
+the greedy verify on its own
 workload (B=32 G=7 N=5 V=32000 bf16), and the CPU oracle on a bounded sample of
 the same round.
 """
@@ -52,6 +54,7 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-greedy", action="store_true")
     ap.add_argument("--no-filtered", action="store_true", help="skip the top-k / top-p filtered leg")
+    ap.add_argument("--no-staged", action="store_true", help="skip the early-exit (staged pass 1) leg")
     ap.add_argument("--eager", action="store_true", help="launch through the Python binding instead of graphs")
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB copy (calibration), then 3 eager verify rounds "
@@ -178,6 +181,7 @@ def cpu_model() -> str:
 
 CHUNK_STEPS = 48   # verify steps per HIP graph (a graph launch costs about as much as a short kernel)
 FILTER_K, FILTER_P = 50, 0.9
+STAGES = [3, 8]  # early-exit leg: pass 1 reads positions 0..2, then 3..7 of the rows still walking
 
 
 class GraphSteps:
@@ -341,6 +345,40 @@ def main() -> int:
         f"pass 1 {t_pass1 * 1e6:.2f} us ({pass1_gbps:.0f} GB/s); mean accepted {n_acc.mean():.3f}")
     del steps
 
+    # ---------------------------------------------------------------- the same round with early exit (pass 1 in stages)
+    staged = None
+    if not args.no_staged:
+        stages = STAGES
+
+        def scall(st, phases=rsv.PHASE_ALL):
+            rsv.verify_sample_staged(st["target"], st["draft"], st["draft_tokens"], st["uniforms"], s.temperature,
+                                     stages, out_tokens=st["out_tokens"], out_num_accepted=st["out_n"], workspace=ws)
+
+        for st in sets:
+            scall(st)
+        torch.cuda.synchronize()
+        sn = sets[0]["out_n"].cpu().numpy()
+        # the outputs match the one-pass verify's except where a decision sits within rounding of
+        # its boundary (the stages split rows into other segments); the parity tests hold both to the oracle
+        same = bool(np.array_equal(sn, n_acc) and np.array_equal(sets[0]["out_tokens"].cpu().numpy(), tok))
+        ssteps = GraphSteps(torch, lambda i, ph: scall(sets[i % M], ph), M, args.eager)
+        ssteps.prepare(rsv.PHASE_ALL, n_list)
+        ssteps.timed(rsv.PHASE_ALL, args.warmup)
+        ts_step = ssteps.timed(rsv.PHASE_ALL, args.steps) / args.steps
+        del ssteps
+        # bytes this design reads: pass 1 through the stage holding each row's first
+        # rejection (every stage when all K are accepted), then pass 2 as before
+        read_pos = [next(e for e in stages if int(n) < e) if int(n) < K else K for n in n_acc]
+        sbytes = int(sum(2 * p * row_bytes for p in read_pos)) + pass2_bytes + small_bytes
+        staged = {"workload": f"{WORKLOAD_NAMES[3]}; pass 1 in stages ending at positions {stages}",
+                  "rounds_per_s": round(1.0 / ts_step, 1), "us_per_round": round(ts_step * 1e6, 3),
+                  "speedup_vs_one_pass": round(t_step / ts_step, 4), "same_outputs_as_one_pass": same,
+                  "algorithmic_bytes_per_step": sbytes, "bytes_vs_one_pass": round(sbytes / step_bytes, 4),
+                  "achieved_gbps": round(sbytes / ts_step / 1e9, 1),
+                  "frac_of_hbm_peak": round(sbytes / ts_step / 1e9 / HBM_PEAK_GBPS, 4)}
+        log(f"staged {stages}: {ts_step * 1e6:.2f} us ({1.0 / ts_step:.0f} rounds/s), "
+            f"{sbytes / 1e6:.1f} MB read ({sbytes / step_bytes:.2f} of one pass)")
+
     # ---------------------------------------------------------------- the same round, top-k 50 / top-p 0.9 filtered
     filtered = None
     if not args.no_filtered:
@@ -473,6 +511,7 @@ def main() -> int:
                      "traffic": traffic, "algorithmic_bytes": pass1_bytes,
                      "us_per_launch": round(t_pass1 * 1e6, 3)},
         "cpu_baseline": cpu,
+        "staged": staged,
         "greedy": greedy,
         "filtered": filtered,
     }

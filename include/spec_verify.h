@@ -68,10 +68,12 @@ typedef enum {
   SPEC_ERR_HIP = -6,         /* a HIP launch failed */
   SPEC_ERR_ALIGN = -7,       /* a pointer is not aligned to its element size */
   SPEC_ERR_PHASE = -8,       /* phase mask outside 1..15 (spec_verify_sample_phases) */
-  SPEC_ERR_FILTER_V = -9     /* V > SPEC_MAX_FILTER_V (spec_verify_sample_filtered) */
+  SPEC_ERR_FILTER_V = -9,    /* V > SPEC_MAX_FILTER_V (spec_verify_sample_filtered) */
+  SPEC_ERR_STAGES = -10      /* invalid stage schedule (spec_verify_sample_staged) */
 } spec_status;
 
 #define SPEC_MAX_FILTER_V (1 << 24) /* vocabulary entries per row of the filtered verify */
+#define SPEC_MAX_STAGES 8           /* pass-1 stages of spec_verify_sample_staged */
 
 /* Bytes of workspace spec_verify_sample needs for these sizes (0 for invalid sizes). */
 size_t spec_verify_sample_workspace_size(int32_t B, int32_t K, int32_t V);
@@ -140,6 +142,33 @@ spec_status spec_verify_sample_phases(const void* target_logits, const void* dra
                                       int32_t V, float temperature, int32_t* out_tokens,
                                       int32_t* out_num_accepted, float* out_probs, void* workspace,
                                       size_t workspace_bytes, void* stream, int32_t phases);
+
+/*
+ * spec_verify_sample with early exit: the draft positions are read in stages, and
+ * a stage reads the rows of a batch row only if every earlier position was
+ * accepted. The walk stops at the first rejection, so the rows past it are never
+ * needed ("Speculative Decoding —— LLM推理优化技术（一）" §2.3: the first rejected
+ * draft ends the round). The stages cost one launch each; a workload whose drafts
+ * are often rejected early reads fewer bytes, one that accepts most drafts pays
+ * the extra launches.
+ *
+ * Arguments, workspace (spec_verify_sample_workspace_size) and outputs as
+ * spec_verify_sample, plus:
+ * stage_ends   HOST array of num_stages draft positions, strictly increasing, in
+ *              [1, K], the last equal to K: stage s reads positions
+ *              [stage_ends[s-1], stage_ends[s]) (from 0 for s = 0). With K = 0,
+ *              num_stages is 0 and stage_ends may be NULL. Otherwise
+ *              1 <= num_stages <= SPEC_MAX_STAGES. SPEC_ERR_STAGES for any other schedule.
+ * Every output equals spec_verify_sample's, except that with more than one stage
+ * out_probs[b, i] is NaN for positions i past the first rejection n (not every
+ * such row is read).
+ */
+spec_status spec_verify_sample_staged(const void* target_logits, const void* draft_logits, int32_t dtype,
+                                      const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t K,
+                                      int32_t V, float temperature, int32_t* out_tokens,
+                                      int32_t* out_num_accepted, float* out_probs, void* workspace,
+                                      size_t workspace_bytes, void* stream, const int32_t* stage_ends,
+                                      int32_t num_stages);
 
 /* Bytes of workspace spec_verify_sample_filtered needs for these sizes (0 for invalid sizes). */
 size_t spec_verify_sample_filtered_workspace_size(int32_t B, int32_t K, int32_t V);

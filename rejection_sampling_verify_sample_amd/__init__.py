@@ -3,17 +3,18 @@
 Entry points (torch tensors in, torch tensors out; every computation runs in HIP):
   verify_sample  -- rejection-sampling verify of K draft tokens per row
   verify_sample_filtered -- the same on top-k / top-p filtered laws (same filter on both sides)
+  verify_sample_staged -- verify_sample with early exit: pass 1 in stages over the draft positions
   verify_greedy  -- greedy longest-prefix verify of G candidate n-grams
   fill_uniforms  -- Philox4x32-10 verify uniforms on the device
 """
 from ._lib import (LIB_PATH, PHASE_ACCEPT, PHASE_ALL, PHASE_DRAW, PHASE_MASS, PHASE_ROW_STATS, SPEC_BF16, SPEC_F32, SPEC_MAX_K, GreedyOutputs, SampleOutputs, SpecVerifyError,
                    abi_version, fill_uniforms, greedy_workspace_size, lib, sample_filtered_workspace_size,
                    sample_workspace_size, status_string, verify_greedy, verify_sample, verify_sample_filtered,
-                   workspace_for)
+                   verify_sample_staged, workspace_for)
 
 __all__ = [
     "LIB_PATH", "PHASE_ACCEPT", "PHASE_ALL", "PHASE_DRAW", "PHASE_MASS", "PHASE_ROW_STATS", "SPEC_BF16", "SPEC_F32", "SPEC_MAX_K", "GreedyOutputs", "SampleOutputs", "SpecVerifyError",
     "abi_version", "fill_uniforms", "greedy_workspace_size", "lib", "sample_filtered_workspace_size",
     "sample_workspace_size", "status_string", "verify_greedy", "verify_sample", "verify_sample_filtered",
-    "workspace_for",
+    "verify_sample_staged", "workspace_for",
 ]

@@ -36,6 +36,9 @@ _SIGNATURES = {
     "spec_verify_sample_phases": (_i32, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                          ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
                                          _c_void_p, _i32]),
+    "spec_verify_sample_staged": (_i32, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                         ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
+                                         _c_void_p, _c_void_p, _i32]),
     "spec_verify_sample_filtered_workspace_size": (_size_t, [_i32, _i32, _i32]),
     "spec_verify_sample_filtered": (_i32, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                            ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
@@ -175,6 +178,22 @@ def verify_sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch
                           out_probs, want_probs, workspace, stream, phases, None)
 
 
+def verify_sample_staged(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                         uniforms: torch.Tensor, temperature: float, stages, *,
+                         out_tokens: torch.Tensor | None = None, out_num_accepted: torch.Tensor | None = None,
+                         out_probs: torch.Tensor | None = None, want_probs: bool = False,
+                         workspace: torch.Tensor | None = None, stream=None) -> SampleOutputs:
+    """spec_verify_sample_staged: the verify with early exit over pass-1 stages.
+
+    `stages` lists the stage ends (strictly increasing draft positions, the last
+    one K; empty when K = 0). Outputs equal verify_sample's, except that with
+    more than one stage out_probs is NaN past the first rejection.
+    """
+    ends = [int(e) for e in stages]
+    return _verify_sample(target, draft, draft_tokens, uniforms, temperature, out_tokens, out_num_accepted,
+                          out_probs, want_probs, workspace, stream, PHASE_ALL, None, ends)
+
+
 def verify_sample_filtered(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
                            uniforms: torch.Tensor, temperature: float, top_k: torch.Tensor | None,
                            top_p: torch.Tensor | None, *, out_tokens: torch.Tensor | None = None,
@@ -192,7 +211,7 @@ def verify_sample_filtered(target: torch.Tensor, draft: torch.Tensor, draft_toke
 
 
 def _verify_sample(target, draft, draft_tokens, uniforms, temperature, out_tokens, out_num_accepted, out_probs,
-                   want_probs, workspace, stream, phases, filt) -> SampleOutputs:
+                   want_probs, workspace, stream, phases, filt, stages=None) -> SampleOutputs:
     if target.dim() != 3:
         raise ValueError("target must be [B, K+1, V]")
     B, K1, V = target.shape
@@ -241,6 +260,9 @@ def _verify_sample(target, draft, draft_tokens, uniforms, temperature, out_token
         else:
             st, where = (lib().spec_verify_sample_filtered_phases(*args, *fargs, int(phases)),
                          "spec_verify_sample_filtered_phases")
+    elif stages is not None:
+        arr = (ctypes.c_int32 * max(1, len(stages)))(*stages)
+        st, where = lib().spec_verify_sample_staged(*args, arr, len(stages)), "spec_verify_sample_staged"
     elif phases == PHASE_ALL:
         st, where = lib().spec_verify_sample(*args), "spec_verify_sample"
     else:

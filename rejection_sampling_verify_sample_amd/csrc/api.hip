@@ -51,6 +51,19 @@ bool sample_shape_ok(int32_t B, int32_t K, int32_t V) {
   return static_cast<int64_t>(B) * (2 * static_cast<int64_t>(K) + 1) <= SPEC_MAX_ROWS;
 }
 
+// A pass-1 schedule: strictly increasing stage ends in [1, K], the last one K
+// (K = 0: no stage).
+bool stages_ok(int32_t K, const int32_t* ends, int32_t n) {
+  if (K == 0) return n == 0;
+  if (!ends || n < 1 || n > SPEC_MAX_STAGES) return false;
+  int32_t prev = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (ends[i] <= prev || ends[i] > K) return false;
+    prev = ends[i];
+  }
+  return prev == K;
+}
+
 bool greedy_shape_ok(int32_t B, int32_t G, int32_t N, int32_t V) {
   if (B < 0 || G < 1 || N < 2 || N > SPEC_MAX_K + 1 || V < 1 || V > SPEC_MAX_V) return false;
   if (static_cast<int64_t>(G) * N > sv::kMaxGreedyRowsPerBatch) return false;
@@ -78,6 +91,7 @@ SampleLayout sample_layout(int32_t B, int32_t K, int32_t V) {
   const size_t p2 = static_cast<size_t>(B) * L.NCmax;
   L.off_p2cm = off; off = align256(off + p2 * sizeof(float));
   L.off_p2cs = off; off = align256(off + p2 * sizeof(double));
+  L.off_alive = off; off = align256(off + static_cast<size_t>(B) * sizeof(int32_t));
   // filtered entry point: one (reference, kept mass, threshold) per logit row
   const size_t rows = static_cast<size_t>(B) * (2 * static_cast<size_t>(K) + 1);
   L.off_fR = off; off = align256(off + rows * sizeof(float));
@@ -124,6 +138,7 @@ SPEC_EXPORT const char* spec_status_string(int32_t status) {
     case SPEC_ERR_ALIGN: return "a pointer is not aligned to its element size";
     case SPEC_ERR_PHASE: return "phase mask outside 1..15";
     case SPEC_ERR_FILTER_V: return "vocabulary too large for the filtered verify";
+    case SPEC_ERR_STAGES: return "invalid stage schedule (strictly increasing ends in [1, K], the last K)";
     default: return "unknown status";
   }
 }
@@ -149,8 +164,10 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
                                  int32_t V, float temperature, int32_t* out_tokens, int32_t* out_num_accepted,
                                  float* out_probs, void* workspace, size_t workspace_bytes, void* stream,
                                  int phases, bool filtered = false, const int32_t* top_k = nullptr,
-                                 const float* top_p = nullptr, int32_t* out_kept = nullptr) {
+                                 const float* top_p = nullptr, int32_t* out_kept = nullptr,
+                                 const int32_t* stage_ends = nullptr, int32_t num_stages = -1) {
   if (!sample_shape_ok(B, K, V)) return SPEC_ERR_SHAPE;
+  if (num_stages >= 0 && !stages_ok(K, stage_ends, num_stages)) return SPEC_ERR_STAGES;
   if (filtered && V > sv::kMaxFilterV) return SPEC_ERR_FILTER_V;
   if (phases < 1 || phases > sv::kPhaseAll) return SPEC_ERR_PHASE;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
@@ -181,6 +198,27 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
   P.c = c;
   P.S1 = L.S1;
   P.S2 = L.S2;
+  P.S1max = L.S1max;
+  if (num_stages > 0) {
+    // early exit: per-stage segment counts from the stage's own row count
+    P.nstage = num_stages;
+    int32_t a = 0;
+    for (int32_t st = 0; st < num_stages; ++st) {
+      P.stage_end[st] = stage_ends[st];
+      // a later stage reads only the batch rows still walking: its segments are sized
+      // as if a quarter of them were, so that few survivors still spread over the chip
+      const int64_t rows = static_cast<int64_t>(B) * 2 * (stage_ends[st] - a);
+      P.stage_S1[st] = seg_choice(st == 0 ? rows : ceil_div(rows, 4), V, 1024, 8192, L.S1max,
+                                  st == 0 ? "SPECVERIFY_S1" : "SPECVERIFY_S1L");
+      a = stage_ends[st];
+    }
+    P.probs_past_n = num_stages == 1;
+  } else {
+    P.nstage = 1;
+    P.stage_end[0] = K;
+    P.stage_S1[0] = L.S1;
+    P.probs_past_n = 1;
+  }
   P.out_tokens = out_tokens;
   P.out_n = out_num_accepted;
   P.out_probs = out_probs;
@@ -193,6 +231,7 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
   P.p1_x = at<float>(workspace, L.off_p1x);
   P.p2_cm = at<float>(workspace, L.off_p2cm);
   P.p2_cs = at<double>(workspace, L.off_p2cs);
+  P.stage_alive = at<int32_t>(workspace, L.off_alive);
   if (filtered) {
     P.top_k = top_k;
     P.top_p = top_p;
@@ -221,6 +260,12 @@ SPEC_EXPORT spec_status spec_verify_sample(SPEC_SAMPLE_ARGS) {
 }
 SPEC_EXPORT spec_status spec_verify_sample_phases(SPEC_SAMPLE_ARGS, int32_t phases) {
   return verify_sample_phases(SPEC_SAMPLE_FWD, phases);
+}
+
+SPEC_EXPORT spec_status spec_verify_sample_staged(SPEC_SAMPLE_ARGS, const int32_t* stage_ends, int32_t num_stages) {
+  if (num_stages < 0) return SPEC_ERR_STAGES;
+  return verify_sample_phases(SPEC_SAMPLE_FWD, sv::kPhaseAll, false, nullptr, nullptr, nullptr, stage_ends,
+                              num_stages);
 }
 
 #define SPEC_FILTER_ARGS const int32_t *top_k, const float *top_p, int32_t *out_kept

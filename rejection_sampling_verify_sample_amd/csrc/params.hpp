@@ -8,6 +8,8 @@ namespace sv {
 
 // ---------------------------------------------------------------- sampling verify
 
+constexpr int kMaxStages = 8;  // pass-1 stages of the early-exit verify
+
 struct SampleParams {
   const void* target;      // [B, K+1, V]
   const void* draft;       // [B, K, V]
@@ -15,14 +17,23 @@ struct SampleParams {
   const float* uniforms;   // [B, K+1, 2]
   int32_t B, K, V;
   float c;                 // log2(e) / T, rounded to fp32
-  int32_t S1, S2;          // segments per row in pass 1 / workgroups per batch row in pass 2
+  int32_t S1, S2;          // segments per row in pass 1 (the widest stage) / workgroups per batch row in pass 2
+  int32_t S1max;           // partial slots per logit row: the stride of p1_m / p1_s
+  // Pass 1 in stages over the draft positions (early exit): stage s reads positions
+  // [stage_end[s-1], stage_end[s]) with stage_S1[s] segments per row, only for batch
+  // rows that accepted every earlier position. One stage: every position at once.
+  int32_t nstage;
+  int32_t stage_end[kMaxStages];
+  int32_t stage_S1[kMaxStages];
+  int32_t probs_past_n;    // out_probs after the first rejection: 1 = computed, 0 = NaN (not every row is read)
+  int32_t* stage_alive;    // [B] 1 when the walk accepted every position before the current stage
   int32_t* out_tokens;     // [B, K+1]
   int32_t* out_n;          // [B]
   float* out_probs;        // [B, K, 2] or null
   // workspace (written by one kernel, read by a later one: no counters, no clearing)
   int32_t NCmax;           // chunk slots per batch row in p2_cm / p2_cs
-  float* p1_m;             // [B*2K*S1] segment maxima (row statistics)
-  double* p1_s;            // [B*2K*S1] segment sums against fl(m*c)
+  float* p1_m;             // [B*2K*S1max] segment maxima (row statistics)
+  double* p1_s;            // [B*2K*S1max] segment sums against fl(m*c)
   float* p1_x;             // [B*2K] logit of the draft token in each row (NaN if the token is out of range)
   int32_t* info_n;         // [B] first rejection n, K when all accepted, -1 on a fault (accept decisions)
   float* info_R;           // [B, 2] reference exponents of target row n, draft row n
@@ -51,7 +62,7 @@ enum SamplePhase : int {
 struct SampleLayout {
   int32_t S1, S2, S1max, S2max;
   int32_t NCmax;
-  size_t off_p1m, off_p1s, off_p1x, off_info_n, off_info_R, off_info_S, off_p2cm, off_p2cs;
+  size_t off_p1m, off_p1s, off_p1x, off_info_n, off_info_R, off_info_S, off_p2cm, off_p2cs, off_alive;
   size_t off_fR, off_fS, off_fthr, off_infoT;  // filtered entry point only
   size_t total;
 };

@@ -100,19 +100,45 @@ __device__ __forceinline__ void online_segment(const T* row, int64_t V, int seg,
   if (seg == S - 1) online_scalar<BS>(row, r.head + ((V - r.head) / VEC) * VEC, V, c, o);
 }
 
-// Merge segment partials (m_j, s_j) of one row, in segment order.
+// Merge segment partials (m_j, s_j) of one row, in segment order. Each partial is
+// rescaled from its reference fl(m_j * c) to the row's by 2^d, with d the exact
+// fp64 difference of the two references and 2^d from the hardware unit (about
+// 1e-7 relative, the order of the fp32 sums inside each partial); the partial
+// holding the maximum needs no rescale.
+// Up to kMergeRegs partials are loaded at once (one round of loads, held in
+// registers); a row split into more segments is read in a loop.
+constexpr int kMergeRegs = 16;
+
+__device__ __forceinline__ double rescaled_partial(double sj, float Rj, float RMf) {
+  if (!(sj > 0.0)) return 0.0;
+  return (Rj == RMf) ? sj
+                     : sj * static_cast<double>(exp2_hw(static_cast<float>(static_cast<double>(Rj) -
+                                                                           static_cast<double>(RMf))));
+}
+
 __device__ __forceinline__ void merge_partials(const float* pm, const double* ps, int S, float c, float& M,
                                                double& Ssum) {
   M = -INFINITY;
+  Ssum = 0.0;
+  if (S <= kMergeRegs) {
+    float mv[kMergeRegs];
+    double sv[kMergeRegs];
+#pragma unroll
+    for (int j = 0; j < kMergeRegs; ++j) {
+      const bool in = j < S;
+      mv[j] = in ? pm[j] : -INFINITY;
+      sv[j] = in ? ps[j] : 0.0;
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeRegs; ++j) M = fmaxf(M, mv[j]);
+    const float RMf = M * c;
+#pragma unroll
+    for (int j = 0; j < kMergeRegs; ++j) Ssum += rescaled_partial(sv[j], mv[j] * c, RMf);
+    return;
+  }
   for (int j = 0; j < S; ++j) M = fmaxf(M, pm[j]);
   const float RMf = M * c;
-  const double RM = static_cast<double>(RMf);
-  Ssum = 0.0;
-  for (int j = 0; j < S; ++j) {
-    const double sj = ps[j];
-    const float Rj = pm[j] * c;
-    if (sj > 0.0) Ssum += (Rj == RMf) ? sj : sj * exp2(static_cast<double>(Rj) - RM);
-  }
+  for (int j = 0; j < S; ++j) Ssum += rescaled_partial(ps[j], pm[j] * c, RMf);
 }
 
 template <typename T>
@@ -202,16 +228,20 @@ __device__ __forceinline__ int64_t block_max_i64(int64_t v) {
 
 // ---------------------------------------------------------------- row statistics (pass 1)
 
+// Segments per row of the pass-1 stage that holds draft position `pos`.
+__device__ __forceinline__ int stage_segments(const SampleParams& P, int pos) {
+  int S = P.stage_S1[0];
+  for (int s = 1; s < P.nstage; ++s)
+    if (pos >= P.stage_end[s - 1]) S = P.stage_S1[s];
+  return S;
+}
+
+// Task `task` of pass-1 stage `stage`: positions [a, e) of every batch row, target
+// rows then draft rows, in memory order.
 template <typename T>
-__device__ __forceinline__ void sample_rowstats_task(const SampleParams& P, const int64_t task) {
-  const int K = P.K, S = P.S1;
-  const int seg = static_cast<int>(task % S);
-  // tasks walk the target rows of every batch row, then the draft rows, in memory order
-  const int t = static_cast<int>(task / S);
-  const bool is_draft = t >= P.B * K;
-  const int tb = is_draft ? t - P.B * K : t;
-  const int b = tb / K;
-  const int pos = tb - b * K;
+__device__ __forceinline__ void rowstats_row(const SampleParams& P, const int b, const int pos, const bool is_draft,
+                                             const int seg, const int S) {
+  const int K = P.K;
   const int j = is_draft ? K + pos : pos;
   const int row = b * 2 * K + j;  // partial slot: j < K target row j, else draft row j-K
   const T* rp = (j < K) ? target_row<T>(P, b, j) : draft_row<T>(P, b, pos);
@@ -228,20 +258,12 @@ __device__ __forceinline__ void sample_rowstats_task(const SampleParams& P, cons
   double s;
   block_online<kRowBlock>(o, P.c, m, s);
   if (threadIdx.x == 0) {
-    P.p1_m[static_cast<int64_t>(row) * S + seg] = m;
-    P.p1_s[static_cast<int64_t>(row) * S + seg] = s;
+    P.p1_m[static_cast<int64_t>(row) * P.S1max + seg] = m;
+    P.p1_s[static_cast<int64_t>(row) * P.S1max + seg] = s;
     if (seg == 0) P.p1_x[row] = xl;
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kRowBlock) void k_sample_rowstats(SampleParams P) {
-  const int64_t ntask = static_cast<int64_t>(P.B) * 2 * P.K * P.S1;
-  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
-    sample_rowstats_task<T>(P, task);
-    __syncthreads();  // shared memory is reused by the next task
-  }
-}
 
 // ---------------------------------------------------------------- accept tests and first rejection
 
@@ -273,14 +295,17 @@ __device__ __forceinline__ int64_t filt_row(const SampleParams& P, int b, int j)
 
 // FILT: the rows' laws are the top-k / top-p filtered ones, described by the
 // filter kernel's (reference, kept mass, key threshold) per row.
+// klim < K replays the walk over positions [0, klim) only (a pass-1 stage asking
+// whether its batch row is still needed): n = klim when none of them stops it.
 template <bool FILT>
-__device__ __forceinline__ void decide_wave(const SampleParams& P, const int b, const bool write, WaveDecision& d) {
-  const int K = P.K, S = P.S1;
+__device__ __forceinline__ void decide_wave(const SampleParams& P, const int b, const bool write, WaveDecision& d,
+                                            const int klim) {
+  const int K = P.K;
   const int lane = threadIdx.x & 63;
   // the draft token and accept uniform of position `lane`, fetched with the row statistics
   int x = 0;
   float r_acc = 0.f;
-  if (lane < K) {
+  if (lane < klim) {
     x = P.tokens[static_cast<int64_t>(b) * K + lane];
     r_acc = P.uniforms[(static_cast<int64_t>(b) * (K + 1) + lane) * 2];
   }
@@ -288,11 +313,12 @@ __device__ __forceinline__ void decide_wave(const SampleParams& P, const int b, 
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int j = lane + 64 * h;
+    const int posj = j < K ? j : j - K;
     prob[h] = __builtin_nanf("");
     d.R[h] = 0.f;
     d.S[h] = 0.0;
     d.T[h] = 0u;
-    if (j < 2 * K) {
+    if (j < 2 * K && posj < klim) {
       const int64_t r = static_cast<int64_t>(b) * 2 * K + j;
       const float xl = P.p1_x[r];
       if constexpr (FILT) {
@@ -310,7 +336,7 @@ __device__ __forceinline__ void decide_wave(const SampleParams& P, const int b, 
       } else {
         float M;
         double Ssum;
-        merge_partials(P.p1_m + r * S, P.p1_s + r * S, S, P.c, M, Ssum);
+        merge_partials(P.p1_m + r * P.S1max, P.p1_s + r * P.S1max, stage_segments(P, posj), P.c, M, Ssum);
         const float R = M * P.c;
         d.R[h] = R;
         d.S[h] = Ssum;
@@ -327,7 +353,7 @@ __device__ __forceinline__ void decide_wave(const SampleParams& P, const int b, 
   const float p = prob[0];
   const float q = (jq < 64) ? q0 : q1;
   bool stop = false, flt = false;
-  if (lane < K) {
+  if (lane < klim) {
     if (x >= 0 && x < P.V && !isnan(p) && !isnan(q)) {
       // alpha = min(1, p/q), truncated to 1 without dividing when p >= q; 0 when p = 0
       const float alpha = (p == 0.f) ? 0.f : ((p >= q) ? 1.f : p / q);
@@ -339,8 +365,8 @@ __device__ __forceinline__ void decide_wave(const SampleParams& P, const int b, 
   }
   const uint64_t stops = __ballot(stop);
   const uint64_t faults = __ballot(flt);
-  const int n = stops ? (__ffsll(static_cast<unsigned long long>(stops)) - 1) : K;
-  const bool fault = (n < K) && ((faults >> n) & 1ull);
+  const int n = stops ? (__ffsll(static_cast<unsigned long long>(stops)) - 1) : klim;
+  const bool fault = (n < klim) && ((faults >> n) & 1ull);
   d.n = n;
   d.fault = fault;
   if (!write) return;
@@ -350,8 +376,10 @@ __device__ __forceinline__ void decide_wave(const SampleParams& P, const int b, 
     else if (i < n) ot[i] = x;  // i < n <= K <= 64, so i is this lane's position
   }
   if (P.out_probs && lane < K) {
-    P.out_probs[(static_cast<int64_t>(b) * K + lane) * 2] = p;
-    P.out_probs[(static_cast<int64_t>(b) * K + lane) * 2 + 1] = q;
+    // positions after the first rejection: NaN when pass 1 may not have read them
+    const bool known = P.probs_past_n || lane <= n;
+    P.out_probs[(static_cast<int64_t>(b) * K + lane) * 2] = known ? p : __builtin_nanf("");
+    P.out_probs[(static_cast<int64_t>(b) * K + lane) * 2 + 1] = known ? q : __builtin_nanf("");
   }
   // the draw descriptor: references and denominators of the rows the draw reads
   float R0 = 0.f, R1 = 0.f;
@@ -397,7 +425,83 @@ template <bool FILT>
 __global__ __launch_bounds__(kAcceptBlock) void k_sample_accept(SampleParams P) {
   for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) {
     WaveDecision d;
-    decide_wave<FILT>(P, static_cast<int>(task), true, d);
+    decide_wave<FILT>(P, static_cast<int>(task), true, d, P.K);
+  }
+}
+
+// ---------------------------------------------------------------- pass-1 kernel
+
+// Pass 1, or its first stage: positions [0, e) of every batch row, target rows
+// then draft rows, in memory order.
+template <typename T>
+__global__ __launch_bounds__(kRowBlock) void k_sample_rowstats(SampleParams P, int stage) {
+  const int e = P.stage_end[stage];
+  const int S = P.stage_S1[stage];
+  const int64_t ntask = static_cast<int64_t>(P.B) * 2 * e * S;
+  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
+    const int seg = static_cast<int>(task % S);
+    const int t = static_cast<int>(task / S);
+    const bool is_draft = t >= P.B * e;
+    const int tb = is_draft ? t - P.B * e : t;
+    const int b = tb / e;
+    rowstats_row<T>(P, b, tb - b * e, is_draft, seg, S);
+    __syncthreads();  // shared memory is reused by the next task
+  }
+}
+
+// Before a later stage: one wave per batch row replays the accept walk over the
+// positions before the stage (from their statistics) and flags the rows it did
+// not stop.
+constexpr int kAliveBlock = 1024;
+
+__global__ __launch_bounds__(kAliveBlock) void k_stage_alive(SampleParams P, int a) {
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * (kAliveBlock / 64) + (threadIdx.x >> 6);
+  if (b >= P.B) return;  // b is uniform across the wave
+  WaveDecision d;
+  decide_wave<false>(P, static_cast<int>(b), false, d, a);
+  if ((threadIdx.x & 63) == 0) P.stage_alive[b] = (!d.fault && d.n == a) ? 1 : 0;
+}
+
+// The li-th flagged batch row (wave-uniform; -1 past the last).
+__device__ __forceinline__ int nth_alive(const SampleParams& P, int64_t li) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t b0 = 0; b0 < P.B; b0 += 64) {
+    const int64_t bb = b0 + lane;
+    uint64_t m = __ballot(bb < P.B && P.stage_alive[bb] != 0);
+    const int c = __popcll(m);
+    if (li < c) {
+      for (int64_t k = 0; k < li; ++k) m &= m - 1;
+      return static_cast<int>(b0 + __ffsll(static_cast<unsigned long long>(m)) - 1);
+    }
+    li -= c;
+  }
+  return -1;
+}
+
+// A later pass-1 stage: positions [a, e) of the flagged batch rows only, their
+// segments spread over a fixed grid (the count of flagged rows is known only on
+// the device).
+template <typename T>
+__global__ __launch_bounds__(kRowBlock) void k_sample_rowstats_alive(SampleParams P, int stage) {
+  const int a = P.stage_end[stage - 1];
+  const int npos = P.stage_end[stage] - a;
+  const int S = P.stage_S1[stage];
+  const int lane = threadIdx.x & 63;
+  int64_t count = 0;
+  for (int64_t b0 = 0; b0 < P.B; b0 += 64) {
+    const int64_t bb = b0 + lane;
+    count += __popcll(__ballot(bb < P.B && P.stage_alive[bb] != 0));
+  }
+  const int64_t per_row = static_cast<int64_t>(2) * npos * S;
+  const int64_t ntask = count * per_row;
+  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
+    const int b = nth_alive(P, task / per_row);
+    const int r = static_cast<int>(task % per_row);
+    const int seg = r % S;
+    const int t = r / S;
+    const bool is_draft = t >= npos;
+    rowstats_row<T>(P, b, a + (is_draft ? t - npos : t), is_draft, seg, S);
+    __syncthreads();  // shared memory is reused by the next task
   }
 }
 
@@ -654,7 +758,7 @@ __device__ __forceinline__ MassTask<FILT> sample_mass_task(const SampleParams& P
   if (FUSE_ACCEPT) {
     // every wave takes the decisions itself (no barrier); wave 0 of segment 0 writes them out
     WaveDecision d;
-    decide_wave<FILT>(P, b, seg == 0 && wave == 0, d);  // with K = 0: n = 0, the bonus draw
+    decide_wave<FILT>(P, b, seg == 0 && wave == 0, d, K);  // with K = 0: n = 0, the bonus draw
     n = d.n;
     if (d.fault) return mt;
     if (n < K) {
@@ -1095,6 +1199,8 @@ __global__ __launch_bounds__(kDrawBlock) void k_sample_draw(SampleParams P) {
 // every kernel loops over its tasks with a workgroup stride.
 constexpr int64_t kMaxGrid = 1 << 20;
 
+constexpr int64_t kAliveGrid = 2048;  // workgroups of a later pass-1 stage (one wave of them on the chip)
+
 inline dim3 grid_for(int64_t tasks) { return dim3(static_cast<uint32_t>(tasks < kMaxGrid ? tasks : kMaxGrid)); }
 
 hipError_t launch_filter_rows(const SampleParams& P, bool bf16, hipStream_t stream);
@@ -1107,8 +1213,16 @@ static hipError_t launch_sample_t(const SampleParams& P, int phases, hipStream_t
       const hipError_t e = launch_filter_rows(P, sizeof(T) == 2, stream);
       if (e != hipSuccess) return e;
     } else if (P.K > 0) {
-      const int64_t g = static_cast<int64_t>(P.B) * 2 * P.K * P.S1;
-      hipLaunchKernelGGL(k_sample_rowstats<T>, grid_for(g), dim3(kRowBlock), 0, stream, P);
+      hipLaunchKernelGGL(k_sample_rowstats<T>, grid_for(static_cast<int64_t>(P.B) * 2 * P.stage_end[0] * P.stage_S1[0]),
+                         dim3(kRowBlock), 0, stream, P, 0);
+      for (int st = 1; st < P.nstage; ++st) {
+        const int a = P.stage_end[st - 1];
+        hipLaunchKernelGGL(k_stage_alive, grid_for((static_cast<int64_t>(P.B) + 15) / 16), dim3(kAliveBlock), 0,
+                           stream, P, a);
+        const int64_t g = static_cast<int64_t>(P.B) * 2 * (P.stage_end[st] - a) * P.stage_S1[st];
+        hipLaunchKernelGGL(k_sample_rowstats_alive<T>, grid_for(g < kAliveGrid ? g : kAliveGrid), dim3(kRowBlock), 0,
+                           stream, P, st);
+      }
     }
   }
   const int64_t gm = static_cast<int64_t>(P.B) * P.S2;

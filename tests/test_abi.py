@@ -16,6 +16,7 @@ import rejection_sampling_verify_sample_amd as rsv
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN, ERR_PHASE = 0, -1, -2, -3, -4, -5, -6, -7, -8
 ERR_FILTER_V = -9
+ERR_STAGES = -10
 P = 0x10000  # aligned, never dereferenced
 
 
@@ -35,7 +36,7 @@ def test_library_is_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     L = ctypes.CDLL(rsv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
@@ -125,6 +126,38 @@ def test_filtered_phases_checks_arguments():
     assert fn(*a, 1) == ERR_FILTER_V
 
 
+def staged(ends, **kw):
+    a = dict(target=P, draft=P, dtype=1, tokens=P, uniforms=P, B=4, K=8, V=100, T=1.0, out_tokens=P, out_n=P,
+             out_probs=None, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    n = kw.pop("num_stages", None)
+    arr = None if ends is None else (ctypes.c_int32 * max(1, len(ends)))(*ends)
+    num = len(ends) if n is None and ends is not None else (n if n is not None else 0)
+    return rsv.lib().spec_verify_sample_staged(a["target"], a["draft"], a["dtype"], a["tokens"], a["uniforms"],
+                                               a["B"], a["K"], a["V"], a["T"], a["out_tokens"], a["out_n"],
+                                               a["out_probs"], a["ws"], a["ws_bytes"], a["stream"], arr, num)
+
+
+@pytest.mark.parametrize("ends,kw,expect", [
+    # valid schedules get through to the workspace check
+    ([8], dict(ws_bytes=16), ERR_WS), ([2, 4, 8], dict(ws_bytes=16), ERR_WS), ([1, 2, 3, 4, 5, 6, 7, 8],
+                                                                                dict(ws_bytes=16), ERR_WS),
+    ([], dict(K=0, ws_bytes=16), ERR_WS), (None, dict(K=0, ws_bytes=16), ERR_WS),
+    # invalid schedules
+    ([], {}, ERR_STAGES), (None, {}, ERR_STAGES), ([4], {}, ERR_STAGES), ([4, 9], {}, ERR_STAGES),
+    ([0, 8], {}, ERR_STAGES), ([4, 4, 8], {}, ERR_STAGES), ([6, 4, 8], {}, ERR_STAGES), ([8, 8], {}, ERR_STAGES),
+    ([1, 2, 3, 4, 5, 6, 7, 8, 8], {}, ERR_STAGES), ([2], dict(K=0), ERR_STAGES),
+    # shape errors come first; B = 0 is a no-op once the schedule is valid
+    ([8], dict(K=65), ERR_SHAPE), ([8], dict(B=0), OK), ([8], dict(T=0.0), ERR_TEMP),
+])
+def test_staged_argument_checks(ends, kw, expect):
+    assert staged(ends, **kw) == expect
+
+
+def test_staged_negative_stage_count():
+    assert staged([8], num_stages=-1) == ERR_STAGES
+
+
 def test_sample_k0_needs_no_draft():
     # K = 0 draws from the bonus row only: draft pointers may be null; still fails on the workspace size
     assert sample(K=0, draft=None, tokens=None, ws_bytes=0) == ERR_WS
@@ -168,7 +201,8 @@ def test_workspace_sizes():
 
 
 def test_status_strings():
-    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN, ERR_PHASE, ERR_FILTER_V, 99):
+    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN, ERR_PHASE, ERR_FILTER_V,
+              ERR_STAGES, 99):
         assert isinstance(rsv.status_string(s), str) and rsv.status_string(s)
 
 

@@ -3,6 +3,7 @@
 Inputs are seeded and synthetic (workloads/), shaped like the five workloads;
 the oracle receives the same arrays (bf16 values widened exactly to float).
 """
+import dataclasses
 import json
 import os
 
@@ -112,6 +113,63 @@ def test_parity_full_size(cfg):
     s = make_sample_inputs(cfg, 0)
     rep = check_inputs(s)
     save_report(f"cfg{cfg} full", rep)
+
+
+# ------------------------------------------------------------------ early exit (pass 1 in stages)
+
+STAGED_CASES = [
+    # (cfg, overrides, stage ends, rounds)
+    (1, {}, [1, 2, 4], 3),
+    (2, {}, [2, 5], 2),
+    (3, dict(B=8), [2, 4, 8], 2),
+    (3, dict(B=6, V=50001), [1, 8], 1),              # V odd: every 16-byte phase
+    (4, dict(B=8), [1, 2, 3, 4], 1),
+    (2, dict(B=4, K=64, V=3000), [8, 16, 32, 64], 1),  # the largest K, stages past one wave of positions
+    (3, dict(B=7, K=0, V=1000), [], 1),               # K = 0: no stage, one draw from the bonus row
+    (3, dict(B=16), [8], 1),                          # one stage: identical to the one-pass verify
+    (3, {}, [2, 4, 8], 1),                            # the full workload in the bench's staged configuration
+]
+
+
+@pytest.mark.parametrize("cfg,kw,stages,rounds", STAGED_CASES, ids=lambda x: str(x))
+def test_staged_parity_with_oracle(cfg, kw, stages, rounds):
+    """Early exit gives the verify's outputs: tokens and counts under the parity rule,
+    p_i(x_i), q_i(x_i) at every position the walk consulted, NaN after it (more than one stage)."""
+    rep = ParityReport()
+    for rnd in range(rounds):
+        s = make_sample_inputs(cfg, rnd, **kw)
+        log(f"staged {stages} case {s.name}")
+        t = sample_tensors(s, DEV)
+        out = rsv.verify_sample_staged(t["target"], t["draft"], t["draft_tokens"], t["uniforms"], t["temperature"],
+                                       stages, want_probs=True)
+        torch.cuda.synchronize()
+        tok, n, probs = out.tokens.cpu().numpy(), out.num_accepted.cpu().numpy(), out.probs.cpu().numpy()
+        assert np.all(n >= 0), "these workloads hold no data fault"
+        tgt, drf = s.target_f32(), s.draft_f32()
+        res = oracle.oracle_sample(tgt, drf, s.draft_tokens, s.uniforms, s.temperature)
+        if len(stages) > 1:
+            past = np.arange(s.shape[1])[None, :] > n[:, None]
+            assert np.all(np.isnan(probs[past])), "positions past the first rejection must be NaN"
+            res = dataclasses.replace(res, probs=np.where(past[:, :, None], np.nan, res.probs))
+        rep.merge(compare_sample(tgt, drf, s.draft_tokens, s.uniforms, s.temperature, res, tok, n, probs))
+        log(f"  {rep.summary()}")
+    save_report(f"staged {stages} cfg{cfg} {kw}", rep)
+
+
+def test_staged_matches_one_pass_on_the_gpu():
+    """With the same segment counts the staged and one-pass verifies take the same
+    row statistics, so every token and count agrees bit for bit."""
+    s = make_sample_inputs(3, 1, B=32, V=20000)
+    t = sample_tensors(s, DEV)
+    os.environ["SPECVERIFY_S1"] = "1"
+    try:
+        b = rsv.verify_sample_staged(t["target"], t["draft"], t["draft_tokens"], t["uniforms"], t["temperature"],
+                                     [1, 3, 8])
+        c = rsv.verify_sample(t["target"], t["draft"], t["draft_tokens"], t["uniforms"], t["temperature"])
+    finally:
+        del os.environ["SPECVERIFY_S1"]
+    torch.cuda.synchronize()
+    assert torch.equal(b.tokens, c.tokens) and torch.equal(b.num_accepted, c.num_accepted)
 
 
 # ------------------------------------------------------------------ edge cases
