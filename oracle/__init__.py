@@ -1,4 +1,4 @@
-"""CPU oracle of the verify step (float64 NumPy).
+"""CPU oracle of the verify step (float64 NumPy) and of the n-gram pool (oracle.ngram, plain Python).
 
 TEST INFRASTRUCTURE: only the tests, the package's smoke check and the bench's
 CPU-baseline leg may import it. The HIP library and its binding never do.
