@@ -13,9 +13,9 @@ Steps are launched from HIP graphs that each hold a run of consecutive steps
 
 Prints ONE JSON line. Also reported: the pass-1 kernel alone (the dominant
 kernel, for the roofline), the same round with early exit (pass 1 in stages,
-spec_verify_sample_staged, which must give the same outputs), the same round
+spec_verify_sample_staged, which gives the same outputs), the same round
 verified on top-k 50 / top-p 0.9 filtered laws (spec_verify_sample_filtered),
-the greedy verify on its own
+the n-gram pool (insert + lookup) and the greedy verify on their own
 workload (B=32 G=7 N=5 V=32000 bf16), and the CPU oracle on a bounded sample of
 the same round.
 """
@@ -55,6 +55,7 @@ def parse_args():
     ap.add_argument("--no-greedy", action="store_true")
     ap.add_argument("--no-filtered", action="store_true", help="skip the top-k / top-p filtered leg")
     ap.add_argument("--no-staged", action="store_true", help="skip the early-exit (staged pass 1) leg")
+    ap.add_argument("--no-pool", action="store_true", help="skip the n-gram pool leg")
     ap.add_argument("--eager", action="store_true", help="launch through the Python binding instead of graphs")
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB copy (calibration), then 3 eager verify rounds "
@@ -425,6 +426,47 @@ def main() -> int:
         del fsteps
     del sets
 
+    # ---------------------------------------------------------------- n-gram pool, B=32 V=32000 G=7 N=5, W=15 per call
+    pool_leg = None
+    if not args.no_pool:
+        from workloads.ngram import lookup_tokens, ngram_steps
+        PB, PV, PG, PN, PW = 32, 32000, 7, 5, 15
+        pool = rsv.NgramPool(PB, PV, PG, PN, dev)
+        host = ngram_steps(3, 16, PB, PW, PN, PV)
+        grams = [torch.from_numpy(g).to(dev) for g in host]
+        lasts = [torch.from_numpy(lookup_tokens(i, PB, PV, host)).to(dev) for i in range(16)]
+        skipped = torch.empty((PB,), dtype=torch.int32, device=dev)
+        pcand = torch.empty((PB, PG, PN - 1), dtype=torch.int32, device=dev)
+        pcount = torch.empty((PB,), dtype=torch.int32, device=dev)
+
+        def pstep(i):
+            pool.insert(grams[i % 16], out_skipped=skipped)
+            pool.lookup(lasts[i % 16], out_cand=pcand, out_count=pcount)
+
+        for i in range(16):
+            pstep(i)
+        torch.cuda.synchronize()
+        psteps = 48
+        if args.eager:
+            pfn = pstep
+            pcalls = 1
+        else:
+            pgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(pgraph):
+                for j in range(psteps):
+                    pstep(j)
+            pfn = lambda i: pgraph.replay()  # noqa: E731
+            pcalls = psteps
+        n_rep = max(1, args.steps // pcalls)
+        timer.time(pfn, max(1, args.warmup // pcalls))
+        t_pool = timer.time(pfn, n_rep) / (n_rep * pcalls)
+        pool_leg = {"workload": f"n-gram pool B={PB} V={PV} G={PG} N={PN}: insert W={PW} n-grams per sequence, "
+                                "then look up each sequence's last token",
+                    "us_per_step": round(t_pool * 1e6, 3), "steps_per_s": round(1.0 / t_pool, 1),
+                    "mean_candidates": round(float(pcount.float().mean().item()), 3)}
+        log(f"n-gram pool insert + lookup: {t_pool * 1e6:.2f} us per step")
+        del pool
+
     # ---------------------------------------------------------------- greedy verify, B=32 G=7 N=5 V=32000 bf16
     greedy = None
     if not args.no_greedy:
@@ -512,6 +554,7 @@ def main() -> int:
                      "us_per_launch": round(t_pass1 * 1e6, 3)},
         "cpu_baseline": cpu,
         "staged": staged,
+        "ngram_pool": pool_leg,
         "greedy": greedy,
         "filtered": filtered,
     }

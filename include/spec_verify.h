@@ -69,11 +69,15 @@ typedef enum {
   SPEC_ERR_ALIGN = -7,       /* a pointer is not aligned to its element size */
   SPEC_ERR_PHASE = -8,       /* phase mask outside 1..15 (spec_verify_sample_phases) */
   SPEC_ERR_FILTER_V = -9,    /* V > SPEC_MAX_FILTER_V (spec_verify_sample_filtered) */
-  SPEC_ERR_STAGES = -10      /* invalid stage schedule (spec_verify_sample_staged) */
+  SPEC_ERR_STAGES = -10,     /* invalid stage schedule (spec_verify_sample_staged) */
+  SPEC_ERR_POOL = -11        /* pool buffer smaller than spec_ngram_pool_bytes */
 } spec_status;
 
 #define SPEC_MAX_FILTER_V (1 << 24) /* vocabulary entries per row of the filtered verify */
 #define SPEC_MAX_STAGES 8           /* pass-1 stages of spec_verify_sample_staged */
+#define SPEC_MAX_POOL_G 64          /* continuations a pool key holds */
+#define SPEC_MAX_POOL_N 17          /* n-gram length: a continuation holds at most 16 tokens */
+#define SPEC_MAX_POOL_W 64          /* n-grams per sequence in one insert call */
 
 /* Bytes of workspace spec_verify_sample needs for these sizes (0 for invalid sizes). */
 size_t spec_verify_sample_workspace_size(int32_t B, int32_t K, int32_t V);
@@ -245,6 +249,47 @@ spec_status spec_verify_greedy(const void* target_logits, int32_t dtype, const i
                                int32_t B, int32_t G, int32_t N, int32_t V, int32_t* out_tokens,
                                int32_t* out_accept_len, int32_t* out_best_cand, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * The n-gram pool that supplies spec_verify_greedy's candidates.
+ * Source: "Lookahead Decoding 完全拆解:Jacobi 迭代与 N-gram 池,不靠草稿模型的投机解码",
+ * sections "Lookahead 分支" (each step yields W n-grams of length N for the pool),
+ * "N-gram 池与身份判定" (only n-grams whose first token equals the last generated
+ * token are verified) and "验证分支" (n-grams not adopted stay in the pool).
+ *
+ * One pool per sequence (batch row), keyed by an n-gram's first token. A key
+ * holds its G most recently inserted distinct continuations (the N-1 tokens after
+ * the first), newest first; inserting a continuation the key holds makes it the
+ * newest; when a key is full its oldest continuation is dropped.
+ *
+ * pool         DEVICE memory of at least spec_ngram_pool_bytes(B, V, G, N) bytes,
+ *              16-byte aligned, owned by the caller: [B][V][G][N-1] int32, a
+ *              key's slots newest first, an empty slot -1 in every token.
+ *              spec_ngram_pool_init must run on it once before any other use.
+ * B, V, G, N   0 <= B, 1 <= V <= SPEC_MAX_V, 1 <= G <= SPEC_MAX_POOL_G,
+ *              2 <= N <= SPEC_MAX_POOL_N; the pool size must fit in size_t.
+ * SPEC_ERR_POOL when pool_bytes is smaller than spec_ngram_pool_bytes.
+ */
+size_t spec_ngram_pool_bytes(int32_t B, int32_t V, int32_t G, int32_t N);  /* 0 for invalid sizes */
+spec_status spec_ngram_pool_init(void* pool, size_t pool_bytes, int32_t B, int32_t V, int32_t G, int32_t N,
+                                 void* stream);
+/*
+ * Insert W n-grams per sequence: ngrams [B, W, N] int32 (device), sequence b's
+ * n-grams in window order (index 0 first), 0 <= W <= SPEC_MAX_POOL_W. An n-gram
+ * with any token outside [0, V) is skipped; out_skipped (NULL or [B] int32)
+ * receives the number skipped per sequence.
+ */
+spec_status spec_ngram_pool_insert(void* pool, size_t pool_bytes, int32_t B, int32_t V, int32_t G, int32_t N,
+                                   const int32_t* ngrams, int32_t W, int32_t* out_skipped, void* stream);
+/*
+ * The candidates for each sequence's last generated token: last_tokens [B]
+ * int32; out_cand [B, G, N-1] int32 receives the key's continuations newest
+ * first and -1 in the slots past out_count [B] (0 for a token outside [0, V)).
+ * The pool is read only. The first out_count[b] rows of out_cand[b] are the
+ * candidate tokens spec_verify_greedy takes after the matched first token.
+ */
+spec_status spec_ngram_pool_lookup(const void* pool, size_t pool_bytes, int32_t B, int32_t V, int32_t G, int32_t N,
+                                   const int32_t* last_tokens, int32_t* out_cand, int32_t* out_count, void* stream);
 
 /*
  * Fill out [B, K+1, 2] with the verify uniforms of one round from

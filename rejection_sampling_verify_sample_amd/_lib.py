@@ -51,6 +51,12 @@ _SIGNATURES = {
     "spec_verify_greedy": (_i32, [_c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
                                   _c_void_p, _c_void_p, _size_t, _c_void_p]),
     "spec_fill_uniforms": (_i32, [_u64, _u64, _i32, _i32, _c_void_p, _c_void_p]),
+    "spec_ngram_pool_bytes": (_size_t, [_i32, _i32, _i32, _i32]),
+    "spec_ngram_pool_init": (_i32, [_c_void_p, _size_t, _i32, _i32, _i32, _i32, _c_void_p]),
+    "spec_ngram_pool_insert": (_i32, [_c_void_p, _size_t, _i32, _i32, _i32, _i32, _c_void_p, _i32, _c_void_p,
+                                      _c_void_p]),
+    "spec_ngram_pool_lookup": (_i32, [_c_void_p, _size_t, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
+                                      _c_void_p]),
 }
 
 _lib = None
@@ -327,3 +333,68 @@ def fill_uniforms(seed: int, rnd: int, B: int, K: int, *, out: torch.Tensor | No
     if st != 0:
         raise SpecVerifyError(st, "spec_fill_uniforms")
     return out
+
+
+# ------------------------------------------------------------------ n-gram pool
+
+def ngram_pool_bytes(B: int, V: int, G: int, N: int) -> int:
+    return int(lib().spec_ngram_pool_bytes(B, V, G, N))
+
+
+class NgramPool:
+    """The n-gram pools of B sequences (spec_ngram_pool_*), held in a device buffer PyTorch allocates.
+
+    `buffer` is the pool memory, [B, V, G, N-1] int32 viewed from its bytes; it is
+    emptied at construction. insert() and lookup() run on `stream` (default: the
+    current stream).
+    """
+
+    def __init__(self, B: int, V: int, G: int, N: int, device="cuda", stream=None):
+        self.B, self.V, self.G, self.N = int(B), int(V), int(G), int(N)
+        self.device = torch.device(device)
+        nbytes = ngram_pool_bytes(B, V, G, N)
+        if nbytes == 0 and B > 0:
+            raise SpecVerifyError(-2, "spec_ngram_pool_bytes")
+        self.buffer = torch.empty(max(nbytes // 4, 1), dtype=torch.int32, device=self.device)
+        self.nbytes = nbytes
+        st = lib().spec_ngram_pool_init(_ptr(self.buffer), nbytes, B, V, G, N,
+                                        ctypes.c_void_p(_stream_handle(stream, self.device)))
+        if st != 0:
+            raise SpecVerifyError(st, "spec_ngram_pool_init")
+
+    def table(self) -> torch.Tensor:
+        """The pool memory as [B, V, G, N-1] int32 (a view, for inspection)."""
+        return self.buffer[: self.B * self.V * self.G * (self.N - 1)].view(self.B, self.V, self.G, self.N - 1)
+
+    def insert(self, ngrams: torch.Tensor, *, out_skipped: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Insert ngrams [B, W, N] int32 (window order); returns the skipped counts [B]."""
+        if ngrams.dim() != 3:
+            raise ValueError("ngrams must be [B, W, N]")
+        W = ngrams.shape[1]
+        _check(ngrams, "ngrams", self.device, torch.int32, (self.B, W, self.N))
+        if out_skipped is None:
+            out_skipped = torch.empty((self.B,), dtype=torch.int32, device=self.device)
+        _check(out_skipped, "out_skipped", self.device, torch.int32, (self.B,))
+        st = lib().spec_ngram_pool_insert(_ptr(self.buffer), self.nbytes, self.B, self.V, self.G, self.N,
+                                          _ptr(ngrams), W, _ptr(out_skipped),
+                                          ctypes.c_void_p(_stream_handle(stream, self.device)))
+        if st != 0:
+            raise SpecVerifyError(st, "spec_ngram_pool_insert")
+        return out_skipped
+
+    def lookup(self, last_tokens: torch.Tensor, *, out_cand: torch.Tensor | None = None,
+               out_count: torch.Tensor | None = None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+        """Candidates [B, G, N-1] (newest first, -1 past the count) and counts [B] for each last token [B]."""
+        _check(last_tokens, "last_tokens", self.device, torch.int32, (self.B,))
+        if out_cand is None:
+            out_cand = torch.empty((self.B, self.G, self.N - 1), dtype=torch.int32, device=self.device)
+        if out_count is None:
+            out_count = torch.empty((self.B,), dtype=torch.int32, device=self.device)
+        _check(out_cand, "out_cand", self.device, torch.int32, (self.B, self.G, self.N - 1))
+        _check(out_count, "out_count", self.device, torch.int32, (self.B,))
+        st = lib().spec_ngram_pool_lookup(_ptr(self.buffer), self.nbytes, self.B, self.V, self.G, self.N,
+                                          _ptr(last_tokens), _ptr(out_cand), _ptr(out_count),
+                                          ctypes.c_void_p(_stream_handle(stream, self.device)))
+        if st != 0:
+            raise SpecVerifyError(st, "spec_ngram_pool_lookup")
+        return out_cand, out_count

@@ -12,6 +12,9 @@
 #define SPEC_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace sv {
+hipError_t launch_pool_fill(int32_t* pool, int64_t n, hipStream_t stream);
+hipError_t launch_pool_insert(const PoolParams& P, hipStream_t stream);
+hipError_t launch_pool_lookup(const PoolParams& P, hipStream_t stream);
 hipError_t launch_sample(const SampleParams& P, bool bf16, bool filtered, int phases, hipStream_t stream);
 hipError_t launch_greedy(const GreedyParams& P, bool bf16, hipStream_t stream);
 hipError_t launch_philox(uint64_t seed, uint64_t round, int32_t B, int32_t K, float* out, hipStream_t stream);
@@ -139,6 +142,7 @@ SPEC_EXPORT const char* spec_status_string(int32_t status) {
     case SPEC_ERR_PHASE: return "phase mask outside 1..15";
     case SPEC_ERR_FILTER_V: return "vocabulary too large for the filtered verify";
     case SPEC_ERR_STAGES: return "invalid stage schedule (strictly increasing ends in [1, K], the last K)";
+    case SPEC_ERR_POOL: return "n-gram pool buffer smaller than spec_ngram_pool_bytes";
     default: return "unknown status";
   }
 }
@@ -317,5 +321,84 @@ SPEC_EXPORT spec_status spec_fill_uniforms(uint64_t seed, uint64_t round, int32_
   if (!out) return SPEC_ERR_NULL;
   if (!aligned(out, 4)) return SPEC_ERR_ALIGN;
   const hipError_t e = sv::launch_philox(seed, round, B, K, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- n-gram pool
+
+namespace {
+
+// Elements of a pool, or -1 for invalid sizes (or a size that does not fit in size_t).
+int64_t pool_elems(int32_t B, int32_t V, int32_t G, int32_t N) {
+  if (B < 0 || V < 1 || V > SPEC_MAX_V || G < 1 || G > SPEC_MAX_POOL_G || N < 2 || N > SPEC_MAX_POOL_N) return -1;
+  const unsigned __int128 n = static_cast<unsigned __int128>(B) * V * G * (N - 1);
+  if (n * 4 > static_cast<unsigned __int128>(INT64_MAX)) return -1;
+  return static_cast<int64_t>(n);
+}
+
+spec_status pool_check(const void* pool, size_t pool_bytes, int32_t B, int32_t V, int32_t G, int32_t N) {
+  const int64_t n = pool_elems(B, V, G, N);
+  if (n < 0) return SPEC_ERR_SHAPE;
+  if (B == 0) return SPEC_OK;
+  if (!pool) return SPEC_ERR_NULL;
+  if (!aligned(pool, 16)) return SPEC_ERR_ALIGN;
+  if (pool_bytes < static_cast<size_t>(n) * 4) return SPEC_ERR_POOL;
+  return SPEC_OK;
+}
+
+}  // namespace
+
+SPEC_EXPORT size_t spec_ngram_pool_bytes(int32_t B, int32_t V, int32_t G, int32_t N) {
+  const int64_t n = pool_elems(B, V, G, N);
+  return n < 0 ? 0 : static_cast<size_t>(n) * 4;
+}
+
+SPEC_EXPORT spec_status spec_ngram_pool_init(void* pool, size_t pool_bytes, int32_t B, int32_t V, int32_t G,
+                                             int32_t N, void* stream) {
+  const spec_status st = pool_check(pool, pool_bytes, B, V, G, N);
+  if (st != SPEC_OK || B == 0) return st;
+  const hipError_t e = sv::launch_pool_fill(static_cast<int32_t*>(pool), pool_elems(B, V, G, N),
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+SPEC_EXPORT spec_status spec_ngram_pool_insert(void* pool, size_t pool_bytes, int32_t B, int32_t V, int32_t G,
+                                               int32_t N, const int32_t* ngrams, int32_t W, int32_t* out_skipped,
+                                               void* stream) {
+  if (W < 0 || W > SPEC_MAX_POOL_W) return SPEC_ERR_SHAPE;
+  const spec_status st = pool_check(pool, pool_bytes, B, V, G, N);
+  if (st != SPEC_OK || B == 0) return st;
+  if (W > 0 && !ngrams) return SPEC_ERR_NULL;
+  if (!aligned(ngrams, 4) || !aligned(out_skipped, 4)) return SPEC_ERR_ALIGN;
+  sv::PoolParams P{};
+  P.pool = static_cast<int32_t*>(pool);
+  P.B = B;
+  P.V = V;
+  P.G = G;
+  P.N = N;
+  P.W = W;
+  P.ngrams = ngrams;
+  P.out_skipped = out_skipped;
+  const hipError_t e = sv::launch_pool_insert(P, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+SPEC_EXPORT spec_status spec_ngram_pool_lookup(const void* pool, size_t pool_bytes, int32_t B, int32_t V, int32_t G,
+                                               int32_t N, const int32_t* last_tokens, int32_t* out_cand,
+                                               int32_t* out_count, void* stream) {
+  const spec_status st = pool_check(pool, pool_bytes, B, V, G, N);
+  if (st != SPEC_OK || B == 0) return st;
+  if (!last_tokens || !out_cand || !out_count) return SPEC_ERR_NULL;
+  if (!aligned(last_tokens, 4) || !aligned(out_cand, 4) || !aligned(out_count, 4)) return SPEC_ERR_ALIGN;
+  sv::PoolParams P{};
+  P.pool = const_cast<int32_t*>(static_cast<const int32_t*>(pool));
+  P.B = B;
+  P.V = V;
+  P.G = G;
+  P.N = N;
+  P.last = last_tokens;
+  P.out_cand = out_cand;
+  P.out_count = out_count;
+  const hipError_t e = sv::launch_pool_lookup(P, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

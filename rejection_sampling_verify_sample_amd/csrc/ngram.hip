@@ -1,0 +1,194 @@
+// The n-gram pool that feeds the greedy verify with candidates (gfx950).
+//
+// Source: "Lookahead Decoding 完全拆解:Jacobi 迭代与 N-gram 池", sections "Lookahead
+// 分支" (every step the window yields W new n-grams of length N, gathered into a
+// pool), "N-gram 池与身份判定" (only n-grams whose first token equals the last
+// generated token are verified) and "验证分支" (n-grams not adopted stay in the pool).
+//
+// Layout: one pool per sequence, direct-indexed by the first token (the key):
+//   pool[b][key][slot][N-1] int32,
+// a key's slots holding its continuations newest first, compacted, empty slots
+// with -1 in every token. A key keeps its G most recently inserted distinct
+// continuations; a continuation inserted again becomes the newest.
+//
+// Kernels:
+//   k_pool_fill    marks every slot empty (16-byte stores, grid-stride).
+//   k_pool_insert  one workgroup per sequence. Wave 0 stages the call's W n-grams
+//                  in LDS and finds, for every distinct key, its last valid n-gram
+//                  of the call (the key's leader). Then the waves take the
+//                  distinct keys in turn (distinct keys are distinct buckets, so
+//                  no two waves touch one), and a wave rebuilds its key's bucket
+//                  lane-parallel: the call's continuations of the key, each at
+//                  its last occurrence, newest first, then the old slots they do
+//                  not repeat, cut to G. This equals inserting the n-grams one by
+//                  one in window order.
+//   k_pool_lookup  one wave per sequence: the slots of the last token's key.
+#include "../../include/spec_verify.h"
+#include "common.hpp"
+#include "params.hpp"
+
+namespace sv {
+
+__device__ __forceinline__ int32_t* bucket(const PoolParams& P, int b, int key) {
+  return P.pool + ((static_cast<int64_t>(b) * P.V + key) * P.G) * (P.N - 1);
+}
+
+// ---------------------------------------------------------------- fill
+
+__global__ __launch_bounds__(256) void k_pool_fill(int32_t* pool, int64_t n) {
+  const int64_t nvec = n / 4;
+  u32x4* v = reinterpret_cast<u32x4*>(pool);
+  const u32x4 empty = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < nvec; i += stride) v[i] = empty;
+  for (int64_t i = nvec * 4 + static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    pool[i] = -1;
+}
+
+// ---------------------------------------------------------------- insert
+
+constexpr int kPoolWaves = 16;
+constexpr int kPoolBlock = 64 * kPoolWaves;
+
+struct PoolShared {
+  int32_t ng[SPEC_MAX_POOL_W * SPEC_MAX_POOL_N];  // the call's n-grams, [W][N]
+  int32_t key[SPEC_MAX_POOL_W];                    // first token, -1 for a skipped n-gram
+  int32_t leader[SPEC_MAX_POOL_W];                 // distinct keys: index of their last n-gram in the call
+  int32_t nleader;
+};
+
+// Do n-grams w1 and w2 (both valid, same key) carry the same continuation?
+__device__ __forceinline__ bool same_cont(const PoolShared& sh, int N, int w1, int w2) {
+  for (int i = 1; i < N; ++i)
+    if (sh.ng[w1 * N + i] != sh.ng[w2 * N + i]) return false;
+  return true;
+}
+
+__global__ __launch_bounds__(kPoolBlock) void k_pool_insert(PoolParams P) {
+  __shared__ PoolShared sh;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int W = P.W, N = P.N, G = P.G;
+  for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) {
+    const int b = static_cast<int>(task);
+    for (int i = threadIdx.x; i < W * N; i += kPoolBlock) sh.ng[i] = P.ngrams[static_cast<int64_t>(b) * W * N + i];
+    __syncthreads();
+    if (wave == 0) {
+      bool valid = false;
+      if (lane < W) {
+        valid = true;
+        for (int i = 0; i < N; ++i) {
+          const int t = sh.ng[lane * N + i];
+          valid = valid && t >= 0 && t < P.V;
+        }
+        sh.key[lane] = valid ? sh.ng[lane * N] : -1;
+      }
+      const uint64_t bad = __ballot(lane < W && !valid);
+      if (lane == 0 && P.out_skipped) P.out_skipped[b] = __popcll(bad);
+      // a valid n-gram leads its key when no later n-gram of the call has that key
+      bool lead = valid;
+      if (lane < W)
+        for (int w2 = lane + 1; w2 < W; ++w2) lead = lead && sh.key[w2] != sh.key[lane];
+      const uint64_t leads = __ballot(lead);
+      if (lead) sh.leader[__popcll(leads & ((1ull << lane) - 1))] = lane;
+      if (lane == 0) sh.nleader = __popcll(leads);
+    }
+    __syncthreads();
+    const int nlead = sh.nleader;
+    for (int li = wave; li < nlead; li += kPoolWaves) {
+      const int key = sh.key[sh.leader[li]];
+      int32_t* bk = bucket(P, b, key);
+      // the key's n-grams of this call at their last occurrence, newest (highest w) first
+      bool fresh = false;
+      if (lane < W && sh.key[lane] == key) {
+        fresh = true;
+        for (int w2 = lane + 1; w2 < W; ++w2)
+          if (sh.key[w2] == key && same_cont(sh, N, lane, w2)) fresh = false;
+      }
+      const uint64_t freshm = __ballot(fresh);
+      const int nfresh = __popcll(freshm);
+      // rank among the fresh ones: the fresh n-grams after this one come first
+      const int rank = __popcll(freshm >> lane) - 1;
+      // the old slot `lane` (lanes < G): kept when no fresh continuation repeats it
+      int32_t old[SPEC_MAX_POOL_N - 1];
+      bool held = false;
+      if (lane < G) {
+#pragma unroll
+        for (int i = 0; i < SPEC_MAX_POOL_N - 1; ++i) old[i] = (i < N - 1) ? bk[lane * (N - 1) + i] : -1;
+        held = old[0] >= 0;
+      }
+      bool keep = held;
+      if (held) {
+        for (int w2 = 0; w2 < W && keep; ++w2) {
+          if (!((freshm >> w2) & 1ull)) continue;
+          bool eq = true;
+#pragma unroll
+          for (int i = 0; i < SPEC_MAX_POOL_N - 1; ++i)
+            if (i < N - 1) eq = eq && sh.ng[w2 * N + i + 1] == old[i];
+          keep = !eq;
+        }
+      }
+      const uint64_t keepm = __ballot(keep);
+      const int okeep = __popcll(keepm & ((1ull << lane) - 1));  // kept old slots before this one
+      const int total = min(nfresh + __popcll(keepm), G);
+      // every old slot is read above, before any slot is written (the wave runs in lockstep)
+      __builtin_amdgcn_wave_barrier();
+      if (fresh && rank < G)
+        for (int i = 1; i < N; ++i) bk[rank * (N - 1) + (i - 1)] = sh.ng[lane * N + i];
+      if (keep && nfresh + okeep < G) {
+#pragma unroll
+        for (int i = 0; i < SPEC_MAX_POOL_N - 1; ++i)
+          if (i < N - 1) bk[(nfresh + okeep) * (N - 1) + i] = old[i];
+      }
+      if (lane >= total && lane < G)
+        for (int i = 0; i < N - 1; ++i) bk[lane * (N - 1) + i] = -1;
+    }
+    __syncthreads();  // LDS is reused by the next sequence
+  }
+}
+
+// ---------------------------------------------------------------- lookup
+
+__global__ __launch_bounds__(64) void k_pool_lookup(PoolParams P) {
+  const int lane = threadIdx.x & 63;
+  const int G = P.G, N = P.N;
+  for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) {
+    const int b = static_cast<int>(task);
+    const int key = P.last[b];
+    const bool in = key >= 0 && key < P.V;
+    int32_t* oc = P.out_cand + static_cast<int64_t>(b) * G * (N - 1);
+    bool full = false;
+    if (lane < G) {
+      const int32_t* bk = in ? bucket(P, b, key) + lane * (N - 1) : nullptr;
+      for (int i = 0; i < N - 1; ++i) {
+        const int32_t t = in ? bk[i] : -1;
+        oc[lane * (N - 1) + i] = t;
+        if (i == 0) full = t >= 0;
+      }
+    }
+    const uint64_t fm = __ballot(full);
+    if (lane == 0) P.out_count[b] = __popcll(fm);
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+static dim3 pool_grid(int64_t tasks) { return dim3(static_cast<uint32_t>(tasks < (1 << 20) ? tasks : (1 << 20))); }
+
+hipError_t launch_pool_fill(int32_t* pool, int64_t n, hipStream_t stream) {
+  const int64_t blocks = (n / 4 + 255) / 256;
+  hipLaunchKernelGGL(k_pool_fill, pool_grid(blocks > 0 ? blocks : 1), dim3(256), 0, stream, pool, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_insert(const PoolParams& P, hipStream_t stream) {
+  hipLaunchKernelGGL(k_pool_insert, pool_grid(P.B), dim3(kPoolBlock), 0, stream, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_lookup(const PoolParams& P, hipStream_t stream) {
+  hipLaunchKernelGGL(k_pool_lookup, pool_grid(P.B), dim3(64), 0, stream, P);
+  return hipGetLastError();
+}
+
+}  // namespace sv

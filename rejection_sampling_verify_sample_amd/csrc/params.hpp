@@ -92,4 +92,16 @@ struct GreedyLayout {
 
 constexpr int32_t kMaxGreedyRowsPerBatch = 8192;  // G*N: argmaxes of one batch row held in LDS
 
+// ---------------------------------------------------------------- n-gram pool
+
+struct PoolParams {
+  int32_t* pool;           // [B][V][G][N-1]
+  int32_t B, V, G, N, W;
+  const int32_t* ngrams;   // [B, W, N] (insert)
+  int32_t* out_skipped;    // [B] or null (insert)
+  const int32_t* last;     // [B] (lookup)
+  int32_t* out_cand;       // [B, G, N-1] (lookup)
+  int32_t* out_count;      // [B] (lookup)
+};
+
 }  // namespace sv

@@ -17,6 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN, ERR_PHASE = 0, -1, -2, -3, -4, -5, -6, -7, -8
 ERR_FILTER_V = -9
 ERR_STAGES = -10
+ERR_POOL = -11
 P = 0x10000  # aligned, never dereferenced
 
 
@@ -36,7 +37,7 @@ def test_library_is_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 16, names
     L = ctypes.CDLL(rsv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
@@ -158,6 +159,46 @@ def test_staged_negative_stage_count():
     assert staged([8], num_stages=-1) == ERR_STAGES
 
 
+def test_ngram_pool_bytes():
+    assert rsv.ngram_pool_bytes(32, 32000, 7, 5) == 32 * 32000 * 7 * 4 * 4
+    assert rsv.ngram_pool_bytes(0, 32000, 7, 5) == 0
+    for bad in ((-1, 10, 2, 3), (1, 0, 2, 3), (1, 10, 0, 3), (1, 10, 65, 3), (1, 10, 2, 1), (1, 10, 2, 18),
+                (1, (1 << 30) + 1, 2, 3)):
+        assert rsv.ngram_pool_bytes(*bad) == 0, bad
+    # sizes past what int64 byte offsets can address are rejected, not wrapped
+    assert rsv.ngram_pool_bytes(1 << 30, 1 << 30, 64, 17) == 0
+
+
+def pool_call(fn, **kw):
+    a = dict(pool=P, nbytes=1 << 40, B=2, V=10, G=3, N=4, W=5, ngrams=P, skipped=None, last=P, cand=P, count=P,
+             stream=None)
+    a.update(kw)
+    L = rsv.lib()
+    if fn == "init":
+        return L.spec_ngram_pool_init(a["pool"], a["nbytes"], a["B"], a["V"], a["G"], a["N"], a["stream"])
+    if fn == "insert":
+        return L.spec_ngram_pool_insert(a["pool"], a["nbytes"], a["B"], a["V"], a["G"], a["N"], a["ngrams"], a["W"],
+                                        a["skipped"], a["stream"])
+    return L.spec_ngram_pool_lookup(a["pool"], a["nbytes"], a["B"], a["V"], a["G"], a["N"], a["last"], a["cand"],
+                                    a["count"], a["stream"])
+
+
+@pytest.mark.parametrize("fn,kw,expect", [
+    ("init", dict(G=0), ERR_SHAPE), ("init", dict(N=1), ERR_SHAPE), ("init", dict(N=18), ERR_SHAPE),
+    ("init", dict(pool=None), ERR_NULL), ("init", dict(pool=P + 4), ERR_ALIGN), ("init", dict(nbytes=16), ERR_POOL),
+    ("init", dict(B=0, pool=None), OK),
+    ("insert", dict(W=-1), ERR_SHAPE), ("insert", dict(W=65), ERR_SHAPE), ("insert", dict(V=0), ERR_SHAPE),
+    ("insert", dict(ngrams=None), ERR_NULL), ("insert", dict(ngrams=P + 2), ERR_ALIGN),
+    ("insert", dict(skipped=P + 1), ERR_ALIGN), ("insert", dict(nbytes=100), ERR_POOL),
+    ("insert", dict(B=0), OK), ("insert", dict(W=0, ngrams=None, nbytes=16), ERR_POOL),
+    ("lookup", dict(G=65), ERR_SHAPE), ("lookup", dict(last=None), ERR_NULL), ("lookup", dict(cand=None), ERR_NULL),
+    ("lookup", dict(count=None), ERR_NULL), ("lookup", dict(cand=P + 2), ERR_ALIGN), ("lookup", dict(nbytes=8), ERR_POOL),
+    ("lookup", dict(B=0, last=None), OK),
+])
+def test_ngram_pool_argument_checks(fn, kw, expect):
+    assert pool_call(fn, **kw) == expect
+
+
 def test_sample_k0_needs_no_draft():
     # K = 0 draws from the bonus row only: draft pointers may be null; still fails on the workspace size
     assert sample(K=0, draft=None, tokens=None, ws_bytes=0) == ERR_WS
@@ -202,7 +243,7 @@ def test_workspace_sizes():
 
 def test_status_strings():
     for s in (OK, ERR_NULL, ERR_SHAPE, ERR_TEMP, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIGN, ERR_PHASE, ERR_FILTER_V,
-              ERR_STAGES, 99):
+              ERR_STAGES, ERR_POOL, 99):
         assert isinstance(rsv.status_string(s), str) and rsv.status_string(s)
 
 

@@ -41,7 +41,7 @@ def lookup_tokens(seed: int, B: int, V: int, steps: list[np.ndarray]) -> np.ndar
     last = rng.integers(0, V, size=B)
     for b in range(B):
         u = rng.random()
-        if u < 0.7:
+        if u < 0.7 and steps and steps[0].shape[1] > 0:
             s = steps[rng.integers(0, len(steps))]
             last[b] = s[b, rng.integers(0, s.shape[1]), 0]
         elif u < 0.8:
