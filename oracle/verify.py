@@ -245,6 +245,110 @@ def oracle_greedy(logits: np.ndarray, cand: np.ndarray) -> GreedyResult:
     return GreedyResult(tokens, acc_len, best_out, amax)
 
 
+# --------------------------------------------------------------------------- sampling verify of greedy-drafted n-grams
+#
+# [LA] "采样模式的验证": the lookahead branch drafts its n-grams greedily, so each
+# candidate token comes from a one-hot law q = delta_x and only the token id is
+# kept; the verify side still runs a full sampling verification (the paper's
+# Algorithm 4, not printed on the page). Reading: the rule of [SD] §2.1 with
+# q = delta_x accepts x with probability min(1, p(x)/1) = p(x), and on rejection
+# the residual norm(max(0, p - delta_x)) is p with x removed, renormalised. With
+# G disjoint candidates ([LA] "验证分支"), at each position the candidates whose
+# prefix matches the tokens accepted so far ("active") are tried in index order,
+# each rejection removing its token from the current law:
+#   * the law of position i is the target row i of the lowest-index active
+#     candidate (every active candidate has the same prefix);
+#   * candidate h's token x is accepted iff r < p_cur(x), r = uniforms[b, i, h],
+#     p_cur = p with the tokens rejected so far at this position removed,
+#     renormalised (a token already rejected has p_cur(x) = 0);
+#   * on acceptance, the candidates whose token at i is x stay active and the walk
+#     moves to position i + 1; after N-1 accepted tokens a bonus token is drawn
+#     from row N-1 of the lowest-index active candidate with uniforms[b, N-1, G];
+#   * when every active candidate is rejected, the token is drawn from p_cur with
+#     uniforms[b, i, G] by the inverse-CDF rule of oracle_sample (zero remaining
+#     mass falls back to p), and the walk stops.
+# A candidate token outside [0, V), or a consulted row with no finite logit, is a
+# data fault of the batch row.
+
+@dataclass
+class NgramSampleResult:
+    tokens: np.ndarray         # [B, N]: accepted tokens, then the drawn one, rest -1
+    accept_len: np.ndarray     # [B]: L in [0, N-1]; -1 marks a data fault
+    rows: np.ndarray           # [B]: candidate whose rows the final draw used; -1 on a fault
+    accept_margin: np.ndarray  # [B]: smallest |r - p_cur(x)| over the tries taken (+inf if none)
+    draw_margin: np.ndarray    # [B]: margin of the draw (+inf on a fault)
+    residual_mass: np.ndarray  # [B]: mass the draw's weights carry (1 for the bonus; nan on a fault)
+
+    def min_margin(self) -> np.ndarray:
+        return np.minimum(self.accept_margin, self.draw_margin)
+
+
+def oracle_ngram_sample(logits: np.ndarray, cand: np.ndarray, uniforms: np.ndarray,
+                        temperature: float) -> NgramSampleResult:
+    """Sampling verify of G greedy-drafted candidate n-grams ([LA] "采样模式的验证", [SD] §2.1).
+
+    logits [B, G, N, V]: row i of candidate g is the target's law after the
+    candidate's first i tokens (row N-1 the bonus row); cand [B, G, N-1];
+    uniforms [B, N, G+1]: [b, i, h] accepts candidate h at position i, [b, i, G]
+    is the draw uniform of position i.
+    """
+    logits = np.asarray(logits)
+    B, G, N, V = logits.shape
+    assert cand.shape == (B, G, N - 1) and uniforms.shape == (B, N, G + 1)
+    tokens = np.full((B, N), -1, dtype=np.int32)
+    acc_len = np.full(B, -1, dtype=np.int32)
+    rows_out = np.full(B, -1, dtype=np.int32)
+    acc_margin = np.full(B, np.inf)
+    draw_margin = np.full(B, np.inf)
+    zmass = np.full(B, np.nan)
+    for b in range(B):
+        if np.any((cand[b] < 0) | (cand[b] >= V)):
+            continue
+        active = list(range(G))
+        prefix: list[int] = []
+        margin = np.inf
+        fault = False
+        while True:
+            g0 = active[0]
+            i = len(prefix)
+            if not row_is_valid(logits[b, g0, i]):
+                fault = True
+                break
+            p = softmax64(logits[b, g0, i], temperature)
+            if i == N - 1:                                  # every candidate token accepted: bonus draw
+                w = p
+                break
+            live = p.copy()                                 # p_cur, unnormalised
+            accepted = None
+            for h in active:
+                x = int(cand[b, h, i])
+                left = float(np.sum(live))
+                alpha = float(live[x]) / left if left > 0.0 else 0.0   # p_cur(x) / q(x), q = delta_x
+                r = float(uniforms[b, i, h])
+                margin = min(margin, abs(r - alpha))
+                if r < alpha:                               # accept iff r < alpha ([KW] §3.1)
+                    accepted = x
+                    break
+                live[x] = 0.0                               # residual: max(0, p_cur - delta_x)
+            if accepted is None:
+                w = live if np.sum(live) > 0.0 else p       # zero remaining mass: sample p
+                break
+            prefix.append(accepted)
+            active = [h for h in active if int(cand[b, h, i]) == accepted]
+        if fault:
+            continue
+        k, Z, dmargin = inverse_cdf_draw(w, float(uniforms[b, len(prefix), G]))
+        L = len(prefix)
+        tokens[b, :L] = prefix
+        tokens[b, L] = k
+        acc_len[b] = L
+        rows_out[b] = active[0]
+        acc_margin[b] = margin
+        draw_margin[b] = dmargin
+        zmass[b] = Z
+    return NgramSampleResult(tokens, acc_len, rows_out, acc_margin, draw_margin, zmass)
+
+
 # --------------------------------------------------------------------------- top-k / top-p consistent verify
 #
 # [KW] §3.4: the temperature rescales both sides before p and q are formed; a

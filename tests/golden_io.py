@@ -54,3 +54,12 @@ def filtered_case(case: dict) -> dict:
     c["top_p"] = np.array([float(case["top_p"])], dtype=np.float32)
     c["expect_kept"] = np.array([case["kept"]], dtype=np.int64)
     return c
+
+
+def ngram_sample_case(case: dict) -> dict:
+    rows = [[[(-math.inf if v is None else float(v)) for v in r] for r in g] for g in case["logits"]]
+    return dict(logits=np.array(rows, dtype=np.float64)[None], cand=np.array(case["cand"], dtype=np.int32)[None],
+                uniforms=np.array(case["uniforms"], dtype=np.float64)[None], T=float(case["T"]),
+                expect_tokens=np.array([case["tokens"]], dtype=np.int32),
+                expect_len=np.array([case["accept_len"]], dtype=np.int32),
+                expect_rows=np.array([case["rows"]], dtype=np.int32), name=case["name"])

@@ -9,7 +9,9 @@ Sources of the pinned facts (page title, section):
     accept/resample rule is exactly p; §2.4 E[accept] = 1 - TV(p, q);
     §3.1 tokens per round (1 - a^(K+1)) / (1 - a).
   Lookahead Decoding 完全拆解:Jacobi 迭代与 N-gram 池: eq. (5), the expected
-    tokens per step with b disjoint candidates of gamma tokens each.
+    tokens per step with b disjoint candidates of gamma tokens each; section
+    "采样模式的验证": greedy-drafted (one-hot) candidates keep the target's law
+    under a full sampling verification.
   kwkr.cn/news/620797 notes §3.4: top-k / top-p must truncate the draft and
     the target side alike, and the correction is drawn inside the kept set.
   Hand-worked rounds in tests/golden/ (derivations stored beside them).
@@ -22,7 +24,7 @@ from fractions import Fraction
 import numpy as np
 from scipy import special, stats
 
-from golden_io import filtered_case, greedy_case, load, logits_from_probs, sample_case
+from golden_io import filtered_case, greedy_case, load, logits_from_probs, ngram_sample_case, sample_case
 from workloads import make_greedy_inputs, verify_uniforms
 
 
@@ -552,3 +554,97 @@ def check_filtered_exact_law(orc, grid: int = 48) -> None:
         assert first == pf0, ("filtered first-token law", T, k, p, first, pf0)
         assert accepted == 1 - tv, ("filtered acceptance", accepted, 1 - tv)
         assert bonus == [(1 - tv) * v for v in pf1], ("filtered bonus law", bonus)
+
+
+# --------------------------------------------------------------------------- sampling verify of one-hot n-grams
+
+def check_golden_ngram_sample(orc) -> None:
+    for case in load("ngram_sample_worked.json")["cases"]:
+        c = ngram_sample_case(case)
+        res = orc.oracle_ngram_sample(c["logits"], c["cand"], c["uniforms"], c["T"])
+        assert np.array_equal(res.tokens, c["expect_tokens"]), (c["name"], res.tokens, c["expect_tokens"])
+        assert np.array_equal(res.accept_len, c["expect_len"]), (c["name"], res.accept_len)
+        assert np.array_equal(res.rows, c["expect_rows"]), (c["name"], res.rows)
+
+
+def check_ngram_sample_g1_matches_sample(orc) -> None:
+    """One candidate drafted greedily is speculative decoding with a one-hot draft law
+    ([SD] §2.1 with q = delta_x): the n-gram verify must give oracle_sample's outputs
+    when the draft rows are one-hot at the candidate tokens and the uniforms map
+    [b,i,0] -> r_i, [b,i,G] -> u_i."""
+    rng = np.random.default_rng(77)
+    for B, N, V, T, scale in ((300, 5, 40, 1.0, 1.5), (200, 3, 7, 0.7, 3.0), (100, 9, 300, 1.3, 2.0)):
+        logits = rng.normal(0.0, scale, size=(B, 1, N, V))
+        # candidate tokens: the target's argmax half the time (so walks go deep), else uniform
+        amax = np.argmax(logits[:, 0, : N - 1], axis=-1)
+        cand = np.where(rng.random((B, N - 1)) < 0.5, amax, rng.integers(0, V, size=(B, N - 1)))[:, None]
+        cand = cand.astype(np.int32)
+        uni = rng.random((B, N, 2))
+        res = orc.oracle_ngram_sample(logits, cand, uni, T)
+        draft = np.full((B, N - 1, V), -np.inf)
+        for b in range(B):
+            draft[b, np.arange(N - 1), cand[b, 0]] = 0.0
+        su = np.zeros((B, N, 2))
+        su[:, :, 0] = uni[:, :, 0]
+        su[:, :, 1] = uni[:, :, 1]
+        ref = orc.oracle_sample(logits[:, 0], draft, cand[:, 0], su, T, with_probs=False)
+        assert np.array_equal(res.accept_len, ref.n_accepted), (B, N, V)
+        assert np.array_equal(res.tokens, ref.tokens), (B, N, V)
+
+
+# (p0, candidate tokens at position 0, bonus law of each candidate's row 1, mesh);
+# every acceptance probability after renormalisation and every cumulative draw
+# weight (as a fraction of the remaining mass) is a multiple of 1/mesh, so the mesh
+# of uniforms integrates the walk exactly
+NGRAM_LAW_DESIGNS = [
+    (["1/2", "1/4", "1/8", "1/8"], [0, 1], [["1/2", "1/2", "0", "0"], ["0", "0", "1/2", "1/2"]], 8),
+    (["1/2", "1/4", "1/8", "1/8"], [0, 1, 2], [["1/2", "1/2", "0", "0"], ["0", "0", "1/2", "1/2"],
+                                              ["1/4", "1/4", "1/4", "1/4"]], 8),
+    (["0", "1/2", "1/2", "0"], [1, 1, 2], [["1", "0", "0", "0"], ["0", "1", "0", "0"], ["0", "0", "1/4", "3/4"]], 8),
+    (["1/2", "1/4", "1/4", "0"], [3, 0], [["1/4", "1/4", "1/2", "0"], ["0", "1/2", "0", "1/2"]], 8),
+    (["1/2", "1/4", "1/8", "1/8"], [0, 0], [["1/2", "0", "1/2", "0"], ["0", "0", "0", "1"]], 8),
+    # thirds: after 2 is rejected from the uniform law the rest holds 3/4 (draw weights 1/3, 2/3)
+    (["1/4", "1/4", "1/4", "1/4"], [2, 2], [["1/2", "0", "1/2", "0"], ["0", "0", "0", "1"]], 12),
+    (["1/4", "1/4", "1/4", "1/4"], [0, 1], [["1/4", "1/4", "1/4", "1/4"], ["1/2", "1/2", "0", "0"]], 12),
+]
+
+
+def check_ngram_sample_exact_law(orc, designs=NGRAM_LAW_DESIGNS) -> None:
+    """The sampling verify of one-hot candidates keeps the target's law ([LA] "采样模式的验证";
+    the one-candidate case is [SD] §2.2's theorem with q = delta_x). N = 2: the G
+    accept uniforms and the draw uniform run over the midpoints of a 1/grid mesh
+    (the bonus uniform is 1 - u). Exactly in rationals:
+      P(first token = y) = p0(y);
+      P(first token x accepted, bonus y) = P(x accepted) * p1[g(x)](y), g(x) the lowest
+      candidate proposing x (its row is the one the bonus reads).
+    """
+    from itertools import product
+    for p0s, toks, p1s, grid in designs:
+        mids = (np.arange(grid) + 0.5) / grid
+        G = len(toks)
+        V = len(p0s)
+        p0 = [Fraction(x) for x in p0s]
+        p1 = [[Fraction(x) for x in r] for r in p1s]
+        cells = np.array(list(product(range(grid), repeat=G + 1)))
+        Bn = len(cells)
+        logits = np.zeros((Bn, G, 2, V))
+        for g in range(G):
+            logits[:, g, 0] = logits_from_probs(p0s, 1.0)
+            logits[:, g, 1] = logits_from_probs(p1s[g], 1.0)
+        cand = np.broadcast_to(np.array(toks, dtype=np.int32)[None, :, None], (Bn, G, 1)).copy()
+        uni = np.zeros((Bn, 2, G + 1))
+        uni[:, 0, :G] = mids[cells[:, :G]]
+        uni[:, 0, G] = mids[cells[:, G]]
+        uni[:, 1, G] = 1.0 - mids[cells[:, G]]
+        res = orc.oracle_ngram_sample(logits, cand, uni, 1.0)
+        assert np.all(res.accept_len >= 0)
+        w = Fraction(1, Bn)
+        first = [w * int(np.sum(res.tokens[:, 0] == y)) for y in range(V)]
+        assert first == p0, ("first-token law", toks, first, p0)
+        for x in set(toks):
+            acc = res.accept_len == 1
+            px = w * int(np.sum(acc & (res.tokens[:, 0] == x)))
+            gx = toks.index(x)
+            for y in range(V):
+                got = w * int(np.sum(acc & (res.tokens[:, 0] == x) & (res.tokens[:, 1] == y)))
+                assert got == px * p1[gx][y], ("bonus law", toks, x, y, got, px * p1[gx][y])

@@ -73,3 +73,15 @@ def test_filters_off_match_plain_verify():
 
 def test_filtered_output_law_exact_on_a_grid():
     pins.check_filtered_exact_law(oracle)
+
+
+def test_golden_ngram_sample_rounds():
+    pins.check_golden_ngram_sample(oracle)
+
+
+def test_ngram_sample_one_candidate_is_speculative_decoding():
+    pins.check_ngram_sample_g1_matches_sample(oracle)
+
+
+def test_ngram_sample_output_law_exact():
+    pins.check_ngram_sample_exact_law(oracle)

@@ -62,6 +62,24 @@ MUTATIONS = [
      " for j, r in enumerate(rows)]"),
 ]
 
+MUTATIONS += [
+    ("n-gram: no renormalisation after a rejection",
+     "alpha = float(live[x]) / left if left > 0.0 else 0.0", "alpha = float(p[x])"),
+    ("n-gram: a rejected token keeps its mass", "                live[x] = 0.0                               # residual",
+     "                pass                                        # residual"),
+    ("n-gram: the highest active candidate's rows", "            g0 = active[0]\n", "            g0 = active[-1]\n"),
+    ("n-gram: the prefix filter ignored",
+     "            active = [h for h in active if int(cand[b, h, i]) == accepted]", "            active = active"),
+    ("n-gram: accept compares with <=", "                if r < alpha:                               # accept iff r",
+     "                if r <= alpha:                              # accept iff r"),
+    ("n-gram: the draw reads candidate 0's accept uniform", "float(uniforms[b, len(prefix), G])",
+     "float(uniforms[b, len(prefix), 0])"),
+    ("n-gram: accept uniforms indexed by try order, not candidate",
+     "                r = float(uniforms[b, i, h])", "                r = float(uniforms[b, i, active.index(h)])"),
+    ("n-gram: the bonus from the first row", "            if i == N - 1:                                  # every",
+     "            if i == N - 1 and False:                        # every"),
+]
+
 CHECKS = [
     pins.check_golden_sample,
     pins.check_golden_greedy,
@@ -79,6 +97,9 @@ CHECKS = [
     pins.check_filter_special_cases,
     pins.check_filters_off_match_plain,
     pins.check_filtered_exact_law,
+    pins.check_golden_ngram_sample,
+    pins.check_ngram_sample_g1_matches_sample,
+    pins.check_ngram_sample_exact_law,
 ]
 
 
