@@ -15,9 +15,9 @@ Prints ONE JSON line. Also reported: the pass-1 kernel alone (the dominant
 kernel, for the roofline), the same round with early exit (pass 1 in stages,
 spec_verify_sample_staged, which gives the same outputs), the same round
 verified on top-k 50 / top-p 0.9 filtered laws (spec_verify_sample_filtered),
-the n-gram pool (insert + lookup) and the greedy verify on their own
-workload (B=32 G=7 N=5 V=32000 bf16), and the CPU oracle on a bounded sample of
-the same round.
+the n-gram pool (insert + lookup), the greedy verify and the sampling verify
+of greedy-drafted n-grams on their own workload (B=32 G=7 N=5 V=32000 bf16),
+and the CPU oracle on a bounded sample of the same round.
 """
 from __future__ import annotations
 
@@ -37,7 +37,8 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, AMD published peak
 CACHE_BYTES = 256 * 2 ** 20  # MI355X Infinity Cache
 METRIC = "verify rounds/s + achieved HBM GB/s (% peak), B=64 K=8 V=128256 bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["common.hpp", "params.hpp", "sample.hip", "filter.hip", "greedy.hip"]
+KERNEL_SOURCES = ["common.hpp", "params.hpp", "rowstats.hpp", "search.hpp", "sample.hip", "filter.hip",
+                  "greedy.hip"]
 
 
 def log(msg: str) -> None:
@@ -56,6 +57,7 @@ def parse_args():
     ap.add_argument("--no-filtered", action="store_true", help="skip the top-k / top-p filtered leg")
     ap.add_argument("--no-staged", action="store_true", help="skip the early-exit (staged pass 1) leg")
     ap.add_argument("--no-pool", action="store_true", help="skip the n-gram pool leg")
+    ap.add_argument("--no-ngram-sample", action="store_true", help="skip the one-hot n-gram sampling verify leg")
     ap.add_argument("--eager", action="store_true", help="launch through the Python binding instead of graphs")
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB copy (calibration), then 3 eager verify rounds "
@@ -509,6 +511,52 @@ def main() -> int:
                   "algorithmic_bytes": gal}
         log(f"greedy {per * 1e6:.2f} us/round ({gal / per / 1e9:.0f} GB/s)")
 
+    # ---------------------------------------------------------------- sampling verify of one-hot n-grams, same shape
+    ngs = None
+    if not args.no_ngram_sample:
+        from workloads import make_ngram_sample_inputs
+        ns = make_ngram_sample_inputs(0, peak=10.0)
+        nb, ng, nn, nv = ns.shape
+        nlg = torch.from_numpy(ns.logits).to(dev).view(torch.bfloat16)
+        nbytes_set = nlg.numel() * 2
+        MN = max(2, math.ceil(2 * CACHE_BYTES / nbytes_set) + 1)
+        nsets = [dict(lg=nlg.clone(), cand=torch.from_numpy(ns.cand).to(dev), uni=torch.from_numpy(ns.uniforms).to(dev),
+                      ot=torch.empty((nb, nn), dtype=torch.int32, device=dev),
+                      ol=torch.empty((nb,), dtype=torch.int32, device=dev),
+                      orow=torch.empty((nb,), dtype=torch.int32, device=dev)) for _ in range(MN)]
+        del nlg
+        nws = torch.zeros(rsv.ngram_sample_workspace_size(nb, ng, nn, nv), dtype=torch.uint8, device=dev)
+
+        def ncall(st):
+            rsv.verify_ngram_sample(st["lg"], st["cand"], st["uni"], ns.temperature, out_tokens=st["ot"],
+                                    out_accept_len=st["ol"], out_rows=st["orow"], workspace=nws)
+
+        for st in nsets:
+            ncall(st)
+        torch.cuda.synchronize()
+        LN = MN * max(1, 48 // MN)
+        if args.eager:
+            nstep, ncalls = (lambda i: ncall(nsets[i % MN])), 1  # noqa: E731
+        else:
+            ngraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(ngraph):
+                for j in range(LN):
+                    ncall(nsets[j % MN])
+            nstep, ncalls = (lambda i: ngraph.replay()), LN  # noqa: E731
+        nrep = max(1, args.steps // ncalls)
+        timer.time(nstep, max(1, args.warmup // ncalls))
+        tn = timer.time(nstep, nrep) / (nrep * ncalls)
+        nL = nsets[0]["ol"].cpu().numpy()
+        # pass 1 reads every row once; the draw reads one row per sequence (twice, the second time from cache)
+        nalg = nbytes_set + nb * nv * 2
+        ngs = {"workload": f"sampling verify of greedy-drafted n-grams B={nb} G={ng} N={nn} V={nv} bf16 T=1.0, "
+                           "peaked rows, candidates on the peak w.p. 0.6",
+               "rounds_per_s": round(1.0 / tn, 1), "us_per_round": round(tn * 1e6, 3),
+               "achieved_gbps": round(nalg / tn / 1e9, 1), "frac_of_hbm_peak": round(nalg / tn / 1e9 / HBM_PEAK_GBPS, 4),
+               "algorithmic_bytes": nalg, "mean_accepted": round(float(nL.mean()), 4), "rotate": MN}
+        log(f"n-gram sampling verify {tn * 1e6:.2f} us/round ({nalg / tn / 1e9:.0f} GB/s), mean accepted {nL.mean():.3f}")
+        del nsets
+
     # ---------------------------------------------------------------- CPU oracle on a bounded sample
     cpu = None
     if not args.no_cpu_baseline:
@@ -556,6 +604,7 @@ def main() -> int:
         "staged": staged,
         "ngram_pool": pool_leg,
         "greedy": greedy,
+        "ngram_sample": ngs,
         "filtered": filtered,
     }
     print(json.dumps(out), flush=True)

@@ -78,6 +78,8 @@ typedef enum {
 #define SPEC_MAX_POOL_G 64          /* continuations a pool key holds */
 #define SPEC_MAX_POOL_N 17          /* n-gram length: a continuation holds at most 16 tokens */
 #define SPEC_MAX_POOL_W 64          /* n-grams per sequence in one insert call */
+#define SPEC_MAX_NGRAM_SAMPLE_V (1 << 20) /* vocabulary entries of spec_verify_ngram_sample */
+#define SPEC_MAX_NGRAM_SAMPLE_GN 1024    /* G*N of spec_verify_ngram_sample: one sequence's inputs staged on chip */
 
 /* Bytes of workspace spec_verify_sample needs for these sizes (0 for invalid sizes). */
 size_t spec_verify_sample_workspace_size(int32_t B, int32_t K, int32_t V);
@@ -249,6 +251,46 @@ spec_status spec_verify_greedy(const void* target_logits, int32_t dtype, const i
                                int32_t B, int32_t G, int32_t N, int32_t V, int32_t* out_tokens,
                                int32_t* out_accept_len, int32_t* out_best_cand, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace spec_verify_ngram_sample needs for these sizes (0 for invalid sizes). */
+size_t spec_verify_ngram_sample_workspace_size(int32_t B, int32_t G, int32_t N, int32_t V);
+
+/*
+ * Sampling verify (temperature > 0) of G greedy-drafted candidate n-grams.
+ * Source: "Lookahead Decoding 完全拆解:Jacobi 迭代与 N-gram 池,不靠草稿模型的投机解码",
+ * section "采样模式的验证" (the lookahead branch drafts greedily, so a candidate
+ * token's draft law is one-hot; the verify still samples in full), and
+ * "Speculative Decoding —— LLM推理优化技术（一）" §2.1 (with q = delta_x a token is
+ * accepted with probability p(x) and a rejection removes it from the law).
+ *
+ * target_logits  [B, G, N, V] dtype: row i of candidate g is the target's law
+ *                after the candidate's first i tokens; row N-1 the bonus row.
+ * cand_tokens    [B, G, N-1] int32.
+ * uniforms       [B, N, G+1] float in [0, 1): [b,i,h] accepts candidate h at
+ *                position i; [b,i,G] is the draw uniform of position i.
+ * B, G, N, V     0 <= B, 1 <= G <= 64, 2 <= N <= SPEC_MAX_K + 1,
+ *                G*N <= SPEC_MAX_NGRAM_SAMPLE_GN, 1 <= V <= SPEC_MAX_NGRAM_SAMPLE_V,
+ *                B*G*N <= SPEC_MAX_ROWS.
+ * temperature    finite, > 0; p = softmax(logits / T) in fp32.
+ * out_tokens     [B, N] int32: the accepted tokens, then the drawn token, then -1.
+ * out_accept_len [B] int32: L in [0, N-1], or -1 for a data fault.
+ * out_rows       [B] int32: the candidate whose rows the final draw read (-1 on a fault).
+ *
+ * The walk: at position i the active candidates (those whose first i tokens are
+ * the tokens accepted so far; all of them at i = 0) are tried in index order on
+ * p_cur, the law of the lowest active candidate's row i with the tokens rejected
+ * so far at i removed and renormalised: candidate h's token x is accepted iff
+ * uniforms[b,i,h] < p_cur(x). An acceptance keeps the candidates whose token at i
+ * is x and moves to i + 1; after N-1 acceptances a bonus token is drawn from row
+ * N-1 of the lowest active candidate. When every try at i fails, the token is
+ * drawn from p_cur (the rule of spec_verify_sample; zero remaining mass falls
+ * back to p). Data faults: a candidate token outside [0, V), or a consulted row
+ * with no finite logit.
+ */
+spec_status spec_verify_ngram_sample(const void* target_logits, int32_t dtype, const int32_t* cand_tokens,
+                                     const float* uniforms, int32_t B, int32_t G, int32_t N, int32_t V,
+                                     float temperature, int32_t* out_tokens, int32_t* out_accept_len,
+                                     int32_t* out_rows, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The n-gram pool that supplies spec_verify_greedy's candidates.

@@ -5,19 +5,22 @@ Entry points (torch tensors in, torch tensors out; every computation runs in HIP
   verify_sample_filtered -- the same on top-k / top-p filtered laws (same filter on both sides)
   verify_sample_staged -- verify_sample with early exit: pass 1 in stages over the draft positions
   verify_greedy  -- greedy longest-prefix verify of G candidate n-grams
+  verify_ngram_sample -- sampling verify of G greedy-drafted (one-hot) candidate n-grams
   fill_uniforms  -- Philox4x32-10 verify uniforms on the device
   NgramPool      -- the n-gram pool that supplies verify_greedy's candidates (insert / lookup)
 """
 from ._lib import (LIB_PATH, PHASE_ACCEPT, PHASE_ALL, PHASE_DRAW, PHASE_MASS, PHASE_ROW_STATS, SPEC_BF16, SPEC_F32,
-                   SPEC_MAX_K, GreedyOutputs, NgramPool, SampleOutputs, SpecVerifyError, abi_version, fill_uniforms,
-                   greedy_workspace_size, lib, ngram_pool_bytes, sample_filtered_workspace_size, sample_workspace_size,
-                   status_string, verify_greedy, verify_sample, verify_sample_filtered, verify_sample_staged,
+                   SPEC_MAX_K, GreedyOutputs, NgramPool, NgramSampleOutputs, SampleOutputs, SpecVerifyError,
+                   abi_version, fill_uniforms, greedy_workspace_size, lib, ngram_pool_bytes,
+                   ngram_sample_workspace_size, sample_filtered_workspace_size, sample_workspace_size, status_string,
+                   verify_greedy, verify_ngram_sample, verify_sample, verify_sample_filtered, verify_sample_staged,
                    workspace_for)
 
 __all__ = [
     "LIB_PATH", "PHASE_ACCEPT", "PHASE_ALL", "PHASE_DRAW", "PHASE_MASS", "PHASE_ROW_STATS", "SPEC_BF16", "SPEC_F32",
-    "SPEC_MAX_K", "GreedyOutputs", "NgramPool", "SampleOutputs", "SpecVerifyError", "abi_version", "fill_uniforms",
-    "greedy_workspace_size", "lib", "ngram_pool_bytes", "sample_filtered_workspace_size",
-    "sample_workspace_size", "status_string", "verify_greedy", "verify_sample", "verify_sample_filtered",
-    "verify_sample_staged", "workspace_for",
+    "SPEC_MAX_K", "GreedyOutputs", "NgramPool", "NgramSampleOutputs", "SampleOutputs", "SpecVerifyError",
+    "abi_version", "fill_uniforms", "greedy_workspace_size", "lib", "ngram_pool_bytes", "ngram_sample_workspace_size",
+    "sample_filtered_workspace_size",
+    "sample_workspace_size", "status_string", "verify_greedy", "verify_ngram_sample", "verify_sample",
+    "verify_sample_filtered", "verify_sample_staged", "workspace_for",
 ]

@@ -51,6 +51,10 @@ _SIGNATURES = {
     "spec_verify_greedy": (_i32, [_c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
                                   _c_void_p, _c_void_p, _size_t, _c_void_p]),
     "spec_fill_uniforms": (_i32, [_u64, _u64, _i32, _i32, _c_void_p, _c_void_p]),
+    "spec_verify_ngram_sample_workspace_size": (_size_t, [_i32, _i32, _i32, _i32]),
+    "spec_verify_ngram_sample": (_i32, [_c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32,
+                                        ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
+                                        _c_void_p]),
     "spec_ngram_pool_bytes": (_size_t, [_i32, _i32, _i32, _i32]),
     "spec_ngram_pool_init": (_i32, [_c_void_p, _size_t, _i32, _i32, _i32, _i32, _c_void_p]),
     "spec_ngram_pool_insert": (_i32, [_c_void_p, _size_t, _i32, _i32, _i32, _i32, _c_void_p, _i32, _c_void_p,
@@ -318,6 +322,57 @@ def verify_greedy(logits: torch.Tensor, cand: torch.Tensor, *, out_tokens: torch
     if st != 0:
         raise SpecVerifyError(st, "spec_verify_greedy")
     return GreedyOutputs(out_tokens, out_accept_len, out_best)
+
+
+@dataclass
+class NgramSampleOutputs:
+    tokens: torch.Tensor      # [B, N] int32
+    accept_len: torch.Tensor  # [B] int32
+    rows: torch.Tensor        # [B] int32
+
+
+def ngram_sample_workspace_size(B: int, G: int, N: int, V: int) -> int:
+    return int(lib().spec_verify_ngram_sample_workspace_size(B, G, N, V))
+
+
+def verify_ngram_sample(logits: torch.Tensor, cand: torch.Tensor, uniforms: torch.Tensor, temperature: float, *,
+                        out_tokens: torch.Tensor | None = None, out_accept_len: torch.Tensor | None = None,
+                        out_rows: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        stream=None) -> NgramSampleOutputs:
+    """spec_verify_ngram_sample: sampling verify of G greedy-drafted candidate n-grams.
+
+    logits [B, G, N, V] (bf16 or fp32), cand [B, G, N-1] int32, uniforms [B, N, G+1] float32.
+    """
+    if logits.dim() != 4:
+        raise ValueError("logits must be [B, G, N, V]")
+    B, G, N, V = logits.shape
+    dev = logits.device
+    _check(logits, "logits", dev)
+    code = _dtype_code(logits)
+    _check(cand, "cand", dev, torch.int32, (B, G, N - 1))
+    _check(uniforms, "uniforms", dev, torch.float32, (B, N, G + 1))
+    if out_tokens is None:
+        out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if out_accept_len is None:
+        out_accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_rows is None:
+        out_rows = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", dev, torch.int32, (B, N))
+    _check(out_accept_len, "out_accept_len", dev, torch.int32, (B,))
+    _check(out_rows, "out_rows", dev, torch.int32, (B,))
+    sh = _stream_handle(stream, dev)
+    nbytes = ngram_sample_workspace_size(B, G, N, V)
+    if nbytes == 0 and B > 0:
+        raise SpecVerifyError(-2, "spec_verify_ngram_sample_workspace_size")
+    if workspace is None:
+        workspace = workspace_for(dev, sh, nbytes)
+    _check(workspace, "workspace", dev, torch.uint8)
+    st = lib().spec_verify_ngram_sample(_ptr(logits), code, _ptr(cand), _ptr(uniforms), B, G, N, V,
+                                        float(temperature), _ptr(out_tokens), _ptr(out_accept_len), _ptr(out_rows),
+                                        _ptr(workspace), workspace.numel(), ctypes.c_void_p(sh))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_verify_ngram_sample")
+    return NgramSampleOutputs(out_tokens, out_accept_len, out_rows)
 
 
 def fill_uniforms(seed: int, rnd: int, B: int, K: int, *, out: torch.Tensor | None = None,

@@ -12,6 +12,7 @@
 #define SPEC_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace sv {
+hipError_t launch_ngram_sample(const NgramSampleParams& P, bool bf16, hipStream_t stream);
 hipError_t launch_pool_fill(int32_t* pool, int64_t n, hipStream_t stream);
 hipError_t launch_pool_insert(const PoolParams& P, hipStream_t stream);
 hipError_t launch_pool_lookup(const PoolParams& P, hipStream_t stream);
@@ -400,5 +401,87 @@ SPEC_EXPORT spec_status spec_ngram_pool_lookup(const void* pool, size_t pool_byt
   P.out_cand = out_cand;
   P.out_count = out_count;
   const hipError_t e = sv::launch_pool_lookup(P, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- sampling verify of one-hot n-grams
+
+namespace {
+
+bool ngram_sample_shape_ok(int32_t B, int32_t G, int32_t N, int32_t V) {
+  if (B < 0 || G < 1 || G > SPEC_MAX_POOL_G || N < 2 || N > SPEC_MAX_K + 1 || V < 1 || V > SPEC_MAX_NGRAM_SAMPLE_V)
+    return false;
+  if (G * N > SPEC_MAX_NGRAM_SAMPLE_GN) return false;
+  return static_cast<int64_t>(B) * G * N <= SPEC_MAX_ROWS;
+}
+
+struct NgsLayout {
+  int32_t S1, S1max, nbmax;
+  size_t off_m, off_s, off_gx, off_blk, total;
+};
+
+NgsLayout ngs_layout(int32_t B, int32_t G, int32_t N, int32_t V) {
+  NgsLayout L{};
+  const int64_t rows = static_cast<int64_t>(B) * G * N;
+  L.S1max = seg_max(rows, V);
+  L.S1 = seg_choice(rows, V, 1024, 8192, L.S1max, "SPECVERIFY_S4");
+  size_t off = 0;
+  const size_t p1 = static_cast<size_t>(rows) * L.S1max;
+  L.off_m = off; off = align256(off + p1 * sizeof(float));
+  L.off_s = off; off = align256(off + p1 * sizeof(double));
+  L.off_gx = off; off = align256(off + static_cast<size_t>(B) * G * (N - 1) * G * sizeof(float));
+  // blocks per row: at most ceil(V / (4 * kNgsBlkVecs)), fp32 holding 4 entries per vector
+  L.nbmax = static_cast<int32_t>(ceil_div(V, 4 * sv::kNgsBlkVecs));
+  L.off_blk = off; off = align256(off + static_cast<size_t>(rows) * L.nbmax * 2 * sizeof(float));
+  L.total = std::max<size_t>(off, 256);
+  return L;
+}
+
+}  // namespace
+
+SPEC_EXPORT size_t spec_verify_ngram_sample_workspace_size(int32_t B, int32_t G, int32_t N, int32_t V) {
+  if (!ngram_sample_shape_ok(B, G, N, V)) return 0;
+  return ngs_layout(B, G, N, V).total;
+}
+
+SPEC_EXPORT spec_status spec_verify_ngram_sample(const void* target_logits, int32_t dtype, const int32_t* cand_tokens,
+                                                 const float* uniforms, int32_t B, int32_t G, int32_t N, int32_t V,
+                                                 float temperature, int32_t* out_tokens, int32_t* out_accept_len,
+                                                 int32_t* out_rows, void* workspace, size_t workspace_bytes,
+                                                 void* stream) {
+  if (!ngram_sample_shape_ok(B, G, N, V)) return SPEC_ERR_SHAPE;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
+  if (!(std::isfinite(temperature) && temperature > 0.f)) return SPEC_ERR_TEMPERATURE;
+  const float c = static_cast<float>(1.4426950408889634074 / static_cast<double>(temperature));
+  if (!std::isfinite(c)) return SPEC_ERR_TEMPERATURE;
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !cand_tokens || !uniforms || !out_tokens || !out_accept_len || !out_rows || !workspace)
+    return SPEC_ERR_NULL;
+  const size_t es = dtype == SPEC_BF16 ? 2 : 4;
+  if (!aligned(target_logits, es) || !aligned(cand_tokens, 4) || !aligned(uniforms, 4) || !aligned(out_tokens, 4) ||
+      !aligned(out_accept_len, 4) || !aligned(out_rows, 4) || !aligned(workspace, 8))
+    return SPEC_ERR_ALIGN;
+  const NgsLayout L = ngs_layout(B, G, N, V);
+  if (workspace_bytes < L.total) return SPEC_ERR_WORKSPACE;
+  sv::NgramSampleParams P{};
+  P.logits = target_logits;
+  P.cand = cand_tokens;
+  P.uniforms = uniforms;
+  P.B = B;
+  P.G = G;
+  P.N = N;
+  P.V = V;
+  P.c = c;
+  P.S1 = L.S1;
+  P.S1max = L.S1max;
+  P.out_tokens = out_tokens;
+  P.out_len = out_accept_len;
+  P.out_rows = out_rows;
+  P.p1_m = at<float>(workspace, L.off_m);
+  P.p1_s = at<double>(workspace, L.off_s);
+  P.gx = at<float>(workspace, L.off_gx);
+  P.blk = at<float2>(workspace, L.off_blk);
+  P.nbmax = L.nbmax;
+  const hipError_t e = sv::launch_ngram_sample(P, dtype == SPEC_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

@@ -22,6 +22,19 @@ __device__ __forceinline__ u32x4 load_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// A raw buffer resource over [base, base + bytes), bytes < 2^31: a 16-byte load at
+// an offset past the end returns zero without a memory access (the hardware's
+// range check), so loads need no per-lane guard.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// 16-byte nontemporal load of vector `vi` of a buffer resource (zero past its end).
+__device__ __forceinline__ u32x4 load_stream_buf(__amdgpu_buffer_rsrc_t r, int vi) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, vi * 16, 0, 2);
+}
+
 // ---------------------------------------------------------------- element access
 
 template <typename T>

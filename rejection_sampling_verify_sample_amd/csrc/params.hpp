@@ -92,6 +92,32 @@ struct GreedyLayout {
 
 constexpr int32_t kMaxGreedyRowsPerBatch = 8192;  // G*N: argmaxes of one batch row held in LDS
 
+// ---------------------------------------------------------------- sampling verify of one-hot n-grams
+
+struct NgramSampleParams {
+  const void* logits;      // [B, G, N, V]
+  const int32_t* cand;     // [B, G, N-1]
+  const float* uniforms;   // [B, N, G+1]
+  int32_t B, G, N, V;
+  float c;                 // log2(e) / T, rounded to fp32
+  int32_t S1, S1max;       // segments per row / partial slots per row
+  int32_t* out_tokens;     // [B, N]
+  int32_t* out_len;        // [B]
+  int32_t* out_rows;       // [B]
+  float* p1_m;             // [B*G*N*S1max] segment maxima
+  double* p1_s;            // [B*G*N*S1max] segment sums against fl(m*c)
+  float* gx;               // [B*G*(N-1)*G] logit of candidate h's token at position i in row (g, i)
+  float2* blk;             // [B*G*N*nbmax] per block of kNgsBlkVecs vectors: (R, sum of 2^(x*c - R))
+  int32_t nbmax;           // block slots per row
+};
+
+// 16-byte vectors per block of the n-gram sampling verify's pass 1 (the macro
+// exists for measured sweeps).
+#ifndef SV_NGS_BLK_VECS
+#define SV_NGS_BLK_VECS 256
+#endif
+constexpr int kNgsBlkVecs = SV_NGS_BLK_VECS;
+
 // ---------------------------------------------------------------- n-gram pool
 
 struct PoolParams {

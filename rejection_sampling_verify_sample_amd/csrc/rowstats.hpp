@@ -1,0 +1,114 @@
+// Streaming row statistics shared by the verify kernels (gfx950): the online
+// (max, sum of 2^(x*c - R)) of a row segment, and the merge of a row's segment
+// partials.
+#pragma once
+
+#include "common.hpp"
+
+namespace sv {
+
+// ---------------------------------------------------------------- online softmax over a segment
+
+// Launch geometry, chosen by measured sweeps on gfx950 (the macros exist for such sweeps).
+#ifndef SV_ROW_BLOCK
+#define SV_ROW_BLOCK 128
+#endif
+#ifndef SV_ROW_UNROLL
+#define SV_ROW_UNROLL 4
+#endif
+constexpr int kRowBlock = SV_ROW_BLOCK;  // threads per row-statistics workgroup
+constexpr int kUnroll = SV_ROW_UNROLL;   // 16-byte vectors in flight per thread per step
+
+template <int BS, typename T>
+__device__ __forceinline__ void online_scalar(const T* row, int64_t lo, int64_t hi, float c, Online& o) {
+  for (int64_t e = lo + threadIdx.x; e < hi; e += BS) {
+    const float x = Elem<T>::get(row, e);
+    if (x > o.m) o.raise(x, c);
+    o.add(x, c);
+  }
+}
+
+template <int BS, typename T>
+__device__ __forceinline__ void online_segment(const T* row, int64_t V, int seg, int S, float c, Online& o) {
+  constexpr int VEC = Elem<T>::kVec;
+  const SegRange r = seg_range(row, V, seg, S);
+  if (seg == 0) online_scalar<BS>(row, 0, r.head, c, o);
+  const T* vb = row + r.head;
+  int64_t v = r.v0 + threadIdx.x;
+  for (; v + (kUnroll - 1) * BS < r.v1; v += kUnroll * BS) {
+    float x[kUnroll][VEC];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) Elem<T>::vec(vb + (v + u * BS) * VEC, x[u]);
+    float mt = x[0][0];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) mt = fmaxf(mt, x[u][e]);
+    if (mt > o.m) o.raise(mt, c);
+    float t = 0.f;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float a = exp2_hw(fmaf(x[u][0], c, -o.R));
+#pragma unroll
+      for (int e = 1; e < VEC; ++e) a += exp2_hw(fmaf(x[u][e], c, -o.R));
+      t += a;
+    }
+    o.s += t;
+  }
+  for (; v < r.v1; v += BS) {
+    float x[VEC];
+    Elem<T>::vec(vb + v * VEC, x);
+    float mt = x[0];
+#pragma unroll
+    for (int e = 1; e < VEC; ++e) mt = fmaxf(mt, x[e]);
+    if (mt > o.m) o.raise(mt, c);
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) a += exp2_hw(fmaf(x[e], c, -o.R));
+    o.s += a;
+  }
+  if (seg == S - 1) online_scalar<BS>(row, r.head + ((V - r.head) / VEC) * VEC, V, c, o);
+}
+
+// Merge segment partials (m_j, s_j) of one row, in segment order. Each partial is
+// rescaled from its reference fl(m_j * c) to the row's by 2^d, with d the exact
+// fp64 difference of the two references and 2^d from the hardware unit (about
+// 1e-7 relative, the order of the fp32 sums inside each partial); the partial
+// holding the maximum needs no rescale.
+// Up to kMergeRegs partials are loaded at once (one round of loads, held in
+// registers); a row split into more segments is read in a loop.
+constexpr int kMergeRegs = 16;
+
+__device__ __forceinline__ double rescaled_partial(double sj, float Rj, float RMf) {
+  if (!(sj > 0.0)) return 0.0;
+  return (Rj == RMf) ? sj
+                     : sj * static_cast<double>(exp2_hw(static_cast<float>(static_cast<double>(Rj) -
+                                                                           static_cast<double>(RMf))));
+}
+
+__device__ __forceinline__ void merge_partials(const float* pm, const double* ps, int S, float c, float& M,
+                                               double& Ssum) {
+  M = -INFINITY;
+  Ssum = 0.0;
+  if (S <= kMergeRegs) {
+    float mv[kMergeRegs];
+    double sv[kMergeRegs];
+#pragma unroll
+    for (int j = 0; j < kMergeRegs; ++j) {
+      const bool in = j < S;
+      mv[j] = in ? pm[j] : -INFINITY;
+      sv[j] = in ? ps[j] : 0.0;
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeRegs; ++j) M = fmaxf(M, mv[j]);
+    const float RMf = M * c;
+#pragma unroll
+    for (int j = 0; j < kMergeRegs; ++j) Ssum += rescaled_partial(sv[j], mv[j] * c, RMf);
+    return;
+  }
+  for (int j = 0; j < S; ++j) M = fmaxf(M, pm[j]);
+  const float RMf = M * c;
+  for (int j = 0; j < S; ++j) Ssum += rescaled_partial(ps[j], pm[j] * c, RMf);
+}
+
+}  // namespace sv

@@ -199,3 +199,39 @@ def compare_filtered(target, draft, tokens_in, uniforms, T, top_k, top_p, res: "
         d = _interval_distance(w, float(uniforms[b, n, 1]), int(gpu_tokens[b, n]))
         assert d < window, f"row {b}: GPU token {gpu_tokens[b, n]} is {d:.3e} from u*Z"
     return rep
+
+
+# --------------------------------------------------------------------------- sampling verify of one-hot n-grams
+
+def compare_ngram_sample(cand, V, res: "oracle.NgramSampleResult", gpu_tokens, gpu_len, gpu_rows,
+                         window: float = WINDOW) -> ParityReport:
+    """Bit-exact tokens, accepted length and row choice outside the window; inside it,
+    a valid walk: the accepted tokens follow some candidate, the drawn token is in
+    range and the tail is -1."""
+    B, G, Nm1 = cand.shape
+    N = Nm1 + 1
+    rep = ParityReport(rows=B)
+    margin = res.min_margin()
+    for b in range(B):
+        on, gn = int(res.accept_len[b]), int(gpu_len[b])
+        same = (on == gn and np.array_equal(res.tokens[b], gpu_tokens[b]) and int(res.rows[b]) == int(gpu_rows[b]))
+        if margin[b] >= window:
+            if not same:
+                rep.mismatches.append(b)
+                raise AssertionError(f"row {b}: oracle L={on} tokens={res.tokens[b].tolist()} rows={res.rows[b]} vs "
+                                     f"GPU L={gn} tokens={gpu_tokens[b].tolist()} rows={gpu_rows[b]} "
+                                     f"(margin {margin[b]:.3e})")
+            continue
+        rep.ambiguous += 1
+        if same:
+            rep.ambiguous_agree += 1
+            continue
+        assert on >= 0 and gn >= 0, f"row {b}: fault status differs ({on} vs {gn})"
+        active = list(range(G))
+        for t in range(gn):
+            x = int(gpu_tokens[b, t])
+            active = [h for h in active if int(cand[b, h, t]) == x]
+            assert active, f"row {b}: accepted token {x} at {t} is no active candidate's"
+        assert 0 <= int(gpu_tokens[b, gn]) < V and np.all(gpu_tokens[b, gn + 1:] == -1)
+        assert int(gpu_rows[b]) == active[0], f"row {b}: rows {gpu_rows[b]} is not the lowest active candidate"
+    return rep

@@ -37,7 +37,7 @@ def test_library_is_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     L = ctypes.CDLL(rsv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
@@ -197,6 +197,37 @@ def pool_call(fn, **kw):
 ])
 def test_ngram_pool_argument_checks(fn, kw, expect):
     assert pool_call(fn, **kw) == expect
+
+
+def ngram_sample(**kw):
+    a = dict(logits=P, dtype=1, cand=P, uniforms=P, B=2, G=3, N=4, V=100, T=1.0, out_tokens=P, out_len=P,
+             out_rows=P, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return rsv.lib().spec_verify_ngram_sample(a["logits"], a["dtype"], a["cand"], a["uniforms"], a["B"], a["G"],
+                                              a["N"], a["V"], a["T"], a["out_tokens"], a["out_len"], a["out_rows"],
+                                              a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), ERR_SHAPE), (dict(G=0), ERR_SHAPE), (dict(G=65), ERR_SHAPE), (dict(N=1), ERR_SHAPE),
+    (dict(N=66), ERR_SHAPE), (dict(V=0), ERR_SHAPE), (dict(V=(1 << 20) + 1), ERR_SHAPE),
+    (dict(B=1 << 20, G=64, N=2), ERR_SHAPE), (dict(G=64, N=17), ERR_SHAPE), (dict(G=16, N=65), ERR_SHAPE),
+    (dict(dtype=2), ERR_DTYPE), (dict(T=0.0), ERR_TEMP), (dict(T=float("inf")), ERR_TEMP),
+    (dict(logits=None), ERR_NULL), (dict(cand=None), ERR_NULL), (dict(uniforms=None), ERR_NULL),
+    (dict(out_rows=None), ERR_NULL), (dict(ws=None), ERR_NULL),
+    (dict(logits=P + 1), ERR_ALIGN), (dict(cand=P + 2), ERR_ALIGN), (dict(ws=P + 4), ERR_ALIGN),
+    (dict(ws_bytes=16), ERR_WS), (dict(B=0), OK), (dict(B=0, logits=None), OK),
+])
+def test_ngram_sample_argument_checks(kw, expect):
+    assert ngram_sample(**kw) == expect
+
+
+def test_ngram_sample_workspace_size():
+    assert rsv.ngram_sample_workspace_size(32, 7, 5, 32000) > 0
+    assert rsv.ngram_sample_workspace_size(32, 65, 5, 32000) == 0
+    assert rsv.ngram_sample_workspace_size(32, 7, 66, 32000) == 0
+    assert rsv.ngram_sample_workspace_size(32, 64, 16, 32000) > 0
+    assert rsv.ngram_sample_workspace_size(32, 64, 17, 32000) == 0
 
 
 def test_sample_k0_needs_no_draft():

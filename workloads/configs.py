@@ -45,7 +45,7 @@ import numpy as np
 from scipy.special import ndtri
 
 from .bf16 import bf16_bits_to_f32, f32_to_bf16_bits
-from .philox import verify_uniforms
+from .philox import ngram_uniforms, verify_uniforms
 
 F32 = "f32"
 BF16 = "bf16"
@@ -268,3 +268,45 @@ def make_filter_params(B: int, seed: int = 0, *, top_k: int | None = None, top_p
     p = (np.full(B, top_p, dtype=np.float32) if top_p is not None
          else rng.choice(FILTER_TOP_P, size=B).astype(np.float32))
     return k, p
+
+
+@dataclass
+class NgramSampleInputs:
+    logits: np.ndarray          # [B, G, N, V] float32 values, or bf16 bits (uint16)
+    dtype: str
+    cand: np.ndarray            # [B, G, N-1] int32
+    uniforms: np.ndarray        # [B, N, G+1] float32
+    temperature: float
+    name: str = ""
+
+    @property
+    def shape(self):
+        return self.logits.shape
+
+    def logits_f32(self) -> np.ndarray:
+        return bf16_bits_to_f32(self.logits) if self.dtype == BF16 else self.logits
+
+
+def make_ngram_sample_inputs(rnd: int = 0, *, B: int = 32, G: int = 7, N: int = 5, V: int = 32000,
+                             dtype: str = BF16, T: float = 1.0, peak: float = 8.0, match_prob: float = 0.6,
+                             seed: int = 0) -> NgramSampleInputs:
+    """A sampling verify of greedy-drafted n-grams at the greedy workload's shape.
+
+    Rows are N(0, 1) with one token raised by `peak` (placed uniformly), so the
+    tempered law puts a visible mass on it (peak 8 at T = 1 over V = 32000: about
+    0.08); a candidate token is the placed token with probability `match_prob`
+    (the greedy draft saw the same peak), else uniform on [0, V). Uniforms from
+    ngram_uniforms (Philox, seed, round).
+    """
+    rng = _rng(seed, 6, rnd, 0)
+    n = B * G * N
+    rows = rng.normal(0.0, 1.0, size=(n, V))
+    pos = rng.integers(0, V, size=n)
+    rows[np.arange(n), pos] += peak
+    logits = _store(rows.reshape(B, G, N, V), dtype)
+    placed = pos.reshape(B, G, N)[:, :, : N - 1]
+    hit = rng.random((B, G, N - 1)) < match_prob
+    cand = np.where(hit, placed, rng.integers(0, V, size=(B, G, N - 1))).astype(np.int32)
+    uni = ngram_uniforms(seed, rnd, B, N, G)
+    return NgramSampleInputs(logits, dtype, cand, uni, float(np.float32(T)),
+                             name=f"ngram-sample B={B} G={G} N={N} V={V} {dtype} T={T} round={rnd}")

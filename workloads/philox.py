@@ -77,3 +77,27 @@ def verify_uniforms(seed: int, rnd: int, B: int, K: int) -> np.ndarray:
     u[..., 0] = words_to_unit(out[..., 0])
     u[..., 1] = words_to_unit(out[..., 1])
     return u
+
+
+def ngram_uniforms(seed: int, rnd: int, B: int, N: int, G: int) -> np.ndarray:
+    """Uniforms [B, N, G+1] float32 for the sampling verify of n-gram candidates.
+
+    Philox4x32-10 (same key as verify_uniforms) with counter (i | j << 16, b,
+    round lo32, round hi32 | 1 << 31), j = h // 4, word h % 4 -> [b, i, h]: a
+    stream of its own, disjoint from verify_uniforms' counters.
+    """
+    if B < 0 or N < 1 or G < 1:
+        raise ValueError("bad sizes")
+    H = G + 1
+    nj = (H + 3) // 4
+    i = np.arange(N, dtype=np.uint32)[None, :, None]
+    j = np.arange(nj, dtype=np.uint32)[None, None, :]
+    b = np.arange(B, dtype=np.uint32)[:, None, None]
+    ctr = np.zeros((B, N, nj, 4), dtype=np.uint32)
+    ctr[..., 0] = i | (j << np.uint32(16))
+    ctr[..., 1] = b
+    ctr[..., 2] = np.uint32(rnd & 0xFFFFFFFF)
+    ctr[..., 3] = np.uint32(((rnd >> 32) & 0x7FFFFFFF) | 0x80000000)
+    key = np.array([seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF], dtype=np.uint32)
+    out = philox4x32_10(ctr, key).reshape(B, N, nj * 4)[:, :, :H]
+    return words_to_unit(out).astype(np.float32)
