@@ -196,8 +196,8 @@ __global__ __launch_bounds__(kNgsRowBlock) void k_ngs_rowstats(NgramSampleParams
       double Ssum = 0.0;
 #pragma unroll
       for (int w = 0; w < kNgsRowWaves; ++w) Ssum += rescaled_partial(sh_s[w], sh_m[w] * c, RM);
-      P.p1_m[row * P.S1max + seg] = M;
-      P.p1_s[row * P.S1max + seg] = Ssum;
+      P.p1_m[seg * rows + row] = M;
+      P.p1_s[seg * rows + row] = Ssum;
     }
     if (seg == 0 && i < P.N - 1 && h < P.G) P.gx[(bg * (P.N - 1) + i) * P.G + h] = xg;
     __syncthreads();  // shared memory is reused by the next task
@@ -240,7 +240,7 @@ __device__ __forceinline__ bool ngs_stage(const NgramSampleParams& P, int b, Ngs
     const int64_t row = static_cast<int64_t>(b) * G * N + r;
     float M;
     double Z;
-    merge_partials(P.p1_m + row * P.S1max, P.p1_s + row * P.S1max, P.S1, P.c, M, Z);
+    merge_partials(P.p1_m + row, P.p1_s + row, static_cast<int64_t>(P.B) * G * N, P.S1, P.c, M, Z);
     sh.M[r] = M;
     sh.Z[r] = Z;
   }

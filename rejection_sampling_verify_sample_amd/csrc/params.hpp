@@ -18,7 +18,7 @@ struct SampleParams {
   int32_t B, K, V;
   float c;                 // log2(e) / T, rounded to fp32
   int32_t S1, S2;          // segments per row in pass 1 (the widest stage) / workgroups per batch row in pass 2
-  int32_t S1max;           // partial slots per logit row: the stride of p1_m / p1_s
+  int32_t S1max;           // partial slots per logit row
   // Pass 1 in stages over the draft positions (early exit): stage s reads positions
   // [stage_end[s-1], stage_end[s]) with stage_S1[s] segments per row, only for batch
   // rows that accepted every earlier position. One stage: every position at once.
@@ -32,8 +32,8 @@ struct SampleParams {
   float* out_probs;        // [B, K, 2] or null
   // workspace (written by one kernel, read by a later one: no counters, no clearing)
   int32_t NCmax;           // chunk slots per batch row in p2_cm / p2_cs
-  float* p1_m;             // [B*2K*S1max] segment maxima (row statistics)
-  double* p1_s;            // [B*2K*S1max] segment sums against fl(m*c)
+  float* p1_m;             // [S1max][B*2K] segment maxima (row statistics), segment-major
+  double* p1_s;            // [S1max][B*2K] segment sums against fl(m*c)
   float* p1_x;             // [B*2K] logit of the draft token in each row (NaN if the token is out of range)
   int32_t* info_n;         // [B] first rejection n, K when all accepted, -1 on a fault (accept decisions)
   float* info_R;           // [B, 2] reference exponents of target row n, draft row n
@@ -104,8 +104,8 @@ struct NgramSampleParams {
   int32_t* out_tokens;     // [B, N]
   int32_t* out_len;        // [B]
   int32_t* out_rows;       // [B]
-  float* p1_m;             // [B*G*N*S1max] segment maxima
-  double* p1_s;            // [B*G*N*S1max] segment sums against fl(m*c)
+  float* p1_m;             // [S1max][B*G*N] segment maxima, segment-major
+  double* p1_s;            // [S1max][B*G*N] segment sums against fl(m*c)
   float* gx;               // [B*G*(N-1)*G] logit of candidate h's token at position i in row (g, i)
   float2* blk;             // [B*G*N*nbmax] per block of kNgsBlkVecs vectors: (R, sum of 2^(x*c - R))
   int32_t nbmax;           // block slots per row

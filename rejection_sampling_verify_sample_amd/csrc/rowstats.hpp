@@ -70,7 +70,9 @@ __device__ __forceinline__ void online_segment(const T* row, int64_t V, int seg,
   if (seg == S - 1) online_scalar<BS>(row, r.head + ((V - r.head) / VEC) * VEC, V, c, o);
 }
 
-// Merge segment partials (m_j, s_j) of one row, in segment order. Each partial is
+// Merge segment partials (m_j, s_j) = (pm[j*stride], ps[j*stride]) of one row, in
+// segment order (the partial arrays are segment-major, so a one-segment layout
+// packs the rows' partials densely). Each partial is
 // rescaled from its reference fl(m_j * c) to the row's by 2^d, with d the exact
 // fp64 difference of the two references and 2^d from the hardware unit (about
 // 1e-7 relative, the order of the fp32 sums inside each partial); the partial
@@ -86,8 +88,8 @@ __device__ __forceinline__ double rescaled_partial(double sj, float Rj, float RM
                                                                            static_cast<double>(RMf))));
 }
 
-__device__ __forceinline__ void merge_partials(const float* pm, const double* ps, int S, float c, float& M,
-                                               double& Ssum) {
+__device__ __forceinline__ void merge_partials(const float* pm, const double* ps, int64_t stride, int S, float c,
+                                               float& M, double& Ssum) {
   M = -INFINITY;
   Ssum = 0.0;
   if (S <= kMergeRegs) {
@@ -96,8 +98,8 @@ __device__ __forceinline__ void merge_partials(const float* pm, const double* ps
 #pragma unroll
     for (int j = 0; j < kMergeRegs; ++j) {
       const bool in = j < S;
-      mv[j] = in ? pm[j] : -INFINITY;
-      sv[j] = in ? ps[j] : 0.0;
+      mv[j] = in ? pm[j * stride] : -INFINITY;
+      sv[j] = in ? ps[j * stride] : 0.0;
     }
 #pragma unroll
     for (int j = 0; j < kMergeRegs; ++j) M = fmaxf(M, mv[j]);
@@ -106,9 +108,9 @@ __device__ __forceinline__ void merge_partials(const float* pm, const double* ps
     for (int j = 0; j < kMergeRegs; ++j) Ssum += rescaled_partial(sv[j], mv[j] * c, RMf);
     return;
   }
-  for (int j = 0; j < S; ++j) M = fmaxf(M, pm[j]);
+  for (int j = 0; j < S; ++j) M = fmaxf(M, pm[j * stride]);
   const float RMf = M * c;
-  for (int j = 0; j < S; ++j) Ssum += rescaled_partial(ps[j], pm[j] * c, RMf);
+  for (int j = 0; j < S; ++j) Ssum += rescaled_partial(ps[j * stride], pm[j * stride] * c, RMf);
 }
 
 }  // namespace sv

@@ -51,6 +51,9 @@ __device__ __forceinline__ const T* draft_row(const SampleParams& P, int b, int 
 // ---------------------------------------------------------------- row statistics (pass 1)
 
 // Segments per row of the pass-1 stage that holds draft position `pos`.
+// Rows of the pass-1 partial arrays: the stride between their segments.
+__device__ __forceinline__ int64_t p1_rows(const SampleParams& P) { return static_cast<int64_t>(P.B) * 2 * P.K; }
+
 __device__ __forceinline__ int stage_segments(const SampleParams& P, int pos) {
   int S = P.stage_S1[0];
   for (int s = 1; s < P.nstage; ++s)
@@ -80,8 +83,8 @@ __device__ __forceinline__ void rowstats_row(const SampleParams& P, const int b,
   double s;
   block_online<kRowBlock>(o, P.c, m, s);
   if (threadIdx.x == 0) {
-    P.p1_m[static_cast<int64_t>(row) * P.S1max + seg] = m;
-    P.p1_s[static_cast<int64_t>(row) * P.S1max + seg] = s;
+    P.p1_m[seg * p1_rows(P) + row] = m;
+    P.p1_s[seg * p1_rows(P) + row] = s;
     if (seg == 0) P.p1_x[row] = xl;
   }
 }
@@ -158,7 +161,7 @@ __device__ __forceinline__ void decide_wave(const SampleParams& P, const int b, 
       } else {
         float M;
         double Ssum;
-        merge_partials(P.p1_m + r * P.S1max, P.p1_s + r * P.S1max, stage_segments(P, posj), P.c, M, Ssum);
+        merge_partials(P.p1_m + r, P.p1_s + r, p1_rows(P), stage_segments(P, posj), P.c, M, Ssum);
         const float R = M * P.c;
         d.R[h] = R;
         d.S[h] = Ssum;
