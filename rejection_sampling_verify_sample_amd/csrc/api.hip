@@ -101,6 +101,7 @@ SampleLayout sample_layout(int32_t B, int32_t K, int32_t V) {
   L.off_fR = off; off = align256(off + rows * sizeof(float));
   L.off_fS = off; off = align256(off + rows * sizeof(double));
   L.off_fthr = off; off = align256(off + rows * sizeof(uint32_t));
+  L.off_fcnt = off; off = align256(off + rows * sizeof(uint32_t));
   L.off_infoT = off; off = align256(off + static_cast<size_t>(B) * 2 * sizeof(uint32_t));
   L.total = std::max<size_t>(off, 256);
   return L;
@@ -244,6 +245,7 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
     P.f_R = at<float>(workspace, L.off_fR);
     P.f_S = at<double>(workspace, L.off_fS);
     P.f_thr = at<uint32_t>(workspace, L.off_fthr);
+    P.f_cnt = at<uint32_t>(workspace, L.off_fcnt);
     P.info_T = at<uint32_t>(workspace, L.off_infoT);
   }
   const hipError_t e =

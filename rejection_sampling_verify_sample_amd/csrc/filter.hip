@@ -20,6 +20,17 @@
 // row is re-read from cache by the later passes (plain loads, not streaming).
 // Per row the kernel leaves the reference R, the kept mass against it, the key
 // threshold and the kept count; the accept, mass and draw kernels apply them.
+//
+// With top-k on and k <= 64 the row is read once instead (k_filter_fast): every
+// thread publishes its running maximum in LDS, and the k-th largest of those 256
+// maxima (each the maximum of a disjoint part of the row) is a lower bound of the
+// row's k-th largest logit. Entries at or above the bound (every entry top-k
+// keeps, plus a few hundred others) go to an LDS buffer. One wave then finds the
+// k-th largest key by a bitwise search and sorts the kept keys, and the top-p
+// group comes from an exact scan of the same fixed-point masses, so the results
+// are those of the multi-pass select. A row whose candidates overflow the buffer
+// (many entries tied at the top), and every other filtered row, take the
+// multi-pass select (k_filter_rows, which skips the rows finished before it).
 #include "common.hpp"
 #include "params.hpp"
 
@@ -29,6 +40,9 @@ constexpr int kFiltBlock = 256;
 constexpr int kFiltUnroll = 2;
 constexpr int kHistBins = 2048;
 constexpr int kFixBits = 40;
+constexpr int kFiltCap = 2048;   // candidate buffer of the one-pass top-k path (a power of two)
+constexpr int kFiltFastK = 64;   // the largest k it takes: one running maximum per lane
+constexpr int kFastUnroll = 4;   // 16-byte vectors per thread per step of the one-pass read
 
 // round(m * 2^40) for 0 <= m <= 1, from the bits of m (integer arithmetic only).
 __device__ __forceinline__ uint64_t to_fixed(float m) {
@@ -87,6 +101,18 @@ struct FiltShared {
   uint64_t pick_above_cnt, pick_above_mass, pick_cnt, pick_mass;
   float M;
   double S;
+};
+
+// The one-pass top-k path's shared memory.
+struct FastBuf {
+  uint32_t key[kFiltCap];   // candidates: logits while collecting, then their order keys, sorted
+  uint32_t kept[64];        // the wave-level cut's kept keys
+  uint32_t res_thr, res_n;  // its results
+  unsigned long long res_m;
+  uint32_t nbuf;
+  uint32_t lmax[kFiltBlock];  // every thread's running maximum (float bits), published for the bound
+  float wmax[kFiltBlock / 64];
+  int32_t wmin[kFiltBlock / 64];
 };
 
 __device__ __forceinline__ void clear_hist(FiltShared& sh) {
@@ -191,13 +217,13 @@ __device__ void scan_hist(FiltShared& sh, int nb, uint64_t r, double P, uint64_t
 // One refinement pass: histogram of the digit (key >> dshift) & (nb - 1) over the
 // entries with key in [max(lo, rlo), rhi]; entries with key > rhi (and >= lo) are
 // counted, with their mass, in ab_cnt / ab_mass.
-template <typename T>
-__device__ void refine_pass(FiltShared& sh, const T* row, int64_t V, float c, float Rf, uint32_t lo, uint32_t rlo,
+template <typename Visit>
+__device__ void refine_pass(FiltShared& sh, Visit&& visit, float c, float Rf, uint32_t lo, uint32_t rlo,
                             uint32_t rhi, int dshift, int nb, uint64_t& ab_cnt, uint64_t& ab_mass) {
   clear_hist(sh);
   const uint32_t rl = rlo > lo ? rlo : lo;
   uint64_t acnt = 0, amass = 0;
-  visit_row(row, V, [&](float x) {
+  visit([&](float x) {
     const uint32_t k = order_key(x);
     if (k < lo) return;
     if (k > rhi) {
@@ -214,40 +240,534 @@ __device__ void refine_pass(FiltShared& sh, const T* row, int64_t V, float c, fl
   ab_mass = block_sum_u64(amass);
 }
 
+// ---------------------------------------------------------------- one-pass top-k candidates
+
+// Lower bound of the k-th largest key of a row from 256 of its entries (k <= 64),
+// four per lane: the largest key t, searched over its top 16 bits, with at least k
+// of them at or above it, so at least k entries of the row are >= t.
+__device__ __forceinline__ uint32_t kth_bound(const float (&v)[kFiltBlock / 64], int k) {
+  uint32_t key[kFiltBlock / 64];
+#pragma unroll
+  for (int o = 0; o < kFiltBlock / 64; ++o) key[o] = order_key(v[o]);
+  uint32_t t = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 16; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int o = 0; o < kFiltBlock / 64; ++o) cnt += __popcll(__ballot(key[o] >= cand));
+    if (cnt >= k) t = cand;
+  }
+  return t;
+}
+
+// The float f with x >= f exactly when order_key(x) >= t (x not NaN); every value
+// when t is at or below the key of -inf.
+__device__ __forceinline__ float key_floor_value(uint32_t t) {
+  constexpr uint32_t kKeyNegInf = 0x007FFFFFu;
+  if (t <= kKeyNegInf) return -INFINITY;
+  return __uint_as_float((t & 0x80000000u) ? (t & 0x7FFFFFFFu) : ~t);
+}
+
+// Inclusive prefix sum of 32-bit counts over the lanes of a wave (DPP moves).
+__device__ __forceinline__ uint32_t wave_scan_add_u32(uint32_t v) {
+  v += dpp::mov<dpp::kShr1, 0xf>(v, 0u);
+  v += dpp::mov<dpp::kShr2, 0xf>(v, 0u);
+  v += dpp::mov<dpp::kShr4, 0xf>(v, 0u);
+  v += dpp::mov<dpp::kShr8, 0xf>(v, 0u);
+  v += dpp::mov<dpp::kBcast15, 0xa>(v, 0u);
+  v += dpp::mov<dpp::kBcast31, 0xc>(v, 0u);
+  return v;
+}
+
+// Reserve room for `cnt` values of every lane of the wave (lane order): one wave
+// scan and one LDS atomic. Returns the lane's first slot. Every lane takes part.
+__device__ __forceinline__ uint32_t reserve_slots(FastBuf& fb, uint32_t cnt) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t incl = wave_scan_add_u32(cnt);
+  uint32_t base = 0;
+  if (lane == 63 && incl) base = atomicAdd(&fb.nbuf, incl);
+  base = __builtin_amdgcn_readlane(base, 63);
+  return base + incl - cnt;
+}
+
+// Append the lane's values whose bit is set in `take` (bit i for x[i]).
+template <int N>
+__device__ __forceinline__ void append_masked(FastBuf& fb, const float (&x)[N], uint32_t take) {
+  uint32_t pos = reserve_slots(fb, static_cast<uint32_t>(__popc(take)));
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if ((take >> i) & 1u) {
+      if (pos < static_cast<uint32_t>(kFiltCap)) fb.key[pos] = __float_as_uint(x[i]);
+      ++pos;
+    }
+}
+
+// Read the row once: its maximum, and into fb.key every entry at or above a running
+// lower bound of the k-th largest key (k <= kFiltFastK), which includes every entry
+// top-k keeps. Returns the number of candidates (more than kFiltCap: overflow).
 template <typename T>
-__device__ void filter_row_task(const SampleParams& P, const int64_t task, FiltShared& sh) {
+__device__ uint32_t collect_candidates(const T* row, int64_t V, int kk, FastBuf& fb, float& rowmax) {
+  constexpr int VEC = Elem<T>::kVec;
+  constexpr int BS = kFiltBlock, U = kFastUnroll, W = kFiltBlock / 64;
+  static_assert(U * VEC <= 32, "one take bit per entry of a step");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) fb.nbuf = 0;
+  __atomic_store_n(&fb.lmax[threadIdx.x], __float_as_uint(-INFINITY), __ATOMIC_RELAXED);
+  __syncthreads();
+  float m = -INFINITY;  // this thread's running maximum
+  uint32_t thr = 0u;
+  float thrf = -INFINITY;
+  const int64_t h = head_elems(row, V);
+  const int64_t nvec = (V - h) / VEC;
+  const u32x4* vb = reinterpret_cast<const u32x4*>(row + h);
+  // steps of U*BS vectors taken by every thread together (the loop bound is uniform:
+  // the wave scans and ballots below need every lane)
+  int64_t base = 0;
+  int it = 0;
+  for (; base + U * BS <= nvec; base += U * BS, ++it) {
+    const int64_t v = base + threadIdx.x;
+    u32x4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw[u] = load_stream(vb + v + u * BS);
+    float im = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float y[VEC];
+      Elem<T>::unpack(raw[u], y);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) im = fmaxf(im, y[e]);
+    }
+    m = fmaxf(m, im);
+    __atomic_store_n(&fb.lmax[threadIdx.x], __float_as_uint(m), __ATOMIC_RELAXED);
+    if ((it & (it + 1)) == 0 || (it & 3) == 3) {  // steps 0, 1, 3, then every 4th
+      // any published maximum is an entry of its thread's part of the row
+      float pub[W];
+#pragma unroll
+      for (int o = 0; o < W; ++o) pub[o] = __uint_as_float(__atomic_load_n(&fb.lmax[lane + 64 * o], __ATOMIC_RELAXED));
+      const uint32_t t = kth_bound(pub, kk);
+      if (t > thr) {
+        thr = t;
+        thrf = key_floor_value(t);
+      }
+    }
+    if (__ballot(im >= thrf)) {  // rare once the bound has risen: unpack again
+      uint32_t take = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float y[VEC];
+        Elem<T>::unpack(raw[u], y);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) take |= (y[e] >= thrf ? 1u : 0u) << (u * VEC + e);
+      }
+      uint32_t pos = reserve_slots(fb, static_cast<uint32_t>(__popc(take)));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float y[VEC];
+        Elem<T>::unpack(raw[u], y);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if ((take >> (u * VEC + e)) & 1u) {
+            if (pos < static_cast<uint32_t>(kFiltCap)) fb.key[pos] = __float_as_uint(y[e]);
+            ++pos;
+          }
+      }
+    }
+  }
+  // the last vectors, one per thread, then the scalar head (lanes 0-7 of wave 0) and
+  // tail (lanes 8-15): every lane of each wave takes part in the appends
+  for (; base < nvec; base += BS) {
+    const int64_t vr = base + threadIdx.x;
+    float x[VEC];
+    const bool in = vr < nvec;
+    if (in) {
+      Elem<T>::unpack(load_stream(vb + vr), x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) x[e] = -INFINITY;
+    }
+    uint32_t take = 0;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      m = fmaxf(m, x[e]);
+      take |= (in && x[e] >= thrf ? 1u : 0u) << e;
+    }
+    append_masked(fb, x, take);
+  }
+  if (w == 0) {
+    const int64_t tail_lo = h + nvec * VEC;
+    const int64_t e = lane < 8 ? lane : tail_lo + (lane - 8);
+    const bool in = lane < 8 ? lane < h : (lane < 16 && e < V);
+    float x[1];
+    x[0] = in ? Elem<T>::get(row, e) : -INFINITY;
+    m = fmaxf(m, x[0]);
+    append_masked(fb, x, in ? 1u : 0u);
+  }
+  const float wm = wave_max(m);
+  if (lane == 0) fb.wmax[w] = wm;
+  __syncthreads();
+  float M = fb.wmax[0];
+#pragma unroll
+  for (int o = 1; o < W; ++o) M = fmaxf(M, fb.wmax[o]);
+  rowmax = M;
+  return fb.nbuf;
+}
+
+// Sort key[0..npad) in descending order (bitonic network; npad a power of two).
+__device__ void sort_keys_desc(uint32_t* key, int npad) {
+  for (int size = 2; size <= npad; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < npad / 2; i += kFiltBlock) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint32_t a = key[lo], b = key[hi];
+        if ((a < b) == up) {
+          key[lo] = b;
+          key[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Smallest value over the block (thread 0's argument order is irrelevant).
+__device__ __forceinline__ int32_t block_min_i32(FastBuf& fb, int32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) fb.wmin[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int32_t r = fb.wmin[0];
+#pragma unroll
+  for (int o = 1; o < kFiltBlock / 64; ++o) r = min(r, fb.wmin[o]);
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------- the cut
+
+// Top-k then top-p thresholds over the entries `visit` presents (every entry of the
+// row, or a candidate buffer holding every entry top-k keeps). With top-k on, the
+// histogram of the top key digit must already be in sh.cnt.
+template <bool kBf16, typename Visit>
+__device__ __forceinline__ void cut_row(FiltShared& sh, Visit&& visit, int kk, float pp, bool k_on, bool p_on, float c, float Rf,
+                        uint32_t& thr, uint64_t& kept_n, uint64_t& kept_m, bool& fixed_mass) {
+  constexpr int L = kBf16 ? 2 : 3;
+  if (k_on) {
+    scan_hist<false>(sh, kHistBins, static_cast<uint64_t>(kk), 0.0, 0);
+    uint32_t prefix = sh.pick_bin;
+    uint64_t r = static_cast<uint64_t>(kk) - sh.pick_above_cnt;
+    __syncthreads();
+    for (int lev = 1; lev < L; ++lev) {
+      const int shift = lev == 1 ? 21 : 10;
+      const int dshift = lev == 1 ? 10 : 0;
+      const int nb = lev == 1 ? kHistBins : 1024;
+      const uint32_t rlo = prefix << shift, rhi = rlo | ((1u << shift) - 1u);
+      uint64_t ab_cnt, ab_mass;
+      refine_pass(sh, visit, c, Rf, 0u, rlo, rhi, dshift, nb, ab_cnt, ab_mass);
+      scan_hist<false>(sh, nb, r, 0.0, 0);
+      r -= sh.pick_above_cnt;
+      prefix = (prefix << (lev == 1 ? 11 : 10)) | sh.pick_bin;
+      if (lev == L - 1) {
+        thr = prefix << (kBf16 ? 10 : 0);
+        kept_n = ab_cnt + sh.pick_above_cnt + sh.pick_cnt;
+        kept_m = ab_mass + sh.pick_above_mass + sh.pick_mass;
+        fixed_mass = true;
+      }
+      __syncthreads();
+    }
+  }
+  if (p_on) {
+    const uint32_t lo = thr;
+    uint64_t ab_cnt = 0, ab_mass = 0;
+    refine_pass(sh, visit, c, Rf, lo, 0u, 0xFFFFFFFFu, 21, kHistBins, ab_cnt, ab_mass);
+    uint64_t zt = 0;
+    for (int i = threadIdx.x; i < kHistBins; i += kFiltBlock) zt += sh.mass[i];
+    const uint64_t Z = block_sum_u64(zt);
+    const double Pm = static_cast<double>(pp) * static_cast<double>(Z);
+    scan_hist<true>(sh, kHistBins, 0, Pm, 0);
+    uint32_t prefix = sh.pick_bin;
+    __syncthreads();
+    for (int lev = 1; lev < L; ++lev) {
+      const int shift = lev == 1 ? 21 : 10;
+      const int dshift = lev == 1 ? 10 : 0;
+      const int nb = lev == 1 ? kHistBins : 1024;
+      const uint32_t rlo = prefix << shift, rhi = rlo | ((1u << shift) - 1u);
+      refine_pass(sh, visit, c, Rf, lo, rlo, rhi, dshift, nb, ab_cnt, ab_mass);
+      scan_hist<true>(sh, nb, 0, Pm, ab_mass);
+      prefix = (prefix << (lev == 1 ? 11 : 10)) | sh.pick_bin;
+      if (lev == L - 1) {
+        thr = prefix << (kBf16 ? 10 : 0);
+        kept_n = ab_cnt + sh.pick_above_cnt + sh.pick_cnt;
+        kept_m = ab_mass + sh.pick_above_mass + sh.pick_mass;
+        fixed_mass = true;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// A logit row of the round: target rows 0..K of every batch row first (memory
+// order), then draft rows 0..K-1. fr indexes the per-row filter results.
+struct FiltRow {
+  int b, tok_slot;  // tok_slot: slot of the row's draft-token logit in p1_x, -1 for the bonus row
+  int64_t fr;
+  const void* row;
+};
+
+__device__ __forceinline__ FiltRow filt_row(const SampleParams& P, int64_t task, size_t esize) {
   const int K = P.K;
-  const int64_t V = P.V;
   const int64_t ntgt = static_cast<int64_t>(P.B) * (K + 1);
-  int b, j, tok_slot = -1;
-  const T* row;
-  if (task < ntgt) {  // target rows first, in memory order
-    b = static_cast<int>(task / (K + 1));
-    j = static_cast<int>(task - static_cast<int64_t>(b) * (K + 1));
-    row = static_cast<const T*>(P.target) + task * V;
-    if (j < K) tok_slot = j;
+  FiltRow r;
+  int j;
+  r.tok_slot = -1;
+  if (task < ntgt) {
+    r.b = static_cast<int>(task / (K + 1));
+    j = static_cast<int>(task - static_cast<int64_t>(r.b) * (K + 1));
+    r.row = static_cast<const char*>(P.target) + task * P.V * static_cast<int64_t>(esize);
+    if (j < K) r.tok_slot = j;
   } else {
     const int64_t t = task - ntgt;
-    b = static_cast<int>(t / K);
-    const int i = static_cast<int>(t - static_cast<int64_t>(b) * K);
+    r.b = static_cast<int>(t / K);
+    const int i = static_cast<int>(t - static_cast<int64_t>(r.b) * K);
     j = K + 1 + i;
-    row = static_cast<const T*>(P.draft) + t * V;
-    tok_slot = K + i;
+    r.row = static_cast<const char*>(P.draft) + t * P.V * static_cast<int64_t>(esize);
+    r.tok_slot = K + i;
   }
-  const int64_t fr = static_cast<int64_t>(b) * (2 * K + 1) + j;
+  r.fr = static_cast<int64_t>(r.b) * (2 * K + 1) + j;
+  return r;
+}
+
+// The draft-token logit of the row (thread 0; NaN if the token is out of range).
+template <typename T>
+__device__ __forceinline__ float filt_token_logit(const SampleParams& P, const FiltRow& r) {
+  float xl = __builtin_nanf("");
+  if (r.tok_slot >= 0 && threadIdx.x == 0) {
+    const int K = P.K;
+    const int x = P.tokens[static_cast<int64_t>(r.b) * K + (r.tok_slot < K ? r.tok_slot : r.tok_slot - K)];
+    if (x >= 0 && x < P.V) xl = Elem<T>::get(static_cast<const T*>(r.row), x);
+  }
+  return xl;
+}
+
+__device__ __forceinline__ void filt_write(const SampleParams& P, const FiltRow& r, float Rf, double fS, uint32_t thr,
+                                           uint64_t kept_n, float xl) {
+  if (threadIdx.x == 0) {
+    P.f_R[r.fr] = Rf;
+    P.f_S[r.fr] = fS;
+    P.f_thr[r.fr] = thr;
+    if (P.out_kept) P.out_kept[r.fr] = static_cast<int32_t>(kept_n);
+    if (r.tok_slot >= 0) P.p1_x[static_cast<int64_t>(r.b) * 2 * P.K + r.tok_slot] = xl;
+  }
+}
+
+// The logit with order key k (k the key of a number).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Descending bitonic sort of one key per lane across the wave (shuffles, no LDS).
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), stride, 64));
+      const bool up = (lane & size) == 0;
+      const bool first = (lane & stride) == 0;
+      v = (first == up) ? max(v, o) : min(v, o);
+    }
+  return v;
+}
+
+// The cut by wave 0 alone when the candidates fit its registers (n <= 512) and
+// top-k keeps at most 64 entries: the k-th largest key by a bitwise search, the
+// kept keys sorted one per lane, and the top-p group from an exact fp64 lane scan
+// of their fixed-point masses (integers below 2^47). False (nothing written) when
+// it does not apply.
+template <typename MassF>
+__device__ bool wave_cut(FastBuf& fb, int n, int kk, float pp, MassF&& mass) {
+  constexpr int R = 8;
+  const int lane = threadIdx.x & 63;
+  uint32_t kr[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) kr[j] = (j * 64 + lane < n) ? fb.key[j * 64 + lane] : 0u;
+  uint32_t tk = 0;
+#pragma unroll 1
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tk | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) cnt += __popcll(__ballot(kr[j] >= cand));
+    if (cnt >= kk) tk = cand;
+  }
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < R; ++j) c += __popcll(__ballot(kr[j] >= tk));
+  if (c > 64) return false;
+  int at = 0;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const uint64_t bal = __ballot(kr[j] >= tk);
+    if (kr[j] >= tk) fb.kept[at + __popcll(bal & ((1ull << lane) - 1))] = kr[j];
+    at += __popcll(bal);
+  }
+  // the wave reads what its own lanes wrote
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint32_t key = wave_sort_desc(lane < c ? fb.kept[lane] : 0u);
+  const double m = lane < c ? static_cast<double>(mass(key)) : 0.0;
+  const double incl = wave_scan_add(m);
+  const double Z = lane_d(incl, 63);
+  uint32_t tp = tk;
+  if (pp < 1.f) {
+    const double Pm = static_cast<double>(pp) * Z;
+    const int j = first_lane(lane < c && incl >= Pm);
+    tp = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), j < 64 ? j : 0));
+  }
+  const bool kept = lane < c && key >= tp;
+  const double km = lane_d(wave_scan_add(kept ? m : 0.0), 63);
+  const uint32_t kn = static_cast<uint32_t>(__popcll(__ballot(kept)));
+  if (lane == 0) {
+    fb.res_thr = tp;
+    fb.res_n = kn;
+    fb.res_m = static_cast<unsigned long long>(km);
+  }
+  return true;
+}
+
+// Top-k with a small k reads the row once.
+__device__ __forceinline__ bool fast_eligible(const SampleParams& P, int b) {
   const int kk = P.top_k ? P.top_k[b] : 0;
-  const float pp = P.top_p ? P.top_p[b] : 1.f;
+  return kk > 0 && kk < P.V && kk <= kFiltFastK;
+}
+
+// The cut of a one-pass row from its candidates (n <= kFiltCap order keys in fb.key;
+// M the row maximum).
+template <typename T>
+__device__ void cut_candidates(const SampleParams& P, const FiltRow& r, FastBuf& fb, int n, float M, int kk,
+                               float pp, float xl) {
+  if (!(M > -INFINITY)) {  // no finite logit: the row keeps nothing
+    filt_write(P, r, 0.f, 0.0, 0xFFFFFFFFu, 0, xl);
+    __syncthreads();
+    return;
+  }
+  // keys padded with 0 (below the key of every number) to a power of two; n >= k,
+  // since at least k entries reach the final bound
+  int npad = 1;
+  while (npad < n) npad <<= 1;
+  for (int i = n + threadIdx.x; i < npad; i += kFiltBlock) fb.key[i] = 0u;
+  __syncthreads();
+  const float c = P.c;
+  const float Rf = M * c + 1.f;  // masses 2^(x*c - Rf) stay <= 1, as in the multi-pass path
+  auto mass = [&](uint32_t key) {
+    return to_fixed(fminf(exp2_hw(fmaf(key_value(key), c, -Rf)), 1.f));
+  };
+  if (n <= 512) {  // the common case: wave 0 alone
+    __shared__ int wave_done;
+    if (threadIdx.x < 64) {
+      const bool done = wave_cut(fb, n, kk, pp, mass);
+      if (threadIdx.x == 0) wave_done = done;
+    }
+    __syncthreads();
+    if (wave_done) {
+      uint32_t thr = fb.res_thr;
+      if (sizeof(T) == 2) thr &= ~0x3FFu;
+      filt_write(P, r, Rf, static_cast<double>(fb.res_m) * 0x1p-40, thr, fb.res_n, xl);
+      __syncthreads();  // shared memory is reused by the next row
+      return;
+    }
+  }
+  // otherwise the whole workgroup sorts the candidates
+  sort_keys_desc(fb.key, npad);
+  // each thread takes a contiguous run of sorted positions
+  const int per = (npad + kFiltBlock - 1) / kFiltBlock;
+  const int i0 = min(static_cast<int>(threadIdx.x) * per, npad), i1 = min(i0 + per, npad);
+  // top-k: the k-th largest key; the row keeps every entry at or above it
+  const uint32_t tk = fb.key[kk - 1];
+  uint64_t ms = 0, cn = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = fb.key[i];
+    if (key >= tk) {
+      ms += mass(key);
+      ++cn;
+    }
+  }
+  uint64_t Z;
+  const uint64_t before = block_excl_u64(ms, Z);
+  uint32_t thr = tk;
+  uint64_t kept_n = block_sum_u64(cn), kept_m = Z;
+  if (pp < 1.f) {
+    // top-p on the top-k law: the first key group (descending) whose running mass
+    // reaches p * Z, and every key above it (p <= 0: the largest key's group)
+    const double Pm = static_cast<double>(pp) * static_cast<double>(Z);
+    int32_t first = INT32_MAX;
+    uint64_t run = before;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t key = fb.key[i];
+      if (key < tk) break;
+      run += mass(key);
+      if (static_cast<double>(run) >= Pm) {
+        first = i;
+        break;
+      }
+    }
+    const uint32_t tp = fb.key[block_min_i32(fb, first)];
+    uint64_t ms2 = 0, cn2 = 0;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t key = fb.key[i];
+      if (key >= tp) {
+        ms2 += mass(key);
+        ++cn2;
+      }
+    }
+    thr = tp;
+    kept_m = block_sum_u64(ms2);
+    kept_n = block_sum_u64(cn2);
+  }
+  // bf16 keys carry 16 bits: the threshold the multi-pass select gives has its low 10 bits clear
+  if (sizeof(T) == 2) thr &= ~0x3FFu;
+  filt_write(P, r, Rf, static_cast<double>(kept_m) * 0x1p-40, thr, kept_n, xl);
+  __syncthreads();  // shared memory is reused by the next row
+}
+
+// One-pass path of a row: the candidates, then the cut. The candidate count goes to
+// f_cnt, so that k_filter_rows skips the rows finished here.
+template <typename T>
+__device__ void filter_row_fast(const SampleParams& P, int64_t task, FastBuf& fb) {
+  const FiltRow r = filt_row(P, task, sizeof(T));
+  if (!fast_eligible(P, r.b)) return;
+  const int kk = P.top_k[r.b];
+  const float pp = P.top_p ? P.top_p[r.b] : 1.f;
+  const float xl = filt_token_logit<T>(P, r);
+  float M;
+  const uint32_t n = collect_candidates(static_cast<const T*>(r.row), P.V, kk, fb, M);
+  if (threadIdx.x == 0) P.f_cnt[r.fr] = n;
+  if (n > static_cast<uint32_t>(kFiltCap)) {
+    __syncthreads();  // the buffer is reused by the next row
+    return;
+  }
+  for (int i = threadIdx.x; i < static_cast<int>(n); i += kFiltBlock) fb.key[i] = order_key(__uint_as_float(fb.key[i]));
+  cut_candidates<T>(P, r, fb, static_cast<int>(n), M, kk, pp, xl);
+}
+
+// The multi-pass select of a row the one-pass path does not finish (no small top-k,
+// or a half whose candidates overflowed).
+template <typename T>
+__device__ void filter_row_task(const SampleParams& P, int64_t task, FiltShared& sh) {
+  const FiltRow r = filt_row(P, task, sizeof(T));
+  if (fast_eligible(P, r.b) && P.f_cnt[r.fr] <= static_cast<uint32_t>(kFiltCap)) return;
+  const int64_t V = P.V;
+  const T* row = static_cast<const T*>(r.row);
+  const int kk = P.top_k ? P.top_k[r.b] : 0;
+  const float pp = P.top_p ? P.top_p[r.b] : 1.f;
   const bool k_on = kk > 0 && kk < V;
   const bool p_on = pp < 1.f;  // false for NaN
-  constexpr bool kBf16 = sizeof(T) == 2;
-  constexpr int L = kBf16 ? 2 : 3;
   const float c = P.c;
-
-  float xl = __builtin_nanf("");
-  if (tok_slot >= 0 && threadIdx.x == 0) {
-    const int x = P.tokens[static_cast<int64_t>(b) * K + (tok_slot < K ? tok_slot : tok_slot - K)];
-    if (x >= 0 && x < V) xl = Elem<T>::get(row, x);
-  }
+  const float xl = filt_token_logit<T>(P, r);
 
   // pass 1: online maximum and sum; with top-k also the histogram of the top digit
   if (k_on) clear_hist(sh);
@@ -271,13 +791,7 @@ __device__ void filter_row_task(const SampleParams& P, const int64_t task, FiltS
   const float M = sh.M;
   const double S = sh.S;
   if (!(M > -INFINITY)) {  // no finite logit: the row keeps nothing
-    if (threadIdx.x == 0) {
-      P.f_R[fr] = 0.f;
-      P.f_S[fr] = 0.0;
-      P.f_thr[fr] = 0xFFFFFFFFu;
-      if (P.out_kept) P.out_kept[fr] = 0;
-      if (tok_slot >= 0) P.p1_x[static_cast<int64_t>(b) * 2 * K + tok_slot] = xl;
-    }
+    filt_write(P, r, 0.f, 0.0, 0xFFFFFFFFu, 0, xl);
     __syncthreads();
     return;
   }
@@ -287,69 +801,20 @@ __device__ void filter_row_task(const SampleParams& P, const int64_t task, FiltS
   uint32_t thr = 0;
   uint64_t kept_n = static_cast<uint64_t>(V), kept_m = 0;
   bool fixed_mass = false;
-
-  if (k_on) {
-    scan_hist<false>(sh, kHistBins, static_cast<uint64_t>(kk), 0.0, 0);
-    uint32_t prefix = sh.pick_bin;
-    uint64_t r = static_cast<uint64_t>(kk) - sh.pick_above_cnt;
-    __syncthreads();
-    for (int lev = 1; lev < L; ++lev) {
-      const int shift = lev == 1 ? 21 : 10;
-      const int dshift = lev == 1 ? 10 : 0;
-      const int nb = lev == 1 ? kHistBins : 1024;
-      const uint32_t rlo = prefix << shift, rhi = rlo | ((1u << shift) - 1u);
-      uint64_t ab_cnt, ab_mass;
-      refine_pass(sh, row, V, c, Rf, 0u, rlo, rhi, dshift, nb, ab_cnt, ab_mass);
-      scan_hist<false>(sh, nb, r, 0.0, 0);
-      r -= sh.pick_above_cnt;
-      prefix = (prefix << (lev == 1 ? 11 : 10)) | sh.pick_bin;
-      if (lev == L - 1) {
-        thr = prefix << (kBf16 ? 10 : 0);
-        kept_n = ab_cnt + sh.pick_above_cnt + sh.pick_cnt;
-        kept_m = ab_mass + sh.pick_above_mass + sh.pick_mass;
-        fixed_mass = true;
-      }
-      __syncthreads();
-    }
-  }
-  if (p_on) {
-    const uint32_t lo = thr;
-    uint64_t ab_cnt = 0, ab_mass = 0;
-    refine_pass(sh, row, V, c, Rf, lo, 0u, 0xFFFFFFFFu, 21, kHistBins, ab_cnt, ab_mass);
-    uint64_t zt = 0;
-    for (int i = threadIdx.x; i < kHistBins; i += kFiltBlock) zt += sh.mass[i];
-    const uint64_t Z = block_sum_u64(zt);
-    const double Pm = static_cast<double>(pp) * static_cast<double>(Z);
-    scan_hist<true>(sh, kHistBins, 0, Pm, 0);
-    uint32_t prefix = sh.pick_bin;
-    __syncthreads();
-    for (int lev = 1; lev < L; ++lev) {
-      const int shift = lev == 1 ? 21 : 10;
-      const int dshift = lev == 1 ? 10 : 0;
-      const int nb = lev == 1 ? kHistBins : 1024;
-      const uint32_t rlo = prefix << shift, rhi = rlo | ((1u << shift) - 1u);
-      refine_pass(sh, row, V, c, Rf, lo, rlo, rhi, dshift, nb, ab_cnt, ab_mass);
-      scan_hist<true>(sh, nb, 0, Pm, ab_mass);
-      prefix = (prefix << (lev == 1 ? 11 : 10)) | sh.pick_bin;
-      if (lev == L - 1) {
-        thr = prefix << (kBf16 ? 10 : 0);
-        kept_n = ab_cnt + sh.pick_above_cnt + sh.pick_cnt;
-        kept_m = ab_mass + sh.pick_above_mass + sh.pick_mass;
-        fixed_mass = true;
-      }
-      __syncthreads();
-    }
-  }
-  if (threadIdx.x == 0) {
-    P.f_R[fr] = Rf;
-    // without a filter the online sum serves, moved from reference R to Rf
-    P.f_S[fr] = fixed_mass ? static_cast<double>(kept_m) * 0x1p-40
-                           : S * exp2(static_cast<double>(R) - static_cast<double>(Rf));
-    P.f_thr[fr] = thr;
-    if (P.out_kept) P.out_kept[fr] = static_cast<int32_t>(kept_n);
-    if (tok_slot >= 0) P.p1_x[static_cast<int64_t>(b) * 2 * K + tok_slot] = xl;
-  }
+  auto visit_all = [&](auto&& f) { visit_row(row, V, f); };
+  cut_row<sizeof(T) == 2>(sh, visit_all, kk, pp, k_on, p_on, c, Rf, thr, kept_n, kept_m, fixed_mass);
+  // without a filter the online sum serves, moved from reference R to Rf
+  filt_write(P, r, Rf,
+             fixed_mass ? static_cast<double>(kept_m) * 0x1p-40 : S * exp2(static_cast<double>(R) - static_cast<double>(Rf)),
+             thr, kept_n, xl);
   __syncthreads();
+}
+
+template <typename T>
+__global__ __launch_bounds__(kFiltBlock, 5) void k_filter_fast(SampleParams P) {
+  __shared__ FastBuf fb;
+  const int64_t ntask = static_cast<int64_t>(P.B) * (2 * P.K + 1);
+  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) filter_row_fast<T>(P, task, fb);
 }
 
 template <typename T>
@@ -359,13 +824,17 @@ __global__ __launch_bounds__(kFiltBlock) void k_filter_rows(SampleParams P) {
   for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) filter_row_task<T>(P, task, sh);
 }
 
+static dim3 filt_grid(int64_t tasks) { return dim3(static_cast<uint32_t>(tasks < (1 << 20) ? tasks : (1 << 20))); }
+
 hipError_t launch_filter_rows(const SampleParams& P, bool bf16, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(P.B) * (2 * P.K + 1);
-  const dim3 grid(static_cast<uint32_t>(rows < (1 << 20) ? rows : (1 << 20)));
-  if (bf16)
-    hipLaunchKernelGGL(k_filter_rows<bf16_t>, grid, dim3(kFiltBlock), 0, stream, P);
-  else
-    hipLaunchKernelGGL(k_filter_rows<float>, grid, dim3(kFiltBlock), 0, stream, P);
+  if (bf16) {
+    hipLaunchKernelGGL(k_filter_fast<bf16_t>, filt_grid(rows), dim3(kFiltBlock), 0, stream, P);
+    hipLaunchKernelGGL(k_filter_rows<bf16_t>, filt_grid(rows), dim3(kFiltBlock), 0, stream, P);
+  } else {
+    hipLaunchKernelGGL(k_filter_fast<float>, filt_grid(rows), dim3(kFiltBlock), 0, stream, P);
+    hipLaunchKernelGGL(k_filter_rows<float>, filt_grid(rows), dim3(kFiltBlock), 0, stream, P);
+  }
   return hipGetLastError();
 }
 

@@ -183,3 +183,42 @@ def test_filtered_is_deterministic():
     b = run_gpu(t, k, p)
     for x, y in zip(a, b):
         assert np.array_equal(x, y, equal_nan=True) if x.dtype.kind == "f" else np.array_equal(x, y)
+
+
+def _bf16_tensors(tgt, drf, toks, uni, T=1.0):
+    tb = torch.from_numpy(np.ascontiguousarray(tgt, dtype=np.float32)).to(torch.bfloat16)
+    db = torch.from_numpy(np.ascontiguousarray(drf, dtype=np.float32)).to(torch.bfloat16)
+    t = dict(target=tb.to(DEV), draft=db.to(DEV),
+             draft_tokens=torch.from_numpy(np.asarray(toks, dtype=np.int32)).to(DEV),
+             uniforms=torch.from_numpy(np.asarray(uni, dtype=np.float32)).to(DEV), temperature=T)
+    return t, tb.float().numpy(), db.float().numpy()
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 20011), ("bf16", 20011), ("f32", 3001), ("bf16", 3001)])
+def test_one_pass_top_k_and_its_fallbacks(dtype, V):
+    """Top-k with k <= 64 reads a row once into a candidate buffer; a row whose
+    candidates overflow the buffer (ties at the top, ascending rows, -inf ties
+    that top-k keeps) goes to the multi-pass select. At V = 3001 every row fits
+    the buffer. Kept counts exact, the round against the oracle."""
+    log(f"one-pass top-k {dtype} V={V}")
+    rng = np.random.default_rng(11)
+    B, K = 8, 1
+    tgt = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+    tgt[1, :, : V // 3] = 9.0                        # a third of the row tied at the maximum; k = 5 keeps them all
+    tgt[2] = np.linspace(-10, 10, V, dtype=np.float32)[None]  # ascending: every entry beats the running bound
+    tgt[3, :, 5:] = -np.inf                          # five finite entries; k = 10 keeps the -inf ties too
+    tgt[4] = np.round(tgt[4] * 2) / 2                # coarse ties
+    drf = (tgt[:, :K] + rng.normal(0, 0.5, (B, K, V))).astype(np.float32)
+    toks = rng.integers(0, 5, (B, K))
+    uni = rng.random((B, K + 1, 2)).astype(np.float32)
+    ks = np.array([64, 5, 50, 10, 20, 65, 1, 64], dtype=np.int32)
+    ps = np.array([1.0, 0.9, 1.0, 0.9, 0.8, 0.9, 1.0, 0.5], dtype=np.float32)
+    if dtype == "f32":
+        t, tg, dr = _f32_tensors(tgt, drf, toks, uni), tgt, drf
+    else:
+        t, tg, dr = _bf16_tensors(tgt, drf, toks, uni)
+    tok, n, probs, kept = run_gpu(t, ks, ps)
+    res = oracle.oracle_sample_filtered(tg, dr, toks, uni, 1.0, ks, ps)
+    top_k_only = ps >= 1.0
+    assert np.array_equal(kept[top_k_only], res.kept[top_k_only]), (kept, res.kept)
+    compare_filtered(tg, dr, toks, uni, 1.0, ks, ps, res, tok, n, probs, kept)
