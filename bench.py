@@ -347,6 +347,17 @@ def main() -> int:
     log(f"step {t_step * 1e6:.2f} us ({rounds_per_s:.0f} rounds/s, {step_gbps:.0f} GB/s); "
         f"pass 1 {t_pass1 * 1e6:.2f} us ({pass1_gbps:.0f} GB/s); mean accepted {n_acc.mean():.3f}")
     del steps
+    # the same round on one input copy every step ("hot": part of it may stay in the
+    # 256 MB Infinity Cache); labelled apart from the rotated measurement above
+    hsteps = GraphSteps(torch, lambda i, ph: call(sets[0], ph), 1, args.eager)
+    hn = max(CHUNK_STEPS, min(args.steps, 500))
+    hsteps.prepare(rsv.PHASE_ALL, [hn])
+    hsteps.timed(rsv.PHASE_ALL, hn)
+    t_hot = hsteps.timed(rsv.PHASE_ALL, hn) / hn
+    hot = {"workload": WORKLOAD_NAMES[3] + "; one input copy reused every step", "steps": hn,
+           "us_per_round": round(t_hot * 1e6, 3), "rounds_per_s": round(1.0 / t_hot, 1)}
+    log(f"hot (one copy): {t_hot * 1e6:.2f} us per round")
+    del hsteps
 
     # ---------------------------------------------------------------- the same round with early exit (pass 1 in stages)
     staged = None
@@ -602,6 +613,7 @@ def main() -> int:
                      "traffic": traffic, "algorithmic_bytes": pass1_bytes,
                      "us_per_launch": round(t_pass1 * 1e6, 3)},
         "cpu_baseline": cpu,
+        "hot_single_copy": hot,
         "staged": staged,
         "ngram_pool": pool_leg,
         "greedy": greedy,
