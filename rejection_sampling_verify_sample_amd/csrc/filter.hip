@@ -715,7 +715,9 @@ __device__ void cut_candidates(const SampleParams& P, const FiltRow& r, FastBuf&
         break;
       }
     }
-    const uint32_t tp = fb.key[block_min_i32(fb, first)];
+    // a crossing always exists (the last kept entry brings the run to Z >= p * Z); the
+    // clamp only guards the index
+    const uint32_t tp = fb.key[min(block_min_i32(fb, first), npad - 1)];
     uint64_t ms2 = 0, cn2 = 0;
     for (int i = i0; i < i1; ++i) {
       const uint32_t key = fb.key[i];
