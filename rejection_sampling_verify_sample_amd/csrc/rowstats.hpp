@@ -11,10 +11,10 @@ namespace sv {
 
 // Launch geometry, chosen by measured sweeps on gfx950 (the macros exist for such sweeps).
 #ifndef SV_ROW_BLOCK
-#define SV_ROW_BLOCK 128
+#define SV_ROW_BLOCK 256
 #endif
 #ifndef SV_ROW_UNROLL
-#define SV_ROW_UNROLL 4
+#define SV_ROW_UNROLL 3
 #endif
 constexpr int kRowBlock = SV_ROW_BLOCK;  // threads per row-statistics workgroup
 constexpr int kUnroll = SV_ROW_UNROLL;   // 16-byte vectors in flight per thread per step
@@ -28,14 +28,60 @@ __device__ __forceinline__ void online_scalar(const T* row, int64_t lo, int64_t 
   }
 }
 
+// The online (max, sum) of a segment's whole vectors: the software-pipelined loop
+// reads through a raw buffer resource over the segment (bytes < 2^31), so the next
+// step's loads are issued before this step is reduced and need no per-lane guard
+// (past the segment they read nothing); only the segment's last step masks.
 template <int BS, typename T>
-__device__ __forceinline__ void online_segment(const T* row, int64_t V, int seg, int S, float c, Online& o) {
+__device__ __forceinline__ void online_vectors_pipelined(const T* vb, int nv, float c, Online& o) {
   constexpr int VEC = Elem<T>::kVec;
-  const SegRange r = seg_range(row, V, seg, S);
-  if (seg == 0) online_scalar<BS>(row, 0, r.head, c, o);
-  const T* vb = row + r.head;
-  int64_t v = r.v0 + threadIdx.x;
-  for (; v + (kUnroll - 1) * BS < r.v1; v += kUnroll * BS) {
+  constexpr int U = kUnroll;
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(vb, static_cast<int64_t>(nv) * 16);
+  const int t = threadIdx.x;
+  u32x4 cur[U], nxt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) cur[u] = load_stream_buf(rs, t + u * BS);
+  for (int base = 0; base < nv; base += U * BS) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) nxt[u] = load_stream_buf(rs, base + U * BS + t + u * BS);
+    float x[U][VEC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) Elem<T>::unpack(cur[u], x[u]);
+    if (base + U * BS > nv) {  // the segment's last step
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool in = base + t + u * BS < nv;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (!in) x[u][e] = -INFINITY;
+      }
+    }
+    float mt = x[0][0];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) mt = fmaxf(mt, x[u][e]);
+    if (mt > o.m) o.raise(mt, c);
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float a = exp2_hw(fmaf(x[u][0], c, -o.R));
+#pragma unroll
+      for (int e = 1; e < VEC; ++e) a += exp2_hw(fmaf(x[u][e], c, -o.R));
+      acc += a;
+    }
+    o.s += acc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+  }
+}
+
+// The same over vectors [v0, v1) of a segment too large for a buffer resource.
+template <int BS, typename T>
+__device__ __forceinline__ void online_vectors_plain(const T* vb, int64_t v0, int64_t v1, float c, Online& o) {
+  constexpr int VEC = Elem<T>::kVec;
+  int64_t v = v0 + threadIdx.x;
+  for (; v + (kUnroll - 1) * BS < v1; v += kUnroll * BS) {
     float x[kUnroll][VEC];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) Elem<T>::vec(vb + (v + u * BS) * VEC, x[u]);
@@ -55,7 +101,7 @@ __device__ __forceinline__ void online_segment(const T* row, int64_t V, int seg,
     }
     o.s += t;
   }
-  for (; v < r.v1; v += BS) {
+  for (; v < v1; v += BS) {
     float x[VEC];
     Elem<T>::vec(vb + v * VEC, x);
     float mt = x[0];
@@ -67,6 +113,19 @@ __device__ __forceinline__ void online_segment(const T* row, int64_t V, int seg,
     for (int e = 0; e < VEC; ++e) a += exp2_hw(fmaf(x[e], c, -o.R));
     o.s += a;
   }
+}
+
+template <int BS, typename T>
+__device__ __forceinline__ void online_segment(const T* row, int64_t V, int seg, int S, float c, Online& o) {
+  constexpr int VEC = Elem<T>::kVec;
+  const SegRange r = seg_range(row, V, seg, S);
+  if (seg == 0) online_scalar<BS>(row, 0, r.head, c, o);
+  const T* vb = row + r.head;
+  // the pipelined loop's byte offsets reach two steps past the segment's end
+  if ((r.v1 - r.v0) * 16 < (int64_t(1) << 31) - 32 * kUnroll * BS)
+    online_vectors_pipelined<BS>(vb + r.v0 * VEC, static_cast<int>(r.v1 - r.v0), c, o);
+  else
+    online_vectors_plain<BS>(vb, r.v0, r.v1, c, o);
   if (seg == S - 1) online_scalar<BS>(row, r.head + ((V - r.head) / VEC) * VEC, V, c, o);
 }
 
