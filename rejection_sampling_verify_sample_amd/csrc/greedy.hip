@@ -52,7 +52,45 @@ __device__ __forceinline__ void argmax_merge(float& v, int64_t& i, float v2, int
   }
 }
 
-constexpr int kArgBlock = 128;  // threads per argmax workgroup (measured best on gfx950)
+// Launch shape, chosen by measured sweeps on gfx950 (the macros exist for such sweeps).
+#ifndef SV_ARG_BLOCK
+#define SV_ARG_BLOCK 256
+#endif
+#ifndef SV_ARG_UNROLL
+#define SV_ARG_UNROLL 3
+#endif
+constexpr int kArgBlock = SV_ARG_BLOCK;    // threads per argmax workgroup
+constexpr int kArgUnroll = SV_ARG_UNROLL;  // 16-byte vectors per thread per step
+
+// The segment's whole vectors [0, nv) from vb, software-pipelined through a raw
+// buffer resource (bytes < 2^31): the next step's loads are issued before this step
+// is reduced, and loads past the segment read nothing. base_e is the row index of
+// vb's first element. Every thread visits its elements in increasing index order.
+template <int BS, typename T>
+__device__ __forceinline__ void argmax_vectors_pipelined(const T* vb, int nv, int64_t base_e, ArgMax& a) {
+  constexpr int VEC = Elem<T>::kVec;
+  constexpr int U = kArgUnroll;
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(vb, static_cast<int64_t>(nv) * 16);
+  const int t = threadIdx.x;
+  u32x4 cur[U], nxt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) cur[u] = load_stream_buf(rs, t + u * BS);
+  for (int base = 0; base < nv; base += U * BS) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) nxt[u] = load_stream_buf(rs, base + U * BS + t + u * BS);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = base + t + u * BS;
+      if (v < nv) {
+        float x[VEC];
+        Elem<T>::unpack(cur[u], x);
+        a.take_vec(x, base_e + static_cast<int64_t>(v) * VEC);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+  }
+}
 
 template <int BS, typename T, bool NT = true>
 __device__ __forceinline__ void argmax_segment(const T* row, int64_t V, int seg, int S, ArgMax& a) {
@@ -61,6 +99,14 @@ __device__ __forceinline__ void argmax_segment(const T* row, int64_t V, int seg,
   if (seg == 0)
     for (int64_t e = threadIdx.x; e < r.head; e += BS) a.take(Elem<T>::get(row, e), e);
   const T* vb = row + r.head;
+  // the pipelined loop's byte offsets reach two steps past the segment's end
+  if (NT && (r.v1 - r.v0) * 16 < (int64_t(1) << 31) - 32 * kArgUnroll * BS) {
+    argmax_vectors_pipelined<BS>(vb + r.v0 * VEC, static_cast<int>(r.v1 - r.v0), r.head + r.v0 * VEC, a);
+    if (seg == S - 1)
+      for (int64_t e = r.head + ((V - r.head) / VEC) * VEC + threadIdx.x; e < V; e += BS)
+        a.take(Elem<T>::get(row, e), e);
+    return;
+  }
   int64_t v = r.v0 + threadIdx.x;
   for (; v + BS < r.v1; v += 2 * BS) {
     float x0[VEC], x1[VEC];
