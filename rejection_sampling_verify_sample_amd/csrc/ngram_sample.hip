@@ -18,11 +18,12 @@
 //                   of a row (g, i < N-1) also gathers the logits of every
 //                   candidate's token at position i, so the walk needs no further
 //                   look at a row.
-//   k_ngs_verify    one workgroup per sequence. Wave 0 walks the positions and
-//                   tries (a few dozen scalar steps from the gathered logits); the
-//                   draw then takes the block masses from pass 1, reloads only the
-//                   blocks holding a rejected token, picks the block and reloads it
-//                   to find the token.
+//   k_ngs_verify    one workgroup per sequence. One round of loads stages the
+//                   sequence's row statistics, candidates, uniforms and gathered
+//                   logits in LDS; wave 0 walks the positions and tries (a few dozen
+//                   scalar steps); the draw then takes the block masses from pass 1,
+//                   reloads only the blocks holding a rejected token, picks the block
+//                   and reloads it to find the token.
 #include "../../include/spec_verify.h"
 #include "common.hpp"
 #include "params.hpp"
@@ -83,11 +84,12 @@ __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, int64_t k,
 
 // One workgroup per (row, segment); a segment is a run of whole blocks (segment 0
 // also takes the head, the last segment the tail). Each wave takes every
-// kNgsRowWaves-th block: one round of kBlkChunks loads, the block's maximum (a
-// wave reduction) raises the wave's running reference R = fl(m*c) when larger, and
-// the block's sum of 2^(x*c - R) is stored with that R, so any later reference R'
-// recovers the block's mass as sum * 2^(R - R'). The waves' running (m, sum) then
-// merge into the segment's partial, as the online softmax does.
+// kNgsRowWaves-th block, issuing the next block's kBlkChunks loads before it reduces
+// the current one. A ballot spots a new maximum, whose wave reduction then raises
+// the wave's running reference R = fl(m*c); the block's sum of 2^(x*c - R) is stored
+// with that R, so any later reference R' recovers the block's mass as
+// sum * 2^(R - R'). The waves' running (m, sum) then merge into the segment's
+// partial, as the online softmax does.
 #ifndef SV_NGS_ROW_WAVES
 #define SV_NGS_ROW_WAVES 4
 #endif
