@@ -80,7 +80,7 @@ SampleLayout sample_layout(int32_t B, int32_t K, int32_t V) {
   L.S1max = seg_max(rows1, V);
   L.S2max = seg_max(B, V, 256);
   L.S1 = seg_choice(rows1, V, 1024, 8192, L.S1max, "SPECVERIFY_S1");
-  L.S2 = seg_choice(B, V, 1024, 1024, L.S2max, "SPECVERIFY_S2");
+  L.S2 = seg_choice(B, V, sv::kMassThreads / sv::kMassBlock, 1024, L.S2max, "SPECVERIFY_S2");
   size_t off = 0;
   const size_t p1 = static_cast<size_t>(rows1) * L.S1max;
   L.off_p1m = off; off = align256(off + p1 * sizeof(float));

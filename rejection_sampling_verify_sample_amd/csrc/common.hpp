@@ -229,6 +229,34 @@ __device__ __forceinline__ int last_lane(bool pred) {
   return m ? 63 - __clzll(static_cast<long long>(m)) : -1;
 }
 
+// A kernel's parameter block is read with scalar loads where each field is
+// first used, often several dependent rounds apart, and a cold line costs its
+// round a scalar-cache miss. One round at kernel entry that touches every
+// 64-byte line of the block (dwords 48 bytes apart, and the grid size just past
+// it) makes the later rounds hits.
+template <typename Params>
+__device__ __forceinline__ void touch_kernargs(const Params& P) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&P);
+#pragma unroll
+  for (size_t i = 0; i < sizeof(Params) / 4; i += 12) asm volatile("" ::"s"(w[i]));
+  asm volatile("" ::"s"(w[sizeof(Params) / 4 - 1]), "s"(gridDim.x));
+}
+
+// Quotient and remainder of a workgroup-uniform task index by d > 0. A 64-bit
+// division is a scalar sequence of about a hundred instructions, each on the
+// short kernels' critical path, so indices below 2^31 take the 32-bit one.
+__device__ __forceinline__ void split_task(int64_t task, int d, int64_t& q, int& r) {
+  if (task < (int64_t{1} << 31)) {
+    const uint32_t t = static_cast<uint32_t>(task), ud = static_cast<uint32_t>(d);
+    const uint32_t qq = t / ud;
+    q = qq;
+    r = static_cast<int>(t - qq * ud);
+  } else {
+    q = task / d;
+    r = static_cast<int>(task - q * d);
+  }
+}
+
 // ---------------------------------------------------------------- online softmax state
 //
 // A partial softmax denominator over some elements x, kept against the

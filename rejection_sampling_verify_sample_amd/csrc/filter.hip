@@ -523,14 +523,17 @@ __device__ __forceinline__ FiltRow filt_row(const SampleParams& P, int64_t task,
   int j;
   r.tok_slot = -1;
   if (task < ntgt) {
-    r.b = static_cast<int>(task / (K + 1));
-    j = static_cast<int>(task - static_cast<int64_t>(r.b) * (K + 1));
+    int64_t q;
+    split_task(task, K + 1, q, j);
+    r.b = static_cast<int>(q);
     r.row = static_cast<const char*>(P.target) + task * P.V * static_cast<int64_t>(esize);
     if (j < K) r.tok_slot = j;
   } else {
     const int64_t t = task - ntgt;
-    r.b = static_cast<int>(t / K);
-    const int i = static_cast<int>(t - static_cast<int64_t>(r.b) * K);
+    int64_t q;
+    int i;
+    split_task(t, K, q, i);
+    r.b = static_cast<int>(q);
     j = K + 1 + i;
     r.row = static_cast<const char*>(P.draft) + t * P.V * static_cast<int64_t>(esize);
     r.tok_slot = K + i;
@@ -814,6 +817,7 @@ __device__ void filter_row_task(const SampleParams& P, int64_t task, FiltShared&
 
 template <typename T>
 __global__ __launch_bounds__(kFiltBlock, 5) void k_filter_fast(SampleParams P) {
+  touch_kernargs(P);
   __shared__ FastBuf fb;
   const int64_t ntask = static_cast<int64_t>(P.B) * (2 * P.K + 1);
   for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) filter_row_fast<T>(P, task, fb);
@@ -821,6 +825,7 @@ __global__ __launch_bounds__(kFiltBlock, 5) void k_filter_fast(SampleParams P) {
 
 template <typename T>
 __global__ __launch_bounds__(kFiltBlock) void k_filter_rows(SampleParams P) {
+  touch_kernargs(P);
   __shared__ FiltShared sh;
   const int64_t ntask = static_cast<int64_t>(P.B) * (2 * P.K + 1);
   for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) filter_row_task<T>(P, task, sh);

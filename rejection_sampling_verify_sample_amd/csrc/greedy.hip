@@ -149,8 +149,10 @@ __device__ __forceinline__ void block_argmax(float& v, int64_t& i) {
 template <typename T, int BS, bool NT>
 __device__ __forceinline__ void greedy_argmax_task(const GreedyParams& P, const int64_t task) {
   const int S = P.S3;
-  const int seg = static_cast<int>(task % S);
-  const int row = static_cast<int>(task / S);  // in [0, B*G*N)
+  int64_t rq;
+  int seg;
+  split_task(task, S, rq, seg);
+  const int row = static_cast<int>(rq);  // in [0, B*G*N)
   const T* rp = static_cast<const T*>(P.logits) + static_cast<int64_t>(row) * P.V;
   ArgMax a{-INFINITY, -1};
   argmax_segment<BS, T, NT>(rp, P.V, seg, S, a);
@@ -166,6 +168,7 @@ __device__ __forceinline__ void greedy_argmax_task(const GreedyParams& P, const 
 
 template <typename T, int BS = kArgBlock, bool NT = true>
 __global__ __launch_bounds__(BS) void k_greedy_argmax(GreedyParams P) {
+  touch_kernargs(P);
   const int64_t ntask = static_cast<int64_t>(P.B) * P.G * P.N * P.S3;
   for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
     greedy_argmax_task<T, BS, NT>(P, task);
@@ -235,6 +238,7 @@ __device__ __forceinline__ void greedy_select_task(const GreedyParams& P, const 
 }
 
 __global__ __launch_bounds__(kBlock) void k_greedy_select(GreedyParams P) {
+  touch_kernargs(P);
   const int64_t ntask = P.B;
   for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
     greedy_select_task(P, task);

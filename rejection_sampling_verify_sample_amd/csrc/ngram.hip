@@ -65,6 +65,7 @@ __device__ __forceinline__ bool same_cont(const PoolShared& sh, int N, int w1, i
 }
 
 __global__ __launch_bounds__(kPoolBlock) void k_pool_insert(PoolParams P) {
+  touch_kernargs(P);
   __shared__ PoolShared sh;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -150,6 +151,7 @@ __global__ __launch_bounds__(kPoolBlock) void k_pool_insert(PoolParams P) {
 // ---------------------------------------------------------------- lookup
 
 __global__ __launch_bounds__(64) void k_pool_lookup(PoolParams P) {
+  touch_kernargs(P);
   const int lane = threadIdx.x & 63;
   const int G = P.G, N = P.N;
   for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) {

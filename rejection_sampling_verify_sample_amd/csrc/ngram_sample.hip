@@ -98,6 +98,7 @@ constexpr int kNgsRowBlock = 64 * kNgsRowWaves;
 
 template <typename T>
 __global__ __launch_bounds__(kNgsRowBlock) void k_ngs_rowstats(NgramSampleParams P) {
+  touch_kernargs(P);
   constexpr int VEC = Elem<T>::kVec;
   __shared__ float sh_m[kNgsRowWaves];
   __shared__ double sh_s[kNgsRowWaves];
@@ -107,11 +108,12 @@ __global__ __launch_bounds__(kNgsRowBlock) void k_ngs_rowstats(NgramSampleParams
   const float c = P.c;
   const int64_t rows = static_cast<int64_t>(P.B) * P.G * P.N;
   for (int64_t task = blockIdx.x; task < rows * S; task += gridDim.x) {
-    const int seg = static_cast<int>(task % S);
-    const int64_t row = task / S;
-    const int i = static_cast<int>(row % P.N);
-    const int64_t bg = row / P.N;
-    const int b = static_cast<int>(bg / P.G);
+    int64_t row, bg, bq;
+    int seg, i, g;
+    split_task(task, S, row, seg);
+    split_task(row, P.N, bg, i);
+    split_task(bg, P.G, bq, g);  // b = bg / G
+    const int b = static_cast<int>(bq);
     const T* rp = ngs_row_ptr<T>(P, row);
     const RowBlocks rb = blocks_of(rp, P.V);
     // segment 0 gathers the logits at every candidate's token for this position
@@ -581,6 +583,7 @@ __device__ int64_t ngs_draw(const NgramSampleParams& P, int64_t row, const T* rp
 
 template <typename T>
 __global__ __launch_bounds__(kNgsBlock) void k_ngs_verify(NgramSampleParams P) {
+  touch_kernargs(P);
   __shared__ NgsShared sh;
   const int N = P.N;
   for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) {

@@ -60,6 +60,14 @@ enum SamplePhase : int {
   kPhaseAll = 15
 };
 
+// Threads per pass-2 workgroup. Pass 2 is sized to about 2^18 threads in all
+// (SampleLayout::S2 workgroups per batch row).
+#ifndef SV_MASS_BLOCK
+#define SV_MASS_BLOCK 256
+#endif
+constexpr int kMassBlock = SV_MASS_BLOCK;
+constexpr int kMassThreads = 1 << 18;
+
 struct SampleLayout {
   int32_t S1, S2, S1max, S2max;
   int32_t NCmax;

@@ -151,6 +151,14 @@ __device__ __forceinline__ void merge_partials(const float* pm, const double* ps
                                                float& M, double& Ssum) {
   M = -INFINITY;
   Ssum = 0.0;
+  if (S == 1) {  // one segment: the same values as the general merge below, without its loop
+    const float m0 = pm[0];
+    const double s0 = ps[0];
+    M = fmaxf(M, m0);
+    // m0 == M unless m0 is NaN, whose rescale factor leaves a NaN sum
+    Ssum = (s0 > 0.0) ? ((m0 == M) ? s0 : static_cast<double>(__builtin_nanf(""))) : 0.0;
+    return;
+  }
   if (S <= kMergeRegs) {
     float mv[kMergeRegs];
     double sv[kMergeRegs];

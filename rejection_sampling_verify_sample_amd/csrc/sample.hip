@@ -248,6 +248,7 @@ constexpr int kAcceptBlock = 64;  // one wave per batch row
 
 template <bool FILT>
 __global__ __launch_bounds__(kAcceptBlock) void k_sample_accept(SampleParams P) {
+  touch_kernargs(P);
   for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) {
     WaveDecision d;
     decide_wave<FILT>(P, static_cast<int>(task), true, d, P.K);
@@ -260,12 +261,15 @@ __global__ __launch_bounds__(kAcceptBlock) void k_sample_accept(SampleParams P) 
 // then draft rows, in memory order.
 template <typename T>
 __global__ __launch_bounds__(kRowBlock) void k_sample_rowstats(SampleParams P, int stage) {
+  touch_kernargs(P);
   const int e = P.stage_end[stage];
   const int S = P.stage_S1[stage];
   const int64_t ntask = static_cast<int64_t>(P.B) * 2 * e * S;
   for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
-    const int seg = static_cast<int>(task % S);
-    const int t = static_cast<int>(task / S);
+    int64_t tq;
+    int seg;
+    split_task(task, S, tq, seg);
+    const int t = static_cast<int>(tq);
     const bool is_draft = t >= P.B * e;
     const int tb = is_draft ? t - P.B * e : t;
     const int b = tb / e;
@@ -280,6 +284,7 @@ __global__ __launch_bounds__(kRowBlock) void k_sample_rowstats(SampleParams P, i
 constexpr int kAliveBlock = 1024;
 
 __global__ __launch_bounds__(kAliveBlock) void k_stage_alive(SampleParams P, int a) {
+  touch_kernargs(P);
   const int64_t b = static_cast<int64_t>(blockIdx.x) * (kAliveBlock / 64) + (threadIdx.x >> 6);
   if (b >= P.B) return;  // b is uniform across the wave
   WaveDecision d;
@@ -308,6 +313,7 @@ __device__ __forceinline__ int nth_alive(const SampleParams& P, int64_t li) {
 // the device).
 template <typename T>
 __global__ __launch_bounds__(kRowBlock) void k_sample_rowstats_alive(SampleParams P, int stage) {
+  touch_kernargs(P);
   const int a = P.stage_end[stage - 1];
   const int npos = P.stage_end[stage] - a;
   const int S = P.stage_S1[stage];
@@ -540,7 +546,7 @@ struct MassTask {
   ResOf<FILT> res;   // the draw weights (residual, or the filtered bonus row)
 };
 
-template <typename T, bool FUSE_ACCEPT, bool FILT, int BS = kBlock>
+template <typename T, bool FUSE_ACCEPT, bool FILT, int BS = kMassBlock>
 __device__ __forceinline__ MassTask<FILT> sample_mass_task(const SampleParams& P, const int b, const int seg,
                                                            const int S) {
   const int K = P.K;
@@ -603,10 +609,15 @@ __device__ __forceinline__ MassTask<FILT> sample_mass_task(const SampleParams& P
 }
 
 template <typename T, bool FUSE_ACCEPT, bool FILT>
-__global__ __launch_bounds__(kBlock) void k_sample_mass(SampleParams P) {
+__global__ __launch_bounds__(kMassBlock) void k_sample_mass(SampleParams P) {
+  touch_kernargs(P);
   const int64_t ntask = static_cast<int64_t>(P.B) * P.S2;
-  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x)
-    sample_mass_task<T, FUSE_ACCEPT, FILT>(P, static_cast<int>(task / P.S2), static_cast<int>(task % P.S2), P.S2);
+  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
+    int64_t b;
+    int seg;
+    split_task(task, P.S2, b, seg);
+    sample_mass_task<T, FUSE_ACCEPT, FILT>(P, static_cast<int>(b), seg, P.S2);
+  }
 }
 
 // ---------------------------------------------------------------- pass 2: the draw
@@ -932,6 +943,7 @@ __device__ __forceinline__ void sample_draw_task(const SampleParams& P, const in
 
 template <typename T, bool FILT>
 __global__ __launch_bounds__(kDrawBlock) void k_sample_draw(SampleParams P) {
+  touch_kernargs(P);
   for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) sample_draw_task<T, FILT>(P, static_cast<int>(task));
 }
 
@@ -969,11 +981,11 @@ static hipError_t launch_sample_t(const SampleParams& P, int phases, hipStream_t
   }
   const int64_t gm = static_cast<int64_t>(P.B) * P.S2;
   if ((phases & kPhaseAccept) && (phases & kPhaseMass)) {
-    hipLaunchKernelGGL((k_sample_mass<T, true, FILT>), grid_for(gm), dim3(kBlock), 0, stream, P);
+    hipLaunchKernelGGL((k_sample_mass<T, true, FILT>), grid_for(gm), dim3(kMassBlock), 0, stream, P);
   } else if (phases & kPhaseAccept) {
     hipLaunchKernelGGL(k_sample_accept<FILT>, grid_for(P.B), dim3(kAcceptBlock), 0, stream, P);
   } else if (phases & kPhaseMass) {
-    hipLaunchKernelGGL((k_sample_mass<T, false, FILT>), grid_for(gm), dim3(kBlock), 0, stream, P);
+    hipLaunchKernelGGL((k_sample_mass<T, false, FILT>), grid_for(gm), dim3(kMassBlock), 0, stream, P);
   }
   if (phases & kPhaseDraw)
     hipLaunchKernelGGL((k_sample_draw<T, FILT>), grid_for(P.B), dim3(kDrawBlock), 0, stream, P);
