@@ -44,6 +44,10 @@ template <>
 struct Elem<float> {
   static constexpr int kVec = 4;  // elements per 16-byte load
   __device__ __forceinline__ static float get(const float* p, size_t i) { return p[i]; }
+  // element e in [0, 4) of a raw vector (e may differ across lanes)
+  __device__ __forceinline__ static float lane_elem(const u32x4& v, int e) {
+    return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
+  }
   __device__ __forceinline__ static void unpack(const u32x4& v, float (&x)[4]) {
     x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
     x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
@@ -61,6 +65,12 @@ struct Elem<bf16_t> {
   static constexpr int kVec = 8;
   __device__ __forceinline__ static float get(const bf16_t* p, size_t i) {
     return __uint_as_float(static_cast<uint32_t>(p[i].bits) << 16);
+  }
+  // element e in [0, 8) of a raw vector (e may differ across lanes)
+  __device__ __forceinline__ static float lane_elem(const u32x4& v, int e) {
+    const int j = e >> 1;
+    const uint32_t w = j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
   }
   __device__ __forceinline__ static void unpack(const u32x4& v, float (&x)[8]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};

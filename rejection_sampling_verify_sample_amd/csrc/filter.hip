@@ -42,7 +42,13 @@ constexpr int kHistBins = 2048;
 constexpr int kFixBits = 40;
 constexpr int kFiltCap = 2048;   // candidate buffer of the one-pass top-k path (a power of two)
 constexpr int kFiltFastK = 64;   // the largest k it takes: one running maximum per lane
-constexpr int kFastUnroll = 4;   // 16-byte vectors per thread per step of the one-pass read
+#ifndef SV_FAST_MINB
+#define SV_FAST_MINB 5  // workgroups per CU the one-pass kernel is compiled for (register budget)
+#endif
+#ifndef SV_FAST_UNROLL
+#define SV_FAST_UNROLL 4
+#endif
+constexpr int kFastUnroll = SV_FAST_UNROLL;  // 16-byte vectors per thread per step of the one-pass read
 
 // round(m * 2^40) for 0 <= m <= 1, from the bits of m (integer arithmetic only).
 __device__ __forceinline__ uint64_t to_fixed(float m) {
@@ -307,10 +313,9 @@ __device__ __forceinline__ void append_masked(FastBuf& fb, const float (&x)[N], 
 // lower bound of the k-th largest key (k <= kFiltFastK), which includes every entry
 // top-k keeps. Returns the number of candidates (more than kFiltCap: overflow).
 template <typename T>
-__device__ uint32_t collect_candidates(const T* row, int64_t V, int kk, FastBuf& fb, float& rowmax) {
+__device__ uint32_t collect_candidates(const T* row, int64_t V, int kk, FastBuf& fb, float& rowmax, uint32_t& lbound) {
   constexpr int VEC = Elem<T>::kVec;
   constexpr int BS = kFiltBlock, U = kFastUnroll, W = kFiltBlock / 64;
-  static_assert(U * VEC <= 32, "one take bit per entry of a step");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (threadIdx.x == 0) fb.nbuf = 0;
   __atomic_store_n(&fb.lmax[threadIdx.x], __float_as_uint(-INFINITY), __ATOMIC_RELAXED);
@@ -351,26 +356,30 @@ __device__ uint32_t collect_candidates(const T* row, int64_t V, int kk, FastBuf&
         thrf = key_floor_value(t);
       }
     }
-    if (__ballot(im >= thrf)) {  // rare once the bound has risen: unpack again
-      uint32_t take = 0;
+    if (__ballot(im >= thrf)) {  // rare once the bound has risen
+      // each vector's take bits, then one slot reservation and a loop over the set
+      // bits (few after the first steps; a fully unrolled store of every entry
+      // would hold all of them in registers)
+      uint32_t tk[U];
+      uint32_t cnt = 0;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float y[VEC];
         Elem<T>::unpack(raw[u], y);
+        uint32_t t = 0;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) take |= (y[e] >= thrf ? 1u : 0u) << (u * VEC + e);
+        for (int e = 0; e < VEC; ++e) t |= (y[e] >= thrf ? 1u : 0u) << e;
+        tk[u] = t;
+        cnt += __popc(t);
       }
-      uint32_t pos = reserve_slots(fb, static_cast<uint32_t>(__popc(take)));
+      uint32_t pos = reserve_slots(fb, cnt);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        float y[VEC];
-        Elem<T>::unpack(raw[u], y);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          if ((take >> (u * VEC + e)) & 1u) {
-            if (pos < static_cast<uint32_t>(kFiltCap)) fb.key[pos] = __float_as_uint(y[e]);
-            ++pos;
-          }
+        for (uint32_t t = tk[u]; t != 0u; t &= t - 1u) {
+          if (pos < static_cast<uint32_t>(kFiltCap))
+            fb.key[pos] = __float_as_uint(Elem<T>::lane_elem(raw[u], __ffs(t) - 1));
+          ++pos;
+        }
       }
     }
   }
@@ -410,6 +419,7 @@ __device__ uint32_t collect_candidates(const T* row, int64_t V, int kk, FastBuf&
 #pragma unroll
   for (int o = 1; o < W; ++o) M = fmaxf(M, fb.wmax[o]);
   rowmax = M;
+  lbound = thr;
   return fb.nbuf;
 }
 
@@ -570,18 +580,44 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Descending bitonic sort of one key per lane across the wave (shuffles, no LDS).
-__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v) {
+// The value of lane ^ S. Strides inside a row of 16 lanes take two DPP row shifts
+// (lane + S for lanes with bit S clear, lane - S for the others, both inside the
+// row); 16 and 32 take an LDS-routed shuffle.
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (S <= 8) {
+    const uint32_t up = dpp::mov<0x100 + S, 0xf>(v, v);  // row_shl:S, lane + S
+    const uint32_t dn = dpp::mov<0x110 + S, 0xf>(v, v);  // row_shr:S, lane - S
+    return (threadIdx.x & S) ? dn : up;
+  } else {
+    return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), S, 64));
+  }
+}
+
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint32_t bitonic_step(uint32_t v) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1)
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), stride, 64));
-      const bool up = (lane & size) == 0;
-      const bool first = (lane & stride) == 0;
-      v = (first == up) ? max(v, o) : min(v, o);
-    }
+  const uint32_t o = lane_xor<STRIDE>(v);
+  const bool up = (lane & SIZE) == 0;
+  const bool first = (lane & STRIDE) == 0;
+  return (first == up) ? max(v, o) : min(v, o);
+}
+
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint32_t bitonic_merge(uint32_t v) {
+  v = bitonic_step<SIZE, STRIDE>(v);
+  if constexpr (STRIDE > 1) v = bitonic_merge<SIZE, STRIDE / 2>(v);
+  return v;
+}
+
+// Descending bitonic sort of one key per lane across the wave (every lane active).
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v) {
+  v = bitonic_merge<2, 1>(v);
+  v = bitonic_merge<4, 2>(v);
+  v = bitonic_merge<8, 4>(v);
+  v = bitonic_merge<16, 8>(v);
+  v = bitonic_merge<32, 16>(v);
+  v = bitonic_merge<64, 32>(v);
   return v;
 }
 
@@ -590,22 +626,32 @@ __device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v) {
 // kept keys sorted one per lane, and the top-p group from an exact fp64 lane scan
 // of their fixed-point masses (integers below 2^47). False (nothing written) when
 // it does not apply.
-template <typename MassF>
-__device__ bool wave_cut(FastBuf& fb, int n, int kk, float pp, MassF&& mass) {
+template <bool kBf16, typename MassF>
+__device__ bool wave_cut(FastBuf& fb, int n, int kk, float pp, MassF&& mass, uint32_t lo, uint32_t hi) {
   constexpr int R = 8;
   const int lane = threadIdx.x & 63;
   uint32_t kr[R];
 #pragma unroll
-  for (int j = 0; j < R; ++j) kr[j] = (j * 64 + lane < n) ? fb.key[j * 64 + lane] : 0u;
-  uint32_t tk = 0;
+  for (int j = 0; j < R; ++j) kr[j] = (j * 64 + lane < n) ? order_key(__uint_as_float(fb.key[j * 64 + lane])) : 0u;
+  // The k-th largest key t lies in [lo, hi], so it has their common leading bits:
+  // the bitwise search starts below them. bf16 keys end in 16 zero bits (sign bit
+  // set) or 16 one bits (clear), so their search stops at bit 16.
+  constexpr int kBottom = kBf16 ? 16 : 0;
+  uint32_t tk = lo;
+  int top = -1;
+  if (lo != hi) {
+    top = 31 - __clz(lo ^ hi);
+    tk = (top == 31) ? 0u : (lo & ~((2u << top) - 1u));
+  }
 #pragma unroll 1
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = top; bit >= kBottom; --bit) {
     const uint32_t cand = tk | (1u << bit);
     int cnt = 0;
 #pragma unroll
     for (int j = 0; j < R; ++j) cnt += __popcll(__ballot(kr[j] >= cand));
     if (cnt >= kk) tk = cand;
   }
+  if (kBf16) tk = (tk & 0xFFFF0000u) | ((tk & 0x80000000u) ? 0u : 0xFFFFu);
   int c = 0;
 #pragma unroll
   for (int j = 0; j < R; ++j) c += __popcll(__ballot(kr[j] >= tk));
@@ -652,27 +698,22 @@ __device__ __forceinline__ bool fast_eligible(const SampleParams& P, int b) {
 // M the row maximum).
 template <typename T>
 __device__ void cut_candidates(const SampleParams& P, const FiltRow& r, FastBuf& fb, int n, float M, int kk,
-                               float pp, float xl) {
+                               float pp, float xl, uint32_t lbound) {
   if (!(M > -INFINITY)) {  // no finite logit: the row keeps nothing
     filt_write(P, r, 0.f, 0.0, 0xFFFFFFFFu, 0, xl);
     __syncthreads();
     return;
   }
-  // keys padded with 0 (below the key of every number) to a power of two; n >= k,
-  // since at least k entries reach the final bound
-  int npad = 1;
-  while (npad < n) npad <<= 1;
-  for (int i = n + threadIdx.x; i < npad; i += kFiltBlock) fb.key[i] = 0u;
-  __syncthreads();
   const float c = P.c;
   const float Rf = M * c + 1.f;  // masses 2^(x*c - Rf) stay <= 1, as in the multi-pass path
   auto mass = [&](uint32_t key) {
     return to_fixed(fminf(exp2_hw(fmaf(key_value(key), c, -Rf)), 1.f));
   };
-  if (n <= 512) {  // the common case: wave 0 alone
+  if (n <= 512) {  // the common case: wave 0 alone, on the raw candidates
     __shared__ int wave_done;
     if (threadIdx.x < 64) {
-      const bool done = wave_cut(fb, n, kk, pp, mass);
+      // wave 0's final bound is at most the k-th largest key, the row maximum at least
+      const bool done = wave_cut<sizeof(T) == 2>(fb, n, kk, pp, mass, lbound, order_key(M));
       if (threadIdx.x == 0) wave_done = done;
     }
     __syncthreads();
@@ -684,7 +725,13 @@ __device__ void cut_candidates(const SampleParams& P, const FiltRow& r, FastBuf&
       return;
     }
   }
-  // otherwise the whole workgroup sorts the candidates
+  // otherwise the whole workgroup sorts the candidates, as order keys padded with 0
+  // (below the key of every number) to a power of two; n >= k, since at least k
+  // entries reach the final bound
+  int npad = 1;
+  while (npad < n) npad <<= 1;
+  for (int i = threadIdx.x; i < npad; i += kFiltBlock) fb.key[i] = i < n ? order_key(__uint_as_float(fb.key[i])) : 0u;
+  __syncthreads();
   sort_keys_desc(fb.key, npad);
   // each thread takes a contiguous run of sorted positions
   const int per = (npad + kFiltBlock - 1) / kFiltBlock;
@@ -749,14 +796,14 @@ __device__ void filter_row_fast(const SampleParams& P, int64_t task, FastBuf& fb
   const float pp = P.top_p ? P.top_p[r.b] : 1.f;
   const float xl = filt_token_logit<T>(P, r);
   float M;
-  const uint32_t n = collect_candidates(static_cast<const T*>(r.row), P.V, kk, fb, M);
+  uint32_t lbound;
+  const uint32_t n = collect_candidates(static_cast<const T*>(r.row), P.V, kk, fb, M, lbound);
   if (threadIdx.x == 0) P.f_cnt[r.fr] = n;
   if (n > static_cast<uint32_t>(kFiltCap)) {
     __syncthreads();  // the buffer is reused by the next row
     return;
   }
-  for (int i = threadIdx.x; i < static_cast<int>(n); i += kFiltBlock) fb.key[i] = order_key(__uint_as_float(fb.key[i]));
-  cut_candidates<T>(P, r, fb, static_cast<int>(n), M, kk, pp, xl);
+  cut_candidates<T>(P, r, fb, static_cast<int>(n), M, kk, pp, xl, lbound);
 }
 
 // The multi-pass select of a row the one-pass path does not finish (no small top-k,
@@ -816,7 +863,7 @@ __device__ void filter_row_task(const SampleParams& P, int64_t task, FiltShared&
 }
 
 template <typename T>
-__global__ __launch_bounds__(kFiltBlock, 5) void k_filter_fast(SampleParams P) {
+__global__ __launch_bounds__(kFiltBlock, SV_FAST_MINB) void k_filter_fast(SampleParams P) {
   touch_kernargs(P);
   __shared__ FastBuf fb;
   const int64_t ntask = static_cast<int64_t>(P.B) * (2 * P.K + 1);
