@@ -199,7 +199,8 @@ def test_one_pass_top_k_and_its_fallbacks(dtype, V):
     """Top-k with k <= 64 reads a row once into a candidate buffer; a row whose
     candidates overflow the buffer (ties at the top, ascending rows, -inf ties
     that top-k keeps) goes to the multi-pass select. At V = 3001 every row fits
-    the buffer. Kept counts exact, the round against the oracle."""
+    the buffer. Rows 0 and 7 hold only negative logits. Kept counts exact, the
+    round against the oracle."""
     log(f"one-pass top-k {dtype} V={V}")
     rng = np.random.default_rng(11)
     B, K = 8, 1
@@ -208,6 +209,8 @@ def test_one_pass_top_k_and_its_fallbacks(dtype, V):
     tgt[2] = np.linspace(-10, 10, V, dtype=np.float32)[None]  # ascending: every entry beats the running bound
     tgt[3, :, 5:] = -np.inf                          # five finite entries; k = 10 keeps the -inf ties too
     tgt[4] = np.round(tgt[4] * 2) / 2                # coarse ties
+    tgt[0] = -np.abs(tgt[0]) - 5.0                   # every logit negative: the k-th largest key
+    tgt[7] = -np.abs(tgt[7]) - 0.5                   # has its sign bit clear (bf16: low half all ones)
     drf = (tgt[:, :K] + rng.normal(0, 0.5, (B, K, V))).astype(np.float32)
     toks = rng.integers(0, 5, (B, K))
     uni = rng.random((B, K + 1, 2)).astype(np.float32)
