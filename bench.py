@@ -94,11 +94,28 @@ def counters_run() -> int:
     for _ in range(3):
         rsv.verify_greedy(g["logits"], g["cand"])
     torch.cuda.synchronize()
+    del g
+    from workloads import make_filter_params, make_ngram_sample_inputs
+    t = sample_tensors(s, dev)
+    fk, fp = make_filter_params(s.shape[0], top_k=FILTER_K, top_p=FILTER_P)
+    fk, fp = torch.from_numpy(fk).to(dev), torch.from_numpy(fp).to(dev)
+    for _ in range(3):
+        rsv.verify_sample_filtered(t["target"], t["draft"], t["draft_tokens"], t["uniforms"], t["temperature"], fk, fp)
+    torch.cuda.synchronize()
+    del t
+    ns = make_ngram_sample_inputs(0, peak=10.0)
+    nlg = torch.from_numpy(ns.logits).to(dev).view(torch.bfloat16)
+    ncand, nuni = torch.from_numpy(ns.cand).to(dev), torch.from_numpy(ns.uniforms).to(dev)
+    for _ in range(3):
+        rsv.verify_ngram_sample(nlg, ncand, nuni, ns.temperature)
+    torch.cuda.synchronize()
     print("counters run done", file=sys.stderr)
     return 0
 
 
-TRAFFIC_KERNELS = ["k_sample_rowstats", "k_sample_mass", "k_sample_draw", "k_greedy_argmax", "k_greedy_select"]
+TRAFFIC_KERNELS = ["k_sample_rowstats", "k_sample_mass", "k_sample_draw", "k_greedy_argmax", "k_greedy_select",
+                   "k_filter_fast", "k_filter_rows", "k_sample_mass_filtered", "k_sample_draw_filtered",
+                   "k_ngs_rowstats", "k_ngs_verify"]
 CALIBRATION_KERNEL = "__amd_rocclr_copyBuffer"
 CALIBRATION_KIB = 256 * 1024
 
@@ -115,6 +132,8 @@ def _counter_means(path: str, counter: str) -> dict:
             key = next((k for k in TRAFFIC_KERNELS + [CALIBRATION_KERNEL] if k in name), None)
             if key is None:
                 continue
+            if key in ("k_sample_mass", "k_sample_draw") and name.split(">(")[0].endswith("true"):
+                key += "_filtered"  # the filtered round's variant (last template argument)
             acc.setdefault(key, []).append(float(row["Counter_Value"]))
     if CALIBRATION_KERNEL in acc:
         # the calibration copies come first; later copy dispatches are the small host-to-device input uploads
@@ -137,7 +156,9 @@ def ingest_counters(fetch_csv: str, write_csv: str) -> int:
                  "(copy bytes / counter bytes). source_sha: the kernel sources the counters were taken on "
                  "(bench.py reports null once they change).",
         "fetch_scale": fs, "write_scale": ws,
-        "workloads": {"k_sample_*": "B=64 K=8 V=128256 bf16", "k_greedy_*": "B=32 G=7 N=5 V=32000 bf16"},
+        "workloads": {"k_sample_*": "B=64 K=8 V=128256 bf16", "k_greedy_*": "B=32 G=7 N=5 V=32000 bf16",
+                      "k_filter_*, *_filtered": "B=64 K=8 V=128256 bf16, top-k 50 and top-p 0.9 on every row",
+                      "k_ngs_*": "n-gram sampling verify B=32 G=7 N=5 V=32000 bf16, peaked rows"},
     }
     for k in TRAFFIC_KERNELS:
         if k in fetch and k in write:
