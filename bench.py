@@ -455,7 +455,8 @@ def main() -> int:
                     "filter_passes_per_row": passes,
                     "filter_frac_of_hbm_peak": round(one_read / tf_filter / 1e9 / HBM_PEAK_GBPS, 4),
                     "mean_kept": round(float(kept.float().mean().item()), 2),
-                    "mean_accepted": round(float(fn_acc.mean()), 4)}
+                    "mean_accepted": round(float(fn_acc.mean()), 4),
+                    "filter_traffic": measured_traffic("k_filter_fast")}
         log(f"filtered step {tf_step * 1e6:.2f} us; filter kernel {tf_filter * 1e6:.2f} us "
             f"({one_read / tf_filter / 1e9:.0f} GB/s on one read of {rows} rows)")
         del fsteps
@@ -541,7 +542,7 @@ def main() -> int:
         greedy = {"workload": WORKLOAD_NAMES[5], "rounds_per_s": round(1.0 / per, 1),
                   "us_per_round": round(per * 1e6, 3), "achieved_gbps": round(gal / per / 1e9, 1),
                   "frac_of_hbm_peak": round(gal / per / 1e9 / HBM_PEAK_GBPS, 4), "rotate": M5,
-                  "algorithmic_bytes": gal}
+                  "algorithmic_bytes": gal, "argmax_traffic": measured_traffic("k_greedy_argmax")}
         log(f"greedy {per * 1e6:.2f} us/round ({gal / per / 1e9:.0f} GB/s)")
 
     # ---------------------------------------------------------------- sampling verify of one-hot n-grams, same shape
@@ -586,7 +587,8 @@ def main() -> int:
                            "peaked rows, candidates on the peak w.p. 0.6",
                "rounds_per_s": round(1.0 / tn, 1), "us_per_round": round(tn * 1e6, 3),
                "achieved_gbps": round(nalg / tn / 1e9, 1), "frac_of_hbm_peak": round(nalg / tn / 1e9 / HBM_PEAK_GBPS, 4),
-               "algorithmic_bytes": nalg, "mean_accepted": round(float(nL.mean()), 4), "rotate": MN}
+               "algorithmic_bytes": nalg, "mean_accepted": round(float(nL.mean()), 4), "rotate": MN,
+               "pass1_traffic": measured_traffic("k_ngs_rowstats")}
         log(f"n-gram sampling verify {tn * 1e6:.2f} us/round ({nalg / tn / 1e9:.0f} GB/s), mean accepted {nL.mean():.3f}")
         del nsets
 
