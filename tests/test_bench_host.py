@@ -1,0 +1,75 @@
+"""bench.py's host logic on the CPU: counter ingestion, the source-hash rule for the
+traffic figures, and the one-GPU guard. No GPU is touched."""
+import csv
+import json
+import subprocess
+import sys
+
+import bench
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _write_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+COPY = "__amd_rocclr_copyBuffer"
+MASS = "void sv::k_sample_mass<sv::bf16_t, true, false>(sv::SampleParams)"
+MASS_F = "void sv::k_sample_mass<sv::bf16_t, true, true>(sv::SampleParams)"
+DRAW = "void sv::k_sample_draw<sv::bf16_t, false>(sv::SampleParams)"
+DRAW_F = "void sv::k_sample_draw<sv::bf16_t, true>(sv::SampleParams)"
+FAST = "void sv::k_filter_fast<sv::bf16_t>(sv::SampleParams)"
+
+
+def test_counter_means_split_filtered_variants_and_keep_three_calibration_copies(tmp_path):
+    p = tmp_path / "fetch.csv"
+    _write_csv(p, "FETCH_SIZE", [(COPY, 131072), (COPY, 131072), (COPY, 131074), (COPY, 5),  # 4th: an input upload
+                                 (MASS, 100), (MASS, 300), (MASS_F, 1000), (DRAW, 7), (DRAW_F, 9), (FAST, 50),
+                                 ("void sv::unrelated_kernel()", 1)])
+    m = bench._counter_means(str(p), "FETCH_SIZE")
+    assert m[COPY] == (131072 + 131072 + 131074) / 3
+    assert m["k_sample_mass"] == 200
+    assert m["k_sample_mass_filtered"] == 1000
+    assert m["k_sample_draw"] == 7 and m["k_sample_draw_filtered"] == 9
+    assert m["k_filter_fast"] == 50
+    assert len(m) == 6
+
+
+def test_ingest_scales_by_the_calibration_copy(tmp_path, monkeypatch):
+    fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
+    # the fetch counter reports half the copy's bytes, the write counter all of them
+    _write_csv(fp, "FETCH_SIZE", [(COPY, bench.CALIBRATION_KIB / 2)] * 3 + [(MASS, 1000.0)])
+    _write_csv(wp, "WRITE_SIZE", [(COPY, bench.CALIBRATION_KIB)] * 3 + [(MASS, 10.0)])
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    assert bench.ingest_counters(str(fp), str(wp)) == 0
+    d = json.loads(out.read_text())
+    assert d["fetch_scale"] == 2.0 and d["write_scale"] == 1.0
+    assert d["k_sample_mass"]["bytes_per_launch"] == 1024 * (1000 * 2 + 10)
+    assert d["k_sample_mass"]["source_sha"] == bench.kernel_source_sha()
+    # the figure is reported while the sources hash as recorded, and null once they do not
+    assert bench.measured_traffic("k_sample_mass") == 1024 * 2010
+    d["k_sample_mass"]["source_sha"] = "0" * 16
+    out.write_text(json.dumps(d))
+    assert bench.measured_traffic("k_sample_mass") is None
+    assert bench.measured_traffic("k_greedy_argmax") is None
+
+
+def test_ingest_refuses_files_without_the_calibration_copy(tmp_path, monkeypatch):
+    fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
+    _write_csv(fp, "FETCH_SIZE", [(MASS, 1.0)])
+    _write_csv(wp, "WRITE_SIZE", [(MASS, 1.0)])
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "t.json"))
+    assert bench.ingest_counters(str(fp), str(wp)) == 1
+    assert not (tmp_path / "t.json").exists()
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU only" in (r.stdout + r.stderr)
