@@ -13,12 +13,12 @@
 //
 // Kernels:
 //   k_pool_fill    marks every slot empty (16-byte stores, grid-stride).
-//   k_pool_insert  one workgroup per sequence. Wave 0 stages the call's W n-grams
-//                  in LDS and finds, for every distinct key, its last valid n-gram
-//                  of the call (the key's leader). Then the waves take the
-//                  distinct keys in turn (distinct keys are distinct buckets, so
-//                  no two waves touch one), and a wave rebuilds its key's bucket
-//                  lane-parallel: the call's continuations of the key, each at
+//   k_pool_insert  one workgroup per sequence. The call's W n-grams are staged
+//                  in LDS; every wave finds each n-gram's key itself, one per lane,
+//                  and wave w takes n-grams w, w + 16, ... An n-gram whose key has
+//                  no later valid n-gram in the call leads that key (distinct keys
+//                  are distinct buckets, so no two waves touch one), and its wave
+//                  rebuilds the key's bucket lane-parallel: the call's continuations of the key, each at
 //                  its last occurrence, newest first, then the old slots they do
 //                  not repeat, cut to G. This equals inserting the n-grams one by
 //                  one in window order.
@@ -52,9 +52,6 @@ constexpr int kPoolBlock = 64 * kPoolWaves;
 
 struct PoolShared {
   int32_t ng[SPEC_MAX_POOL_W * SPEC_MAX_POOL_N];  // the call's n-grams, [W][N]
-  int32_t key[SPEC_MAX_POOL_W];                    // first token, -1 for a skipped n-gram
-  int32_t leader[SPEC_MAX_POOL_W];                 // distinct keys: index of their last n-gram in the call
-  int32_t nleader;
 };
 
 // Do n-grams w1 and w2 (both valid, same key) carry the same continuation?
@@ -74,43 +71,31 @@ __global__ __launch_bounds__(kPoolBlock) void k_pool_insert(PoolParams P) {
     const int b = static_cast<int>(task);
     for (int i = threadIdx.x; i < W * N; i += kPoolBlock) sh.ng[i] = P.ngrams[static_cast<int64_t>(b) * W * N + i];
     __syncthreads();
-    if (wave == 0) {
-      bool valid = false;
-      if (lane < W) {
-        valid = true;
-        for (int i = 0; i < N; ++i) {
-          const int t = sh.ng[lane * N + i];
-          valid = valid && t >= 0 && t < P.V;
-        }
-        sh.key[lane] = valid ? sh.ng[lane * N] : -1;
+    // every wave finds each n-gram's key itself (lane w: n-gram w; -1 when skipped),
+    // so the waves need no second barrier
+    int myk = -1;
+    if (lane < W) {
+      bool valid = true;
+      for (int i = 0; i < N; ++i) {
+        const int t = sh.ng[lane * N + i];
+        valid = valid && t >= 0 && t < P.V;
       }
-      const uint64_t bad = __ballot(lane < W && !valid);
-      if (lane == 0 && P.out_skipped) P.out_skipped[b] = __popcll(bad);
-      // a valid n-gram leads its key when no later n-gram of the call has that key
-      bool lead = valid;
-      if (lane < W)
-        for (int w2 = lane + 1; w2 < W; ++w2) lead = lead && sh.key[w2] != sh.key[lane];
-      const uint64_t leads = __ballot(lead);
-      if (lead) sh.leader[__popcll(leads & ((1ull << lane) - 1))] = lane;
-      if (lane == 0) sh.nleader = __popcll(leads);
+      myk = valid ? sh.ng[lane * N] : -1;
     }
-    __syncthreads();
-    const int nlead = sh.nleader;
-    for (int li = wave; li < nlead; li += kPoolWaves) {
-      const int key = sh.key[sh.leader[li]];
+    if (wave == 0) {
+      const uint64_t bad = __ballot(lane < W && myk < 0);
+      if (lane == 0 && P.out_skipped) P.out_skipped[b] = __popcll(bad);
+    }
+    // wave `wave` takes n-grams wave, wave + 16, ...; an n-gram leads its key (and
+    // its wave rebuilds the key's bucket) when no later n-gram of the call has that
+    // key. Distinct keys are distinct buckets, so no two waves touch one.
+    for (int li = wave; li < W; li += kPoolWaves) {
+      const int key = __builtin_amdgcn_readlane(myk, li);
+      if (key < 0) continue;  // skipped n-gram
+      const uint64_t same = __ballot(lane < W && myk == key);  // the call's n-grams of this key
+      if (same >> li >> 1) continue;                             // a later one leads
       int32_t* bk = bucket(P, b, key);
-      // the key's n-grams of this call at their last occurrence, newest (highest w) first
-      bool fresh = false;
-      if (lane < W && sh.key[lane] == key) {
-        fresh = true;
-        for (int w2 = lane + 1; w2 < W; ++w2)
-          if (sh.key[w2] == key && same_cont(sh, N, lane, w2)) fresh = false;
-      }
-      const uint64_t freshm = __ballot(fresh);
-      const int nfresh = __popcll(freshm);
-      // rank among the fresh ones: the fresh n-grams after this one come first
-      const int rank = __popcll(freshm >> lane) - 1;
-      // the old slot `lane` (lanes < G): kept when no fresh continuation repeats it
+      // the old slot `lane` (lanes < G), loaded before the continuations are compared
       int32_t old[SPEC_MAX_POOL_N - 1];
       bool held = false;
       if (lane < G) {
@@ -118,6 +103,23 @@ __global__ __launch_bounds__(kPoolBlock) void k_pool_insert(PoolParams P) {
         for (int i = 0; i < SPEC_MAX_POOL_N - 1; ++i) old[i] = (i < N - 1) ? bk[lane * (N - 1) + i] : -1;
         held = old[0] >= 0;
       }
+      // the key's n-grams of this call at their last occurrence, newest (highest w) first
+      bool fresh = false;
+      if ((same >> lane) & 1ull) {
+        fresh = true;
+        for (uint64_t later = same >> lane >> 1; later != 0ull; later &= later - 1ull) {
+          const int w2 = lane + 1 + __ffsll(static_cast<unsigned long long>(later)) - 1;
+          if (same_cont(sh, N, lane, w2)) {
+            fresh = false;
+            break;
+          }
+        }
+      }
+      const uint64_t freshm = __ballot(fresh);
+      const int nfresh = __popcll(freshm);
+      // rank among the fresh ones: the fresh n-grams after this one come first
+      const int rank = __popcll(freshm >> lane) - 1;
+      // the old slot `lane` is kept when no fresh continuation repeats it
       bool keep = held;
       if (held) {
         for (int w2 = 0; w2 < W && keep; ++w2) {
