@@ -246,10 +246,16 @@ __device__ __forceinline__ int last_lane(bool pred) {
 // it) makes the later rounds hits.
 template <typename Params>
 __device__ __forceinline__ void touch_kernargs(const Params& P) {
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(&P);
+  static_assert(sizeof(Params) % 4 == 0, "whole dwords");
+  const char* base = reinterpret_cast<const char*>(&P);
+  auto dword = [&](size_t i) {
+    uint32_t v;
+    __builtin_memcpy(&v, base + 4 * i, 4);
+    return v;
+  };
 #pragma unroll
-  for (size_t i = 0; i < sizeof(Params) / 4; i += 12) asm volatile("" ::"s"(w[i]));
-  asm volatile("" ::"s"(w[sizeof(Params) / 4 - 1]), "s"(gridDim.x));
+  for (size_t i = 0; i < sizeof(Params) / 4; i += 12) asm volatile("" ::"s"(dword(i)));
+  asm volatile("" ::"s"(dword(sizeof(Params) / 4 - 1)), "s"(gridDim.x));
 }
 
 // Quotient and remainder of a workgroup-uniform task index by d > 0. A 64-bit
