@@ -128,6 +128,7 @@ STAGED_CASES = [
     (3, dict(B=7, K=0, V=1000), [], 1),               # K = 0: no stage, one draw from the bonus row
     (3, dict(B=16), [8], 1),                          # one stage: identical to the one-pass verify
     (3, {}, [2, 4, 8], 1),                            # the full workload in the bench's staged configuration
+    (3, dict(B=48, V=4000), [3, 6, 8], 2),            # three stages, 48 batch rows
 ]
 
 
@@ -156,10 +157,11 @@ def test_staged_parity_with_oracle(cfg, kw, stages, rounds):
     save_report(f"staged {stages} cfg{cfg} {kw}", rep)
 
 
-def test_staged_matches_one_pass_on_the_gpu():
+@pytest.mark.parametrize("B", [32, 128])
+def test_staged_matches_one_pass_on_the_gpu(B):
     """With the same segment counts the staged and one-pass verifies take the same
     row statistics, so every token and count agrees bit for bit."""
-    s = make_sample_inputs(3, 1, B=32, V=20000)
+    s = make_sample_inputs(3, 1, B=B, V=20000)
     t = sample_tensors(s, DEV)
     os.environ["SPECVERIFY_S1"] = "1"
     try:
