@@ -114,3 +114,22 @@ def test_first_token_law_chisquare():
     chi = stats.chisquare(counts, B * p)
     log(f"first-token chi-square p-value {chi.pvalue:.3g}")
     assert chi.pvalue > 1e-3
+
+
+def test_deterministic_and_workspace_reuse():
+    """Repeated calls on one workspace give bitwise-identical outputs, also after a call
+    of another shape has used it."""
+    s = make_ngram_sample_inputs(0, peak=10.0)
+    small = make_ngram_sample_inputs(1, B=3, G=2, N=3, V=1000, peak=10.0)
+    lg, cd, un = to_dev(s)
+    slg, scd, sun = to_dev(small)
+    B, G, N, V = s.shape
+    ws = torch.zeros(rsv.ngram_sample_workspace_size(B, G, N, V), dtype=torch.uint8, device=DEV)
+    outs = []
+    for rep in range(3):
+        out = rsv.verify_ngram_sample(lg, cd, un, s.temperature, workspace=ws)
+        outs.append((out.tokens.clone(), out.accept_len.clone(), out.rows.clone()))
+        rsv.verify_ngram_sample(slg, scd, sun, small.temperature, workspace=ws)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert all(torch.equal(a, b) for a, b in zip(outs[0], o))
