@@ -465,10 +465,11 @@ __device__ __forceinline__ void wave_scalar_chunk_mass(const SampleParams& P, co
 // The masses of vector chunks c, c + cstride, ..., (CU of them, below cend),
 // computed by one wave: the loads of all of them are issued before any is
 // reduced (kept as raw 16-byte vectors, so 2*CU loads per lane cost 8*CU
-// registers), and lane 63 stores (chunk max, chunk mass). Four chunks per wave
-// measured best on gfx950 (one round of loads per wave at the 64 x 128k shape).
+// registers), and lane 63 stores (chunk max, chunk mass). Two chunks per wave
+// measured best on gfx950 (two rounds of loads per wave at the 64 x 128k shape;
+// one, three or four chunks per round were 0.3-0.5 us slower per verify round).
 #ifndef SV_CHUNKS_PER_WAVE
-#define SV_CHUNKS_PER_WAVE 4
+#define SV_CHUNKS_PER_WAVE 2
 #endif
 constexpr int kChunksPerWave = SV_CHUNKS_PER_WAVE;
 
