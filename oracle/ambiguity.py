@@ -2,8 +2,8 @@
 
 TEST INFRASTRUCTURE: run by hand; imports the oracle and the workload generators.
 
-For each sampling workload, counts the rows whose draw margin (distance of u*Z
-from the ends of the chosen token's interval, in probability mass) or accept
+For each sampling workload, counts the rows whose draw margin (distance of u
+from the ends of the chosen token's interval of the normalised CDF) or accept
 margin (|r - alpha|) is below the window. This fraction is a property of the
 inputs: at vocabularies of 10^4-10^5 tokens many tokens carry more mass than the
 window, so a uniform often lands near one of them.

@@ -43,9 +43,11 @@ design notes of the repository):
   * greedy ties: the lowest vocabulary index attains the argmax; among
     candidates with the longest prefix, the lowest candidate index wins.
 Margins (distance of a uniform from the boundary that decided it) are
-returned so that the parity tests can exclude the ambiguous cases; draw
-margins are measured in probability mass, on the unnormalised cumulative
-weights that u * Z is compared with.
+returned so that the parity tests can exclude the ambiguous cases. Both are
+distances on the unit interval the uniform lives on: |r - alpha| for an
+accept test, and for a draw the distance of u from the ends of the chosen
+token's interval of the normalised CDF C_k / Z (the residual law is
+norm(max(0, p - q)), [SD] §2.1, so its CDF boundaries are the C_k / Z).
 """
 from __future__ import annotations
 
@@ -90,7 +92,8 @@ def inverse_cdf_draw(w: np.ndarray, u: float) -> tuple[int, float, float]:
     """Draw from the weights w (not necessarily normalised) with the uniform u.
 
     Returns (k, Z, margin): k = min{k : C_k > u Z} with C_k = sum_{v <= k} w_v and
-    Z = sum w; margin = distance of u Z from the nearer boundary of k's interval.
+    Z = sum w; margin = distance of u from the nearer end of k's interval
+    [C_{k-1} / Z, C_k / Z) of the normalised CDF.
     """
     c = np.cumsum(np.asarray(w, dtype=np.float64))
     Z = float(c[-1])
@@ -101,7 +104,7 @@ def inverse_cdf_draw(w: np.ndarray, u: float) -> tuple[int, float, float]:
     else:
         k = int(np.nonzero(np.asarray(w) > 0)[0][-1])
     lo = float(c[k - 1]) if k > 0 else 0.0
-    margin = min(abs(tau - lo), abs(float(c[k]) - tau))
+    margin = min(abs(tau - lo), abs(float(c[k]) - tau)) / Z
     return k, Z, margin
 
 

@@ -25,6 +25,12 @@ def logits_from_probs(probs: list[str], T: float) -> np.ndarray:
     return np.array(out, dtype=np.float64)
 
 
+def probs_from_case(case: dict) -> np.ndarray:
+    """The case's hand-derived p_i(x_i), q_i(x_i) as a [1, K, 2] float array (null -> NaN)."""
+    return np.array([[[math.nan if v is None else float(Fraction(v)) for v in pair] for pair in case["probs"]]],
+                    dtype=np.float64)
+
+
 def sample_case(case: dict) -> dict:
     T = float(case["T"])
     K = len(case["x"])
@@ -36,7 +42,8 @@ def sample_case(case: dict) -> dict:
     uni[0, :, 1] = case["u"]
     return dict(target=target, draft=draft, tokens=np.array([case["x"]], dtype=np.int32), uniforms=uni, T=T,
                 expect_tokens=np.array([case["tokens"]], dtype=np.int32),
-                expect_n=np.array([case["n_accepted"]], dtype=np.int32), name=case["name"])
+                expect_n=np.array([case["n_accepted"]], dtype=np.int32), expect_probs=probs_from_case(case),
+                name=case["name"])
 
 
 def greedy_case(case: dict) -> dict:

@@ -47,6 +47,73 @@ def check_golden_greedy(orc) -> None:
         assert np.array_equal(res.best, c["expect_best"]), (c["name"], res.best)
 
 
+def _same_probs(got: np.ndarray, expect: np.ndarray, what) -> None:
+    assert np.array_equal(np.isnan(got), np.isnan(expect)), (what, "NaN pattern", got, expect)
+    fin = ~np.isnan(expect)
+    assert np.allclose(got[fin], expect[fin], rtol=1e-12, atol=1e-15), (what, got, expect)
+
+
+def check_token_probs(orc) -> None:
+    """The out_probs values p_i(x_i), q_i(x_i): the two numbers alpha is formed from (§2.1).
+
+    Pinned three ways: the hand-derived values of every golden round (plain and
+    filtered: the filtered values are those of the renormalised kept laws);
+    closed forms on rows with one raised logit per position, distinct on every
+    row, so a swapped pair, a value from the wrong row or of the wrong token, or
+    an unnormalised value shows; and the per-side reading of a value that does
+    not exist -- p_i(x_i) depends on target row i and x_i alone, q_i(x_i) on draft
+    row i and x_i alone, so a row with no finite logit blanks only its own side,
+    and a token outside the vocabulary blanks both.
+    """
+    for case in load("sample_worked.json")["cases"]:
+        c = sample_case(case)
+        res = orc.oracle_sample(c["target"], c["draft"], c["tokens"], c["uniforms"], c["T"])
+        _same_probs(res.probs, c["expect_probs"], c["name"])
+    for case in load("filtered_worked.json")["cases"]:
+        c = filtered_case(case)
+        res = orc.oracle_sample_filtered(c["target"], c["draft"], c["tokens"], c["uniforms"], c["T"],
+                                         c["top_k"], c["top_p"])
+        _same_probs(res.probs, c["expect_probs"], c["name"])
+    # closed forms: target row i is a_i at x_i over V-1 zeros, draft row i is d_i at x_i
+    # over zeros, so p_i(x_i) = e^(a_i/T) / (e^(a_i/T) + V - 1) and likewise q_i(x_i)
+    V, K, T = 37, 5, 0.8
+    T64 = float(np.float32(T))
+    a = np.array([1.5, -0.5, 3.0, 0.25, 2.0, 0.75])       # K + 1 target rows (row K: the bonus row)
+    d = np.array([0.5, 2.5, -1.0, 1.75, -0.25])
+    x = np.array([[3, 11, 0, 36, 20]], dtype=np.int32)
+    tgt = np.zeros((1, K + 1, V))
+    drf = np.zeros((1, K, V))
+    for i in range(K):
+        tgt[0, i, x[0, i]] = a[i]
+        drf[0, i, x[0, i]] = d[i]
+    tgt[0, K, 7] = a[K]
+    uni = np.full((1, K + 1, 2), 0.5, dtype=np.float32)
+
+    def closed(v):
+        return math.exp(v / T64) / (math.exp(v / T64) + V - 1)
+
+    expect = np.array([[[closed(a[i]), closed(d[i])] for i in range(K)]])
+    res = orc.oracle_sample(tgt, drf, x, uni, T)
+    _same_probs(res.probs, expect, "closed forms")
+    # with every raised logit above the zeros, top-k = 1 keeps only the raised entry: every value is 1
+    up_t, up_d = np.abs(tgt) + (tgt != 0) * 0.5, np.abs(drf) + (drf != 0) * 0.5
+    res = orc.oracle_sample_filtered(up_t, up_d, x, uni, T, np.array([1]), np.array([1.0], dtype=np.float32))
+    _same_probs(res.probs, np.ones((1, K, 2)), "top-k 1")
+    # per-side blanks: target row 1 and draft row 3 hold no finite logit; token 4 is outside [0, V)
+    tgt2, drf2, x2 = tgt.copy(), drf.copy(), x.copy()
+    tgt2[0, 1, :] = -np.inf
+    drf2[0, 3, :] = -np.inf
+    x2[0, 4] = V
+    expect2 = expect.copy()
+    expect2[0, 1, 0] = np.nan
+    expect2[0, 3, 1] = np.nan
+    expect2[0, 4, :] = np.nan
+    res = orc.oracle_sample(tgt2, drf2, x2, uni, T)
+    _same_probs(res.probs, expect2, "per-side blanks")
+    res = orc.oracle_sample_filtered(tgt2, drf2, x2, uni, T, np.array([0]), np.array([1.0], dtype=np.float32))
+    _same_probs(res.probs, expect2, "per-side blanks, filters off")
+
+
 # --------------------------------------------------------------------------- closed forms
 
 def check_softmax_closed_forms(orc) -> None:
@@ -131,8 +198,10 @@ def check_inverse_cdf(orc) -> None:
     # unnormalised weights: the draw compares u*Z with the running sums
     w = np.array([1.0, 2.0, 1.0])
     assert [orc.inverse_cdf_draw(w, u)[0] for u in (0.0, 0.24, 0.25, 0.74, 0.75)] == [0, 0, 1, 1, 2]
+    # the margin is the distance of u from the ends of the chosen interval of the
+    # normalised CDF: here [1/4, 3/4) for u = 0.3, so 0.05
     k, Z, margin = orc.inverse_cdf_draw(w, 0.3)
-    assert Z == 4.0 and abs(margin - 0.2) < 1e-15
+    assert k == 1 and Z == 4.0 and abs(margin - 0.05) < 1e-15
 
 
 # --------------------------------------------------------------------------- exact law on a grid
@@ -204,24 +273,46 @@ def _sample_from(q: np.ndarray, rng: np.random.Generator, n: int) -> np.ndarray:
     return rng.choice(q.shape[-1], size=n, p=q / q.sum()).astype(np.int32)
 
 
-def check_chisquare_law(orc, trials: int = 30000) -> None:
-    """Output law = p (§2.2) by chi-square on non-dyadic laws; p-value >= 1e-3."""
-    rng = np.random.default_rng(2024)
-    for V in (2, 5, 16):
-        lt = rng.normal(0, 1.5, V)
-        ld = rng.normal(0, 1.5, V)
-        if V == 16:                       # disjoint-ish supports: half the target mass where q has none
-            ld[:4] = -np.inf
+CHI_V = (2, 5, 16)
+CHI_CHUNK = 50000
+
+
+def _chisquare_laws(V: int):
+    """(target logits, draft logits) of the chi-square law for vocabulary V (fixed seeds)."""
+    rng = np.random.default_rng([2024, V])
+    lt = rng.normal(0, 1.5, V)
+    ld = rng.normal(0, 1.5, V)
+    if V == 16:                       # disjoint-ish supports: part of the target mass where q has none
+        ld[:4] = -np.inf
+    return lt, ld
+
+
+def chisquare_counts(orc, V: int, chunk: int, n: int) -> np.ndarray:
+    """Histogram of the emitted token over n verify rows (K = 1) of chunk `chunk` of the V-token law."""
+    lt, ld = _chisquare_laws(V)
+    q = special.softmax(ld)
+    toks = _sample_from(q, np.random.default_rng([2025, V, chunk]), n)[:, None]
+    tgt = np.broadcast_to(np.stack([lt, lt]), (n, 2, V))
+    drf = np.broadcast_to(ld, (n, 1, V))
+    uni = verify_uniforms(100 + V, chunk, n, 1)
+    res = orc.oracle_sample(tgt, drf, toks, uni, 1.0, with_probs=False)
+    return np.bincount(res.tokens[:, 0], minlength=V)
+
+
+def check_chisquare_law(orc, trials: int = 30000, map_fn=map) -> None:
+    """Output law = p (§2.2) by chi-square on non-dyadic laws; p-value >= 1e-3.
+
+    `trials` rows per vocabulary, in chunks of CHI_CHUNK (each with its own
+    seeds); `map_fn` maps chisquare_counts over (V, chunk, n) argument tuples, so
+    a caller can spread the chunks over worker processes.
+    """
+    for V in CHI_V:
+        jobs = [(V, c, min(CHI_CHUNK, trials - c * CHI_CHUNK)) for c in range((trials + CHI_CHUNK - 1) // CHI_CHUNK)]
+        counts = sum(map_fn(lambda a: chisquare_counts(orc, *a), jobs)) if map_fn is map else sum(map_fn(jobs))
+        lt, _ = _chisquare_laws(V)
         p = special.softmax(lt)
-        q = special.softmax(np.where(np.isinf(ld), -np.inf, ld))
-        toks = _sample_from(q, rng, trials)[:, None]
-        tgt = np.broadcast_to(np.stack([lt, lt]), (trials, 2, V))
-        drf = np.broadcast_to(ld, (trials, 1, V))
-        uni = verify_uniforms(100 + V, 0, trials, 1)
-        res = orc.oracle_sample(tgt, drf, toks, uni, 1.0, with_probs=False)
-        counts = np.bincount(res.tokens[:, 0], minlength=V)
         pv = stats.chisquare(counts, p * trials).pvalue
-        assert pv >= 1e-3, (V, pv)
+        assert pv >= 1e-3, (V, trials, pv)
 
 
 def _fixed_tv_rows(rng, V: int, K: int, alpha: float):

@@ -75,6 +75,8 @@ def test_golden_filtered_on_gpu(case):
     res = oracle.oracle_sample_filtered(c["target"], c["draft"], c["tokens"], c["uniforms"], c["T"], c["top_k"],
                                         c["top_p"])
     assert np.allclose(probs, res.probs, rtol=1e-4, atol=1e-5, equal_nan=True), (probs, res.probs)
+    # and against the hand-derived values of the renormalised kept laws
+    assert np.allclose(probs, c["expect_probs"], rtol=1e-4, atol=1e-5, equal_nan=True), (probs, c["expect_probs"])
 
 
 # ------------------------------------------------------------------ workloads with mixed filters
@@ -99,6 +101,7 @@ def test_filtered_parity_mixed(cfg, kw):
         k, p = make_filter_params(B, seed=rnd, V=V)
         rep.merge(check(s, k, p))
     save_report(f"cfg{cfg} {kw}", rep)
+    rep.check_accounting()
 
 
 def test_filtered_parity_full_size_k50_p09():
@@ -107,6 +110,7 @@ def test_filtered_parity_full_size_k50_p09():
     k, p = make_filter_params(64, top_k=50, top_p=0.9)
     rep = check(s, k, p, "k50 p0.9")
     save_report("cfg3 full k50 p0.9", rep)
+    rep.check_accounting()
 
 
 @pytest.mark.parametrize("k,p", [(None, None), (0, 1.0), (1, 1.0), (0, 1e-30), (0, float("nan")), (2000, 0.999),
@@ -116,7 +120,7 @@ def test_filter_settings(k, p):
     B = 6
     kk = None if k is None else np.full(B, k, dtype=np.int32)
     pp = None if p is None else np.full(B, p, dtype=np.float32)
-    check(s, kk, pp, f"k={k} p={p}")
+    check(s, kk, pp, f"k={k} p={p}").check_accounting()
 
 
 # ------------------------------------------------------------------ exact keys, ties and masks
@@ -170,7 +174,7 @@ def test_faults_and_empty_rows_filtered():
     p = np.array([1.0, 0.9, 0.9, 0.5], dtype=np.float32)
     tok, n, probs, kept = run_gpu(t, k, p)
     res = oracle.oracle_sample_filtered(tgt, drf, toks, uni, 1.0, k, p)
-    compare_filtered(tgt, drf, toks, uni, 1.0, k, p, res, tok, n, probs, kept)
+    compare_filtered(tgt, drf, toks, uni, 1.0, k, p, res, tok, n, probs, kept).check_accounting()
     assert kept[3, K] == 0 and kept[2, K + 2] == 0
 
 
@@ -224,4 +228,4 @@ def test_one_pass_top_k_and_its_fallbacks(dtype, V):
     res = oracle.oracle_sample_filtered(tg, dr, toks, uni, 1.0, ks, ps)
     top_k_only = ps >= 1.0
     assert np.array_equal(kept[top_k_only], res.kept[top_k_only]), (kept, res.kept)
-    compare_filtered(tg, dr, toks, uni, 1.0, ks, ps, res, tok, n, probs, kept)
+    compare_filtered(tg, dr, toks, uni, 1.0, ks, ps, res, tok, n, probs, kept).check_accounting()

@@ -72,6 +72,7 @@ def test_parity_with_oracle(kw, rounds):
         res = oracle.oracle_ngram_sample(s.logits_f32(), s.cand, s.uniforms, s.temperature)
         rep.merge(compare_ngram_sample(s.cand, s.shape[3], res, tok, L, rows))
         log(f"  {rep.summary()} mean accepted {L.mean():.3f}")
+    rep.check_accounting()
 
 
 def test_one_candidate_matches_the_sample_verify_on_gpu():

@@ -14,7 +14,7 @@ import torch
 import oracle
 import rejection_sampling_verify_sample_amd as rsv
 from golden_io import load, sample_case
-from parity import ParityReport, compare_sample
+from parity import AMBIGUOUS_RATE, ParityReport, compare_sample
 from workloads import make_sample_inputs, verify_uniforms
 from workloads.torch_io import sample_tensors
 
@@ -64,10 +64,15 @@ def test_golden_rounds_on_gpu(case):
     tgt = torch.from_numpy(c["target"].astype(np.float32)).to(DEV)
     drf = torch.from_numpy(c["draft"].astype(np.float32)).to(DEV)
     out = rsv.verify_sample(tgt, drf, torch.from_numpy(c["tokens"]).to(DEV),
-                            torch.from_numpy(c["uniforms"]).to(DEV), c["T"])
+                            torch.from_numpy(c["uniforms"]).to(DEV), c["T"], want_probs=True)
     torch.cuda.synchronize()
     assert out.tokens.cpu().numpy().tolist() == c["expect_tokens"].tolist()
     assert out.num_accepted.cpu().numpy().tolist() == c["expect_n"].tolist()
+    # p_i(x_i), q_i(x_i) against the hand-derived values (NaN where a value does not exist)
+    probs, expect = out.probs.cpu().numpy(), c["expect_probs"]
+    assert np.array_equal(np.isnan(probs), np.isnan(expect))
+    fin = ~np.isnan(expect)
+    assert np.allclose(probs[fin], expect[fin], rtol=1e-4, atol=1e-5)
 
 
 # ------------------------------------------------------------------ workloads at parity sizes
@@ -92,6 +97,7 @@ def test_parity_with_oracle(cfg, kw, rounds):
     for rnd in range(rounds):
         rep.merge(check_inputs(make_sample_inputs(cfg, rnd, **kw)))
     save_report(f"cfg{cfg} {kw}", rep)
+    rep.check_accounting(AMBIGUOUS_RATE[cfg])
 
 
 @pytest.mark.parametrize("cfg,kw", [
@@ -105,6 +111,7 @@ def test_parity_many_rows(cfg, kw):
     rep = check_inputs(make_sample_inputs(cfg, 7, **kw))
     save_report(f"cfg{cfg} many {kw}", rep)
     assert rep.rows == kw["B"]
+    rep.check_accounting(AMBIGUOUS_RATE[cfg])
 
 
 @pytest.mark.parametrize("cfg", [3, 4])
@@ -113,6 +120,7 @@ def test_parity_full_size(cfg):
     s = make_sample_inputs(cfg, 0)
     rep = check_inputs(s)
     save_report(f"cfg{cfg} full", rep)
+    rep.check_accounting(AMBIGUOUS_RATE[cfg])
 
 
 # ------------------------------------------------------------------ early exit (pass 1 in stages)
@@ -155,6 +163,7 @@ def test_staged_parity_with_oracle(cfg, kw, stages, rounds):
         rep.merge(compare_sample(tgt, drf, s.draft_tokens, s.uniforms, s.temperature, res, tok, n, probs))
         log(f"  {rep.summary()}")
     save_report(f"staged {stages} cfg{cfg} {kw}", rep)
+    rep.check_accounting(AMBIGUOUS_RATE[cfg])
 
 
 @pytest.mark.parametrize("B", [32, 128])

@@ -1,10 +1,16 @@
 """The CPU oracle against the facts that pin it (no GPU)."""
+import os
+
 import oracle
 import pins
 
 
 def test_golden_sample_rounds():
     pins.check_golden_sample(oracle)
+
+
+def test_token_probabilities():
+    pins.check_token_probs(oracle)
 
 
 def test_golden_greedy_rounds():
@@ -29,6 +35,20 @@ def test_output_law_is_p_exactly_on_a_grid():
 
 def test_output_law_chisquare():
     pins.check_chisquare_law(oracle)
+
+
+def _chi_job(args):
+    import oracle as orc
+    return pins.chisquare_counts(orc, *args)
+
+
+def test_output_law_chisquare_one_million_trials():
+    """The chi-square of the output law at 10^6 verify rows per vocabulary (V = 2, 5, 16), chunks in worker processes."""
+    import concurrent.futures
+    import multiprocessing
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with concurrent.futures.ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("spawn")) as ex:
+        pins.check_chisquare_law(oracle, trials=1_000_000, map_fn=lambda jobs: ex.map(_chi_job, jobs))
 
 
 def test_acceptance_rate_is_one_minus_tv():

@@ -63,6 +63,22 @@ MUTATIONS = [
 ]
 
 MUTATIONS += [
+    ("token probabilities p/q swapped", "    return p, q\n", "    return q, p\n"),
+    ("token probabilities from the next target row", "probs[b, i] = token_probs(target[b, i], draft[b, i],",
+     "probs[b, i] = token_probs(target[b, i + 1], draft[b, i],"),
+    ("token probabilities of the previous draft token", "int(draft_tokens[b, i]), temperature)",
+     "int(draft_tokens[b, max(i - 1, 0)]), temperature)"),
+    ("token probability not normalised", "p = float(softmax64(target_row, temperature)[x])",
+     "p = float(np.exp(np.asarray(target_row, dtype=np.float64)[x] / temperature64(temperature)))"),
+    ("an invalid draft row blanks p too", 'if row_is_valid(target_row) else float("nan")',
+     'if row_is_valid(target_row) and row_is_valid(draft_row) else float("nan")'),
+    ("filtered token probabilities not renormalised", "probs[b, i, side] = float(law(j)[x])",
+     "probs[b, i, side] = float(softmax64(rows[j], temperature)[x]) if keeps[j].keep[x] else 0.0"),
+    ("filtered token probabilities p/q swapped", "for side, j in ((0, i), (1, K + 1 + i)):",
+     "for side, j in ((1, i), (0, K + 1 + i)):"),
+]
+
+MUTATIONS += [
     ("n-gram: no renormalisation after a rejection",
      "alpha = float(live[x]) / left if left > 0.0 else 0.0", "alpha = float(p[x])"),
     ("n-gram: a rejected token keeps its mass", "                live[x] = 0.0                               # residual",
@@ -82,6 +98,7 @@ MUTATIONS += [
 
 CHECKS = [
     pins.check_golden_sample,
+    pins.check_token_probs,
     pins.check_golden_greedy,
     pins.check_softmax_closed_forms,
     pins.check_acceptance_special_cases,
