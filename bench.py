@@ -2,31 +2,37 @@
 """Throughput of the speculative-decoding verify step on one MI355X.
 
 One step = one verify round of the B=64, K=8, V=128256 bf16 workload (T = 1.0):
-both launches of spec_verify_sample (pass 1: row statistics, accept tests and
-the first rejection; pass 2: the residual / bonus draw). Inputs are seeded
-synthetic logits already resident in HBM. The timed steps cycle through
+every launch of spec_verify_sample (pass 1: row statistics; pass 2: accept
+tests, first rejection and the residual / bonus masses; the draw). Inputs are
+seeded synthetic logits already resident in HBM. The timed steps cycle through
 several copies of the inputs (together more than twice the 256 MB Infinity
 Cache), so each step reads its logits from HBM rather than from the cache.
 Steps are launched from HIP graphs that each hold a run of consecutive steps
-(a graph launch costs about as much as a short kernel); the timed region, exactly
---steps steps, is bracketed by HIP events on the stream the kernels run on.
+(a graph launch costs about as much as a short kernel). Each measurement is
+repeated REPS times -- exactly --steps steps between HIP events on the stream
+the kernels run on -- and the median is reported with the spread.
 
 Prints ONE JSON line. Also reported: the pass-1 kernel alone (the dominant
-kernel, for the roofline), the same round with early exit (pass 1 in stages,
-spec_verify_sample_staged, which gives the same outputs), the same round
-verified on top-k 50 / top-p 0.9 filtered laws (spec_verify_sample_filtered),
-the n-gram pool (insert + lookup), the greedy verify and the sampling verify
-of greedy-drafted n-grams on their own workload (B=32 G=7 N=5 V=32000 bf16),
-and the CPU oracle on a bounded sample of the same round.
+kernel, for the roofline); the other three sampling workloads (B=1 K=4 V=32000
+fp32, B=8 K=5 V=32000 bf16, B=256 K=4 V=152064 fp32) measured the same way;
+the headline round with early exit (pass 1 in stages, spec_verify_sample_staged);
+the same round verified on top-k 50 / top-p 0.9 and on top-p 0.9 alone
+(spec_verify_sample_filtered); the n-gram pool (insert + lookup); the greedy
+verify and the sampling verify of greedy-drafted n-grams on their own workload
+(B=32 G=7 N=5 V=32000 bf16); and the CPU oracle on a bounded sample of the
+headline round, which also checks every timed workload's outputs against the
+oracle under the parity rule and counts the rows inside its window.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import math
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -37,8 +43,11 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, AMD published peak
 CACHE_BYTES = 256 * 2 ** 20  # MI355X Infinity Cache
 METRIC = "verify rounds/s + achieved HBM GB/s (% peak), B=64 K=8 V=128256 bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["common.hpp", "params.hpp", "rowstats.hpp", "search.hpp", "sample.hip", "filter.hip",
-                  "greedy.hip"]
+CSRC = os.path.join(ROOT, "rejection_sampling_verify_sample_amd", "csrc")
+REPS = 5                    # repetitions of every timed measurement (median and spread reported)
+SMALL_ROUNDS = 2000         # timed rounds per repetition of the launch-bound workloads
+SMALL_COPIES = 500          # input copies rotated through by the launch-bound workloads
+PARITY_WINDOW = 1e-6        # a decision closer than this to its boundary may differ (the parity rule)
 
 
 def log(msg: str) -> None:
@@ -48,24 +57,50 @@ def log(msg: str) -> None:
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--rotate", type=int, default=0, help="input copies (0: enough to exceed 2x the cache)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the other sampling workloads (1, 2 and 4)")
     ap.add_argument("--no-greedy", action="store_true")
-    ap.add_argument("--no-filtered", action="store_true", help="skip the top-k / top-p filtered leg")
+    ap.add_argument("--no-filtered", action="store_true", help="skip the top-k / top-p filtered legs")
     ap.add_argument("--no-staged", action="store_true", help="skip the early-exit (staged pass 1) leg")
     ap.add_argument("--no-pool", action="store_true", help="skip the n-gram pool leg")
     ap.add_argument("--no-ngram-sample", action="store_true", help="skip the one-hot n-gram sampling verify leg")
     ap.add_argument("--eager", action="store_true", help="launch through the Python binding instead of graphs")
     ap.add_argument("--counters", action="store_true",
-                    help="short run for rocprofv3 --pmc: a 256 MiB copy (calibration), then 3 eager verify rounds "
-                         "and 3 greedy rounds; prints nothing else")
+                    help="short run for rocprofv3 --pmc: a 256 MiB copy (calibration), then 3 eager rounds of "
+                         "each timed workload; prints nothing else")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from the counter_collection.csv files of two "
                          "rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of --counters; no GPU needed")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="print a markdown table of a rocprofv3 --kernel-trace CSV: dispatches, average, minimum "
+                         "and maximum duration per kernel and grid size; no GPU needed")
     return ap.parse_args()
+
+
+def trace_summary(path: str) -> int:
+    """Durations per (kernel, grid size) of a rocprofv3 kernel-trace CSV, as a markdown table."""
+    import csv
+    acc: dict = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            grid = row.get("Grid_Size") or row.get("Grid_Size_X") or "?"
+            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            acc.setdefault((name, grid), []).append(dur)
+    print("| Kernel | Grid (work-items) | Calls | Avg (us) | Min (us) | Max (us) |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for (name, grid), d in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+        short = name.split("(")[0].replace("void ", "").replace("sv::", "")
+        print(f"| {short} | {grid} | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
+    return 0
+
+
+FILTER_K, FILTER_P = 50, 0.9
+STAGES = [3, 8]  # early-exit leg: pass 1 reads positions 0..2, then 3..7 of the rows still walking
 
 
 def counters_run() -> int:
@@ -73,7 +108,7 @@ def counters_run() -> int:
     import torch
 
     import rejection_sampling_verify_sample_amd as rsv
-    from workloads import make_greedy_inputs, make_sample_inputs
+    from workloads import make_filter_params, make_greedy_inputs, make_ngram_sample_inputs, make_sample_inputs
     from workloads.torch_io import greedy_tensors, sample_tensors
 
     dev = torch.device("cuda:0")
@@ -89,33 +124,42 @@ def counters_run() -> int:
     for _ in range(3):
         rsv.verify_sample(t["target"], t["draft"], t["draft_tokens"], t["uniforms"], t["temperature"])
     torch.cuda.synchronize()
+    B = s.shape[0]
+    for top_k, top_p in ((FILTER_K, FILTER_P), (0, FILTER_P)):
+        fk, fp = make_filter_params(B, top_k=top_k, top_p=top_p)
+        fk, fp = torch.from_numpy(fk).to(dev), torch.from_numpy(fp).to(dev)
+        for _ in range(3):
+            rsv.verify_sample_filtered(t["target"], t["draft"], t["draft_tokens"], t["uniforms"], t["temperature"],
+                                       fk, fp)
+        torch.cuda.synchronize()
     del t
     g = greedy_tensors(make_greedy_inputs(0), dev)
     for _ in range(3):
         rsv.verify_greedy(g["logits"], g["cand"])
     torch.cuda.synchronize()
     del g
-    from workloads import make_filter_params, make_ngram_sample_inputs
-    t = sample_tensors(s, dev)
-    fk, fp = make_filter_params(s.shape[0], top_k=FILTER_K, top_p=FILTER_P)
-    fk, fp = torch.from_numpy(fk).to(dev), torch.from_numpy(fp).to(dev)
-    for _ in range(3):
-        rsv.verify_sample_filtered(t["target"], t["draft"], t["draft_tokens"], t["uniforms"], t["temperature"], fk, fp)
-    torch.cuda.synchronize()
-    del t
     ns = make_ngram_sample_inputs(0, peak=10.0)
     nlg = torch.from_numpy(ns.logits).to(dev).view(torch.bfloat16)
     ncand, nuni = torch.from_numpy(ns.cand).to(dev), torch.from_numpy(ns.uniforms).to(dev)
     for _ in range(3):
         rsv.verify_ngram_sample(nlg, ncand, nuni, ns.temperature)
     torch.cuda.synchronize()
+    del nlg
+    t4 = sample_tensors(make_sample_inputs(4, 0), dev)
+    for _ in range(3):
+        rsv.verify_sample(t4["target"], t4["draft"], t4["draft_tokens"], t4["uniforms"], t4["temperature"])
+    torch.cuda.synchronize()
     print("counters run done", file=sys.stderr)
     return 0
 
 
+# Kernel families whose counters are kept. The sampling kernels run at bf16 on
+# the headline workload and at fp32 on the B=256 K=4 V=152064 one; the fp32
+# variants are stored under the family name plus "_f32".
 TRAFFIC_KERNELS = ["k_sample_rowstats", "k_sample_mass", "k_sample_draw", "k_greedy_argmax", "k_greedy_select",
                    "k_filter_fast", "k_filter_rows", "k_sample_mass_filtered", "k_sample_draw_filtered",
-                   "k_ngs_rowstats", "k_ngs_verify"]
+                   "k_ngs_rowstats", "k_ngs_verify", "k_sample_rowstats_f32", "k_sample_mass_f32",
+                   "k_sample_draw_f32"]
 CALIBRATION_KERNEL = "__amd_rocclr_copyBuffer"
 CALIBRATION_KIB = 256 * 1024
 
@@ -134,6 +178,8 @@ def _counter_means(path: str, counter: str) -> dict:
                 continue
             if key in ("k_sample_mass", "k_sample_draw") and name.split(">(")[0].endswith("true"):
                 key += "_filtered"  # the filtered round's variant (last template argument)
+            elif key in ("k_sample_rowstats", "k_sample_mass", "k_sample_draw") and f"{key}<float" in name:
+                key += "_f32"
             acc.setdefault(key, []).append(float(row["Counter_Value"]))
     if CALIBRATION_KERNEL in acc:
         # the calibration copies come first; later copy dispatches are the small host-to-device input uploads
@@ -156,8 +202,10 @@ def ingest_counters(fetch_csv: str, write_csv: str) -> int:
                  "(copy bytes / counter bytes). source_sha: the kernel sources the counters were taken on "
                  "(bench.py reports null once they change).",
         "fetch_scale": fs, "write_scale": ws,
-        "workloads": {"k_sample_*": "B=64 K=8 V=128256 bf16", "k_greedy_*": "B=32 G=7 N=5 V=32000 bf16",
-                      "k_filter_*, *_filtered": "B=64 K=8 V=128256 bf16, top-k 50 and top-p 0.9 on every row",
+        "workloads": {"k_sample_*": "B=64 K=8 V=128256 bf16", "k_sample_*_f32": "B=256 K=4 V=152064 fp32",
+                      "k_greedy_*": "B=32 G=7 N=5 V=32000 bf16",
+                      "k_filter_*, *_filtered": "B=64 K=8 V=128256 bf16; top-k 50 and top-p 0.9 on every row, "
+                                                "then top-p 0.9 alone (means over both)",
                       "k_ngs_*": "n-gram sampling verify B=32 G=7 N=5 V=32000 bf16, peaked rows"},
     }
     for k in TRAFFIC_KERNELS:
@@ -171,10 +219,16 @@ def ingest_counters(fetch_csv: str, write_csv: str) -> int:
     return 0
 
 
+def kernel_sources() -> list:
+    """Every HIP source and header of the library (the counter figures are tied to all of them)."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")))
+
+
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "rejection_sampling_verify_sample_amd", "csrc", f), "rb") as fh:
+    for path in kernel_sources():
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -203,16 +257,23 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def rep_stats(per_step_s: list) -> dict:
+    """Median and spread of REPS per-step times (seconds) in microseconds."""
+    us = sorted(t * 1e6 for t in per_step_s)
+    med = statistics.median(us)
+    return {"us_median": round(med, 3), "us_min": round(us[0], 3), "us_max": round(us[-1], 3),
+            "spread": round((us[-1] - us[0]) / med, 4), "reps": len(us)}
+
+
 CHUNK_STEPS = 48   # verify steps per HIP graph (a graph launch costs about as much as a short kernel)
-FILTER_K, FILTER_P = 50, 0.9
-STAGES = [3, 8]  # early-exit leg: pass 1 reads positions 0..2, then 3..7 of the rows still walking
 
 
 class GraphSteps:
     """Runs verify steps step_fn(i, phases) from HIP graphs holding a run of consecutive steps.
 
     Steps cycle over the M input copies; a graph holds a whole number of cycles
-    (about CHUNK_STEPS steps), and a remainder graph makes any count exact.
+    (about CHUNK_STEPS steps, or M when M is larger), and a remainder graph makes
+    any count exact.
     """
 
     def __init__(self, torch, step_fn, M: int, eager: bool):
@@ -235,7 +296,7 @@ class GraphSteps:
             side = t.cuda.Stream()
             side.wait_stream(t.cuda.current_stream())
             with t.cuda.stream(side):
-                for j in range(self.M):
+                for j in range(min(self.M, self.chunk)):
                     self.step_fn(j, phases)
             t.cuda.current_stream().wait_stream(side)
             t.cuda.synchronize()
@@ -259,33 +320,180 @@ class GraphSteps:
         if r:
             tails[r].replay()
 
-    def timed(self, phases, n: int) -> float:
-        """Seconds for n steps, between HIP events on the stream the graphs run on."""
+    def timed(self, phases, n: int, lead: int = 0) -> float:
+        """Seconds for n steps, between HIP events on the stream the graphs run on.
+
+        `lead` untimed steps are queued first and not waited for: the GPU runs them
+        while the timed graphs are submitted, so the host's launch latency stays
+        outside the timed region (as in a decode loop, where the verify is queued
+        behind the model's forward pass).
+        """
         t = self.torch
         t.cuda.synchronize()
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        if lead:
+            self.run(phases, lead)
         a.record()
         self.run(phases, n)
         b.record()
         t.cuda.synchronize()
         return a.elapsed_time(b) / 1e3
 
+    def reps(self, phases, n: int, warmup: int) -> list:
+        """REPS measurements of n steps each (seconds per step), after `warmup` untimed steps;
+        each measurement is led by one untimed graph of steps."""
+        lead = self.chunk if not self.eager else 0
+        self.prepare(phases, [n, warmup, lead])
+        if warmup:
+            self.timed(phases, warmup)
+        return [self.timed(phases, n, lead) / n for _ in range(REPS)]
+
 
 class Timer:
     def __init__(self, torch):
         self.torch = torch
 
-    def time(self, fn, n: int) -> float:
-        """Seconds for n calls of fn(i), bracketed by events on the current stream."""
+    def time(self, fn, n: int, lead: int = 0) -> float:
+        """Seconds for n calls of fn(i), bracketed by events on the current stream, after `lead`
+        untimed calls that are queued first and not waited for."""
         t = self.torch
         t.cuda.synchronize()
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        for i in range(lead):
+            fn(i)
         a.record()
         for i in range(n):
             fn(i)
         b.record()
         t.cuda.synchronize()
         return a.elapsed_time(b) / 1e3
+
+    def reps(self, fn, n: int, warmup: int) -> list:
+        if warmup:
+            self.time(fn, warmup)
+        return [self.time(fn, n, 1) for _ in range(REPS)]
+
+
+def sample_bytes(B: int, K: int, V: int, esz: int, n_acc) -> dict:
+    """Algorithmic bytes of one round of the one-pass verify.
+
+    Pass 1 reads the 2K logit rows of every batch row once; pass 2 rereads target
+    and draft row n after a rejection, or the bonus row when all K are accepted;
+    plus the draft tokens, the uniforms and the outputs.
+    """
+    row = V * esz
+    pass1 = B * 2 * K * row
+    pass2 = int(sum(2 * row if int(n) < K else row for n in n_acc))
+    small = B * K * 4 + B * (K + 1) * 2 * 4 + B * (K + 1) * 4 + B * 4
+    return {"row": row, "pass1": pass1, "pass2": pass2, "small": small, "step": pass1 + pass2 + small}
+
+
+class SampleLeg:
+    """One sampling workload on the device: M rotated input copies, a shared workspace, graph-launched steps."""
+
+    def __init__(self, torch, rsv, dev, cfg: int, rotate: int, eager: bool, small: bool):
+        from workloads import make_sample_inputs
+        from workloads.torch_io import sample_tensors
+
+        self.torch, self.rsv, self.cfg, self.eager = torch, rsv, cfg, eager
+        t0 = time.time()
+        self.inputs = s = make_sample_inputs(cfg, 0)
+        self.B, self.K, self.V = B, K, V = s.shape
+        self.esz = 2 if s.dtype == "bf16" else 4
+        base = sample_tensors(s, dev)
+        set_bytes = (base["target"].numel() + base["draft"].numel()) * self.esz
+        if rotate:
+            M = rotate
+        elif small:
+            M = SMALL_COPIES
+        else:
+            M = max(2, math.ceil(2 * CACHE_BYTES / set_bytes) + 1)
+        self.M, self.set_bytes = M, set_bytes
+        self.sets = []
+        for _ in range(M):
+            self.sets.append(dict(target=base["target"].clone(), draft=base["draft"].clone(),
+                                  draft_tokens=base["draft_tokens"].clone(), uniforms=base["uniforms"].clone(),
+                                  out_tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                                  out_n=torch.empty((B,), dtype=torch.int32, device=dev)))
+        del base
+        self.ws = torch.zeros(rsv.sample_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
+        log(f"workload {cfg}: inputs in {time.time() - t0:.1f}s; {M} copies of {set_bytes / 1e6:.2f} MB")
+
+    def call(self, st, phases=None):
+        rsv = self.rsv
+        rsv.verify_sample(st["target"], st["draft"], st["draft_tokens"], st["uniforms"], self.inputs.temperature,
+                          out_tokens=st["out_tokens"], out_num_accepted=st["out_n"], workspace=self.ws,
+                          phases=rsv.PHASE_ALL if phases is None else phases)
+
+    def steps(self) -> GraphSteps:
+        return GraphSteps(self.torch, lambda i, ph: self.call(self.sets[i % self.M], ph), self.M, self.eager)
+
+    def outputs(self):
+        """Outputs of a fresh round on copy 0 (identical inputs give identical outputs)."""
+        self.call(self.sets[0])
+        self.torch.cuda.synchronize()
+        return self.sets[0]["out_tokens"].cpu().numpy(), self.sets[0]["out_n"].cpu().numpy()
+
+    def measure(self, n: int, warmup: int) -> dict:
+        """The whole round and pass 1 alone, REPS times each."""
+        import numpy as np
+        rsv = self.rsv
+        for st in self.sets[: min(self.M, 3)]:
+            self.call(st)
+        self.torch.cuda.synchronize()
+        steps = self.steps()
+        t_all = steps.reps(rsv.PHASE_ALL, n, warmup)
+        t_p1 = steps.reps(rsv.PHASE_ROW_STATS, n, warmup)
+        del steps
+        tok, n_acc = self.outputs()
+        B, K, V = self.B, self.K, self.V
+        assert np.all(n_acc >= 0) and np.all(n_acc <= K), "invalid accepted counts"
+        assert np.all((tok[np.arange(B), n_acc] >= 0) & (tok[np.arange(B), n_acc] < V))
+        by = sample_bytes(B, K, V, self.esz, n_acc)
+        st_all, st_p1 = rep_stats(t_all), rep_stats(t_p1)
+        t_step, t_pass1 = st_all["us_median"] / 1e6, st_p1["us_median"] / 1e6
+        self.tokens, self.n_acc = tok, n_acc
+        return {"t_step": t_step, "t_pass1": t_pass1, "round": st_all, "pass1": st_p1, "bytes": by,
+                "rounds_per_s": 1.0 / t_step, "gbps": by["step"] / t_step / 1e9,
+                "pass1_gbps": by["pass1"] / t_pass1 / 1e9, "mean_accepted": float(n_acc.mean())}
+
+
+def workload_record(leg: SampleLeg, m: dict, n: int, kernel_key: str) -> dict:
+    """The bench fields of one sampling workload."""
+    from workloads import WORKLOAD_NAMES
+    B, K = leg.B, leg.K
+    by = m["bytes"]
+    return {"workload": WORKLOAD_NAMES[leg.cfg], "B": B, "K": K, "V": leg.V, "dtype": leg.inputs.dtype,
+            "T": leg.inputs.temperature, "input_copies": leg.M, "steps_per_rep": n, "round": m["round"],
+            "us_per_round": m["round"]["us_median"], "rounds_per_s": round(m["rounds_per_s"], 1),
+            "draft_tokens_per_s": round(B * K * m["rounds_per_s"], 1),
+            "algorithmic_bytes_per_step": by["step"], "achieved_gbps": round(m["gbps"], 1),
+            "frac_of_hbm_peak": round(m["gbps"] / HBM_PEAK_GBPS, 4),
+            "pass1": {"kernel": kernel_key, "us_per_launch": m["pass1"]["us_median"], "spread": m["pass1"]["spread"],
+                      "algorithmic_bytes": by["pass1"], "achieved_gbps": round(m["pass1_gbps"], 1),
+                      "frac": round(m["pass1_gbps"] / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(kernel_key)},
+            "mean_accepted": round(m["mean_accepted"], 4)}
+
+
+def oracle_parity(leg: SampleLeg) -> dict:
+    """The oracle on every batch row of the leg's round, compared with the GPU outputs under the parity rule.
+
+    A row is in the window when a decision it took lies within PARITY_WINDOW of
+    its boundary (or its residual mass is below it); outside the window tokens and
+    counts must agree exactly. Returns the counts.
+    """
+    import numpy as np
+
+    import oracle
+    s = leg.inputs
+    res = oracle.oracle_sample(s.target_f32(), s.draft_f32(), s.draft_tokens, s.uniforms, s.temperature,
+                               with_probs=False)
+    margin = res.min_margin()
+    small_z = np.nan_to_num(res.residual_mass, nan=1.0) < PARITY_WINDOW
+    amb = (margin < PARITY_WINDOW) | small_z
+    same = (res.n_accepted == leg.n_acc) & np.all(res.tokens == leg.tokens, axis=1)
+    return {"rows": int(leg.B), "ambiguous_rows": int(amb.sum()), "ambiguous_agree": int((amb & same).sum()),
+            "mismatches_outside_window": int((~amb & ~same).sum())}
 
 
 def main() -> int:
@@ -294,6 +502,8 @@ def main() -> int:
         return counters_run()
     if args.ingest_counters:
         return ingest_counters(*args.ingest_counters)
+    if args.trace_summary:
+        return trace_summary(args.trace_summary)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -302,8 +512,7 @@ def main() -> int:
     import torch
 
     import rejection_sampling_verify_sample_amd as rsv
-    from workloads import WORKLOAD_NAMES, make_greedy_inputs, make_sample_inputs
-    from workloads.torch_io import greedy_tensors, sample_tensors
+    from workloads import WORKLOAD_NAMES
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -311,73 +520,23 @@ def main() -> int:
     dev = torch.device("cuda:0")
     timer = Timer(torch)
 
-    # ---------------------------------------------------------------- sampling verify, B=64 K=8 V=128256 bf16
-    t0 = time.time()
-    s = make_sample_inputs(3, 0)
-    B, K, V = s.shape
-    esz = 2
-    base = sample_tensors(s, dev)
-    set_bytes = (base["target"].numel() + base["draft"].numel()) * esz
-    M = args.rotate or max(2, math.ceil(2 * CACHE_BYTES / set_bytes) + 1)
-    log(f"inputs generated in {time.time() - t0:.1f}s; {M} copies of {set_bytes / 1e6:.1f} MB")
-    sets = []
-    for m in range(M):
-        sets.append(dict(target=base["target"].clone(), draft=base["draft"].clone(),
-                         draft_tokens=base["draft_tokens"].clone(), uniforms=base["uniforms"].clone(),
-                         out_tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
-                         out_n=torch.empty((B,), dtype=torch.int32, device=dev)))
-    del base
-    ws = torch.zeros(rsv.sample_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
-
-    def call(st, phases=rsv.PHASE_ALL):
-        rsv.verify_sample(st["target"], st["draft"], st["draft_tokens"], st["uniforms"], s.temperature,
-                          out_tokens=st["out_tokens"], out_num_accepted=st["out_n"], workspace=ws, phases=phases)
-
-    for i in range(3):
-        call(sets[i % M])
-    torch.cuda.synchronize()
-    steps = GraphSteps(torch, lambda i, ph: call(sets[i % M], ph), M, args.eager)
-    n_list = [args.warmup, args.steps]
-    steps.prepare(rsv.PHASE_ALL, n_list)
-    steps.prepare(rsv.PHASE_ROW_STATS, n_list)
-    steps.timed(rsv.PHASE_ALL, args.warmup)
-    t_step = steps.timed(rsv.PHASE_ALL, args.steps) / args.steps
-    steps.timed(rsv.PHASE_ROW_STATS, args.warmup)
-    t_pass1 = steps.timed(rsv.PHASE_ROW_STATS, args.steps) / args.steps
-    # outputs of the last full step of each copy (identical inputs -> identical outputs)
-    for st in sets:
-        call(st)
-    torch.cuda.synchronize()
-    n_acc = sets[0]["out_n"].cpu().numpy()
-    assert np.all(n_acc >= 0) and np.all(n_acc <= K), "invalid accepted counts"
-    tok = sets[0]["out_tokens"].cpu().numpy()
-    assert np.all((tok[np.arange(B), n_acc] >= 0) & (tok[np.arange(B), n_acc] < V))
-
-    # algorithmic bytes. Row statistics (pass 1): the 2K logit rows of every batch
-    # row, read once. Pass 2: target + draft row n after a rejection, or the bonus
-    # row. Plus the draft tokens, the uniforms and the outputs.
-    row_bytes = V * esz
-    pass1_bytes = B * 2 * K * row_bytes
-    pass2_bytes = int(sum(2 * row_bytes if n < K else row_bytes for n in n_acc))
-    small_bytes = B * K * 4 + B * (K + 1) * 2 * 4 + B * (K + 1) * 4 + B * 4
-    step_bytes = pass1_bytes + pass2_bytes + small_bytes
-    rounds_per_s = 1.0 / t_step
-    step_gbps = step_bytes / t_step / 1e9
-    pass1_gbps = pass1_bytes / t_pass1 / 1e9
-    traffic = measured_traffic("k_sample_rowstats")
-    log(f"step {t_step * 1e6:.2f} us ({rounds_per_s:.0f} rounds/s, {step_gbps:.0f} GB/s); "
-        f"pass 1 {t_pass1 * 1e6:.2f} us ({pass1_gbps:.0f} GB/s); mean accepted {n_acc.mean():.3f}")
-    del steps
+    # ---------------------------------------------------------------- headline: B=64 K=8 V=128256 bf16
+    head = SampleLeg(torch, rsv, dev, 3, args.rotate, args.eager, small=False)
+    B, K, V = head.B, head.K, head.V
+    m3 = head.measure(args.steps, args.warmup)
+    t_step = m3["t_step"]
+    by3 = m3["bytes"]
+    log(f"step {t_step * 1e6:.2f} us (median of {REPS}; spread {m3['round']['spread']:.3f}; "
+        f"{m3['rounds_per_s']:.0f} rounds/s, {m3['gbps']:.0f} GB/s); pass 1 {m3['t_pass1'] * 1e6:.2f} us "
+        f"({m3['pass1_gbps']:.0f} GB/s); mean accepted {m3['mean_accepted']:.3f}")
     # the same round on one input copy every step ("hot": part of it may stay in the
     # 256 MB Infinity Cache); labelled apart from the rotated measurement above
-    hsteps = GraphSteps(torch, lambda i, ph: call(sets[0], ph), 1, args.eager)
+    hsteps = GraphSteps(torch, lambda i, ph: head.call(head.sets[0], ph), 1, args.eager)
     hn = max(CHUNK_STEPS, min(args.steps, 500))
-    hsteps.prepare(rsv.PHASE_ALL, [hn])
-    hsteps.timed(rsv.PHASE_ALL, hn)
-    t_hot = hsteps.timed(rsv.PHASE_ALL, hn) / hn
-    hot = {"workload": WORKLOAD_NAMES[3] + "; one input copy reused every step", "steps": hn,
-           "us_per_round": round(t_hot * 1e6, 3), "rounds_per_s": round(1.0 / t_hot, 1)}
-    log(f"hot (one copy): {t_hot * 1e6:.2f} us per round")
+    t_hot = rep_stats(hsteps.reps(rsv.PHASE_ALL, hn, hn))
+    hot = {"workload": WORKLOAD_NAMES[3] + "; one input copy reused every step", "steps_per_rep": hn,
+           "round": t_hot, "us_per_round": t_hot["us_median"], "rounds_per_s": round(1e6 / t_hot["us_median"], 1)}
+    log(f"hot (one copy): {t_hot['us_median']:.2f} us per round")
     del hsteps
 
     # ---------------------------------------------------------------- the same round with early exit (pass 1 in stages)
@@ -386,81 +545,104 @@ def main() -> int:
         stages = STAGES
 
         def scall(st, phases=rsv.PHASE_ALL):
-            rsv.verify_sample_staged(st["target"], st["draft"], st["draft_tokens"], st["uniforms"], s.temperature,
-                                     stages, out_tokens=st["out_tokens"], out_num_accepted=st["out_n"], workspace=ws)
+            rsv.verify_sample_staged(st["target"], st["draft"], st["draft_tokens"], st["uniforms"],
+                                     head.inputs.temperature, stages, out_tokens=st["out_tokens"],
+                                     out_num_accepted=st["out_n"], workspace=head.ws)
 
-        for st in sets:
+        for st in head.sets:
             scall(st)
         torch.cuda.synchronize()
-        sn = sets[0]["out_n"].cpu().numpy()
+        sn = head.sets[0]["out_n"].cpu().numpy()
         # the outputs match the one-pass verify's except where a decision sits within rounding of
         # its boundary (the stages split rows into other segments); the parity tests hold both to the oracle
-        same = bool(np.array_equal(sn, n_acc) and np.array_equal(sets[0]["out_tokens"].cpu().numpy(), tok))
-        ssteps = GraphSteps(torch, lambda i, ph: scall(sets[i % M], ph), M, args.eager)
-        ssteps.prepare(rsv.PHASE_ALL, n_list)
-        ssteps.timed(rsv.PHASE_ALL, args.warmup)
-        ts_step = ssteps.timed(rsv.PHASE_ALL, args.steps) / args.steps
+        same = bool(np.array_equal(sn, head.n_acc) and np.array_equal(head.sets[0]["out_tokens"].cpu().numpy(),
+                                                                      head.tokens))
+        ssteps = GraphSteps(torch, lambda i, ph: scall(head.sets[i % head.M], ph), head.M, args.eager)
+        ts = rep_stats(ssteps.reps(rsv.PHASE_ALL, args.steps, args.warmup))
+        ts_step = ts["us_median"] / 1e6
         del ssteps
         # bytes this design reads: pass 1 through the stage holding each row's first
         # rejection (every stage when all K are accepted), then pass 2 as before
-        read_pos = [next(e for e in stages if int(n) < e) if int(n) < K else K for n in n_acc]
-        sbytes = int(sum(2 * p * row_bytes for p in read_pos)) + pass2_bytes + small_bytes
+        read_pos = [next(e for e in stages if int(n) < e) if int(n) < K else K for n in head.n_acc]
+        sbytes = int(sum(2 * p * by3["row"] for p in read_pos)) + by3["pass2"] + by3["small"]
         staged = {"workload": f"{WORKLOAD_NAMES[3]}; pass 1 in stages ending at positions {stages}",
-                  "rounds_per_s": round(1.0 / ts_step, 1), "us_per_round": round(ts_step * 1e6, 3),
+                  "round": ts, "rounds_per_s": round(1.0 / ts_step, 1), "us_per_round": ts["us_median"],
                   "speedup_vs_one_pass": round(t_step / ts_step, 4), "same_outputs_as_one_pass": same,
-                  "algorithmic_bytes_per_step": sbytes, "bytes_vs_one_pass": round(sbytes / step_bytes, 4),
+                  "algorithmic_bytes_per_step": sbytes, "bytes_vs_one_pass": round(sbytes / by3["step"], 4),
                   "achieved_gbps": round(sbytes / ts_step / 1e9, 1),
                   "frac_of_hbm_peak": round(sbytes / ts_step / 1e9 / HBM_PEAK_GBPS, 4)}
         log(f"staged {stages}: {ts_step * 1e6:.2f} us ({1.0 / ts_step:.0f} rounds/s), "
-            f"{sbytes / 1e6:.1f} MB read ({sbytes / step_bytes:.2f} of one pass)")
+            f"{sbytes / 1e6:.1f} MB read ({sbytes / by3['step']:.2f} of one pass)")
 
-    # ---------------------------------------------------------------- the same round, top-k 50 / top-p 0.9 filtered
-    filtered = None
+    # ---------------------------------------------------------------- the same round on filtered laws
+    filtered = []
     if not args.no_filtered:
         from workloads import make_filter_params
-        fk, fp = make_filter_params(B, top_k=FILTER_K, top_p=FILTER_P)
-        topk = torch.from_numpy(fk).to(dev)
-        topp = torch.from_numpy(fp).to(dev)
         fws = torch.zeros(rsv.sample_filtered_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
         kept = torch.empty((B, 2 * K + 1), dtype=torch.int32, device=dev)
+        for top_k, top_p in ((FILTER_K, FILTER_P), (0, FILTER_P)):
+            fk, fp = make_filter_params(B, top_k=top_k, top_p=top_p)
+            topk, topp = torch.from_numpy(fk).to(dev), torch.from_numpy(fp).to(dev)
 
-        def fcall(st, phases=rsv.PHASE_ALL):
-            rsv.verify_sample_filtered(st["target"], st["draft"], st["draft_tokens"], st["uniforms"], s.temperature,
-                                       topk, topp, out_tokens=st["out_tokens"], out_num_accepted=st["out_n"],
-                                       out_kept=kept, workspace=fws, phases=phases)
+            def fcall(st, phases=rsv.PHASE_ALL, topk=topk, topp=topp):
+                rsv.verify_sample_filtered(st["target"], st["draft"], st["draft_tokens"], st["uniforms"],
+                                           head.inputs.temperature, topk, topp, out_tokens=st["out_tokens"],
+                                           out_num_accepted=st["out_n"], out_kept=kept, workspace=fws,
+                                           phases=phases)
 
-        for st in sets:
-            fcall(st)
-        torch.cuda.synchronize()
-        fsteps = GraphSteps(torch, lambda i, ph: fcall(sets[i % M], ph), M, args.eager)
-        fn = max(CHUNK_STEPS, args.steps // 4)
-        fsteps.prepare(rsv.PHASE_ALL, [fn])
-        fsteps.prepare(rsv.PHASE_ROW_STATS, [fn])
-        fsteps.timed(rsv.PHASE_ALL, fn)
-        tf_step = fsteps.timed(rsv.PHASE_ALL, fn) / fn
-        fsteps.timed(rsv.PHASE_ROW_STATS, fn)
-        tf_filter = fsteps.timed(rsv.PHASE_ROW_STATS, fn) / fn
-        fcall(sets[0])
-        torch.cuda.synchronize()
-        fn_acc = sets[0]["out_n"].cpu().numpy()
-        assert np.all(fn_acc >= 0) and np.all(fn_acc <= K), "invalid accepted counts (filtered)"
-        rows = B * (2 * K + 1)
-        one_read = rows * row_bytes
-        # top-k 50 takes the one-pass path (k <= 64): each row is read once
-        passes = 1
-        filtered = {"workload": f"{WORKLOAD_NAMES[3]}; top-k {FILTER_K} and top-p {FILTER_P} on every row",
-                    "rounds_per_s": round(1.0 / tf_step, 1), "us_per_round": round(tf_step * 1e6, 3),
-                    "filter_kernel_us": round(tf_filter * 1e6, 3), "rows_filtered": rows,
-                    "one_read_bytes": one_read, "filter_gbps_one_read": round(one_read / tf_filter / 1e9, 1),
-                    "filter_passes_per_row": passes,
-                    "filter_frac_of_hbm_peak": round(one_read / tf_filter / 1e9 / HBM_PEAK_GBPS, 4),
-                    "mean_kept": round(float(kept.float().mean().item()), 2),
-                    "mean_accepted": round(float(fn_acc.mean()), 4),
-                    "filter_traffic": measured_traffic("k_filter_fast")}
-        log(f"filtered step {tf_step * 1e6:.2f} us; filter kernel {tf_filter * 1e6:.2f} us "
-            f"({one_read / tf_filter / 1e9:.0f} GB/s on one read of {rows} rows)")
-        del fsteps
-    del sets
+            for st in head.sets:
+                fcall(st)
+            torch.cuda.synchronize()
+            fsteps = GraphSteps(torch, lambda i, ph, f=fcall: f(head.sets[i % head.M], ph), head.M, args.eager)
+            fn = max(CHUNK_STEPS, args.steps // 4)
+            tf = rep_stats(fsteps.reps(rsv.PHASE_ALL, fn, fn))
+            tff = rep_stats(fsteps.reps(rsv.PHASE_ROW_STATS, fn, fn))
+            del fsteps
+            fcall(head.sets[0])
+            torch.cuda.synchronize()
+            fn_acc = head.sets[0]["out_n"].cpu().numpy()
+            assert np.all(fn_acc >= 0) and np.all(fn_acc <= K), "invalid accepted counts (filtered)"
+            rows = B * (2 * K + 1)
+            one_read = rows * by3["row"]
+            tf_step, tf_filter = tf["us_median"] / 1e6, tff["us_median"] / 1e6
+            what = (f"top-k {top_k} and top-p {top_p}" if top_k else f"top-p {top_p} alone") + " on every row"
+            filtered.append({
+                "workload": f"{WORKLOAD_NAMES[3]}; {what}", "top_k": top_k, "top_p": top_p,
+                "round": tf, "rounds_per_s": round(1.0 / tf_step, 1), "us_per_round": tf["us_median"],
+                "filter_kernels": tff, "filter_kernel_us": tff["us_median"], "rows_filtered": rows,
+                "one_read_bytes": one_read, "filter_gbps_one_read": round(one_read / tf_filter / 1e9, 1),
+                "filter_frac_of_hbm_peak": round(one_read / tf_filter / 1e9 / HBM_PEAK_GBPS, 4),
+                "mean_kept": round(float(kept.float().mean().item()), 2),
+                "mean_accepted": round(float(fn_acc.mean()), 4)})
+            log(f"filtered ({what}): step {tf_step * 1e6:.2f} us; filter kernels {tf_filter * 1e6:.2f} us "
+                f"({one_read / tf_filter / 1e9:.0f} GB/s on one read of {rows} rows)")
+        filtered[0]["filter_traffic"] = measured_traffic("k_filter_fast")
+        del fws
+    head_inputs_for_cpu = head
+    for st in head.sets[1:]:
+        st.clear()
+    head.sets = head.sets[:1]
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- the other sampling workloads
+    workloads = {}
+    legs = {3: head}
+    if not args.no_workloads:
+        for cfg in (1, 2, 4):
+            small = cfg in (1, 2)
+            leg = SampleLeg(torch, rsv, dev, cfg, 0, args.eager, small=small)
+            n = max(args.steps, SMALL_ROUNDS) if small else args.steps
+            m = leg.measure(n, max(args.warmup, 100) if small else args.warmup)
+            key = "k_sample_rowstats_f32" if leg.esz == 4 else "k_sample_rowstats"
+            workloads[str(cfg)] = workload_record(leg, m, n, key)
+            log(f"workload {cfg}: {m['t_step'] * 1e6:.2f} us per round ({m['rounds_per_s']:.0f} rounds/s, "
+                f"{m['gbps']:.0f} GB/s = {m['gbps'] / HBM_PEAK_GBPS:.3f} of peak); pass 1 {m['t_pass1'] * 1e6:.2f} us "
+                f"({m['pass1_gbps'] / HBM_PEAK_GBPS:.3f} of peak)")
+            for st in leg.sets[1:]:
+                st.clear()
+            leg.sets = leg.sets[:1]
+            legs[cfg] = leg
+            torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- n-gram pool, B=32 V=32000 G=7 N=5, W=15 per call
     pool_leg = None
@@ -484,28 +666,27 @@ def main() -> int:
         torch.cuda.synchronize()
         psteps = 48
         if args.eager:
-            pfn = pstep
-            pcalls = 1
+            pfn, pcalls = pstep, 1
         else:
             pgraph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(pgraph):
                 for j in range(psteps):
                     pstep(j)
-            pfn = lambda i: pgraph.replay()  # noqa: E731
-            pcalls = psteps
+            pfn, pcalls = (lambda i: pgraph.replay()), psteps  # noqa: E731
         n_rep = max(1, args.steps // pcalls)
-        timer.time(pfn, max(1, args.warmup // pcalls))
-        t_pool = timer.time(pfn, n_rep) / (n_rep * pcalls)
+        tp = rep_stats([t / (n_rep * pcalls) for t in timer.reps(pfn, n_rep, max(1, args.warmup // pcalls))])
         pool_leg = {"workload": f"n-gram pool B={PB} V={PV} G={PG} N={PN}: insert W={PW} n-grams per sequence, "
                                 "then look up each sequence's last token",
-                    "us_per_step": round(t_pool * 1e6, 3), "steps_per_s": round(1.0 / t_pool, 1),
+                    "step": tp, "us_per_step": tp["us_median"], "steps_per_s": round(1e6 / tp["us_median"], 1),
                     "mean_candidates": round(float(pcount.float().mean().item()), 3)}
-        log(f"n-gram pool insert + lookup: {t_pool * 1e6:.2f} us per step")
+        log(f"n-gram pool insert + lookup: {tp['us_median']:.2f} us per step")
         del pool
 
     # ---------------------------------------------------------------- greedy verify, B=32 G=7 N=5 V=32000 bf16
     greedy = None
     if not args.no_greedy:
+        from workloads import make_greedy_inputs
+        from workloads.torch_io import greedy_tensors
         g5 = make_greedy_inputs(0)
         gb, gg, gn, gv = g5.shape
         gt = greedy_tensors(g5, dev)
@@ -526,24 +707,23 @@ def main() -> int:
         torch.cuda.synchronize()
         L5 = M5 * max(1, 48 // M5)
         if args.eager:
-            gstep = lambda i: gcall(gsets[i % M5])   # noqa: E731
-            per_call = 1
+            gstep, per_call = (lambda i: gcall(gsets[i % M5])), 1  # noqa: E731
         else:
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
                 for j in range(L5):
                     gcall(gsets[j % M5])
-            gstep = lambda i: graph.replay()         # noqa: E731
-            per_call = L5
+            gstep, per_call = (lambda i: graph.replay()), L5  # noqa: E731
         reps = max(1, args.steps // per_call)
-        timer.time(gstep, max(1, args.warmup // per_call))
-        per = (timer.time(gstep, reps) / reps) / per_call
+        tg = rep_stats([t / (reps * per_call) for t in timer.reps(gstep, reps, max(1, args.warmup // per_call))])
+        per = tg["us_median"] / 1e6
         gal = gbytes + gb * gg * (gn - 1) * 4 + gb * (gn + 2) * 4
-        greedy = {"workload": WORKLOAD_NAMES[5], "rounds_per_s": round(1.0 / per, 1),
-                  "us_per_round": round(per * 1e6, 3), "achieved_gbps": round(gal / per / 1e9, 1),
+        greedy = {"workload": WORKLOAD_NAMES[5], "round": tg, "rounds_per_s": round(1.0 / per, 1),
+                  "us_per_round": tg["us_median"], "achieved_gbps": round(gal / per / 1e9, 1),
                   "frac_of_hbm_peak": round(gal / per / 1e9 / HBM_PEAK_GBPS, 4), "rotate": M5,
                   "algorithmic_bytes": gal, "argmax_traffic": measured_traffic("k_greedy_argmax")}
         log(f"greedy {per * 1e6:.2f} us/round ({gal / per / 1e9:.0f} GB/s)")
+        del gsets
 
     # ---------------------------------------------------------------- sampling verify of one-hot n-grams, same shape
     ngs = None
@@ -578,24 +758,26 @@ def main() -> int:
                     ncall(nsets[j % MN])
             nstep, ncalls = (lambda i: ngraph.replay()), LN  # noqa: E731
         nrep = max(1, args.steps // ncalls)
-        timer.time(nstep, max(1, args.warmup // ncalls))
-        tn = timer.time(nstep, nrep) / (nrep * ncalls)
+        tnr = rep_stats([t / (nrep * ncalls) for t in timer.reps(nstep, nrep, max(1, args.warmup // ncalls))])
+        tn = tnr["us_median"] / 1e6
         nL = nsets[0]["ol"].cpu().numpy()
         # pass 1 reads every row once; the draw reads one row per sequence (twice, the second time from cache)
         nalg = nbytes_set + nb * nv * 2
         ngs = {"workload": f"sampling verify of greedy-drafted n-grams B={nb} G={ng} N={nn} V={nv} bf16 T=1.0, "
                            "peaked rows, candidates on the peak w.p. 0.6",
-               "rounds_per_s": round(1.0 / tn, 1), "us_per_round": round(tn * 1e6, 3),
+               "round": tnr, "rounds_per_s": round(1.0 / tn, 1), "us_per_round": tnr["us_median"],
                "achieved_gbps": round(nalg / tn / 1e9, 1), "frac_of_hbm_peak": round(nalg / tn / 1e9 / HBM_PEAK_GBPS, 4),
                "algorithmic_bytes": nalg, "mean_accepted": round(float(nL.mean()), 4), "rotate": MN,
                "pass1_traffic": measured_traffic("k_ngs_rowstats")}
         log(f"n-gram sampling verify {tn * 1e6:.2f} us/round ({nalg / tn / 1e9:.0f} GB/s), mean accepted {nL.mean():.3f}")
         del nsets
 
-    # ---------------------------------------------------------------- CPU oracle on a bounded sample
+    # ---------------------------------------------------------------- CPU oracle: baseline timing and parity accounting
     cpu = None
+    parity = None
     if not args.no_cpu_baseline:
         import oracle
+        s = head_inputs_for_cpu.inputs
         tgt, drf = s.target_f32(), s.draft_f32()
         rows = 0
         t1 = time.perf_counter()
@@ -610,10 +792,12 @@ def main() -> int:
                          f"{el:.1f} s, scaled to rounds of 64 rows",
                "host_cpu": cpu_model(), "host_logical_cpus": os.cpu_count()}
         log(f"cpu oracle {rows} rows in {el:.1f}s")
+        parity = {str(c): oracle_parity(leg) for c, leg in sorted(legs.items())}
+        log(f"parity vs oracle: {parity}")
 
     out = {
         "metric": METRIC,
-        "value": round(rounds_per_s, 2),
+        "value": round(m3["rounds_per_s"], 2),
         "unit": "verify rounds/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -624,24 +808,29 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[3], "B": B, "K": K, "V": V, "T": s.temperature,
-                   "input_copies": M, "graph": not args.eager},
-        "draft_tokens_per_s": round(B * K * rounds_per_s, 1),
-        "achieved_gbps": round(step_gbps, 1),
-        "frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
-        "algorithmic_bytes_per_step": step_bytes,
-        "mean_accepted": round(float(n_acc.mean()), 4),
-        "roofline": {"kernel": "k_sample_rowstats", "bound": "hbm", "achieved": round(pass1_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(pass1_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes": pass1_bytes,
-                     "us_per_launch": round(t_pass1 * 1e6, 3)},
+        "config": {"workload": WORKLOAD_NAMES[3], "B": B, "K": K, "V": V, "T": head.inputs.temperature,
+                   "input_copies": head.M, "graph": not args.eager},
+        "round": m3["round"],
+        "draft_tokens_per_s": round(B * K * m3["rounds_per_s"], 1),
+        "achieved_gbps": round(m3["gbps"], 1),
+        "frac_of_hbm_peak": round(m3["gbps"] / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": by3["step"],
+        "mean_accepted": round(m3["mean_accepted"], 4),
+        "ambiguous_rows": parity["3"]["ambiguous_rows"] if parity else None,
+        "ambiguous_agree": parity["3"]["ambiguous_agree"] if parity else None,
+        "roofline": {"kernel": "k_sample_rowstats", "bound": "hbm", "achieved": round(m3["pass1_gbps"], 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(m3["pass1_gbps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("k_sample_rowstats"), "algorithmic_bytes": by3["pass1"],
+                     "us_per_launch": round(m3["t_pass1"] * 1e6, 3), "spread": m3["pass1"]["spread"]},
         "cpu_baseline": cpu,
+        "parity": parity,
+        "workloads": workloads,
         "hot_single_copy": hot,
         "staged": staged,
+        "filtered": filtered,
         "ngram_pool": pool_leg,
         "greedy": greedy,
         "ngram_sample": ngs,
-        "filtered": filtered,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -73,3 +73,38 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU only" in (r.stdout + r.stderr)
+
+
+def test_source_hash_covers_every_kernel_source():
+    import glob
+    import os
+    csrc = os.path.join(os.path.dirname(bench.__file__), "rejection_sampling_verify_sample_amd", "csrc")
+    every = sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp")))
+    assert bench.kernel_sources() == every and len(every) >= 10
+
+
+def test_counter_means_keep_fp32_variants_apart(tmp_path):
+    p = tmp_path / "fetch.csv"
+    rows = [(COPY, 131072)] * 3 + [
+        ("void sv::k_sample_rowstats<sv::bf16_t>(sv::SampleParams, int)", 100),
+        ("void sv::k_sample_rowstats<float>(sv::SampleParams, int)", 500),
+        ("void sv::k_sample_mass<float, true, false>(sv::SampleParams)", 70),
+        (MASS, 30)]
+    _write_csv(p, "FETCH_SIZE", rows)
+    m = bench._counter_means(str(p), "FETCH_SIZE")
+    assert m["k_sample_rowstats"] == 100 and m["k_sample_rowstats_f32"] == 500
+    assert m["k_sample_mass_f32"] == 70 and m["k_sample_mass"] == 30
+
+
+def test_trace_summary_groups_by_kernel_and_grid(tmp_path, capsys):
+    p = tmp_path / "trace.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size_X", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for g, d in ((1024, 4000), (1024, 6000), (64, 1000)):
+            w.writerow({"Kernel_Name": "void sv::k_x<float>(sv::P)", "Grid_Size_X": g, "Start_Timestamp": 10,
+                        "End_Timestamp": 10 + d})
+    assert bench.trace_summary(str(p)) == 0
+    out = capsys.readouterr().out
+    assert "| k_x<float> | 1024 | 2 | 5.00 | 4.00 | 6.00 |" in out
+    assert "| k_x<float> | 64 | 1 | 1.00 | 1.00 | 1.00 |" in out
