@@ -122,6 +122,30 @@ spec_status spec_verify_sample(const void* target_logits, const void* draft_logi
                                size_t workspace_bytes, void* stream);
 
 /*
+ * spec_verify_sample for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Arguments and outputs as spec_verify_sample, without the workspace: the call
+ * uses a fixed device array of SPEC_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on until the process ends, and allocates nothing (no
+ * hipMalloc, no allocating library routine). The array's device address is
+ * looked up once per device, on the first call with that device current.
+ * Sizes whose spec_verify_sample_workspace_size exceeds
+ * SPEC_NOALLOC_SCRATCH_BYTES return SPEC_ERR_WORKSPACE (before any HIP call);
+ * every argument error is found before any HIP call as well. A failed lookup of
+ * the array returns SPEC_ERR_HIP. Every call on one GPU shares that GPU's array:
+ * calls that may overlap on one GPU (different streams without ordering between
+ * them) race and give unspecified outputs. The array needs no clearing between
+ * calls (the kernels keep nothing in it from one call to the next).
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES (4u << 20)
+size_t spec_verify_sample_noalloc_max_bytes(void); /* SPEC_NOALLOC_SCRATCH_BYTES */
+spec_status spec_verify_sample_noalloc(const void* target_logits, const void* draft_logits, int32_t dtype,
+                                       const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t K,
+                                       int32_t V, float temperature, int32_t* out_tokens,
+                                       int32_t* out_num_accepted, float* out_probs, void* stream);
+
+/*
  * spec_verify_sample as its four launches, for callers that schedule or time
  * them apart. Same arguments as spec_verify_sample plus a mask of phases,
  * which run in this order on `stream` (a call with every bit set is

@@ -47,6 +47,9 @@ _SIGNATURES = {
                                                   _i32, ctypes.c_float, _c_void_p, _c_void_p, _c_void_p,
                                                   _c_void_p, _size_t, _c_void_p, _c_void_p, _c_void_p,
                                                   _c_void_p, _i32]),
+    "spec_verify_sample_noalloc_max_bytes": (_size_t, []),
+    "spec_verify_sample_noalloc": (_i32, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                          ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "spec_verify_greedy_workspace_size": (_size_t, [_i32, _i32, _i32, _i32]),
     "spec_verify_greedy": (_i32, [_c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
                                   _c_void_p, _c_void_p, _size_t, _c_void_p]),
@@ -186,6 +189,38 @@ def verify_sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch
     """
     return _verify_sample(target, draft, draft_tokens, uniforms, temperature, out_tokens, out_num_accepted,
                           out_probs, want_probs, workspace, stream, phases, None)
+
+
+def verify_sample_noalloc(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                          uniforms: torch.Tensor, temperature: float, *, out_tokens: torch.Tensor,
+                          out_num_accepted: torch.Tensor, out_probs: torch.Tensor | None = None,
+                          stream=None) -> SampleOutputs:
+    """spec_verify_sample_noalloc: verify_sample with the library's fixed device scratch as workspace.
+
+    The caller passes every output (nothing is allocated here either); sizes whose
+    workspace exceeds spec_verify_sample_noalloc_max_bytes() are refused.
+    """
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    _check(target, "target", dev)
+    code = _dtype_code(target)
+    _check(draft, "draft", dev, target.dtype, (B, K, V))
+    _check(draft_tokens, "draft_tokens", dev, torch.int32, (B, K))
+    _check(uniforms, "uniforms", dev, torch.float32, (B, K + 1, 2))
+    _check(out_tokens, "out_tokens", dev, torch.int32, (B, K + 1))
+    _check(out_num_accepted, "out_num_accepted", dev, torch.int32, (B,))
+    if out_probs is not None:
+        _check(out_probs, "out_probs", dev, torch.float32, (B, K, 2))
+    sh = _stream_handle(stream, dev)
+    st = lib().spec_verify_sample_noalloc(_ptr(target), _ptr(draft), code, _ptr(draft_tokens), _ptr(uniforms), B,
+                                          K, V, float(temperature), _ptr(out_tokens), _ptr(out_num_accepted),
+                                          _ptr(out_probs), ctypes.c_void_p(sh))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_verify_sample_noalloc")
+    return SampleOutputs(out_tokens, out_num_accepted, out_probs)
 
 
 def verify_sample_staged(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,

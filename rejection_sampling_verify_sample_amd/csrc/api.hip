@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 
 #include "../../include/spec_verify.h"
 #include "params.hpp"
@@ -171,7 +172,8 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
                                  float* out_probs, void* workspace, size_t workspace_bytes, void* stream,
                                  int phases, bool filtered = false, const int32_t* top_k = nullptr,
                                  const float* top_p = nullptr, int32_t* out_kept = nullptr,
-                                 const int32_t* stage_ends = nullptr, int32_t num_stages = -1) {
+                                 const int32_t* stage_ends = nullptr, int32_t num_stages = -1,
+                                 bool check_only = false) {
   if (!sample_shape_ok(B, K, V)) return SPEC_ERR_SHAPE;
   if (num_stages >= 0 && !stages_ok(K, stage_ends, num_stages)) return SPEC_ERR_STAGES;
   if (filtered && V > sv::kMaxFilterV) return SPEC_ERR_FILTER_V;
@@ -192,6 +194,7 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
     return SPEC_ERR_ALIGN;
   const SampleLayout L = sample_layout(B, K, V);
   if (workspace_bytes < L.total) return SPEC_ERR_WORKSPACE;
+  if (check_only) return SPEC_OK;
 
   sv::SampleParams P{};
   P.target = target_logits;
@@ -265,6 +268,56 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
 SPEC_EXPORT spec_status spec_verify_sample(SPEC_SAMPLE_ARGS) {
   return verify_sample_phases(SPEC_SAMPLE_FWD, sv::kPhaseAll);
 }
+// ---------------------------------------------------------------- the verify without a caller workspace
+
+// The workspace of spec_verify_sample_noalloc: one fixed device array per GPU,
+// held until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: the device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (null on a HIP error).
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+SPEC_EXPORT size_t spec_verify_sample_noalloc_max_bytes(void) { return SPEC_NOALLOC_SCRATCH_BYTES; }
+
+SPEC_EXPORT spec_status spec_verify_sample_noalloc(const void* target_logits, const void* draft_logits,
+                                                   int32_t dtype, const int32_t* draft_tokens,
+                                                   const float* uniforms, int32_t B, int32_t K, int32_t V,
+                                                   float temperature, int32_t* out_tokens,
+                                                   int32_t* out_num_accepted, float* out_probs, void* stream) {
+  // every argument check first, with a stand-in workspace, so that no HIP call precedes an argument error
+  if (!sample_shape_ok(B, K, V)) return SPEC_ERR_SHAPE;
+  if (sample_layout(B, K, V).total > SPEC_NOALLOC_SCRATCH_BYTES) return SPEC_ERR_WORKSPACE;
+  static double probe_ws;  // a valid, aligned host pointer: only checked, never passed to a kernel
+  const spec_status st = verify_sample_phases(target_logits, draft_logits, dtype, draft_tokens, uniforms, B, K, V,
+                                              temperature, out_tokens, out_num_accepted, out_probs, &probe_ws,
+                                              SPEC_NOALLOC_SCRATCH_BYTES, stream, sv::kPhaseAll, false, nullptr,
+                                              nullptr, nullptr, nullptr, -1, /*check_only=*/true);
+  if (st != SPEC_OK || B == 0) return st;
+  void* ws = scratch_on_current_device();
+  if (!ws) return SPEC_ERR_HIP;
+  return verify_sample_phases(target_logits, draft_logits, dtype, draft_tokens, uniforms, B, K, V, temperature,
+                              out_tokens, out_num_accepted, out_probs, ws, SPEC_NOALLOC_SCRATCH_BYTES, stream,
+                              sv::kPhaseAll);
+}
+
 SPEC_EXPORT spec_status spec_verify_sample_phases(SPEC_SAMPLE_ARGS, int32_t phases) {
   return verify_sample_phases(SPEC_SAMPLE_FWD, phases);
 }

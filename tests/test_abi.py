@@ -37,7 +37,7 @@ def test_library_is_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     L = ctypes.CDLL(rsv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
@@ -286,3 +286,35 @@ def test_binding_checks_tensors_before_the_library():
                           torch.zeros(2, 3, 2), 1.0)
     with pytest.raises((TypeError, ValueError)):
         rsv.verify_greedy(torch.zeros(1, 2, 3, 8), torch.zeros(1, 2, 3, dtype=torch.int32))
+
+
+def noalloc(**kw):
+    a = dict(target=P, draft=P, dtype=1, tokens=P, uniforms=P, B=4, K=3, V=100, T=1.0, out_tokens=P, out_n=P,
+             out_probs=None, stream=None)
+    a.update(kw)
+    return rsv.lib().spec_verify_sample_noalloc(a["target"], a["draft"], a["dtype"], a["tokens"], a["uniforms"],
+                                                a["B"], a["K"], a["V"], a["T"], a["out_tokens"], a["out_n"],
+                                                a["out_probs"], a["stream"])
+
+
+def test_noalloc_limit_is_the_header_value():
+    assert rsv.lib().spec_verify_sample_noalloc_max_bytes() == 4 << 20
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), ERR_SHAPE), (dict(K=65), ERR_SHAPE), (dict(V=0), ERR_SHAPE),
+    (dict(dtype=2), ERR_DTYPE), (dict(T=0.0), ERR_TEMP), (dict(T=float("nan")), ERR_TEMP),
+    (dict(target=None), ERR_NULL), (dict(draft=None), ERR_NULL), (dict(uniforms=None), ERR_NULL),
+    (dict(out_tokens=None), ERR_NULL), (dict(out_n=None), ERR_NULL),
+    (dict(target=P + 1), ERR_ALIGN), (dict(out_probs=P + 2), ERR_ALIGN),
+    # sizes whose workspace exceeds the fixed scratch are refused before any HIP call
+    (dict(B=4096, K=8, V=128256), ERR_WS), (dict(B=1024, K=4, V=152064), ERR_WS),
+    (dict(B=0), OK), (dict(B=0, target=None), OK),
+])
+def test_noalloc_argument_checks(kw, expect):
+    assert noalloc(**kw) == expect
+
+
+def test_noalloc_scratch_covers_the_four_sampling_workloads():
+    for B, K, V in ((1, 4, 32000), (8, 5, 32000), (64, 8, 128256), (256, 4, 152064)):
+        assert 0 < rsv.sample_workspace_size(B, K, V) <= rsv.lib().spec_verify_sample_noalloc_max_bytes()
