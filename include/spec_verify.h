@@ -121,6 +121,32 @@ spec_status spec_verify_sample(const void* target_logits, const void* draft_logi
                                int32_t* out_num_accepted, float* out_probs, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace spec_row_stats needs for these sizes (0 for invalid sizes). */
+size_t spec_row_stats_workspace_size(int32_t rows, int32_t V);
+
+/*
+ * Softmax statistics of logit rows, as the verify computes them for p and q
+ * ("Speculative Decoding —— LLM推理优化技术（一）" §2.1: p and q are softmaxes of
+ * whole rows; §4: the temperature divides the logits; kwkr.cn notes §3.2: fp32
+ * probabilities). With c = fl32(log2(e) / temperature) and R = fl32(m * c):
+ *   out_max[r] = m, the row's largest logit (-inf when none is finite);
+ *   out_sum[r] = S = sum_v 2^(fl32(x_v * c - R)), accumulated as the verify does
+ *                (fp32 per thread, fp64 across threads and segments);
+ * so the row's law is p_v = 2^(x_v * c - R) / S. The same streaming reduction as
+ * the verify's pass 1; a caller (or a test) can rebuild every probability of a
+ * row from these two numbers.
+ *
+ * logits     [rows, V] dtype (device), row-major, aligned to its element size.
+ * rows, V    0 <= rows <= SPEC_MAX_ROWS, 1 <= V <= SPEC_MAX_V; rows = 0 is a no-op.
+ * out_max    [rows] float (device); out_sum [rows] double (device, 8-byte aligned).
+ * workspace  at least spec_row_stats_workspace_size(rows, V) bytes; needs no
+ *            initialisation.
+ * Errors as spec_verify_sample (shape, dtype, temperature, NULL, alignment,
+ * workspace), all before any HIP call.
+ */
+spec_status spec_row_stats(const void* logits, int32_t dtype, int32_t rows, int32_t V, float temperature,
+                           float* out_max, double* out_sum, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * spec_verify_sample for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation.

@@ -47,6 +47,9 @@ _SIGNATURES = {
                                                   _i32, ctypes.c_float, _c_void_p, _c_void_p, _c_void_p,
                                                   _c_void_p, _size_t, _c_void_p, _c_void_p, _c_void_p,
                                                   _c_void_p, _i32]),
+    "spec_row_stats_workspace_size": (_size_t, [_i32, _i32]),
+    "spec_row_stats": (_i32, [_c_void_p, _i32, _i32, _i32, ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _size_t,
+                              _c_void_p]),
     "spec_verify_sample_noalloc_max_bytes": (_size_t, []),
     "spec_verify_sample_noalloc": (_i32, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                           ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
@@ -189,6 +192,34 @@ def verify_sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch
     """
     return _verify_sample(target, draft, draft_tokens, uniforms, temperature, out_tokens, out_num_accepted,
                           out_probs, want_probs, workspace, stream, phases, None)
+
+
+def row_stats(logits: torch.Tensor, temperature: float, *, workspace: torch.Tensor | None = None,
+              stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """spec_row_stats: (row maximum m [rows] float32, denominator S [rows] float64) of logits [rows, V].
+
+    Row r's law is p_v = 2^(x_v * c - fl32(m * c)) / S with c = fl32(log2(e) / T).
+    """
+    if logits.dim() != 2:
+        raise ValueError("logits must be [rows, V]")
+    rows, V = logits.shape
+    dev = logits.device
+    _check(logits, "logits", dev)
+    code = _dtype_code(logits)
+    out_max = torch.empty((rows,), dtype=torch.float32, device=dev)
+    out_sum = torch.empty((rows,), dtype=torch.float64, device=dev)
+    sh = _stream_handle(stream, dev)
+    nbytes = int(lib().spec_row_stats_workspace_size(rows, V))
+    if nbytes == 0 and rows > 0:
+        raise SpecVerifyError(-2, "spec_row_stats_workspace_size")
+    if workspace is None:
+        workspace = workspace_for(dev, sh, nbytes)
+    _check(workspace, "workspace", dev, torch.uint8)
+    st = lib().spec_row_stats(_ptr(logits), code, rows, V, float(temperature), _ptr(out_max), _ptr(out_sum),
+                              _ptr(workspace), workspace.numel(), ctypes.c_void_p(sh))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_row_stats")
+    return out_max, out_sum
 
 
 def verify_sample_noalloc(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,

@@ -20,6 +20,7 @@ hipError_t launch_pool_lookup(const PoolParams& P, hipStream_t stream);
 hipError_t launch_sample(const SampleParams& P, bool bf16, bool filtered, int phases, hipStream_t stream);
 hipError_t launch_greedy(const GreedyParams& P, bool bf16, hipStream_t stream);
 hipError_t launch_philox(uint64_t seed, uint64_t round, int32_t B, int32_t K, float* out, hipStream_t stream);
+hipError_t launch_row_stats(const RowStatsParams& P, bool bf16, hipStream_t stream);
 }  // namespace sv
 
 namespace {
@@ -107,6 +108,7 @@ SampleLayout sample_layout(int32_t B, int32_t K, int32_t V) {
   L.total = std::max<size_t>(off, 256);
   return L;
 }
+
 
 GreedyLayout greedy_layout(int32_t B, int32_t G, int32_t N, int32_t V) {
   GreedyLayout L{};
@@ -538,5 +540,65 @@ SPEC_EXPORT spec_status spec_verify_ngram_sample(const void* target_logits, int3
   P.blk = at<float2>(workspace, L.off_blk);
   P.nbmax = L.nbmax;
   const hipError_t e = sv::launch_ngram_sample(P, dtype == SPEC_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- softmax statistics of rows
+
+namespace {
+
+struct RowStatsLayout {
+  int32_t S;
+  size_t off_m, off_s, total;
+};
+
+RowStatsLayout row_stats_layout(int32_t rows, int32_t V) {
+  RowStatsLayout L{};
+  L.S = seg_choice(rows, V, 1024, 8192, seg_max(rows, V), "SPECVERIFY_S1");
+  const size_t p = static_cast<size_t>(rows) * seg_max(rows, V);
+  size_t off = 0;
+  L.off_m = off; off = align256(off + p * sizeof(float));
+  L.off_s = off; off = align256(off + p * sizeof(double));
+  L.total = std::max<size_t>(off, 256);
+  return L;
+}
+
+bool row_stats_shape_ok(int32_t rows, int32_t V) {
+  return rows >= 0 && rows <= SPEC_MAX_ROWS && V >= 1 && V <= SPEC_MAX_V;
+}
+
+}  // namespace
+
+SPEC_EXPORT size_t spec_row_stats_workspace_size(int32_t rows, int32_t V) {
+  if (!row_stats_shape_ok(rows, V)) return 0;
+  return row_stats_layout(rows, V).total;
+}
+
+SPEC_EXPORT spec_status spec_row_stats(const void* logits, int32_t dtype, int32_t rows, int32_t V, float temperature,
+                                       float* out_max, double* out_sum, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (!row_stats_shape_ok(rows, V)) return SPEC_ERR_SHAPE;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
+  if (!(std::isfinite(temperature) && temperature > 0.f)) return SPEC_ERR_TEMPERATURE;
+  const float c = static_cast<float>(1.4426950408889634074 / static_cast<double>(temperature));
+  if (!std::isfinite(c)) return SPEC_ERR_TEMPERATURE;
+  if (rows == 0) return SPEC_OK;
+  if (!logits || !out_max || !out_sum || !workspace) return SPEC_ERR_NULL;
+  const size_t es = dtype == SPEC_BF16 ? 2 : 4;
+  if (!aligned(logits, es) || !aligned(out_max, 4) || !aligned(out_sum, 8) || !aligned(workspace, 8))
+    return SPEC_ERR_ALIGN;
+  const RowStatsLayout L = row_stats_layout(rows, V);
+  if (workspace_bytes < L.total) return SPEC_ERR_WORKSPACE;
+  sv::RowStatsParams P{};
+  P.logits = logits;
+  P.rows = rows;
+  P.V = V;
+  P.c = c;
+  P.S = L.S;
+  P.pm = at<float>(workspace, L.off_m);
+  P.ps = at<double>(workspace, L.off_s);
+  P.out_max = out_max;
+  P.out_sum = out_sum;
+  const hipError_t e = sv::launch_row_stats(P, dtype == SPEC_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

@@ -51,6 +51,7 @@ struct SampleParams {
   uint32_t* info_T;        // [B, 2] thresholds of the rows the draw reads
 };
 
+
 // Kernels of the sampling verify, in stream order.
 enum SamplePhase : int {
   kPhaseRowStats = 1,  // pass 1: online max / sum-exp of target and draft rows 0..K-1
@@ -79,6 +80,19 @@ struct SampleLayout {
 // Filtered verify: masses are summed in fixed point, round(m * 2^40) per entry with
 // m <= 1, in 64-bit integers, so a row may hold at most 2^24 entries.
 constexpr int64_t kMaxFilterV = int64_t(1) << 24;
+
+// ---------------------------------------------------------------- softmax statistics of rows
+
+struct RowStatsParams {
+  const void* logits;      // [rows, V]
+  int32_t rows, V;
+  float c;                 // log2(e) / T, rounded to fp32
+  int32_t S;               // segments per row
+  float* pm;               // [S][rows] segment maxima
+  double* ps;              // [S][rows] segment sums against fl(m*c)
+  float* out_max;          // [rows]
+  double* out_sum;         // [rows]
+};
 
 // ---------------------------------------------------------------- greedy verify
 

@@ -37,7 +37,7 @@ def test_library_is_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     L = ctypes.CDLL(rsv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
@@ -318,3 +318,21 @@ def test_noalloc_argument_checks(kw, expect):
 def test_noalloc_scratch_covers_the_four_sampling_workloads():
     for B, K, V in ((1, 4, 32000), (8, 5, 32000), (64, 8, 128256), (256, 4, 152064)):
         assert 0 < rsv.sample_workspace_size(B, K, V) <= rsv.lib().spec_verify_sample_noalloc_max_bytes()
+
+
+def rowstats(**kw):
+    a = dict(logits=P, dtype=1, rows=5, V=100, T=1.0, out_max=P, out_sum=P, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return rsv.lib().spec_row_stats(a["logits"], a["dtype"], a["rows"], a["V"], a["T"], a["out_max"], a["out_sum"],
+                                    a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(rows=-1), ERR_SHAPE), (dict(V=0), ERR_SHAPE), (dict(rows=(1 << 24) + 1), ERR_SHAPE),
+    (dict(dtype=3), ERR_DTYPE), (dict(T=0.0), ERR_TEMP), (dict(T=float("inf")), ERR_TEMP),
+    (dict(logits=None), ERR_NULL), (dict(out_max=None), ERR_NULL), (dict(out_sum=None), ERR_NULL),
+    (dict(ws=None), ERR_NULL), (dict(logits=P + 1), ERR_ALIGN), (dict(out_sum=P + 4), ERR_ALIGN),
+    (dict(ws_bytes=8), ERR_WS), (dict(rows=0), OK), (dict(rows=0, logits=None), OK),
+])
+def test_row_stats_argument_checks(kw, expect):
+    assert rowstats(**kw) == expect

@@ -168,7 +168,7 @@ def test_staged_parity_with_oracle(cfg, kw, stages, rounds):
 
 @pytest.mark.parametrize("B", [32, 128])
 def test_staged_matches_one_pass_on_the_gpu(B):
-    """With the same segment counts the staged and one-pass verifies take the same
+    """With the same segment counts the staged and the one-pass verify take the same
     row statistics, so every token and count agrees bit for bit."""
     s = make_sample_inputs(3, 1, B=B, V=20000)
     t = sample_tensors(s, DEV)
