@@ -253,12 +253,16 @@ size_t spec_verify_sample_filtered_workspace_size(int32_t B, int32_t K, int32_t 
  * token outside its draft row's kept set has q' = 0 (accepted when p' > 0); the
  * residual max(0, p'_n - q'_n), its zero-mass fallback p'_n and the bonus law p'_K
  * all lie inside the target row's kept set. out_probs holds p'_i(x_i), q'_i(x_i).
- * Unlike spec_verify_sample, every row is read, the bonus row too. A row of a
- * batch row with 0 < k <= 64 is read once: entries above a running bound are
- * collected on chip and the top-k and top-p cuts are taken from them. Every other
- * row (top-p alone, k > 64, or a one-pass row whose collected entries overflow the
- * on-chip buffer) takes an exact radix select, which reads the row once for its
- * maximum and once per radix digit of each active filter (bf16: 2 digits, fp32: 3).
+ * Unlike spec_verify_sample, every row is read, the bonus row too, and normally
+ * once. With 0 < k <= 64 the entries above a running bound are collected on chip
+ * and both cuts are taken from them. With top-p alone or k > 64 the first step of
+ * the read sets a bound meant to lie below the cut; the entries above it are kept
+ * on chip (long bf16 rows with top-p alone: a count per bf16 value instead) and the
+ * mass below it is summed, and the cut is taken there when they provably hold it.
+ * A row none of these finishes (the kept entries overflow, or do not hold the
+ * cut) takes an exact radix select, which reads the row once for its maximum and
+ * once per radix digit of each active filter (bf16: 2 digits, fp32: 3). Results
+ * do not depend on which path a row took.
  */
 spec_status spec_verify_sample_filtered(const void* target_logits, const void* draft_logits, int32_t dtype,
                                         const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t K,

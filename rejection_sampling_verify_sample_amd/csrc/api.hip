@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "../../include/spec_verify.h"
@@ -103,7 +104,7 @@ SampleLayout sample_layout(int32_t B, int32_t K, int32_t V) {
   L.off_fR = off; off = align256(off + rows * sizeof(float));
   L.off_fS = off; off = align256(off + rows * sizeof(double));
   L.off_fthr = off; off = align256(off + rows * sizeof(uint32_t));
-  L.off_fcnt = off; off = align256(off + rows * sizeof(uint32_t));
+  L.off_fflag = off; off = align256(off + rows * sizeof(uint32_t));
   L.off_infoT = off; off = align256(off + static_cast<size_t>(B) * 2 * sizeof(uint32_t));
   L.total = std::max<size_t>(off, 256);
   return L;
@@ -250,7 +251,10 @@ spec_status verify_sample_phases(const void* target_logits, const void* draft_lo
     P.f_R = at<float>(workspace, L.off_fR);
     P.f_S = at<double>(workspace, L.off_fS);
     P.f_thr = at<uint32_t>(workspace, L.off_fthr);
-    P.f_cnt = at<uint32_t>(workspace, L.off_fcnt);
+    P.f_flag = at<uint32_t>(workspace, L.off_fflag);
+    // SPECVERIFY_FILTER=multi sends every row to the multi-pass select (tuning, testing)
+    const char* fm = std::getenv("SPECVERIFY_FILTER");
+    P.filt_multi = (fm && std::strcmp(fm, "multi") == 0) ? 1 : 0;
     P.info_T = at<uint32_t>(workspace, L.off_infoT);
   }
   const hipError_t e =

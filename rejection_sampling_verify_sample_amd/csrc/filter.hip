@@ -49,6 +49,10 @@ constexpr int kFiltFastK = 64;   // the largest k it takes: one running maximum 
 #define SV_FAST_UNROLL 4
 #endif
 constexpr int kFastUnroll = SV_FAST_UNROLL;  // 16-byte vectors per thread per step of the one-pass read
+#ifndef SV_WIDE_UNROLL
+#define SV_WIDE_UNROLL 3
+#endif
+constexpr int kWideUnroll = SV_WIDE_UNROLL;  // the same for the top-p / large top-k read (its sample is one step)
 
 // round(m * 2^40) for 0 <= m <= 1, from the bits of m (integer arithmetic only).
 __device__ __forceinline__ uint64_t to_fixed(float m) {
@@ -61,6 +65,14 @@ __device__ __forceinline__ uint64_t to_fixed(float m) {
   const int rs = -sh;
   if (rs > 24) return 0;
   return (mant + (uint64_t(1) << (rs - 1))) >> rs;
+}
+
+// 2^d for a double d of moderate size: the hardware exponential of the fraction,
+// then an exact scaling by the integer part (exact when d is an integer). Its
+// relative error is that of one fp32 exponential.
+__device__ __forceinline__ double pow2d(double d) {
+  const double n = floor(d);
+  return ldexp(static_cast<double>(exp2_hw(static_cast<float>(d - n))), static_cast<int>(n));
 }
 
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
@@ -288,11 +300,11 @@ __device__ __forceinline__ uint32_t wave_scan_add_u32(uint32_t v) {
 
 // Reserve room for `cnt` values of every lane of the wave (lane order): one wave
 // scan and one LDS atomic. Returns the lane's first slot. Every lane takes part.
-__device__ __forceinline__ uint32_t reserve_slots(FastBuf& fb, uint32_t cnt) {
+__device__ __forceinline__ uint32_t reserve_slots(uint32_t& nbuf, uint32_t cnt) {
   const int lane = threadIdx.x & 63;
   const uint32_t incl = wave_scan_add_u32(cnt);
   uint32_t base = 0;
-  if (lane == 63 && incl) base = atomicAdd(&fb.nbuf, incl);
+  if (lane == 63 && incl) base = atomicAdd(&nbuf, incl);
   base = __builtin_amdgcn_readlane(base, 63);
   return base + incl - cnt;
 }
@@ -300,7 +312,7 @@ __device__ __forceinline__ uint32_t reserve_slots(FastBuf& fb, uint32_t cnt) {
 // Append the lane's values whose bit is set in `take` (bit i for x[i]).
 template <int N>
 __device__ __forceinline__ void append_masked(FastBuf& fb, const float (&x)[N], uint32_t take) {
-  uint32_t pos = reserve_slots(fb, static_cast<uint32_t>(__popc(take)));
+  uint32_t pos = reserve_slots(fb.nbuf, static_cast<uint32_t>(__popc(take)));
 #pragma unroll
   for (int i = 0; i < N; ++i)
     if ((take >> i) & 1u) {
@@ -372,7 +384,7 @@ __device__ uint32_t collect_candidates(const T* row, int64_t V, int kk, FastBuf&
         tk[u] = t;
         cnt += __popc(t);
       }
-      uint32_t pos = reserve_slots(fb, cnt);
+      uint32_t pos = reserve_slots(fb.nbuf, cnt);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         for (uint32_t t = tk[u]; t != 0u; t &= t - 1u) {
@@ -442,15 +454,15 @@ __device__ void sort_keys_desc(uint32_t* key, int npad) {
   }
 }
 
-// Smallest value over the block (thread 0's argument order is irrelevant).
-__device__ __forceinline__ int32_t block_min_i32(FastBuf& fb, int32_t v) {
+// Smallest value over the block, every thread gets it (wmin: one slot per wave).
+__device__ __forceinline__ int32_t block_min_i32(int32_t* wmin, int32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-  if ((threadIdx.x & 63) == 0) fb.wmin[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) wmin[threadIdx.x >> 6] = v;
   __syncthreads();
-  int32_t r = fb.wmin[0];
+  int32_t r = wmin[0];
 #pragma unroll
-  for (int o = 1; o < kFiltBlock / 64; ++o) r = min(r, fb.wmin[o]);
+  for (int o = 1; o < kFiltBlock / 64; ++o) r = min(r, wmin[o]);
   __syncthreads();
   return r;
 }
@@ -688,12 +700,6 @@ __device__ bool wave_cut(FastBuf& fb, int n, int kk, float pp, MassF&& mass, uin
   return true;
 }
 
-// Top-k with a small k reads the row once.
-__device__ __forceinline__ bool fast_eligible(const SampleParams& P, int b) {
-  const int kk = P.top_k ? P.top_k[b] : 0;
-  return kk > 0 && kk < P.V && kk <= kFiltFastK;
-}
-
 // The cut of a one-pass row from its candidates (n <= kFiltCap order keys in fb.key;
 // M the row maximum).
 template <typename T>
@@ -767,7 +773,7 @@ __device__ void cut_candidates(const SampleParams& P, const FiltRow& r, FastBuf&
     }
     // a crossing always exists (the last kept entry brings the run to Z >= p * Z); the
     // clamp only guards the index
-    const uint32_t tp = fb.key[min(block_min_i32(fb, first), npad - 1)];
+    const uint32_t tp = fb.key[min(block_min_i32(fb.wmin, first), npad - 1)];
     uint64_t ms2 = 0, cn2 = 0;
     for (int i = i0; i < i1; ++i) {
       const uint32_t key = fb.key[i];
@@ -786,40 +792,788 @@ __device__ void cut_candidates(const SampleParams& P, const FiltRow& r, FastBuf&
   __syncthreads();  // shared memory is reused by the next row
 }
 
-// One-pass path of a row: the candidates, then the cut. The candidate count goes to
-// f_cnt, so that k_filter_rows skips the rows finished here.
+// One-pass top-k path of a row (0 < k <= 64): the candidates, then the cut. False
+// (nothing written) when the candidates overflow the buffer.
 template <typename T>
-__device__ void filter_row_fast(const SampleParams& P, int64_t task, FastBuf& fb) {
-  const FiltRow r = filt_row(P, task, sizeof(T));
-  if (!fast_eligible(P, r.b)) return;
-  const int kk = P.top_k[r.b];
-  const float pp = P.top_p ? P.top_p[r.b] : 1.f;
-  const float xl = filt_token_logit<T>(P, r);
+__device__ __forceinline__ bool filter_row_fast(const SampleParams& P, const FiltRow& r, FastBuf& fb, int kk, float pp, float xl) {
   float M;
   uint32_t lbound;
   const uint32_t n = collect_candidates(static_cast<const T*>(r.row), P.V, kk, fb, M, lbound);
-  if (threadIdx.x == 0) P.f_cnt[r.fr] = n;
   if (n > static_cast<uint32_t>(kFiltCap)) {
-    __syncthreads();  // the buffer is reused by the next row
-    return;
+    __syncthreads();  // shared memory is reused by the multi-pass select
+    return false;
   }
   cut_candidates<T>(P, r, fb, static_cast<int>(n), M, kk, pp, xl, lbound);
+  return true;
 }
 
-// The multi-pass select of a row the one-pass path does not finish (no small top-k,
-// or a half whose candidates overflowed).
+// ---------------------------------------------------------------- one-read top-p and large top-k
+//
+// A row with top-p on, or with top-k and k > 64, is read once as well. The first
+// step of the read (kFastUnroll * 256 16-byte vectors) doubles as a sample: a
+// histogram of its entries by their distance below the sample maximum, in bins of
+// half a doubling of the tempered mass, gives a bound L meant to lie below the
+// row's cut. Top-p alone takes the smallest L whose sample mass above it reaches
+// (1 + p) / 2 of the sample's mass; top-k the smallest L whose sample count above
+// it, scaled to the row, reaches 1.25k + 16. The read then keeps every entry >= L
+// in an LDS buffer as an order key and, for top-p alone, sums the mass of the
+// others. The cut runs on the buffer: a radix select over the key span of the
+// candidates, with the masses of the multi-pass select (the same fixed point
+// against the same reference). It is exact whenever the buffer holds the cut: top-k
+// needs k candidates; top-p alone needs the candidates' mass to reach p * Z, where
+// Z adds the rest of the row's mass. A row that fails either test, whose buffer
+// overflows, or whose sample predicts an overflow, takes the multi-pass select.
+
+constexpr int kWideWords = 6144;  // candidate buffer: 24 KB of keys (16-bit keys for bf16 rows, 32-bit for fp32)
+constexpr int kSampleBins = 64;   // half-doubling bins below the sample maximum
+constexpr int kWideBins = 256;    // radix digit of the cut
+constexpr uint32_t kNoPick = 0xFFFFFFFFu;
+static_assert(kWideBins == kFiltBlock, "one bin per thread in the scans");
+
+// Stored keys of the buffer. fp32 rows: the 32-bit order key.
 template <typename T>
-__device__ void filter_row_task(const SampleParams& P, int64_t task, FiltShared& sh) {
-  const FiltRow r = filt_row(P, task, sizeof(T));
-  if (fast_eligible(P, r.b) && P.f_cnt[r.fr] <= static_cast<uint32_t>(kFiltCap)) return;
+struct WideKey {
+  static constexpr int kCap = kWideWords;
+  __device__ __forceinline__ static uint32_t get(const uint32_t* w, int i) { return w[i]; }
+  __device__ __forceinline__ static void put(uint32_t* w, uint32_t i, float x) { w[i] = order_key(x); }
+  __device__ __forceinline__ static uint32_t full(uint32_t k) { return k; }
+  __device__ __forceinline__ static uint32_t thr(uint32_t k) { return k; }
+};
+// bf16 rows: the upper half of the order key (the lower half is 0 for a value with
+// its sign clear, all ones otherwise), so twice as many fit; the threshold takes the
+// form the multi-pass select gives bf16 rows (low 10 bits clear).
+template <>
+struct WideKey<bf16_t> {
+  static constexpr int kCap = 2 * kWideWords;
+  __device__ __forceinline__ static uint32_t get(const uint32_t* w, int i) {
+    return reinterpret_cast<const uint16_t*>(w)[i];
+  }
+  __device__ __forceinline__ static void put(uint32_t* w, uint32_t i, float x) {
+    reinterpret_cast<uint16_t*>(w)[i] = static_cast<uint16_t>(order_key(x) >> 16);
+  }
+  __device__ __forceinline__ static uint32_t full(uint32_t k) { return (k << 16) | ((k & 0x8000u) ? 0u : 0xFFFFu); }
+  __device__ __forceinline__ static uint32_t thr(uint32_t k) { return full(k) & ~0x3FFu; }
+};
+
+constexpr int kHistKeys = 4096;   // long bf16 rows: one count per key, over 32 binades
+constexpr int kHighRoom = 256;    // the counted keys reach two binades above the sample maximum
+constexpr int kHighCap = 256;     // entries above them, kept as keys
+
+struct WideBuf {
+  union {
+    uint32_t key[kWideWords];  // candidate keys
+    struct {
+      uint32_t cnt[kHistKeys];  // entries per bf16 key, from the bottom key up
+      uint32_t high[kHighCap];  // keys above the counted ones
+    } h;
+  };
+  uint32_t cnt[kWideBins];
+  unsigned long long mass[kWideBins];
+  uint32_t nbuf;
+  float L;  // the candidate bound (-inf: every entry)
+  int go;   // 0: the sample predicts more candidates than the buffer holds
+  uint32_t pick_bin;
+  uint64_t pick_above_cnt, pick_above_mass;
+  float wmax[kFiltBlock / 64];
+  int32_t wmin[kFiltBlock / 64];
+  uint32_t wkey[2][kFiltBlock / 64];
+  double wsum[kFiltBlock / 64];
+};
+
+// The candidate bound from the sample: every thread's vectors of the first step.
+template <typename T, int U>
+__device__ void wide_bound(WideBuf& wb, const u32x4 (&raw)[U], int64_t V, int kk, bool k_on, float pp, float c) {
+  constexpr int VEC = Elem<T>::kVec;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float sm = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float y[VEC];
+    Elem<T>::unpack(raw[u], y);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) sm = fmaxf(sm, y[e]);
+  }
+  sm = wave_max(sm);
+  wb.cnt[threadIdx.x] = 0;
+  wb.mass[threadIdx.x] = 0;
+  if (lane == 0) wb.wmax[w] = sm;
+  __syncthreads();
+  float Ms = wb.wmax[0];
+#pragma unroll
+  for (int o = 1; o < kFiltBlock / 64; ++o) Ms = fmaxf(Ms, wb.wmax[o]);
+  if (Ms > -INFINITY) {
+    const float c2 = 2.f * c;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float y[VEC];
+      Elem<T>::unpack(raw[u], y);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float d = (Ms - y[e]) * c2;  // NaN and +inf fail the test
+        if (d < static_cast<float>(kSampleBins)) {
+          const int j = static_cast<int>(d);
+          atomicAdd(&wb.cnt[j], 1u);
+          // the sample's masses against its maximum, in units of 2^-24 (deterministic sums)
+          atomicAdd(&wb.mass[j], static_cast<unsigned long long>(exp2_hw((y[e] - Ms) * c) * 16777216.f + 0.5f));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    float L = -INFINITY;
+    int go = V <= WideKey<T>::kCap;
+    if (Ms > -INFINITY) {
+      const double cn = wave_scan_add(static_cast<double>(wb.cnt[lane]));  // bins 0..lane: within (lane+1)/2 doublings
+      const double ms = wave_scan_add(static_cast<double>(wb.mass[lane]));
+      const double scale = static_cast<double>(V) / static_cast<double>(U * kFiltBlock * VEC);
+      // top-k: the sample count expected above the k-th largest, plus three of its
+      // standard deviations and a little more; top-p: half of the way from p to 1
+      const double a = static_cast<double>(kk) / scale;
+      const bool hit = k_on ? cn >= a + 3.0 * sqrt(a) + 4.0
+                            : ms >= 0.5 * (1.0 + static_cast<double>(fmaxf(pp, 0.f))) * lane_d(ms, 63);
+      const int j = first_lane(hit);
+      if (j < 64) {
+        L = Ms - static_cast<float>(j + 1) * 0.5f / c;
+        go = lane_d(cn, j) * scale <= 0.9 * static_cast<double>(WideKey<T>::kCap);
+      }
+    }
+    if (lane == 0) {
+      wb.L = L;
+      wb.go = go;
+    }
+  }
+  __syncthreads();
+}
+
+// Append the lane's values whose bit is set in `take` to the buffer (lane order).
+template <typename T, int N>
+__device__ __forceinline__ void wide_append(WideBuf& wb, const float (&x)[N], uint32_t take) {
+  uint32_t pos = reserve_slots(wb.nbuf, static_cast<uint32_t>(__popc(take)));
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if ((take >> i) & 1u) {
+      if (pos < static_cast<uint32_t>(WideKey<T>::kCap)) WideKey<T>::put(wb.key, pos, x[i]);
+      ++pos;
+    }
+}
+
+// Read a wide-path row once: its maximum, the candidates (every entry >= L, as keys
+// in wb.key; n_out of them, more than the buffer holds on an overflow) and, with
+// need_rest, each thread's sum of 2^(x*c - fl(L*c)) over its other entries. False
+// when the sample sends the row to the multi-pass select.
+template <typename T, bool need_rest>
+__device__ bool wide_collect(const T* row, int64_t V, WideBuf& wb, int kk, bool k_on, float pp, float c,
+                             float& rowmax, float& L_out, double& rest_out, uint32_t& n_out) {
+  constexpr int VEC = Elem<T>::kVec;
+  constexpr int BS = kFiltBlock, U = kWideUnroll, W = kFiltBlock / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) wb.nbuf = 0;
+  const int64_t h = head_elems(row, V);
+  const int64_t nvec = (V - h) / VEC;
+  const u32x4* vb = reinterpret_cast<const u32x4*>(row + h);
+  const int64_t nsteps = nvec / (U * BS);
+  // a row longer than the buffer has at least one whole step (V > 8192 entries
+  // leaves more than 2047 vectors, and a step is 1024), which is the sample
+  const bool sampling = V > WideKey<T>::kCap;
+  float L = -INFINITY, Lc = -INFINITY;
+  float m = -INFINITY;
+  double rest = 0.0;
+  if (!sampling) __syncthreads();  // nbuf = 0 before any append (the sample's barriers order it otherwise)
+  for (int64_t s = 0; s < nsteps; ++s) {
+    u32x4 cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = load_stream(vb + s * (U * BS) + threadIdx.x + u * BS);
+    if (s == 0 && sampling) {
+      wide_bound<T, U>(wb, cur, V, kk, k_on, pp, c);
+      if (!wb.go) return false;  // uniform
+      L = wb.L;
+      Lc = L * c;
+    }
+    uint32_t tk[U];
+    uint32_t cnt = 0;
+    float rs = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float y[VEC];
+      Elem<T>::unpack(cur[u], y);
+      uint32_t t = 0;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        m = fmaxf(m, y[e]);
+        t |= (y[e] >= L ? 1u : 0u) << e;
+        if (need_rest) rs += (y[e] < L) ? exp2_hw(fmaf(y[e], c, -Lc)) : 0.f;
+      }
+      tk[u] = t;
+      cnt += __popc(t);
+    }
+    rest += static_cast<double>(rs);
+    uint32_t pos = reserve_slots(wb.nbuf, cnt);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      for (uint32_t t = tk[u]; t != 0u; t &= t - 1u) {
+        if (pos < static_cast<uint32_t>(WideKey<T>::kCap))
+          WideKey<T>::put(wb.key, pos, Elem<T>::lane_elem(cur[u], __ffs(t) - 1));
+        ++pos;
+      }
+    }
+  }
+  // the last vectors, one per thread, then the scalar head (lanes 0-7 of wave 0) and
+  // tail (lanes 8-15): every lane of each wave takes part in the appends
+  for (int64_t base = nsteps * (U * BS); base < nvec; base += BS) {
+    const int64_t vr = base + threadIdx.x;
+    const bool in = vr < nvec;
+    float x[VEC];
+    if (in) {
+      Elem<T>::unpack(load_stream(vb + vr), x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) x[e] = -INFINITY;
+    }
+    uint32_t take = 0;
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      m = fmaxf(m, x[e]);
+      take |= (in && x[e] >= L ? 1u : 0u) << e;
+      if (need_rest) rs += (in && x[e] < L) ? exp2_hw(fmaf(x[e], c, -Lc)) : 0.f;
+    }
+    rest += static_cast<double>(rs);
+    wide_append<T>(wb, x, take);
+  }
+  if (w == 0) {
+    const int64_t tail_lo = h + nvec * VEC;
+    const int64_t e = lane < 8 ? lane : tail_lo + (lane - 8);
+    const bool in = lane < 8 ? lane < h : (lane < 16 && e < V);
+    float x[1];
+    x[0] = in ? Elem<T>::get(row, e) : -INFINITY;
+    m = fmaxf(m, x[0]);
+    if (need_rest && in && x[0] < L) rest += static_cast<double>(exp2_hw(fmaf(x[0], c, -Lc)));
+    wide_append<T>(wb, x, (in && x[0] >= L) ? 1u : 0u);
+  }
+  const float wm = wave_max(m);
+  if (lane == 0) wb.wmax[w] = wm;
+  __syncthreads();
+  float M = wb.wmax[0];
+#pragma unroll
+  for (int o = 1; o < W; ++o) M = fmaxf(M, wb.wmax[o]);
+  rowmax = M;
+  L_out = L;
+  rest_out = rest;
+  n_out = wb.nbuf;
+  return true;
+}
+
+// Sum of one fp64 value per thread over the block, in a fixed order (every thread gets it).
+__device__ __forceinline__ double block_sum_f64(WideBuf& wb, double v) {
+  const double s = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) wb.wsum[threadIdx.x >> 6] = s;
+  __syncthreads();
+  double t = wb.wsum[0];
+#pragma unroll
+  for (int o = 1; o < kFiltBlock / 64; ++o) t += wb.wsum[o];
+  __syncthreads();
+  return t;
+}
+
+// Histogram of the digit (key - base) >> shift & 255 over the candidates with key >=
+// lo whose digits above it equal `prefix` (every candidate at the top level); with
+// MASS also their fixed-point masses. The scan's pick is reset to kNoPick.
+template <typename T, bool MASS, typename MassF>
+__device__ void hist_wide(WideBuf& wb, int n, uint32_t base, int shift, bool top, uint32_t prefix, uint32_t lo,
+                          MassF&& mass) {
+  wb.cnt[threadIdx.x] = 0;
+  wb.mass[threadIdx.x] = 0;
+  if (threadIdx.x == 0) wb.pick_bin = kNoPick;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += kFiltBlock) {
+    const uint32_t k = WideKey<T>::get(wb.key, i);
+    const uint32_t d = k - base;
+    // below the top level shift + 8 <= 24
+    if (k < lo || (!top && (d >> (shift + 8)) != prefix)) continue;
+    const int b = static_cast<int>((d >> shift) & 255u);
+    atomicAdd(&wb.cnt[b], 1u);
+    if (MASS) atomicAdd(&wb.mass[b], static_cast<unsigned long long>(mass(k)));
+  }
+  __syncthreads();
+}
+
+// Scan the 256 bins from the top (thread t holds bin 255 - t) and pick, as
+// scan_hist does, the bin where the count from the top reaches r (COUNT) or the
+// first bin holding entries where A0 plus the mass from the top reaches P (MASS;
+// P <= 0: the first bin holding entries). No bin qualifies: the pick stays kNoPick.
+template <bool MASS>
+__device__ void scan_wide(WideBuf& wb, uint64_t r, double P, uint64_t A0) {
+  const int b = kWideBins - 1 - static_cast<int>(threadIdx.x);
+  const uint64_t c = wb.cnt[b], m = wb.mass[b];
+  uint64_t total;
+  const uint64_t ec = block_excl_u64(c, total);
+  const uint64_t em = block_excl_u64(m, total);
+  bool mine;
+  if (MASS) {
+    mine = c > 0 && ((P <= 0.0) ? ec == 0
+                                : (static_cast<double>(A0 + em) < P && static_cast<double>(A0 + em + m) >= P));
+  } else {
+    mine = ec < r && ec + c >= r;
+  }
+  if (mine) {
+    wb.pick_bin = static_cast<uint32_t>(b);
+    wb.pick_above_cnt = ec;
+    wb.pick_above_mass = em;
+  }
+  __syncthreads();
+}
+
+// The cut of a wide-path row from its n candidates: top-k (the k-th largest key),
+// then top-p on the top-k law, or on the whole row when top-k is off (the row's mass
+// outside the buffer is Zrest). False (nothing written) when the buffer does not
+// hold the cut. Results as in the multi-pass select.
+template <typename T>
+__device__ bool wide_cut(WideBuf& wb, int n, int kk, bool k_on, float pp, bool p_on, float c, float Rf,
+                         uint64_t Zrest, uint32_t& thr_out, uint64_t& kept_n, uint64_t& kept_m) {
+  using WK = WideKey<T>;
+  const int w = threadIdx.x >> 6;
+  auto mass = [&](uint32_t k) { return to_fixed(fminf(exp2_hw(fmaf(key_value(WK::full(k)), c, -Rf)), 1.f)); };
+  // the key span of the candidates sets the digits: (key - kmin) in as few 8-bit digits as it needs
+  uint32_t lo_k = 0xFFFFFFFFu, hi_k = 0u;
+  for (int i = threadIdx.x; i < n; i += kFiltBlock) {
+    const uint32_t k = WK::get(wb.key, i);
+    lo_k = min(lo_k, k);
+    hi_k = max(hi_k, k);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo_k = min(lo_k, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo_k), o, 64)));
+    hi_k = max(hi_k, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi_k), o, 64)));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    wb.wkey[0][w] = lo_k;
+    wb.wkey[1][w] = hi_k;
+  }
+  __syncthreads();
+  uint32_t kmin = wb.wkey[0][0], kmax = wb.wkey[1][0];
+#pragma unroll
+  for (int o = 1; o < kFiltBlock / 64; ++o) {
+    kmin = min(kmin, wb.wkey[0][o]);
+    kmax = max(kmax, wb.wkey[1][o]);
+  }
+  const uint32_t span = kmax - kmin;
+  const int levels = span ? (32 - __clz(static_cast<int>(span)) + 7) / 8 : 1;
+  uint32_t lo = 0;
+  if (k_on) {
+    if (n < kk) return false;  // uniform
+    uint32_t prefix = 0;
+    uint64_t r = static_cast<uint64_t>(kk);
+    for (int lev = 0; lev < levels; ++lev) {
+      hist_wide<T, false>(wb, n, kmin, 8 * (levels - 1 - lev), lev == 0, prefix, 0u, mass);
+      scan_wide<false>(wb, r, 0.0, 0);
+      const uint32_t pb = wb.pick_bin;
+      r -= wb.pick_above_cnt;
+      __syncthreads();  // every thread has read the pick before the next level resets it
+      if (pb == kNoPick) return false;
+      prefix = (prefix << 8) | pb;
+    }
+    lo = kmin + prefix;
+  }
+  uint32_t thr = lo;
+  if (p_on) {
+    uint64_t zc = 0;
+    for (int i = threadIdx.x; i < n; i += kFiltBlock) {
+      const uint32_t k = WK::get(wb.key, i);
+      if (k >= lo) zc += mass(k);
+    }
+    const uint64_t Zc = block_sum_u64(zc);
+    const double Pm = static_cast<double>(pp) * static_cast<double>(Zc + Zrest);
+    if (static_cast<double>(Zc) < Pm) return false;  // the cut lies below the bound
+    uint32_t prefix = 0;
+    uint64_t A0 = 0;
+    for (int lev = 0; lev < levels; ++lev) {
+      hist_wide<T, true>(wb, n, kmin, 8 * (levels - 1 - lev), lev == 0, prefix, lo, mass);
+      scan_wide<true>(wb, 0, Pm, A0);
+      const uint32_t pb = wb.pick_bin;
+      A0 += wb.pick_above_mass;
+      __syncthreads();
+      if (pb == kNoPick) return false;
+      prefix = (prefix << 8) | pb;
+    }
+    thr = kmin + prefix;
+  }
+  uint64_t cn = 0, ms = 0;
+  for (int i = threadIdx.x; i < n; i += kFiltBlock) {
+    const uint32_t k = WK::get(wb.key, i);
+    if (k >= thr) {
+      ++cn;
+      ms += mass(k);
+    }
+  }
+  kept_n = block_sum_u64(cn);
+  kept_m = block_sum_u64(ms);
+  thr_out = WK::thr(thr);
+  return true;
+}
+
+// ---------------------------------------------------------------- long bf16 rows: a count per key
+//
+// A bf16 logit takes one of 2^16 keys, and entries with equal keys have equal
+// masses, so counts per key describe the top of a row exactly, whatever the number
+// of entries there. A long bf16 row takes that route instead of the buffer: the
+// sample maximum's key, plus two binades, is the top of kHistKeys bins of one key
+// each (32 binades), and the read adds each entry to its bin. Entries above the bins
+// (a peak the sample missed) go to a short list of keys; entries below them add their
+// mass to the rest (top-p alone). The cut scans the list, sorted, then the bins from
+// the top; the mass of a bin is its count times the fixed-point mass of its key, the
+// sum the multi-pass select forms entry by entry.
+
+// bf16 key (upper half of the order key) of a widened bf16 value, and its value.
+__device__ __forceinline__ uint32_t key16(float x) { return order_key(x) >> 16; }
+__device__ __forceinline__ float key16_value(uint32_t k) { return key_value(WideKey<bf16_t>::full(k)); }
+constexpr uint32_t kKey16NegInf = 0x007Fu;  // the smallest key of a number
+
+// One thread's entries of a bf16 row: two per 32-bit word, `valid` marking the
+// words that hold entries. Keys are formed two at a time (a negative half flips all
+// 16 bits, a positive one its sign bit; -0 takes the key 0x7FFF, merged into +0's
+// bin after the read). Each entry goes to its bin, to the high list (above the
+// bins, rare: a wave-uniform slow path) or, for top-p alone, to the rest sum.
+template <int NW>
+__device__ __forceinline__ void hist16_words(WideBuf& wb, const uint32_t (&w)[NW], uint32_t valid, uint32_t bottom,
+                                             float hiV, float loV, float c, float Lc, bool need_rest, float& m,
+                                             float& rs) {
+  float vmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    if (!((valid >> j) & 1u)) continue;
+    const uint32_t k2 = w[j] ^ ((((w[j] >> 15) & 0x00010001u) * 0x7FFFu) | 0x80008000u);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint32_t k = half ? (k2 >> 16) : (k2 & 0xFFFFu);
+      const float y = __uint_as_float(half ? (w[j] & 0xFFFF0000u) : (w[j] << 16));
+      vmax = fmaxf(vmax, y);
+      // keys bottom .. bottom + 4095 are counted (NaN keys lie outside: see hist16_collect)
+      const uint32_t d = k - bottom;
+      if (d < static_cast<uint32_t>(kHistKeys)) atomicAdd(&wb.h.cnt[d], 1u);
+      if (need_rest) rs += (y < loV) ? exp2_hw(fmaf(y, c, -Lc)) : 0.f;
+    }
+  }
+  m = fmaxf(m, vmax);
+  if (__ballot(vmax > hiV)) {  // rare: entries above the counted keys
+    uint32_t take = 0;
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const float y = __uint_as_float(half ? (w[j] & 0xFFFF0000u) : (w[j] << 16));
+        take |= (((valid >> j) & 1u) && y > hiV ? 1u : 0u) << (2 * j + half);
+      }
+    uint32_t pos = reserve_slots(wb.nbuf, static_cast<uint32_t>(__popc(take)));
+#pragma unroll
+    for (int e = 0; e < 2 * NW; ++e)
+      if ((take >> e) & 1u) {
+        const uint32_t x = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+        if (pos < static_cast<uint32_t>(kHighCap)) wb.h.high[pos] = key16(__uint_as_float(x));
+        ++pos;
+      }
+  }
+}
+
+// Read a long bf16 row once into the key counts. False when the row needs the
+// multi-pass select (a sample with no finite logit). Outputs: the row maximum, the
+// bottom key, each thread's rest sum 2^(x*c - fl(loV*c)) (need_rest) and loV, the
+// value of the bottom key (-inf when every number is counted).
+__device__ bool hist16_collect(const bf16_t* row, int64_t V, WideBuf& wb, float c, bool need_rest, float& rowmax,
+                               uint32_t& bottom_out, float& loV_out, double& rest_out) {
+  constexpr int VEC = 8, BS = kFiltBlock, U = kWideUnroll, W = kFiltBlock / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t h = head_elems(row, V);
+  const int64_t nvec = (V - h) / VEC;
+  const u32x4* vb = reinterpret_cast<const u32x4*>(row + h);
+  const int64_t nsteps = nvec / (U * BS);  // >= 1: the caller takes rows longer than the buffer
+  if (threadIdx.x == 0) wb.nbuf = 0;
+  for (int i = threadIdx.x; i < kHistKeys; i += BS) wb.h.cnt[i] = 0;
+  u32x4 cur[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) cur[u] = load_stream(vb + threadIdx.x + u * BS);
+  float sm = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float y[VEC];
+    Elem<bf16_t>::unpack(cur[u], y);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) sm = fmaxf(sm, y[e]);
+  }
+  sm = wave_max(sm);
+  if (lane == 0) wb.wmax[w] = sm;
+  __syncthreads();
+  float Ms = wb.wmax[0];
+#pragma unroll
+  for (int o = 1; o < W; ++o) Ms = fmaxf(Ms, wb.wmax[o]);
+  __syncthreads();  // wmax is written again at the end
+  if (!(Ms > -INFINITY)) return false;  // uniform
+  // counted keys: bottom .. bottom + 4095, topped kHighRoom keys above the sample
+  // maximum's key; bottom >= the key of -inf and the top <= the key of +inf, so no
+  // NaN key is counted
+  const uint32_t top0 = min(key16(Ms) + static_cast<uint32_t>(kHighRoom), 0xFF80u);
+  uint32_t bottom = max(top0 >= static_cast<uint32_t>(kHistKeys - 1) ? top0 - (kHistKeys - 1) : 0u, kKey16NegInf);
+  // -0 (key 0x7FFF) and +0 (key 0x8000) fall on the same side of each end of the range
+  if (bottom == 0x8000u) bottom = 0x7FFFu;
+  if (bottom + (kHistKeys - 1) == 0x7FFFu) bottom += 1;
+  const uint32_t top = bottom + (kHistKeys - 1);
+  // above the counted keys: y > hiV; below them: y < loV
+  const float hiV = top < 0xFF80u ? key16_value(top) : INFINITY;  // 0xFF80: the key of +inf
+  const float loV = bottom <= kKey16NegInf ? -INFINITY : key16_value(bottom);
+  const float Lc = loV * c;
+  float m = -INFINITY;
+  double rest = 0.0;
+  for (int64_t s = 0; s < nsteps; ++s) {
+    if (s > 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = load_stream(vb + s * (U * BS) + threadIdx.x + u * BS);
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t wd[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+      hist16_words(wb, wd, 0xFu, bottom, hiV, loV, c, Lc, need_rest, m, rs);
+    }
+    rest += static_cast<double>(rs);
+  }
+  // the last vectors, one per thread, then the scalar head (lanes 0-7 of wave 0) and
+  // tail (lanes 8-15): every lane of each wave takes part
+  for (int64_t base = nsteps * (U * BS); base < nvec; base += BS) {
+    const int64_t vr = base + threadIdx.x;
+    const bool in = vr < nvec;
+    const u32x4 v = in ? load_stream(vb + vr) : u32x4{0u, 0u, 0u, 0u};
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    float rs = 0.f;
+    hist16_words(wb, wd, in ? 0xFu : 0u, bottom, hiV, loV, c, Lc, need_rest, m, rs);
+    rest += static_cast<double>(rs);
+  }
+  if (w == 0) {
+    // one entry per lane, in the low half of a word whose high half is a NaN (not counted)
+    const int64_t tail_lo = h + nvec * VEC;
+    const int64_t e = lane < 8 ? lane : tail_lo + (lane - 8);
+    const bool in = lane < 8 ? lane < h : (lane < 16 && e < V);
+    const uint32_t wd[1] = {in ? (0x7FC00000u | static_cast<uint32_t>(row[e].bits)) : 0u};
+    float rs = 0.f;
+    hist16_words(wb, wd, in ? 1u : 0u, bottom, hiV, loV, c, Lc, need_rest, m, rs);
+    rest += static_cast<double>(rs);
+  }
+  __syncthreads();
+  // -0 was counted under key 0x7FFF: it belongs to +0 (key 0x8000; both or neither are counted)
+  if (threadIdx.x == 0 && bottom <= 0x7FFFu && 0x8000u <= top) {
+    wb.h.cnt[0x8000u - bottom] += wb.h.cnt[0x7FFFu - bottom];
+    wb.h.cnt[0x7FFFu - bottom] = 0;
+  }
+  const float wm = wave_max(m);
+  if (lane == 0) wb.wmax[w] = wm;
+  __syncthreads();
+  float M = wb.wmax[0];
+#pragma unroll
+  for (int o = 1; o < W; ++o) M = fmaxf(M, wb.wmax[o]);
+  rowmax = M;
+  bottom_out = bottom;
+  loV_out = loV;
+  rest_out = rest;
+  return true;
+}
+
+// Scan the key counts from the top bin down to bin lo (thread t holds bins 4095 - 16t
+// down to 4080 - 16t) and pick, as scan_hist does, the bin where the count from the
+// top reaches r (COUNT) or the first bin holding entries where A0 plus the mass from
+// the top reaches P (MASS; P <= 0: the first bin holding entries). No bin qualifies:
+// the pick stays kNoPick.
+template <bool MASS, typename FM>
+__device__ void hist16_scan(WideBuf& wb, int lo, uint64_t r, double P, uint64_t A0, FM&& fm) {
+  constexpr int per = kHistKeys / kFiltBlock;
+  const int hi = kHistKeys - 1 - per * static_cast<int>(threadIdx.x);
+  if (threadIdx.x == 0) wb.pick_bin = kNoPick;
+  uint64_t tc = 0, tm = 0;
+#pragma unroll 1
+  for (int i = 0; i < per && hi - i >= lo; ++i) {
+    const uint64_t n = wb.h.cnt[hi - i];
+    tc += n;
+    if (MASS && n) tm += n * fm(hi - i);
+  }
+  uint64_t total;
+  const uint64_t ec = block_excl_u64(tc, total);
+  const uint64_t em = MASS ? block_excl_u64(tm, total) : 0;
+  bool mine;
+  if (MASS) {
+    mine = tc > 0 && ((P <= 0.0) ? ec == 0
+                                 : (static_cast<double>(A0 + em) < P && static_cast<double>(A0 + em + tm) >= P));
+  } else {
+    mine = ec < r && ec + tc >= r;
+  }
+  if (mine) {
+    uint64_t ca = ec, ma = em;
+  #pragma unroll 1
+  for (int i = 0; i < per && hi - i >= lo; ++i) {
+      const uint64_t n = wb.h.cnt[hi - i];
+      const uint64_t mm = (MASS && n) ? n * fm(hi - i) : 0;
+      const bool hit = MASS ? (n > 0 && (P <= 0.0 || static_cast<double>(A0 + ma + mm) >= P)) : (ca + n >= r);
+      if (hit) {
+        wb.pick_bin = static_cast<uint32_t>(hi - i);
+        wb.pick_above_cnt = ca;
+        wb.pick_above_mass = ma;
+        break;
+      }
+      ca += n;
+      ma += mm;
+    }
+  }
+  __syncthreads();
+}
+
+// The top-p cut of a long bf16 row from its key counts and high list (nh keys);
+// Zrest is the mass below the counted keys. False (nothing written) when they do not
+// hold the cut.
+__device__ bool hist16_cut(WideBuf& wb, uint32_t nh, uint32_t bottom, float pp, float c, float Rf, uint64_t Zrest,
+                           uint32_t& thr_out, uint64_t& kept_n, uint64_t& kept_m) {
+  constexpr int per = kHistKeys / kFiltBlock;
+  auto fmk = [&](uint32_t k) -> uint64_t { return to_fixed(fminf(exp2_hw(fmaf(key16_value(k), c, -Rf)), 1.f)); };
+  auto fm = [&](int b) -> uint64_t { return fmk(bottom + static_cast<uint32_t>(b)); };
+  // the high list, sorted descending (padded with key 0, below every number)
+  int npad = 1;
+  while (npad < static_cast<int>(nh)) npad <<= 1;
+  if (nh > 1) {
+    for (int i = static_cast<int>(nh) + threadIdx.x; i < npad; i += kFiltBlock) wb.h.high[i] = 0u;
+    __syncthreads();
+    sort_keys_desc(wb.h.high, npad);
+  }
+  const int t = threadIdx.x;
+  // the list's masses wait in wb.mass (unused on this path): few registers stay live
+  wb.mass[t] = t < static_cast<int>(nh) ? fmk(wb.h.high[t]) : 0u;
+  const uint64_t Hm = block_sum_u64(wb.mass[t]);
+  uint64_t zb = 0;
+#pragma unroll 1
+  for (int i = 0; i < per; ++i) {
+    const int b = kHistKeys - 1 - per * t - i;
+    const uint64_t n = wb.h.cnt[b];
+    if (n) zb += n * fm(b);
+  }
+  const double Pm = static_cast<double>(pp) * static_cast<double>(Hm + block_sum_u64(zb) + Zrest);
+  uint32_t thr;
+  if (nh > 0 && (Pm <= 0.0 || static_cast<double>(Hm) >= Pm)) {
+    // the cut is in the high list: the first entry (descending) whose running mass reaches p * Z
+    uint64_t Ht;
+    const uint64_t hbefore = block_excl_u64(wb.mass[t], Ht);  // list mass above entry t
+    const bool hit = t < static_cast<int>(nh) && (Pm <= 0.0 || static_cast<double>(hbefore + wb.mass[t]) >= Pm);
+    const int j = block_min_i32(wb.wmin, hit ? t : INT32_MAX);
+    if (j == INT32_MAX) return false;
+    thr = wb.h.high[j];
+  } else {
+    hist16_scan<true>(wb, 0, 0, Pm, Hm, fm);
+    const uint32_t pb = wb.pick_bin;
+    __syncthreads();
+    if (pb == kNoPick) return false;  // the cut lies below the counted keys
+    thr = bottom + pb;
+  }
+  // kept entries: the list's and the bins' at or above the threshold
+  const bool hkept = t < static_cast<int>(nh) && wb.h.high[t] >= thr;
+  uint64_t cn = hkept ? 1u : 0u, ms = hkept ? wb.mass[t] : 0u;
+#pragma unroll 1
+  for (int i = 0; i < per; ++i) {
+    const int b = kHistKeys - 1 - per * t - i;
+    if (bottom + static_cast<uint32_t>(b) < thr) break;
+    const uint64_t n = wb.h.cnt[b];
+    cn += n;
+    if (n) ms += n * fm(b);
+  }
+  kept_n = block_sum_u64(cn);
+  kept_m = block_sum_u64(ms);
+  thr_out = WideKey<bf16_t>::thr(thr);
+  return true;
+}
+
+// The mass of entries outside the buffer or the counted keys, summed by each
+// thread against fl(L*c), moved to Rf in the fixed-point unit.
+__device__ __forceinline__ uint64_t rest_fixed(WideBuf& wb, double rest, float L, float c, float Rf) {
+  const double rt = block_sum_f64(wb, rest);
+  return static_cast<uint64_t>(llrint(rt * pow2d(static_cast<double>(L * c) - static_cast<double>(Rf) + kFixBits)));
+}
+
+// The buffer route of a row (fp32 rows, short bf16 rows, top-k rows). False
+// (nothing written) when it does not finish the row.
+template <typename T>
+__device__ __forceinline__ bool buffer_row(const SampleParams& P, const FiltRow& r, WideBuf& wb, int kk, bool k_on,
+                                           float pp, bool p_on, float xl) {
+  const float c = P.c;
+  const bool need_rest = p_on && !k_on;
+  float M, L;
+  double rest;
+  uint32_t n;
+  const bool read = need_rest ? wide_collect<T, true>(static_cast<const T*>(r.row), P.V, wb, kk, k_on, pp, c, M, L, rest, n)
+                              : wide_collect<T, false>(static_cast<const T*>(r.row), P.V, wb, kk, k_on, pp, c, M, L, rest, n);
+  if (!read) {
+    __syncthreads();
+    return false;
+  }
+  if (!(M > -INFINITY)) {  // no finite logit: the row keeps nothing
+    filt_write(P, r, 0.f, 0.0, 0xFFFFFFFFu, 0, xl);
+    __syncthreads();
+    return true;
+  }
+  if (n == 0 || n > static_cast<uint32_t>(WideKey<T>::kCap)) {
+    __syncthreads();
+    return false;
+  }
+  const float Rf = M * c + 1.f;  // as in the multi-pass select
+  const uint64_t Zrest = (need_rest && L > -INFINITY) ? rest_fixed(wb, rest, L, c, Rf) : 0u;
+  uint32_t thr;
+  uint64_t kn, km;
+  const bool ok = wide_cut<T>(wb, static_cast<int>(n), kk, k_on, pp, p_on, c, Rf, Zrest, thr, kn, km);
+  if (ok) filt_write(P, r, Rf, static_cast<double>(km) * 0x1p-40, thr, kn, xl);
+  __syncthreads();  // shared memory is reused by the next row
+  return ok;
+}
+
+// The key-count route of a long bf16 row with top-p alone. False (nothing written)
+// when it does not finish the row.
+__device__ __forceinline__ bool hist16_row(const SampleParams& P, const FiltRow& r, WideBuf& wb, float pp, float xl) {
+  const float c = P.c;
+  constexpr bool need_rest = true;
+  float M, L;
+  double rest;
+  uint32_t bottom;
+  if (!hist16_collect(static_cast<const bf16_t*>(r.row), P.V, wb, c, need_rest, M, bottom, L, rest)) {
+    __syncthreads();
+    return false;
+  }
+  const uint32_t nh = wb.nbuf;
+  if (nh > static_cast<uint32_t>(kHighCap)) {
+    __syncthreads();
+    return false;
+  }
+  const float Rf = M * c + 1.f;  // as in the multi-pass select
+  const uint64_t Zrest = L > -INFINITY ? rest_fixed(wb, rest, L, c, Rf) : 0u;
+  uint32_t thr;
+  uint64_t kn, km;
+  const bool ok = hist16_cut(wb, nh, bottom, pp, c, Rf, Zrest, thr, kn, km);
+  if (ok) filt_write(P, r, Rf, static_cast<double>(km) * 0x1p-40, thr, kn, xl);
+  __syncthreads();  // shared memory is reused by the next row
+  return ok;
+}
+
+// The one-read path of a row with top-p on, or with top-k and k > 64: top-p alone on
+// a long bf16 row goes through the key counts, every other row through the buffer.
+// False (nothing written) when the row needs the multi-pass select.
+template <typename T>
+__device__ __forceinline__ bool filter_row_wide(const SampleParams& P, const FiltRow& r, WideBuf& wb, int kk,
+                                                bool k_on, float pp, bool p_on, float xl) {
+  if constexpr (sizeof(T) == 2) {
+    if (!k_on && P.V > WideKey<T>::kCap) return hist16_row(P, r, wb, pp, xl);
+  }
+  return buffer_row<T>(P, r, wb, kk, k_on, pp, p_on, xl);
+}
+
+// The multi-pass select of a row (any filter setting): a radix select over the
+// whole row, one pass per digit.
+template <typename T>
+__device__ __forceinline__ void filter_row_task(const SampleParams& P, const FiltRow& r, FiltShared& sh, int kk, float pp, float xl) {
   const int64_t V = P.V;
   const T* row = static_cast<const T*>(r.row);
-  const int kk = P.top_k ? P.top_k[r.b] : 0;
-  const float pp = P.top_p ? P.top_p[r.b] : 1.f;
   const bool k_on = kk > 0 && kk < V;
   const bool p_on = pp < 1.f;  // false for NaN
   const float c = P.c;
-  const float xl = filt_token_logit<T>(P, r);
 
   // pass 1: online maximum and sum; with top-k also the histogram of the top digit
   if (k_on) clear_hist(sh);
@@ -862,32 +1616,129 @@ __device__ void filter_row_task(const SampleParams& P, int64_t task, FiltShared&
   __syncthreads();
 }
 
+// A row with no filter: its maximum and softmax denominator, one read.
 template <typename T>
-__global__ __launch_bounds__(kFiltBlock, SV_FAST_MINB) void k_filter_fast(SampleParams P) {
-  touch_kernargs(P);
-  __shared__ FastBuf fb;
-  const int64_t ntask = static_cast<int64_t>(P.B) * (2 * P.K + 1);
-  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) filter_row_fast<T>(P, task, fb);
+__device__ __forceinline__ void filter_row_plain(const SampleParams& P, const FiltRow& r, float xl) {
+  const float c = P.c;
+  Online o;
+  o.init();
+  visit_row(static_cast<const T*>(r.row), static_cast<int64_t>(P.V), [&](float x) {
+    if (x > o.m) o.raise(x, c);
+    o.add(x, c);
+  });
+  float M;
+  double S;
+  block_online<kFiltBlock>(o, c, M, S);  // valid in thread 0, the only writer
+  if (threadIdx.x == 0) {
+    if (!(M > -INFINITY)) {
+      filt_write(P, r, 0.f, 0.0, 0xFFFFFFFFu, 0, xl);
+    } else {
+      const float R = M * c;
+      const float Rf = R + 1.f;  // as in the multi-pass select
+      filt_write(P, r, Rf, S * pow2d(static_cast<double>(R) - static_cast<double>(Rf)), 0u,
+                 static_cast<uint64_t>(P.V), xl);
+    }
+  }
+  __syncthreads();
 }
 
+// Shared memory of the one-read paths (a workgroup runs one at a time).
+union FiltLds {
+  FastBuf fast;
+  WideBuf wide;
+};
+
+#ifndef SV_FILT_ROWS_GRID
+#define SV_FILT_ROWS_GRID 256  // workgroups of the multi-pass kernel
+#endif
+#ifndef SV_FILT_MINB
+#define SV_FILT_MINB 5  // workgroups per CU the one-read kernel is compiled for (its LDS allows five)
+#endif
+
+// One workgroup per logit row, read once: no filter, top-k with k <= 64, or top-p /
+// larger top-k. A row these paths do not finish is flagged (f_flag = 1) for the
+// multi-pass select; every row's flag is written.
+// The grid is two-dimensional, one workgroup per row (no loop over rows: values
+// derived from the thread index are not kept live across rows).
+template <typename T>
+__global__ __launch_bounds__(kFiltBlock, SV_FILT_MINB) void k_filter(SampleParams P) {
+  touch_kernargs(P);
+  __shared__ FiltLds lds;
+  const int64_t ntask = static_cast<int64_t>(P.B) * (2 * P.K + 1);
+  const int64_t task = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+  if (task < ntask) {
+    const FiltRow r = filt_row(P, task, sizeof(T));
+    const int kk = P.top_k ? P.top_k[r.b] : 0;
+    const float pp = P.top_p ? P.top_p[r.b] : 1.f;
+    const bool k_on = kk > 0 && kk < P.V;
+    const bool p_on = pp < 1.f;  // false for NaN
+    bool done = false;
+    if (!P.filt_multi) {
+      const float xl = filt_token_logit<T>(P, r);
+      if (k_on && kk <= kFiltFastK) {
+        done = filter_row_fast<T>(P, r, lds.fast, kk, pp, xl);
+      } else if (k_on || p_on) {
+        done = filter_row_wide<T>(P, r, lds.wide, kk, k_on, pp, p_on, xl);
+      } else {
+        filter_row_plain<T>(P, r, xl);
+        done = true;
+      }
+    }
+    if (threadIdx.x == 0) P.f_flag[r.fr] = done ? 0u : 1u;
+  }
+}
+
+// The multi-pass select of the flagged rows. Workgroup w takes rows w, w + G, ...;
+// each batch of 256 of its rows reads their flags at once.
 template <typename T>
 __global__ __launch_bounds__(kFiltBlock) void k_filter_rows(SampleParams P) {
   touch_kernargs(P);
   __shared__ FiltShared sh;
+  __shared__ uint64_t flagged[kFiltBlock / 64];
   const int64_t ntask = static_cast<int64_t>(P.B) * (2 * P.K + 1);
-  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) filter_row_task<T>(P, task, sh);
+  const int64_t G = gridDim.x;
+  for (int64_t base = blockIdx.x; base < ntask; base += G * kFiltBlock) {
+    const int64_t mine = base + static_cast<int64_t>(threadIdx.x) * G;
+    bool f = false;
+    if (mine < ntask) {
+      const FiltRow r = filt_row(P, mine, sizeof(T));
+      f = P.f_flag[r.fr] != 0u;
+    }
+    const uint64_t bal = __ballot(f);
+    if ((threadIdx.x & 63) == 0) flagged[threadIdx.x >> 6] = bal;
+    __syncthreads();
+    for (int wv = 0; wv < kFiltBlock / 64; ++wv) {
+      for (uint64_t bits = flagged[wv]; bits != 0; bits &= bits - 1) {
+        const int64_t task = base + static_cast<int64_t>(wv * 64 + __ffsll(static_cast<unsigned long long>(bits)) - 1) * G;
+        const FiltRow r = filt_row(P, task, sizeof(T));
+        const int kk = P.top_k ? P.top_k[r.b] : 0;
+        const float pp = P.top_p ? P.top_p[r.b] : 1.f;
+        filter_row_task<T>(P, r, sh, kk, pp, filt_token_logit<T>(P, r));
+      }
+    }
+    __syncthreads();  // the flags of the next batch overwrite these
+  }
 }
 
-static dim3 filt_grid(int64_t tasks) { return dim3(static_cast<uint32_t>(tasks < (1 << 20) ? tasks : (1 << 20))); }
+static dim3 filt_grid(int64_t tasks, int64_t cap) { return dim3(static_cast<uint32_t>(tasks < cap ? tasks : cap)); }
+
+// One workgroup per row: x up to 2^16, y the rest.
+static dim3 filt_grid_2d(int64_t tasks) {
+  const int64_t x = tasks < 65536 ? tasks : 65536;
+  return dim3(static_cast<uint32_t>(x), static_cast<uint32_t>((tasks + x - 1) / x));
+}
 
 hipError_t launch_filter_rows(const SampleParams& P, bool bf16, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(P.B) * (2 * P.K + 1);
+  // the multi-pass kernel: every row when the one-read paths are off, else a few
+  // workgroups, since flagged rows are rare
+  const int64_t g2 = P.filt_multi ? rows : (SV_FILT_ROWS_GRID);
   if (bf16) {
-    hipLaunchKernelGGL(k_filter_fast<bf16_t>, filt_grid(rows), dim3(kFiltBlock), 0, stream, P);
-    hipLaunchKernelGGL(k_filter_rows<bf16_t>, filt_grid(rows), dim3(kFiltBlock), 0, stream, P);
+    hipLaunchKernelGGL(k_filter<bf16_t>, filt_grid_2d(rows), dim3(kFiltBlock), 0, stream, P);
+    hipLaunchKernelGGL(k_filter_rows<bf16_t>, filt_grid(rows, g2), dim3(kFiltBlock), 0, stream, P);
   } else {
-    hipLaunchKernelGGL(k_filter_fast<float>, filt_grid(rows), dim3(kFiltBlock), 0, stream, P);
-    hipLaunchKernelGGL(k_filter_rows<float>, filt_grid(rows), dim3(kFiltBlock), 0, stream, P);
+    hipLaunchKernelGGL(k_filter<float>, filt_grid_2d(rows), dim3(kFiltBlock), 0, stream, P);
+    hipLaunchKernelGGL(k_filter_rows<float>, filt_grid(rows, g2), dim3(kFiltBlock), 0, stream, P);
   }
   return hipGetLastError();
 }

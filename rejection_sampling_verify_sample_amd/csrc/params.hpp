@@ -47,7 +47,8 @@ struct SampleParams {
   float* f_R;              // [B*(2K+1)] reference exponent of each row's masses (same row order as out_kept)
   double* f_S;             // [B*(2K+1)] kept mass against f_R (0: the row has no finite logit)
   uint32_t* f_thr;         // [B*(2K+1)] a row keeps the entries whose order key is >= this
-  uint32_t* f_cnt;         // [B*(2K+1)] one-pass top-k candidates of each row (above the buffer: overflow)
+  uint32_t* f_flag;        // [B*(2K+1)] 1: the row needs the multi-pass select (written for every row)
+  int32_t filt_multi;      // 1: every row takes the multi-pass select (no one-read path)
   uint32_t* info_T;        // [B, 2] thresholds of the rows the draw reads
 };
 
@@ -73,7 +74,7 @@ struct SampleLayout {
   int32_t S1, S2, S1max, S2max;
   int32_t NCmax;
   size_t off_p1m, off_p1s, off_p1x, off_info_n, off_info_R, off_info_S, off_p2cm, off_p2cs, off_alive;
-  size_t off_fR, off_fS, off_fthr, off_fcnt, off_infoT;  // filtered entry point only
+  size_t off_fR, off_fS, off_fthr, off_fflag, off_infoT;  // filtered entry point only
   size_t total;
 };
 

@@ -229,3 +229,59 @@ def test_one_pass_top_k_and_its_fallbacks(dtype, V):
     top_k_only = ps >= 1.0
     assert np.array_equal(kept[top_k_only], res.kept[top_k_only]), (kept, res.kept)
     compare_filtered(tg, dr, toks, uni, 1.0, ks, ps, res, tok, n, probs, kept).check_accounting()
+
+
+def _run_multi_pass(t, k, p):
+    """The same call with every row sent to the multi-pass select."""
+    os.environ["SPECVERIFY_FILTER"] = "multi"
+    try:
+        return run_gpu(t, k, p)
+    finally:
+        del os.environ["SPECVERIFY_FILTER"]
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 128256), ("f32", 40003), ("bf16", 20011), ("f32", 8000),
+                                     ("bf16", 3001)])
+def test_one_read_top_p_and_large_top_k(dtype, V):
+    """Top-p alone, and top-k with k > 64, read a row once: a bound from the first
+    step of the read, the entries above it in a buffer, the cut there. Rows cover a
+    buffer that holds the cut, a sample that puts the bound above the cut (its mass
+    sits far below the sample's), rows too flat for the buffer (multi-pass select),
+    ties, masked halves and all-negative rows; V at or below the buffer takes every
+    entry. Kept counts and rounds against the oracle, and against the multi-pass
+    select of the same rows."""
+    log(f"one-read top-p / large top-k {dtype} V={V}")
+    rng = np.random.default_rng(17)
+    B, K = 10, 1
+    tgt = (rng.normal(0, 3, (B, K + 1, V))).astype(np.float32)
+    tgt[1] = np.float32(-20.0)                        # the sample's mass sits at 10, the row's at 5
+    tgt[1, :, 64:74] = 10.0
+    tgt[1, :, 20000 % V:] = np.where(rng.random((K + 1, V - 20000 % V)) < 0.8, 5.0, -20.0)
+    tgt[2] = rng.normal(0, 0.3, (K + 1, V))           # flat: the nucleus is most of the row
+    tgt[3] = np.round(tgt[3] * 2) / 2                 # ties
+    tgt[4, :, : V // 2] = -np.inf                     # masked half
+    tgt[5] = -np.abs(tgt[5]) - 1.0                    # every logit negative
+    tgt[6] = np.sort(tgt[6], axis=-1)                 # ascending
+    drf = (tgt[:, :K] + rng.normal(0, 0.5, (B, K, V))).astype(np.float32)
+    drf[1] = tgt[1, :K]
+    toks = rng.integers(0, V, (B, K))
+    toks[1] = 70
+    uni = rng.random((B, K + 1, 2)).astype(np.float32)
+    ks = np.array([0, 0, 0, 0, 0, 0, 100, 1000, 5000, 300], dtype=np.int32)
+    ps = np.array([0.9, 0.9, 0.95, 0.8, 0.5, 0.99, 1.0, 1.0, 0.9, 0.0], dtype=np.float32)
+    if dtype == "f32":
+        t, tg, dr = _f32_tensors(tgt, drf, toks, uni), tgt, drf
+    else:
+        t, tg, dr = _bf16_tensors(tgt, drf, toks, uni)
+    tok, n, probs, kept = run_gpu(t, ks, ps)
+    res = oracle.oracle_sample_filtered(tg, dr, toks, uni, 1.0, ks, ps)
+    rep = compare_filtered(tg, dr, toks, uni, 1.0, ks, ps, res, tok, n, probs, kept)
+    log(f"  {rep.summary()}")
+    rep.check_accounting()
+    top_k_only = ps >= 1.0
+    assert np.array_equal(kept[top_k_only], res.kept[top_k_only]), (kept, res.kept)
+    tok2, n2, probs2, kept2 = _run_multi_pass(t, ks, ps)
+    sure = res.filter_margin >= 1e-6
+    assert np.array_equal(kept[sure], kept2[sure]), (kept, kept2)
+    same_rows = (res.min_margin() >= 1e-6)
+    assert np.array_equal(tok[same_rows], tok2[same_rows]) and np.array_equal(n[same_rows], n2[same_rows])
