@@ -298,7 +298,16 @@ def noalloc(**kw):
 
 
 def test_noalloc_limit_is_the_header_value():
-    assert rsv.lib().spec_verify_sample_noalloc_max_bytes() == 4 << 20
+    hdr = open(os.path.join(ROOT, "include", "spec_verify.h")).read()
+    m = re.search(r"#define SPEC_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m, "the header states the scratch size"
+    assert rsv.lib().spec_verify_sample_noalloc_max_bytes() == int(m.group(1)) << int(m.group(2))
+
+
+def test_noalloc_scratch_holds_the_sampling_workloads():
+    # B=1 K=4 V=32000, B=8 K=5 V=32000, B=64 K=8 V=128256, B=256 K=4 V=152064
+    for B, K, V in ((1, 4, 32000), (8, 5, 32000), (64, 8, 128256), (256, 4, 152064)):
+        assert rsv.sample_workspace_size(B, K, V) <= rsv.lib().spec_verify_sample_noalloc_max_bytes()
 
 
 @pytest.mark.parametrize("kw,expect", [
