@@ -60,6 +60,9 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--rotate", type=int, default=0, help="input copies (0: enough to exceed 2x the cache)")
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="untimed headline rounds run before the first measurement, in ms of GPU time, so that "
+                         "the device's clocks reach the steady state of a busy decode loop (0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the other sampling workloads (1, 2 and 4)")
@@ -349,6 +352,24 @@ class GraphSteps:
         return [self.timed(phases, n, lead) / n for _ in range(REPS)]
 
 
+def settle(steps: GraphSteps, ms: float, phases: int) -> float:
+    """Run untimed graphs of the workload's rounds for about `ms` of GPU time (the device's
+    clocks ramp over the first milliseconds of work; a decode loop runs at the steady state).
+    Returns the GPU time spent, in ms."""
+    t = steps.torch
+    steps.prepare(phases, [steps.chunk])
+    spent = 0.0
+    while spent < ms:
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(8):
+            steps.run(phases, steps.chunk)
+        b.record()
+        t.cuda.synchronize()
+        spent += a.elapsed_time(b)
+    return spent
+
+
 class Timer:
     def __init__(self, torch):
         self.torch = torch
@@ -434,14 +455,16 @@ class SampleLeg:
         self.torch.cuda.synchronize()
         return self.sets[0]["out_tokens"].cpu().numpy(), self.sets[0]["out_n"].cpu().numpy()
 
-    def measure(self, n: int, warmup: int) -> dict:
-        """The whole round and pass 1 alone, REPS times each."""
+    def measure(self, n: int, warmup: int, settle_ms: float = 0.0) -> dict:
+        """The whole round and pass 1 alone, REPS times each (after `settle_ms` of untimed rounds)."""
         import numpy as np
         rsv = self.rsv
         for st in self.sets[: min(self.M, 3)]:
             self.call(st)
         self.torch.cuda.synchronize()
         steps = self.steps()
+        if settle_ms > 0:
+            settle(steps, settle_ms, rsv.PHASE_ALL)
         t_all = steps.reps(rsv.PHASE_ALL, n, warmup)
         t_p1 = steps.reps(rsv.PHASE_ROW_STATS, n, warmup)
         del steps
@@ -523,7 +546,7 @@ def main() -> int:
     # ---------------------------------------------------------------- headline: B=64 K=8 V=128256 bf16
     head = SampleLeg(torch, rsv, dev, 3, args.rotate, args.eager, small=False)
     B, K, V = head.B, head.K, head.V
-    m3 = head.measure(args.steps, args.warmup)
+    m3 = head.measure(args.steps, args.warmup, args.settle_ms)
     t_step = m3["t_step"]
     by3 = m3["bytes"]
     log(f"step {t_step * 1e6:.2f} us (median of {REPS}; spread {m3['round']['spread']:.3f}; "
@@ -802,6 +825,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(t_step * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
