@@ -366,6 +366,9 @@ SPEC_EXPORT spec_status spec_verify_greedy(const void* target_logits, int32_t dt
   P.N = N;
   P.V = V;
   P.S3 = L.S3;
+  // SPECVERIFY_SELECT=block keeps the workgroup select for every shape (tests, tuning)
+  const char* sel = std::getenv("SPECVERIFY_SELECT");
+  P.select_block = (sel && std::strcmp(sel, "block") == 0) ? 1 : 0;
   P.out_tokens = out_tokens;
   P.out_len = out_accept_len;
   P.out_best = out_best_cand;

@@ -246,6 +246,80 @@ __global__ __launch_bounds__(kBlock) void k_greedy_select(GreedyParams P) {
   }
 }
 
+constexpr int kSelectMaxT = 16;  // candidate tokens the one-wave select holds per lane
+
+// The select of batch row b by one wave with no barrier, when its G*N rows fit the
+// wave (lane r holds row r's argmax): one round of loads (the rows' segment partials
+// and the candidates), shuffles for the prefix matches, a wave maximum of the
+// (prefix length, lowest candidate) key. The same results as greedy_select_task.
+__device__ __forceinline__ void greedy_select_wave(const GreedyParams& P, const int b) {
+  const int S = P.S3, N = P.N, G = P.G;
+  const int GN = G * N;
+  const int lane = threadIdx.x & 63;
+  // candidate lane g's tokens (N - 1 <= kSelectMaxT of them), issued with the partials
+  const int32_t* cb = P.cand + static_cast<int64_t>(b) * G * (N - 1);
+  int32_t ct[kSelectMaxT];
+#pragma unroll
+  for (int t = 0; t < kSelectMaxT; ++t) ct[t] = (lane < G && t < N - 1) ? cb[lane * (N - 1) + t] : 0;
+  // row r = lane: its segments in index order (strict > keeps the lowest index)
+  float bv = -INFINITY;
+  int32_t bi = -1;
+  if (lane < GN) {
+    const int64_t base = (static_cast<int64_t>(b) * GN + lane) * S;
+    for (int j = 0; j < S; ++j) {
+      const int32_t ij = P.p3_i[base + j];
+      const float vj = P.p3_v[base + j];
+      if (ij >= 0 && (bi < 0 || vj > bv)) {
+        bv = vj;
+        bi = ij;
+      }
+    }
+  }
+  bool bad = lane < GN && bi < 0;
+  // candidate g = lane: its matched prefix against the argmaxes of its rows
+  int L = 0;
+  bool run = true;
+#pragma unroll
+  for (int t = 0; t < kSelectMaxT; ++t) {
+    if (t >= N - 1) break;  // wave-uniform
+    const int32_t am = __shfl(bi, min(lane, G - 1) * N + t, 64);  // every lane takes part
+    if (lane < G) {
+      const int32_t c = ct[t];
+      bad = bad || c < 0 || c >= P.V;
+      if (run && c == am) ++L;
+      else run = false;
+    }
+  }
+  const bool fault = __ballot(bad) != 0;
+  // longer prefix first, then the lower candidate index
+  uint32_t key = lane < G ? (static_cast<uint32_t>(L) << 16) | static_cast<uint32_t>(0xFFFF - lane) : 0u;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) key = max(key, static_cast<uint32_t>(__shfl_xor(static_cast<int>(key), o, 64)));
+  const int Lb = static_cast<int>(key >> 16);
+  const int best = 0xFFFF - static_cast<int>(key & 0xFFFF);
+  const int32_t bonus = __shfl(bi, best * N + Lb, 64);  // the argmax right after the prefix
+  int32_t* ot = P.out_tokens + static_cast<int64_t>(b) * N;
+  if (lane < N) {
+    int32_t tok = -1;
+    if (!fault) {
+      if (lane < Lb) tok = cb[best * (N - 1) + lane];
+      else if (lane == Lb) tok = bonus;
+    }
+    ot[lane] = tok;
+  }
+  if (lane == 0) {
+    P.out_len[b] = fault ? -1 : Lb;
+    P.out_best[b] = fault ? -1 : best;
+  }
+}
+
+constexpr int kSelectWaveBlock = 64;  // one wave per batch row
+
+__global__ __launch_bounds__(kSelectWaveBlock) void k_greedy_select_wave(GreedyParams P) {
+  touch_kernargs(P);
+  for (int64_t task = blockIdx.x; task < P.B; task += gridDim.x) greedy_select_wave(P, static_cast<int>(task));
+}
+
 constexpr int64_t kMaxGrid = 1 << 20;  // workgroups per launch; kernels loop over their tasks
 
 inline dim3 grid_for(int64_t tasks) { return dim3(static_cast<uint32_t>(tasks < kMaxGrid ? tasks : kMaxGrid)); }
@@ -254,8 +328,12 @@ template <typename T>
 static hipError_t launch_greedy_t(const GreedyParams& P, hipStream_t stream) {
   const int64_t g = static_cast<int64_t>(P.B) * P.G * P.N * P.S3;
   hipLaunchKernelGGL((k_greedy_argmax<T>), grid_for(g), dim3(kArgBlock), 0, stream, P);
-  const size_t lds = static_cast<size_t>(P.G) * P.N * sizeof(int32_t);
-  hipLaunchKernelGGL(k_greedy_select, grid_for(P.B), dim3(kBlock), lds, stream, P);
+  if (static_cast<int64_t>(P.G) * P.N <= 64 && P.N - 1 <= kSelectMaxT && !P.select_block) {
+    hipLaunchKernelGGL(k_greedy_select_wave, grid_for(P.B), dim3(kSelectWaveBlock), 0, stream, P);
+  } else {
+    const size_t lds = static_cast<size_t>(P.G) * P.N * sizeof(int32_t);
+    hipLaunchKernelGGL(k_greedy_select, grid_for(P.B), dim3(kBlock), lds, stream, P);
+  }
   return hipGetLastError();
 }
 

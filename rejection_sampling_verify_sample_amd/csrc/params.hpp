@@ -102,6 +102,7 @@ struct GreedyParams {
   const int32_t* cand;     // [B, G, N-1]
   int32_t B, G, N, V;
   int32_t S3;
+  int32_t select_block;    // 1: the workgroup select for every shape (SPECVERIFY_SELECT=block; tests)
   int32_t* out_tokens;     // [B, N]
   int32_t* out_len;        // [B]
   int32_t* out_best;       // [B]

@@ -107,3 +107,27 @@ def test_deterministic():
     for _ in range(3):
         b = run(t["logits"], t["cand"])
         assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=32, G=7, N=5, V=32000),       # the workload's shape: 35 rows per batch row
+    dict(B=9, G=16, N=4, V=3001),        # 64 rows: a full wave
+    dict(B=5, G=1, N=17, V=2000),        # 16 candidate tokens: the wave select's longest
+])
+def test_wave_select_equals_workgroup_select(kw):
+    """The one-wave select (G*N <= 64, N - 1 <= 16) and the workgroup select give the same
+    outputs on the same argmax partials, faults included."""
+    import os
+    g = make_greedy_inputs(12, **kw)
+    cand = g.cand.copy()
+    cand[0, 0, 0] = kw["V"]              # a fault in batch row 0
+    t = greedy_tensors(g, DEV)
+    ct = torch.from_numpy(cand).to(DEV)
+    a = run(t["logits"], ct)
+    os.environ["SPECVERIFY_SELECT"] = "block"
+    try:
+        b = run(t["logits"], ct)
+    finally:
+        del os.environ["SPECVERIFY_SELECT"]
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+    compare_greedy(oracle.oracle_greedy(g.logits_f32(), cand), *a)
