@@ -23,21 +23,28 @@ MASS = "void sv::k_sample_mass<sv::bf16_t, true, false>(sv::SampleParams)"
 MASS_F = "void sv::k_sample_mass<sv::bf16_t, true, true>(sv::SampleParams)"
 DRAW = "void sv::k_sample_draw<sv::bf16_t, false>(sv::SampleParams)"
 DRAW_F = "void sv::k_sample_draw<sv::bf16_t, true>(sv::SampleParams)"
-FAST = "void sv::k_filter_fast<sv::bf16_t>(sv::SampleParams)"
+FILT = "void sv::k_filter<sv::bf16_t>(sv::SampleParams)"
+FROWS = "void sv::k_filter_rows<sv::bf16_t>(sv::SampleParams)"
 
 
 def test_counter_means_split_filtered_variants_and_keep_three_calibration_copies(tmp_path):
     p = tmp_path / "fetch.csv"
     _write_csv(p, "FETCH_SIZE", [(COPY, 131072), (COPY, 131072), (COPY, 131074), (COPY, 5),  # 4th: an input upload
-                                 (MASS, 100), (MASS, 300), (MASS_F, 1000), (DRAW, 7), (DRAW_F, 9), (FAST, 50),
+                                 (MASS, 100), (MASS, 300), (DRAW, 7),
+                                 # the filtered rounds: top-k 50 / top-p 0.9 first, then top-p 0.9 alone
+                                 (FILT, 50), (FROWS, 2), (MASS_F, 1000), (DRAW_F, 9),
+                                 (FILT, 70), (FROWS, 4), (MASS_F, 1100), (DRAW_F, 11),
                                  ("void sv::unrelated_kernel()", 1)])
     m = bench._counter_means(str(p), "FETCH_SIZE")
     assert m[COPY] == (131072 + 131072 + 131074) / 3
     assert m["k_sample_mass"] == 200
-    assert m["k_sample_mass_filtered"] == 1000
-    assert m["k_sample_draw"] == 7 and m["k_sample_draw_filtered"] == 9
-    assert m["k_filter_fast"] == 50
-    assert len(m) == 6
+    assert m["k_sample_draw"] == 7
+    # k_filter_rows is not taken for k_filter (a prefix of its name), and each setting keeps its own figures
+    assert m["k_filter"] == 50 and m["k_filter_topp"] == 70
+    assert m["k_filter_rows"] == 2 and m["k_filter_rows_topp"] == 4
+    assert m["k_sample_mass_filtered"] == 1000 and m["k_sample_mass_filtered_topp"] == 1100
+    assert m["k_sample_draw_filtered"] == 9 and m["k_sample_draw_filtered_topp"] == 11
+    assert len(m) == 11
 
 
 def test_ingest_scales_by_the_calibration_copy(tmp_path, monkeypatch):
