@@ -23,6 +23,19 @@ notes of the repository):
   * an n-gram with any token outside [0, V) is skipped (not inserted) and counted;
   * a lookup returns the key's continuations newest first; a token outside
     [0, V) has none.
+
+The hashed pool (NgramCache) is the same pool held in a bounded table, the GPU hash
+map the verify's candidate source asks for; the page is silent on its capacity, so
+these are readings too:
+  * a sequence's table has `sets` sets of `ways` entries (sets a power of two); a
+    key lives in set h(key) = floor((key * 2654435769 mod 2^32) / 2^(32 - log2 sets))
+    (Knuth's multiplicative hashing, the constant floor(2^32 / golden ratio));
+  * every inserted (not skipped) n-gram gets the next value of the sequence's
+    insertion clock; a key's stamp is the clock value of its newest n-gram;
+  * a new key in a set that holds `ways` keys evicts the key with the oldest stamp,
+    continuations and all; a key that comes back starts empty;
+  * within a key, everything is as in the direct pool above. While no set
+    overflows, the hashed pool holds exactly what the direct pool holds.
 """
 from __future__ import annotations
 
@@ -91,3 +104,67 @@ def pool_lookup(pools: list[NgramPool], last_tokens: np.ndarray) -> tuple[np.nda
 def pool_contents(pools: list[NgramPool]) -> dict[tuple[int, int], list[tuple[int, ...]]]:
     """Every non-empty (sequence, key) bucket, for comparisons."""
     return {(b, k): list(v) for b, p in enumerate(pools) for k, v in p.buckets.items() if v}
+
+
+# ---------------------------------------------------------------- the hashed pool
+
+GOLDEN32 = 2654435769  # floor(2^32 / golden ratio), Knuth's multiplicative hashing constant
+
+
+def cache_set(key: int, sets: int) -> int:
+    """The home set of `key` among `sets` (a power of two) sets."""
+    bits = sets.bit_length() - 1
+    if bits == 0:
+        return 0
+    return ((int(key) * GOLDEN32) % (1 << 32)) >> (32 - bits)
+
+
+class NgramCache:
+    """The hashed pool of one sequence: `sets` sets of at most `ways` keys, each key with
+    its stamp and its continuations (newest first, at most G)."""
+
+    def __init__(self, V: int, G: int, N: int, sets: int, ways: int):
+        assert sets >= 1 and sets & (sets - 1) == 0 and ways >= 1
+        self.V, self.G, self.N, self.sets, self.ways = int(V), int(G), int(N), int(sets), int(ways)
+        self.clock = 0
+        self.table: list[dict[int, list]] = [dict() for _ in range(sets)]  # set -> key -> [stamp, conts]
+
+    def insert(self, ngram) -> bool:
+        """Insert one n-gram of N tokens; False when it is skipped (a token out of range)."""
+        toks = [int(t) for t in ngram]
+        assert len(toks) == self.N
+        if any(t < 0 or t >= self.V for t in toks):
+            return False
+        key, cont = toks[0], tuple(toks[1:])
+        stamp = self.clock
+        self.clock += 1
+        entries = self.table[cache_set(key, self.sets)]
+        if key not in entries:
+            if len(entries) == self.ways:
+                oldest = min(entries, key=lambda k: entries[k][0])
+                del entries[oldest]
+            entries[key] = [stamp, []]
+        ent = entries[key]
+        ent[0] = stamp
+        held = ent[1]
+        if cont in held:
+            held.remove(cont)
+        held.insert(0, cont)
+        del held[self.G:]
+        return True
+
+    def lookup(self, token: int) -> list[tuple[int, ...]]:
+        """The continuations of `token`, newest first (at most G)."""
+        token = int(token)
+        if token < 0 or token >= self.V:
+            return []
+        ent = self.table[cache_set(token, self.sets)].get(token)
+        return list(ent[1]) if ent else []
+
+    def contents(self) -> dict[int, tuple[int, list[tuple[int, ...]]]]:
+        """key -> (stamp, continuations) over every set."""
+        return {k: (e[0], list(e[1])) for tab in self.table for k, e in tab.items()}
+
+
+def new_caches(B: int, V: int, G: int, N: int, sets: int, ways: int) -> list[NgramCache]:
+    return [NgramCache(V, G, N, sets, ways) for _ in range(B)]
