@@ -69,7 +69,7 @@ def parse_args():
     ap.add_argument("--no-greedy", action="store_true")
     ap.add_argument("--no-filtered", action="store_true", help="skip the top-k / top-p filtered legs")
     ap.add_argument("--no-staged", action="store_true", help="skip the early-exit (staged pass 1) leg")
-    ap.add_argument("--no-pool", action="store_true", help="skip the n-gram pool leg")
+    ap.add_argument("--no-pool", action="store_true", help="skip the n-gram pool legs (direct and hashed)")
     ap.add_argument("--no-ngram-sample", action="store_true", help="skip the one-hot n-gram sampling verify leg")
     ap.add_argument("--eager", action="store_true", help="launch through the Python binding instead of graphs")
     ap.add_argument("--counters", action="store_true",
@@ -679,43 +679,57 @@ def main() -> int:
             legs[cfg] = leg
             torch.cuda.empty_cache()
 
-    # ---------------------------------------------------------------- n-gram pool, B=32 V=32000 G=7 N=5, W=15 per call
-    pool_leg = None
+    # ---------------------------------------------------------------- n-gram pools, B=32 V=32000 G=7 N=5, W=15 per call
+    pool_leg = cache_leg = None
     if not args.no_pool:
         from workloads.ngram import lookup_tokens, ngram_steps
         PB, PV, PG, PN, PW = 32, 32000, 7, 5, 15
-        pool = rsv.NgramPool(PB, PV, PG, PN, dev)
+        CS, CW = 512, 8  # hashed pool: 512 sets of 8 ways, 4096 keys per sequence
         host = ngram_steps(3, 16, PB, PW, PN, PV)
         grams = [torch.from_numpy(g).to(dev) for g in host]
         lasts = [torch.from_numpy(lookup_tokens(i, PB, PV, host)).to(dev) for i in range(16)]
-        skipped = torch.empty((PB,), dtype=torch.int32, device=dev)
-        pcand = torch.empty((PB, PG, PN - 1), dtype=torch.int32, device=dev)
-        pcount = torch.empty((PB,), dtype=torch.int32, device=dev)
 
-        def pstep(i):
-            pool.insert(grams[i % 16], out_skipped=skipped)
-            pool.lookup(lasts[i % 16], out_cand=pcand, out_count=pcount)
+        def time_pool(pool):
+            skipped = torch.empty((PB,), dtype=torch.int32, device=dev)
+            pcand = torch.empty((PB, PG, PN - 1), dtype=torch.int32, device=dev)
+            pcount = torch.empty((PB,), dtype=torch.int32, device=dev)
 
-        for i in range(16):
-            pstep(i)
-        torch.cuda.synchronize()
-        psteps = 48
-        if args.eager:
-            pfn, pcalls = pstep, 1
-        else:
-            pgraph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(pgraph):
-                for j in range(psteps):
-                    pstep(j)
-            pfn, pcalls = (lambda i: pgraph.replay()), psteps  # noqa: E731
-        n_rep = max(1, args.steps // pcalls)
-        tp = rep_stats([t / (n_rep * pcalls) for t in timer.reps(pfn, n_rep, max(1, args.warmup // pcalls))])
-        pool_leg = {"workload": f"n-gram pool B={PB} V={PV} G={PG} N={PN}: insert W={PW} n-grams per sequence, "
-                                "then look up each sequence's last token",
+            def pstep(i):
+                pool.insert(grams[i % 16], out_skipped=skipped)
+                pool.lookup(lasts[i % 16], out_cand=pcand, out_count=pcount)
+
+            for i in range(16):
+                pstep(i)
+            torch.cuda.synchronize()
+            psteps = 48
+            if args.eager:
+                pfn, pcalls = pstep, 1
+            else:
+                pgraph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(pgraph):
+                    for j in range(psteps):
+                        pstep(j)
+                pfn, pcalls = (lambda i: pgraph.replay()), psteps  # noqa: E731
+            n_rep = max(1, args.steps // pcalls)
+            tp = rep_stats([t / (n_rep * pcalls) for t in timer.reps(pfn, n_rep, max(1, args.warmup // pcalls))])
+            return tp, round(float(pcount.float().mean().item()), 3)
+
+        what = f"B={PB} V={PV} G={PG} N={PN}: insert W={PW} n-grams per sequence, then look up each sequence's last token"
+        pool = rsv.NgramPool(PB, PV, PG, PN, dev)
+        tp, mean_c = time_pool(pool)
+        pool_leg = {"workload": f"n-gram pool {what}", "table_bytes": pool.nbytes,
                     "step": tp, "us_per_step": tp["us_median"], "steps_per_s": round(1e6 / tp["us_median"], 1),
-                    "mean_candidates": round(float(pcount.float().mean().item()), 3)}
-        log(f"n-gram pool insert + lookup: {tp['us_median']:.2f} us per step")
+                    "mean_candidates": mean_c}
+        log(f"n-gram pool insert + lookup: {tp['us_median']:.2f} us per step ({pool.nbytes / 1e6:.1f} MB table)")
         del pool
+        cache = rsv.NgramCache(PB, PV, PG, PN, CS, CW, dev)
+        tc, mean_c = time_pool(cache)
+        cache_leg = {"workload": f"hashed n-gram pool, {CS} sets x {CW} ways per sequence, {what}",
+                     "table_bytes": cache.nbytes, "step": tc, "us_per_step": tc["us_median"],
+                     "steps_per_s": round(1e6 / tc["us_median"], 1), "mean_candidates": mean_c}
+        log(f"hashed n-gram pool insert + lookup: {tc['us_median']:.2f} us per step "
+            f"({cache.nbytes / 1e6:.1f} MB table)")
+        del cache
 
     # ---------------------------------------------------------------- greedy verify, B=32 G=7 N=5 V=32000 bf16
     greedy = None
@@ -865,6 +879,7 @@ def main() -> int:
         "staged": staged,
         "filtered": filtered,
         "ngram_pool": pool_leg,
+        "ngram_cache": cache_leg,
         "greedy": greedy,
         "ngram_sample": ngs,
     }

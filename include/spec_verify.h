@@ -70,7 +70,7 @@ typedef enum {
   SPEC_ERR_PHASE = -8,       /* phase mask outside 1..15 (spec_verify_sample_phases) */
   SPEC_ERR_FILTER_V = -9,    /* V > SPEC_MAX_FILTER_V (spec_verify_sample_filtered) */
   SPEC_ERR_STAGES = -10,     /* invalid stage schedule (spec_verify_sample_staged) */
-  SPEC_ERR_POOL = -11        /* pool buffer smaller than spec_ngram_pool_bytes */
+  SPEC_ERR_POOL = -11        /* pool buffer smaller than spec_ngram_pool_bytes / spec_ngram_cache_bytes */
 } spec_status;
 
 #define SPEC_MAX_FILTER_V (1 << 24) /* vocabulary entries per row of the filtered verify */
@@ -78,6 +78,8 @@ typedef enum {
 #define SPEC_MAX_POOL_G 64          /* continuations a pool key holds */
 #define SPEC_MAX_POOL_N 17          /* n-gram length: a continuation holds at most 16 tokens */
 #define SPEC_MAX_POOL_W 64          /* n-grams per sequence in one insert call */
+#define SPEC_MAX_CACHE_SETS (1 << 24) /* sets per sequence of the hashed pool (a power of two) */
+#define SPEC_MAX_CACHE_WAYS 64        /* keys a set of the hashed pool holds */
 #define SPEC_MAX_NGRAM_SAMPLE_V (1 << 20) /* vocabulary entries of spec_verify_ngram_sample */
 #define SPEC_MAX_NGRAM_SAMPLE_GN 1024    /* G*N of spec_verify_ngram_sample: one sequence's inputs staged on chip */
 
@@ -389,6 +391,52 @@ spec_status spec_ngram_pool_insert(void* pool, size_t pool_bytes, int32_t B, int
  */
 spec_status spec_ngram_pool_lookup(const void* pool, size_t pool_bytes, int32_t B, int32_t V, int32_t G, int32_t N,
                                    const int32_t* last_tokens, int32_t* out_cand, int32_t* out_count, void* stream);
+
+/*
+ * The hashed n-gram pool: the same pool as spec_ngram_pool_*, held in a bounded
+ * table whose size follows its capacity instead of B*V. Source: as above (the
+ * Lookahead Decoding page, sections "Lookahead 分支", "N-gram 池与身份判定" and
+ * "验证分支"); the page leaves the pool's capacity open, so this bound is a reading.
+ *
+ * Per sequence, `sets` sets of `ways` keys. A key's home set is the top log2(sets)
+ * bits of (key * 2654435769) mod 2^32 (Knuth's multiplicative hashing with
+ * floor(2^32 / golden ratio)). Every inserted n-gram takes the next value of its
+ * sequence's 32-bit clock (skipped ones take none) and a key's stamp is its newest
+ * n-gram's value. A new key in a full set evicts the key with the oldest stamp,
+ * continuations and all (ages modulo 2^32: exact while every held key was inserted
+ * within the sequence's last 2^32 insertions); a key that comes back starts empty.
+ * Within a key the direct pool's rule holds: its G most recently inserted distinct
+ * continuations, newest first. While no set overflows, inserts and lookups give
+ * exactly what the direct pool gives. Lookups change nothing.
+ *
+ * cache        DEVICE memory of at least spec_ngram_cache_bytes(B, sets, ways, G, N)
+ *              bytes, 16-byte aligned, owned by the caller. Per sequence:
+ *              seq = 4 + sets * (2*ways + ways*G*(N-1)) int32 rounded up to a
+ *              multiple of 4; word 0 the clock, words 1..3 zero; then set s at word
+ *              4 + s*(2*ways + ways*G*(N-1)): keys[ways] int32 (-1: empty),
+ *              stamps[ways] uint32, slots[ways][G][N-1] int32 (newest first, an
+ *              empty slot -1 throughout). spec_ngram_cache_init must run on it once
+ *              before any other use, and every call passes the same sizes.
+ * B, sets, ways, G, N   0 <= B, 1 <= sets <= SPEC_MAX_CACHE_SETS (a power of two),
+ *              1 <= ways <= SPEC_MAX_CACHE_WAYS, 1 <= G <= SPEC_MAX_POOL_G,
+ *              2 <= N <= SPEC_MAX_POOL_N; the table must fit in size_t.
+ * V            1 <= V <= SPEC_MAX_V: tokens outside [0, V) are skipped (insert) or
+ *              have no continuation (lookup).
+ * SPEC_ERR_POOL when cache_bytes is smaller than spec_ngram_cache_bytes.
+ */
+size_t spec_ngram_cache_bytes(int32_t B, int32_t sets, int32_t ways, int32_t G, int32_t N); /* 0: invalid sizes */
+spec_status spec_ngram_cache_init(void* cache, size_t cache_bytes, int32_t B, int32_t sets, int32_t ways, int32_t G,
+                                  int32_t N, void* stream);
+/* As spec_ngram_pool_insert: ngrams [B, W, N] int32 (device) in window order,
+ * 0 <= W <= SPEC_MAX_POOL_W; out_skipped NULL or [B] int32. */
+spec_status spec_ngram_cache_insert(void* cache, size_t cache_bytes, int32_t B, int32_t V, int32_t sets, int32_t ways,
+                                    int32_t G, int32_t N, const int32_t* ngrams, int32_t W, int32_t* out_skipped,
+                                    void* stream);
+/* As spec_ngram_pool_lookup: last_tokens [B] int32; out_cand [B, G, N-1] int32 (newest
+ * first, -1 past out_count [B]). The table is read only. */
+spec_status spec_ngram_cache_lookup(const void* cache, size_t cache_bytes, int32_t B, int32_t V, int32_t sets,
+                                    int32_t ways, int32_t G, int32_t N, const int32_t* last_tokens, int32_t* out_cand,
+                                    int32_t* out_count, void* stream);
 
 /*
  * Fill out [B, K+1, 2] with the verify uniforms of one round from

@@ -10,20 +10,20 @@ Entry points (torch tensors in, torch tensors out; every computation runs in HIP
   fill_uniforms  -- Philox4x32-10 verify uniforms on the device
   row_stats      -- softmax statistics (max, denominator) of logit rows, as the verify computes them
   NgramPool      -- the n-gram pool that supplies verify_greedy's candidates (insert / lookup)
+  NgramCache     -- the same pool in a bounded hash table (sets x ways keys per sequence, LRU eviction)
 """
 from ._lib import (LIB_PATH, PHASE_ACCEPT, PHASE_ALL, PHASE_DRAW, PHASE_MASS, PHASE_ROW_STATS, SPEC_BF16, SPEC_F32,
-                   SPEC_MAX_K, GreedyOutputs, NgramPool, NgramSampleOutputs, SampleOutputs, SpecVerifyError,
-                   abi_version, fill_uniforms, greedy_workspace_size, lib, ngram_pool_bytes,
-                   ngram_sample_workspace_size, row_stats, sample_filtered_workspace_size, sample_workspace_size,
-                   status_string,
-                   verify_greedy, verify_ngram_sample, verify_sample, verify_sample_filtered, verify_sample_noalloc,
-                   verify_sample_staged, workspace_for)
+                   SPEC_MAX_K, GreedyOutputs, NgramCache, NgramPool, NgramSampleOutputs, SampleOutputs,
+                   SpecVerifyError, abi_version, fill_uniforms, greedy_workspace_size, lib, ngram_cache_bytes,
+                   ngram_pool_bytes, ngram_sample_workspace_size, row_stats, sample_filtered_workspace_size,
+                   sample_workspace_size, status_string, verify_greedy, verify_ngram_sample, verify_sample,
+                   verify_sample_filtered, verify_sample_noalloc, verify_sample_staged, workspace_for)
 
 __all__ = [
     "LIB_PATH", "PHASE_ACCEPT", "PHASE_ALL", "PHASE_DRAW", "PHASE_MASS", "PHASE_ROW_STATS", "SPEC_BF16", "SPEC_F32",
-    "SPEC_MAX_K", "GreedyOutputs", "NgramPool", "NgramSampleOutputs", "SampleOutputs", "SpecVerifyError",
-    "abi_version", "fill_uniforms", "greedy_workspace_size", "lib", "ngram_pool_bytes", "ngram_sample_workspace_size",
-    "row_stats", "sample_filtered_workspace_size",
+    "SPEC_MAX_K", "GreedyOutputs", "NgramCache", "NgramPool", "NgramSampleOutputs", "SampleOutputs",
+    "SpecVerifyError", "abi_version", "fill_uniforms", "greedy_workspace_size", "lib", "ngram_cache_bytes",
+    "ngram_pool_bytes", "ngram_sample_workspace_size", "row_stats", "sample_filtered_workspace_size",
     "sample_workspace_size", "status_string", "verify_greedy", "verify_ngram_sample", "verify_sample",
     "verify_sample_filtered", "verify_sample_noalloc", "verify_sample_staged", "workspace_for",
 ]

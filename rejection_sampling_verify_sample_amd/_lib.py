@@ -67,6 +67,12 @@ _SIGNATURES = {
                                       _c_void_p]),
     "spec_ngram_pool_lookup": (_i32, [_c_void_p, _size_t, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
                                       _c_void_p]),
+    "spec_ngram_cache_bytes": (_size_t, [_i32, _i32, _i32, _i32, _i32]),
+    "spec_ngram_cache_init": (_i32, [_c_void_p, _size_t, _i32, _i32, _i32, _i32, _i32, _c_void_p]),
+    "spec_ngram_cache_insert": (_i32, [_c_void_p, _size_t, _i32, _i32, _i32, _i32, _i32, _i32, _c_void_p, _i32,
+                                       _c_void_p, _c_void_p]),
+    "spec_ngram_cache_lookup": (_i32, [_c_void_p, _size_t, _i32, _i32, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
+                                       _c_void_p, _c_void_p]),
 }
 
 _lib = None
@@ -519,3 +525,84 @@ class NgramPool:
         if st != 0:
             raise SpecVerifyError(st, "spec_ngram_pool_lookup")
         return out_cand, out_count
+
+
+# ------------------------------------------------------------------ hashed n-gram pool
+
+def ngram_cache_bytes(B: int, sets: int, ways: int, G: int, N: int) -> int:
+    return int(lib().spec_ngram_cache_bytes(B, sets, ways, G, N))
+
+
+class NgramCache:
+    """The hashed n-gram pools of B sequences (spec_ngram_cache_*): per sequence `sets` sets
+    (a power of two) of `ways` keys, the least recently inserted key of a full set evicted.
+
+    Same insert() / lookup() as NgramPool. `buffer` is the table memory (int32), emptied at
+    construction; sequence b starts at int32 b * seq_elems: the clock, three zero words,
+    then set s at 4 + s * set_elems: keys[ways], stamps[ways] (uint32 bits), slots[ways][G][N-1].
+    """
+
+    def __init__(self, B: int, V: int, G: int, N: int, sets: int, ways: int, device="cuda", stream=None):
+        self.B, self.V, self.G, self.N, self.sets, self.ways = int(B), int(V), int(G), int(N), int(sets), int(ways)
+        self.device = torch.device(device)
+        nbytes = ngram_cache_bytes(B, sets, ways, G, N)
+        if nbytes == 0 and B > 0:
+            raise SpecVerifyError(-2, "spec_ngram_cache_bytes")
+        self.set_elems = 2 * self.ways + self.ways * self.G * (self.N - 1)
+        self.seq_elems = (4 + self.sets * self.set_elems + 3) // 4 * 4
+        self.buffer = torch.empty(max(nbytes // 4, 1), dtype=torch.int32, device=self.device)
+        self.nbytes = nbytes
+        st = lib().spec_ngram_cache_init(_ptr(self.buffer), nbytes, B, sets, ways, G, N,
+                                         ctypes.c_void_p(_stream_handle(stream, self.device)))
+        if st != 0:
+            raise SpecVerifyError(st, "spec_ngram_cache_init")
+
+    def _sizes(self):
+        return self.B, self.V, self.sets, self.ways, self.G, self.N
+
+    def insert(self, ngrams: torch.Tensor, *, out_skipped: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Insert ngrams [B, W, N] int32 (window order); returns the skipped counts [B]."""
+        if ngrams.dim() != 3:
+            raise ValueError("ngrams must be [B, W, N]")
+        W = ngrams.shape[1]
+        _check(ngrams, "ngrams", self.device, torch.int32, (self.B, W, self.N))
+        if out_skipped is None:
+            out_skipped = torch.empty((self.B,), dtype=torch.int32, device=self.device)
+        _check(out_skipped, "out_skipped", self.device, torch.int32, (self.B,))
+        st = lib().spec_ngram_cache_insert(_ptr(self.buffer), self.nbytes, *self._sizes(), _ptr(ngrams), W,
+                                           _ptr(out_skipped), ctypes.c_void_p(_stream_handle(stream, self.device)))
+        if st != 0:
+            raise SpecVerifyError(st, "spec_ngram_cache_insert")
+        return out_skipped
+
+    def lookup(self, last_tokens: torch.Tensor, *, out_cand: torch.Tensor | None = None,
+               out_count: torch.Tensor | None = None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+        """Candidates [B, G, N-1] (newest first, -1 past the count) and counts [B] for each last token [B]."""
+        _check(last_tokens, "last_tokens", self.device, torch.int32, (self.B,))
+        if out_cand is None:
+            out_cand = torch.empty((self.B, self.G, self.N - 1), dtype=torch.int32, device=self.device)
+        if out_count is None:
+            out_count = torch.empty((self.B,), dtype=torch.int32, device=self.device)
+        _check(out_cand, "out_cand", self.device, torch.int32, (self.B, self.G, self.N - 1))
+        _check(out_count, "out_count", self.device, torch.int32, (self.B,))
+        st = lib().spec_ngram_cache_lookup(_ptr(self.buffer), self.nbytes, *self._sizes(), _ptr(last_tokens),
+                                           _ptr(out_cand), _ptr(out_count),
+                                           ctypes.c_void_p(_stream_handle(stream, self.device)))
+        if st != 0:
+            raise SpecVerifyError(st, "spec_ngram_cache_lookup")
+        return out_cand, out_count
+
+    def entries(self) -> tuple[list[int], dict[tuple[int, int], tuple[int, int, int, list[tuple[int, ...]]]]]:
+        """Copy the table to the host and read it: (clock per sequence,
+        {(b, key): (set, way, stamp, held continuations)}), for inspection."""
+        t = self.buffer[: self.B * self.seq_elems].view(self.B, self.seq_elems).cpu()
+        clocks = [int(v) & 0xFFFFFFFF for v in t[:, 0].tolist()]
+        sets = t[:, 4: 4 + self.sets * self.set_elems].view(self.B, self.sets, self.set_elems)
+        keys = sets[:, :, : self.ways]
+        stamps = sets[:, :, self.ways: 2 * self.ways]
+        slots = sets[:, :, 2 * self.ways:].reshape(self.B, self.sets, self.ways, self.G, self.N - 1)
+        out = {}
+        for b, s, w in torch.nonzero(keys >= 0).tolist():
+            held = [tuple(r) for r in slots[b, s, w].tolist() if r[0] >= 0]
+            out[(b, int(keys[b, s, w]))] = (s, w, int(stamps[b, s, w]) & 0xFFFFFFFF, held)
+        return clocks, out

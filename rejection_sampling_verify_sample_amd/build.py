@@ -14,8 +14,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "sample.hip", "filter.hip", "greedy.hip", "ngram.hip", "ngram_sample.hip", "philox.hip",
-           "stats.hip"]
+SOURCES = ["api.hip", "sample.hip", "filter.hip", "greedy.hip", "ngram.hip", "ngram_cache.hip", "ngram_sample.hip",
+           "philox.hip", "stats.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -18,6 +18,9 @@ hipError_t launch_ngram_sample(const NgramSampleParams& P, bool bf16, hipStream_
 hipError_t launch_pool_fill(int32_t* pool, int64_t n, hipStream_t stream);
 hipError_t launch_pool_insert(const PoolParams& P, hipStream_t stream);
 hipError_t launch_pool_lookup(const PoolParams& P, hipStream_t stream);
+hipError_t launch_cache_fill(int32_t* cache, int64_t seq_elems, int64_t n, hipStream_t stream);
+hipError_t launch_cache_insert(const CacheParams& P, hipStream_t stream);
+hipError_t launch_cache_lookup(const CacheParams& P, hipStream_t stream);
 hipError_t launch_sample(const SampleParams& P, bool bf16, bool filtered, int phases, hipStream_t stream);
 hipError_t launch_greedy(const GreedyParams& P, bool bf16, hipStream_t stream);
 hipError_t launch_philox(uint64_t seed, uint64_t round, int32_t B, int32_t K, float* out, hipStream_t stream);
@@ -148,7 +151,7 @@ SPEC_EXPORT const char* spec_status_string(int32_t status) {
     case SPEC_ERR_PHASE: return "phase mask outside 1..15";
     case SPEC_ERR_FILTER_V: return "vocabulary too large for the filtered verify";
     case SPEC_ERR_STAGES: return "invalid stage schedule (strictly increasing ends in [1, K], the last K)";
-    case SPEC_ERR_POOL: return "n-gram pool buffer smaller than spec_ngram_pool_bytes";
+    case SPEC_ERR_POOL: return "n-gram pool buffer smaller than spec_ngram_pool_bytes / spec_ngram_cache_bytes";
     default: return "unknown status";
   }
 }
@@ -465,6 +468,112 @@ SPEC_EXPORT spec_status spec_ngram_pool_lookup(const void* pool, size_t pool_byt
   P.out_cand = out_cand;
   P.out_count = out_count;
   const hipError_t e = sv::launch_pool_lookup(P, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- hashed n-gram pool
+
+namespace {
+
+struct CacheGeometry {
+  int64_t seq_elems = -1;  // int32 per sequence; -1 for invalid sizes
+  int64_t elems = -1;      // int32 in all
+  int32_t set_elems = 0;
+  int32_t set_shift = 32;
+};
+
+CacheGeometry cache_geometry(int32_t B, int32_t sets, int32_t ways, int32_t G, int32_t N) {
+  CacheGeometry g;
+  if (B < 0 || sets < 1 || sets > SPEC_MAX_CACHE_SETS || (sets & (sets - 1)) != 0 || ways < 1 ||
+      ways > SPEC_MAX_CACHE_WAYS || G < 1 || G > SPEC_MAX_POOL_G || N < 2 || N > SPEC_MAX_POOL_N)
+    return g;
+  const int64_t set_elems = 2 * static_cast<int64_t>(ways) + static_cast<int64_t>(ways) * G * (N - 1);
+  const int64_t seq_elems = (4 + sets * set_elems + 3) / 4 * 4;
+  const unsigned __int128 n = static_cast<unsigned __int128>(B) * static_cast<uint64_t>(seq_elems);
+  if (n * 4 > static_cast<unsigned __int128>(INT64_MAX) || n * 4 > static_cast<unsigned __int128>(SIZE_MAX)) return g;
+  g.seq_elems = seq_elems;
+  g.elems = static_cast<int64_t>(n);
+  g.set_elems = static_cast<int32_t>(set_elems);
+  int log2 = 0;
+  while ((1 << log2) < sets) ++log2;
+  g.set_shift = 32 - log2;
+  return g;
+}
+
+spec_status cache_check(const void* cache, size_t cache_bytes, const CacheGeometry& g, int32_t B) {
+  if (g.elems < 0) return SPEC_ERR_SHAPE;
+  if (B == 0) return SPEC_OK;
+  if (!cache) return SPEC_ERR_NULL;
+  if (!aligned(cache, 16)) return SPEC_ERR_ALIGN;
+  if (cache_bytes < static_cast<size_t>(g.elems) * 4) return SPEC_ERR_POOL;
+  return SPEC_OK;
+}
+
+sv::CacheParams cache_params(void* cache, const CacheGeometry& g, int32_t B, int32_t V, int32_t sets, int32_t ways,
+                             int32_t G, int32_t N) {
+  sv::CacheParams P{};
+  P.cache = static_cast<int32_t*>(cache);
+  P.seq_elems = g.seq_elems;
+  P.set_elems = g.set_elems;
+  P.set_shift = g.set_shift;
+  P.B = B;
+  P.V = V;
+  P.sets = sets;
+  P.ways = ways;
+  P.G = G;
+  P.N = N;
+  return P;
+}
+
+}  // namespace
+
+SPEC_EXPORT size_t spec_ngram_cache_bytes(int32_t B, int32_t sets, int32_t ways, int32_t G, int32_t N) {
+  const CacheGeometry g = cache_geometry(B, sets, ways, G, N);
+  return g.elems < 0 ? 0 : static_cast<size_t>(g.elems) * 4;
+}
+
+SPEC_EXPORT spec_status spec_ngram_cache_init(void* cache, size_t cache_bytes, int32_t B, int32_t sets, int32_t ways,
+                                              int32_t G, int32_t N, void* stream) {
+  const CacheGeometry g = cache_geometry(B, sets, ways, G, N);
+  const spec_status st = cache_check(cache, cache_bytes, g, B);
+  if (st != SPEC_OK || B == 0) return st;
+  const hipError_t e = sv::launch_cache_fill(static_cast<int32_t*>(cache), g.seq_elems, g.elems,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+SPEC_EXPORT spec_status spec_ngram_cache_insert(void* cache, size_t cache_bytes, int32_t B, int32_t V, int32_t sets,
+                                                int32_t ways, int32_t G, int32_t N, const int32_t* ngrams, int32_t W,
+                                                int32_t* out_skipped, void* stream) {
+  if (W < 0 || W > SPEC_MAX_POOL_W || V < 1 || V > SPEC_MAX_V) return SPEC_ERR_SHAPE;
+  const CacheGeometry g = cache_geometry(B, sets, ways, G, N);
+  const spec_status st = cache_check(cache, cache_bytes, g, B);
+  if (st != SPEC_OK || B == 0) return st;
+  if (W > 0 && !ngrams) return SPEC_ERR_NULL;
+  if (!aligned(ngrams, 4) || !aligned(out_skipped, 4)) return SPEC_ERR_ALIGN;
+  sv::CacheParams P = cache_params(cache, g, B, V, sets, ways, G, N);
+  P.W = W;
+  P.ngrams = ngrams;
+  P.out_skipped = out_skipped;
+  const hipError_t e = sv::launch_cache_insert(P, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+SPEC_EXPORT spec_status spec_ngram_cache_lookup(const void* cache, size_t cache_bytes, int32_t B, int32_t V,
+                                                int32_t sets, int32_t ways, int32_t G, int32_t N,
+                                                const int32_t* last_tokens, int32_t* out_cand, int32_t* out_count,
+                                                void* stream) {
+  if (V < 1 || V > SPEC_MAX_V) return SPEC_ERR_SHAPE;
+  const CacheGeometry g = cache_geometry(B, sets, ways, G, N);
+  const spec_status st = cache_check(cache, cache_bytes, g, B);
+  if (st != SPEC_OK || B == 0) return st;
+  if (!last_tokens || !out_cand || !out_count) return SPEC_ERR_NULL;
+  if (!aligned(last_tokens, 4) || !aligned(out_cand, 4) || !aligned(out_count, 4)) return SPEC_ERR_ALIGN;
+  sv::CacheParams P = cache_params(const_cast<void*>(cache), g, B, V, sets, ways, G, N);
+  P.last = last_tokens;
+  P.out_cand = out_cand;
+  P.out_count = out_count;
+  const hipError_t e = sv::launch_cache_lookup(P, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

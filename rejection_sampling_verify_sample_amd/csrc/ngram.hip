@@ -26,6 +26,7 @@
 #include "../../include/spec_verify.h"
 #include "common.hpp"
 #include "params.hpp"
+#include "pool_bucket.hpp"
 
 namespace sv {
 
@@ -53,13 +54,6 @@ constexpr int kPoolBlock = 64 * kPoolWaves;
 struct PoolShared {
   int32_t ng[SPEC_MAX_POOL_W * SPEC_MAX_POOL_N];  // the call's n-grams, [W][N]
 };
-
-// Do n-grams w1 and w2 (both valid, same key) carry the same continuation?
-__device__ __forceinline__ bool same_cont(const PoolShared& sh, int N, int w1, int w2) {
-  for (int i = 1; i < N; ++i)
-    if (sh.ng[w1 * N + i] != sh.ng[w2 * N + i]) return false;
-  return true;
-}
 
 __global__ __launch_bounds__(kPoolBlock) void k_pool_insert(PoolParams P) {
   touch_kernargs(P);
@@ -94,57 +88,7 @@ __global__ __launch_bounds__(kPoolBlock) void k_pool_insert(PoolParams P) {
       if (key < 0) continue;  // skipped n-gram
       const uint64_t same = __ballot(lane < W && myk == key);  // the call's n-grams of this key
       if (same >> li >> 1) continue;                             // a later one leads
-      int32_t* bk = bucket(P, b, key);
-      // the old slot `lane` (lanes < G), loaded before the continuations are compared
-      int32_t old[SPEC_MAX_POOL_N - 1];
-      bool held = false;
-      if (lane < G) {
-#pragma unroll
-        for (int i = 0; i < SPEC_MAX_POOL_N - 1; ++i) old[i] = (i < N - 1) ? bk[lane * (N - 1) + i] : -1;
-        held = old[0] >= 0;
-      }
-      // the key's n-grams of this call at their last occurrence, newest (highest w) first
-      bool fresh = false;
-      if ((same >> lane) & 1ull) {
-        fresh = true;
-        for (uint64_t later = same >> lane >> 1; later != 0ull; later &= later - 1ull) {
-          const int w2 = lane + 1 + __ffsll(static_cast<unsigned long long>(later)) - 1;
-          if (same_cont(sh, N, lane, w2)) {
-            fresh = false;
-            break;
-          }
-        }
-      }
-      const uint64_t freshm = __ballot(fresh);
-      const int nfresh = __popcll(freshm);
-      // rank among the fresh ones: the fresh n-grams after this one come first
-      const int rank = __popcll(freshm >> lane) - 1;
-      // the old slot `lane` is kept when no fresh continuation repeats it
-      bool keep = held;
-      if (held) {
-        for (int w2 = 0; w2 < W && keep; ++w2) {
-          if (!((freshm >> w2) & 1ull)) continue;
-          bool eq = true;
-#pragma unroll
-          for (int i = 0; i < SPEC_MAX_POOL_N - 1; ++i)
-            if (i < N - 1) eq = eq && sh.ng[w2 * N + i + 1] == old[i];
-          keep = !eq;
-        }
-      }
-      const uint64_t keepm = __ballot(keep);
-      const int okeep = __popcll(keepm & ((1ull << lane) - 1));  // kept old slots before this one
-      const int total = min(nfresh + __popcll(keepm), G);
-      // every old slot is read above, before any slot is written (the wave runs in lockstep)
-      __builtin_amdgcn_wave_barrier();
-      if (fresh && rank < G)
-        for (int i = 1; i < N; ++i) bk[rank * (N - 1) + (i - 1)] = sh.ng[lane * N + i];
-      if (keep && nfresh + okeep < G) {
-#pragma unroll
-        for (int i = 0; i < SPEC_MAX_POOL_N - 1; ++i)
-          if (i < N - 1) bk[(nfresh + okeep) * (N - 1) + i] = old[i];
-      }
-      if (lane >= total && lane < G)
-        for (int i = 0; i < N - 1; ++i) bk[lane * (N - 1) + i] = -1;
+      rebuild_bucket(sh.ng, N, G, lane, same, bucket(P, b, key), true);
     }
     __syncthreads();  // LDS is reused by the next sequence
   }

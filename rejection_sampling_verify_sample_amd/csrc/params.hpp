@@ -155,4 +155,19 @@ struct PoolParams {
   int32_t* out_count;      // [B] (lookup)
 };
 
+// ---------------------------------------------------------------- hashed n-gram pool
+
+struct CacheParams {
+  int32_t* cache;          // B sequences of seq_elems int32: the clock, then `sets` sets
+  int64_t seq_elems;       // int32 per sequence: 4 + sets * set_elems, rounded up to a multiple of 4
+  int32_t set_elems;       // int32 per set: keys[ways], stamps[ways], slots[ways][G][N-1]
+  int32_t set_shift;       // 32 - log2(sets); 32 when there is one set
+  int32_t B, V, sets, ways, G, N, W;
+  const int32_t* ngrams;   // [B, W, N] (insert)
+  int32_t* out_skipped;    // [B] or null (insert)
+  const int32_t* last;     // [B] (lookup)
+  int32_t* out_cand;       // [B, G, N-1] (lookup)
+  int32_t* out_count;      // [B] (lookup)
+};
+
 }  // namespace sv

@@ -37,7 +37,7 @@ def test_library_is_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 26, names
     L = ctypes.CDLL(rsv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
@@ -197,6 +197,56 @@ def pool_call(fn, **kw):
 ])
 def test_ngram_pool_argument_checks(fn, kw, expect):
     assert pool_call(fn, **kw) == expect
+
+
+def test_ngram_cache_bytes():
+    # per sequence: 4 + sets * (2 * ways + ways * G * (N - 1)) int32, rounded up to a multiple of 4
+    assert rsv.ngram_cache_bytes(32, 512, 8, 7, 5) == 32 * (4 + 512 * (16 + 8 * 7 * 4)) * 4
+    assert rsv.ngram_cache_bytes(3, 1, 1, 1, 2) == 3 * 8 * 4
+    assert rsv.ngram_cache_bytes(2, 2, 3, 2, 3) == 2 * 40 * 4   # 4 + 2 * (6 + 12) = 40
+    assert rsv.ngram_cache_bytes(1, 1, 3, 1, 2) == 16 * 4       # 4 + (6 + 3) = 13 -> 16
+    assert rsv.ngram_cache_bytes(0, 512, 8, 7, 5) == 0
+    for bad in ((-1, 1, 1, 1, 2), (1, 0, 1, 1, 2), (1, 3, 1, 1, 2), (1, 12, 1, 1, 2), (1, (1 << 24) * 2, 1, 1, 2),
+                (1, 1, 0, 1, 2), (1, 1, 65, 1, 2), (1, 1, 1, 0, 2), (1, 1, 1, 65, 2), (1, 1, 1, 1, 1),
+                (1, 1, 1, 1, 18)):
+        assert rsv.ngram_cache_bytes(*bad) == 0, bad
+    assert rsv.ngram_cache_bytes(1, 1 << 24, 1, 1, 2) == (4 + (1 << 24) * 3) * 4
+    # sizes past what int64 byte offsets can address are rejected, not wrapped
+    assert rsv.ngram_cache_bytes(1 << 30, 1 << 24, 64, 64, 17) == 0
+
+
+def cache_call(fn, **kw):
+    a = dict(cache=P, nbytes=1 << 40, B=2, V=10, sets=4, ways=2, G=3, N=4, W=5, ngrams=P, skipped=None, last=P,
+             cand=P, count=P, stream=None)
+    a.update(kw)
+    L = rsv.lib()
+    geo = (a["sets"], a["ways"], a["G"], a["N"])
+    if fn == "init":
+        return L.spec_ngram_cache_init(a["cache"], a["nbytes"], a["B"], *geo, a["stream"])
+    if fn == "insert":
+        return L.spec_ngram_cache_insert(a["cache"], a["nbytes"], a["B"], a["V"], *geo, a["ngrams"], a["W"],
+                                         a["skipped"], a["stream"])
+    return L.spec_ngram_cache_lookup(a["cache"], a["nbytes"], a["B"], a["V"], *geo, a["last"], a["cand"],
+                                     a["count"], a["stream"])
+
+
+@pytest.mark.parametrize("fn,kw,expect", [
+    ("init", dict(sets=3), ERR_SHAPE), ("init", dict(sets=0), ERR_SHAPE), ("init", dict(ways=65), ERR_SHAPE),
+    ("init", dict(G=0), ERR_SHAPE), ("init", dict(N=18), ERR_SHAPE),
+    ("init", dict(cache=None), ERR_NULL), ("init", dict(cache=P + 4), ERR_ALIGN), ("init", dict(nbytes=16), ERR_POOL),
+    ("init", dict(B=0, cache=None), OK),
+    ("insert", dict(W=-1), ERR_SHAPE), ("insert", dict(W=65), ERR_SHAPE), ("insert", dict(V=0), ERR_SHAPE),
+    ("insert", dict(V=(1 << 30) + 1), ERR_SHAPE), ("insert", dict(ways=0), ERR_SHAPE),
+    ("insert", dict(ngrams=None), ERR_NULL), ("insert", dict(ngrams=P + 2), ERR_ALIGN),
+    ("insert", dict(skipped=P + 1), ERR_ALIGN), ("insert", dict(nbytes=100), ERR_POOL),
+    ("insert", dict(B=0), OK), ("insert", dict(W=0, ngrams=None, nbytes=16), ERR_POOL),
+    ("lookup", dict(G=65), ERR_SHAPE), ("lookup", dict(V=0), ERR_SHAPE), ("lookup", dict(sets=6), ERR_SHAPE),
+    ("lookup", dict(last=None), ERR_NULL), ("lookup", dict(cand=None), ERR_NULL),
+    ("lookup", dict(count=None), ERR_NULL), ("lookup", dict(cand=P + 2), ERR_ALIGN),
+    ("lookup", dict(nbytes=8), ERR_POOL), ("lookup", dict(B=0, last=None), OK),
+])
+def test_ngram_cache_argument_checks(fn, kw, expect):
+    assert cache_call(fn, **kw) == expect
 
 
 def ngram_sample(**kw):
