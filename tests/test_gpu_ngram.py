@@ -81,10 +81,12 @@ def test_pool_matches_oracle(B, W, N, V, G, steps, hot, bad):
         assert np.array_equal(cand.cpu().numpy(), ocand)
 
 
-def test_lookup_feeds_the_greedy_verify():
-    """Candidates from the pool verified against logits whose argmax follows one of them."""
+@pytest.mark.parametrize("kind", ["direct", "hashed"])
+def test_lookup_feeds_the_greedy_verify(kind):
+    """Candidates from the pool (direct table, or the hashed one with 4 sets of 2 ways) verified
+    against logits whose argmax follows one of them."""
     B, G, N, V = 8, 4, 5, 300
-    pool = rsv.NgramPool(B, V, G, N, DEV)
+    pool = rsv.NgramPool(B, V, G, N, DEV) if kind == "direct" else rsv.NgramCache(B, V, G, N, 4, 2, DEV)
     rng = np.random.default_rng(5)
     grams = rng.integers(0, V, size=(B, G, N)).astype(np.int32)
     grams[:, :, 0] = np.arange(B)[:, None] % V  # every sequence's grams share its last token
