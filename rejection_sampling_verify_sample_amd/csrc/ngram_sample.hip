@@ -17,7 +17,8 @@
 //                   every block of 256 16-byte vectors with its reference R; segment 0
 //                   of a row (g, i < N-1) also gathers the logits of every
 //                   candidate's token at position i, so the walk needs no further
-//                   look at a row.
+//                   look at a row. A row of at most 16 blocks (64 KB) is read in one
+//                   shot, every load issued at once; longer ones block after block.
 //   k_ngs_verify    one workgroup per sequence. One round of loads stages the
 //                   sequence's row statistics, candidates, uniforms and gathered
 //                   logits in LDS; wave 0 walks the positions and tries (a few dozen
@@ -96,10 +97,163 @@ __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, int64_t k,
 constexpr int kNgsRowWaves = SV_NGS_ROW_WAVES;
 constexpr int kNgsRowBlock = 64 * kNgsRowWaves;
 
+// A row of at most kNgsShotBlocks blocks per wave is read in one shot: every wave
+// issues the loads of all its blocks at once (the whole row is in flight), takes its
+// maximum over them, fixes R = fl(m*c) and then sums each block against that R.
+#ifndef SV_NGS_SHOT_BLOCKS
+#define SV_NGS_SHOT_BLOCKS 4
+#endif
+constexpr int kNgsShotBlocks = SV_NGS_SHOT_BLOCKS;
+
+// Raw words that widen to -inf: two bf16 -inf, or one fp32 -inf.
+template <typename T>
+__device__ __forceinline__ uint32_t neg_inf_word();
+template <>
+__device__ __forceinline__ uint32_t neg_inf_word<bf16_t>() { return 0xFF80FF80u; }
+template <>
+__device__ __forceinline__ uint32_t neg_inf_word<float>() { return 0xFF800000u; }
+
+// The wave's (m, sum of 2^(x*c - fl(m*c))) over its blocks wave, wave + kNgsRowWaves, ...
+// of a row with rb.nb <= kNgsShotBlocks * kNgsRowWaves, and the scalar entries xs (-inf
+// where a lane holds none); each block's sum is stored with that reference.
+template <typename T>
+__device__ __forceinline__ void ngs_row_shot(__amdgpu_buffer_rsrc_t rs, const RowBlocks& rb, int wave, float xs,
+                                             float c, float2* bs, float& m_out, double& s_out) {
+  constexpr int VEC = Elem<T>::kVec;
+  const int lane = threadIdx.x & 63;
+  const int nvec = static_cast<int>(rb.nvec);  // < 2^31: the row's bytes fit a buffer resource
+  u32x4 raw[kNgsShotBlocks][kBlkChunks];
+#pragma unroll
+  for (int j = 0; j < kNgsShotBlocks; ++j) {
+    const int k = wave + j * kNgsRowWaves;
+    load_block(rs, k < rb.nb ? k : rb.nb, raw[j]);  // past the row: reads zeros, replaced below
+  }
+  // vectors past the row's last whole one (the last block's tail, and every block past
+  // the row) become -inf words, so the passes below need no mask
+#pragma unroll
+  for (int j = 0; j < kNgsShotBlocks; ++j) {
+    const int k = wave + j * kNgsRowWaves;
+    if ((k + 1) * kNgsBlkVecs > nvec) {  // wave-uniform
+#pragma unroll
+      for (int u = 0; u < kBlkChunks; ++u) {
+        const bool in = k * kNgsBlkVecs + u * 64 + lane < nvec;
+        const uint32_t ni = neg_inf_word<T>();
+        raw[j][u] = in ? raw[j][u] : u32x4{ni, ni, ni, ni};
+      }
+    }
+  }
+  float mt = xs;
+#pragma unroll
+  for (int j = 0; j < kNgsShotBlocks; ++j)
+#pragma unroll
+    for (int u = 0; u < kBlkChunks; ++u) {
+      float x[VEC];
+      Elem<T>::unpack(raw[j][u], x);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) mt = fmaxf(mt, x[e]);
+    }
+  const float m = lane_f(wave_scan_maxf(mt), 63);
+  const float R = (m > -INFINITY) ? m * c : 0.f;  // 0 while the wave holds no number: every term is 0
+  // the sums widen the raw words again rather than keep every widened entry alive
+  // from the maximum's pass (which would double the registers)
+#pragma unroll
+  for (int j = 0; j < kNgsShotBlocks; ++j)
+#pragma unroll
+    for (int u = 0; u < kBlkChunks; ++u) asm volatile("" : "+v"(raw[j][u]));
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < kNgsShotBlocks; ++j) {
+    const int k = wave + j * kNgsRowWaves;
+    float a = 0.f;
+#pragma unroll
+    for (int u = 0; u < kBlkChunks; ++u) {
+      float x[VEC];
+      Elem<T>::unpack(raw[j][u], x);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) a += exp2_hw(fmaf(x[e], c, -R));
+    }
+    const float sb = lane_f(wave_scan_addf(a), 63);
+    s += static_cast<double>(sb);
+    if (lane == 0 && k < rb.nb) bs[k] = make_float2(R, sb);
+  }
+  if (wave == 0) s += static_cast<double>(lane_f(wave_scan_addf(exp2_hw(fmaf(xs, c, -R))), 63));
+  m_out = m;
+  s_out = s;
+}
+
+// The wave's (m, sum of 2^(x*c - fl(m*c))) over its blocks of segment seg of S, read
+// block after block (the next block's loads issued before this one is reduced), and
+// the scalar entries xs; each block's sum is stored with the reference it was summed
+// against.
+template <typename T>
+__device__ __forceinline__ void ngs_row_pipelined(__amdgpu_buffer_rsrc_t rs, const RowBlocks& rb, int seg, int S,
+                                                  int wave, float xs, float c, float2* bs, float& m_out,
+                                                  double& s_out) {
+  constexpr int VEC = Elem<T>::kVec;
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY;  // the wave's running maximum; R = fl(m*c), 0 while m == -inf
+  float R = 0.f;
+  double s = 0.0;
+  const int64_t b0 = static_cast<int64_t>(rb.nb) * seg / S, b1 = static_cast<int64_t>(rb.nb) * (seg + 1) / S;
+  // software pipeline: the next block's loads are issued before this block is
+  // reduced; past the segment they aim past the row's end, which reads nothing
+  u32x4 raw[kBlkChunks], nxt[kBlkChunks];
+  int64_t k = b0 + wave;
+  load_block(rs, k < b1 ? k : rb.nb, raw);
+  for (; k < b1; k += kNgsRowWaves) {
+    load_block(rs, k + kNgsRowWaves < b1 ? k + kNgsRowWaves : rb.nb, nxt);
+    float x[kBlkChunks][VEC];
+#pragma unroll
+    for (int u = 0; u < kBlkChunks; ++u) Elem<T>::unpack(raw[u], x[u]);
+    if ((k + 1) * kNgsBlkVecs > rb.nvec) {  // the row's last block, not whole
+#pragma unroll
+      for (int u = 0; u < kBlkChunks; ++u) {
+        const bool in = k * kNgsBlkVecs + u * 64 + lane < rb.nvec;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (!in) x[u][e] = -INFINITY;
+      }
+    }
+    float mt = x[0][0];
+#pragma unroll
+    for (int u = 0; u < kBlkChunks; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) mt = fmaxf(mt, x[u][e]);
+    if (__ballot(mt > m)) {  // a new running maximum (the wave reduction only then)
+      const float bm = lane_f(wave_scan_maxf(mt), 63);
+      const float Rn = bm * c;
+      s = (s > 0.0) ? s * static_cast<double>(exp2_hw(static_cast<float>(static_cast<double>(R) - Rn))) : 0.0;
+      m = bm;
+      R = Rn;
+    }
+    float a = 0.f;
+#pragma unroll
+    for (int u = 0; u < kBlkChunks; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) a += exp2_hw(fmaf(x[u][e], c, -R));
+    const float sb = lane_f(wave_scan_addf(a), 63);
+    s += static_cast<double>(sb);
+    if (lane == 0) bs[k] = make_float2(R, sb);
+#pragma unroll
+    for (int u = 0; u < kBlkChunks; ++u) raw[u] = nxt[u];
+  }
+  if (wave == 0) {
+    const float bm = lane_f(wave_scan_maxf(xs), 63);
+    if (bm > m) {
+      const float Rn = bm * c;
+      s = (s > 0.0) ? s * static_cast<double>(exp2_hw(static_cast<float>(static_cast<double>(R) - Rn))) : 0.0;
+      m = bm;
+      R = Rn;
+    }
+    s += static_cast<double>(lane_f(wave_scan_addf(exp2_hw(fmaf(xs, c, -R))), 63));
+  }
+  m_out = m;
+  s_out = s;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kNgsRowBlock) void k_ngs_rowstats(NgramSampleParams P) {
   touch_kernargs(P);
-  constexpr int VEC = Elem<T>::kVec;
   __shared__ float sh_m[kNgsRowWaves];
   __shared__ double sh_s[kNgsRowWaves];
   const int lane = threadIdx.x & 63;
@@ -129,64 +283,14 @@ __global__ __launch_bounds__(kNgsRowBlock) void k_ngs_rowstats(NgramSampleParams
       if (seg == 0 && lane < rb.h) xs = Elem<T>::get(rp, lane);
       if (seg == S - 1 && lane >= 8 && lane - 8 < P.V - rb.tail_lo) xs = Elem<T>::get(rp, rb.tail_lo + lane - 8);
     }
-    float m = -INFINITY;  // the wave's running maximum; R = fl(m*c), 0 while m == -inf
-    float R = 0.f;
-    double s = 0.0;
+    float m;
+    double s;
     float2* bs = P.blk + row * P.nbmax;
-    const int64_t b0 = static_cast<int64_t>(rb.nb) * seg / S, b1 = static_cast<int64_t>(rb.nb) * (seg + 1) / S;
-    // software pipeline: the next block's loads are issued before this block is
-    // reduced; past the segment they aim past the row's end, which reads nothing
     const __amdgpu_buffer_rsrc_t rs = vectors_of(rp, rb);
-    u32x4 raw[kBlkChunks], nxt[kBlkChunks];
-    int64_t k = b0 + wave;
-    load_block(rs, k < b1 ? k : rb.nb, raw);
-    for (; k < b1; k += kNgsRowWaves) {
-      load_block(rs, k + kNgsRowWaves < b1 ? k + kNgsRowWaves : rb.nb, nxt);
-      float x[kBlkChunks][VEC];
-#pragma unroll
-      for (int u = 0; u < kBlkChunks; ++u) Elem<T>::unpack(raw[u], x[u]);
-      if ((k + 1) * kNgsBlkVecs > rb.nvec) {  // the row's last block, not whole
-#pragma unroll
-        for (int u = 0; u < kBlkChunks; ++u) {
-          const bool in = k * kNgsBlkVecs + u * 64 + lane < rb.nvec;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e)
-            if (!in) x[u][e] = -INFINITY;
-        }
-      }
-      float mt = x[0][0];
-#pragma unroll
-      for (int u = 0; u < kBlkChunks; ++u)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) mt = fmaxf(mt, x[u][e]);
-      if (__ballot(mt > m)) {  // a new running maximum (the wave reduction only then)
-        const float bm = lane_f(wave_scan_maxf(mt), 63);
-        const float Rn = bm * c;
-        s = (s > 0.0) ? s * static_cast<double>(exp2_hw(static_cast<float>(static_cast<double>(R) - Rn))) : 0.0;
-        m = bm;
-        R = Rn;
-      }
-      float a = 0.f;
-#pragma unroll
-      for (int u = 0; u < kBlkChunks; ++u)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) a += exp2_hw(fmaf(x[u][e], c, -R));
-      const float sb = lane_f(wave_scan_addf(a), 63);
-      s += static_cast<double>(sb);
-      if (lane == 0) bs[k] = make_float2(R, sb);
-#pragma unroll
-      for (int u = 0; u < kBlkChunks; ++u) raw[u] = nxt[u];
-    }
-    if (wave == 0) {
-      const float bm = lane_f(wave_scan_maxf(xs), 63);
-      if (bm > m) {
-        const float Rn = bm * c;
-        s = (s > 0.0) ? s * static_cast<double>(exp2_hw(static_cast<float>(static_cast<double>(R) - Rn))) : 0.0;
-        m = bm;
-        R = Rn;
-      }
-      s += static_cast<double>(lane_f(wave_scan_addf(exp2_hw(fmaf(xs, c, -R))), 63));
-    }
+    if (S == 1 && rb.nb <= kNgsShotBlocks * kNgsRowWaves)
+      ngs_row_shot<T>(rs, rb, wave, xs, c, bs, m, s);
+    else
+      ngs_row_pipelined<T>(rs, rb, seg, S, wave, xs, c, bs, m, s);
     if (lane == 0) {
       sh_m[wave] = m;
       sh_s[wave] = s;
