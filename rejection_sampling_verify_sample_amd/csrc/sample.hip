@@ -358,9 +358,20 @@ struct ResidualF {
   __device__ __forceinline__ float target(float xt) const {
     return order_key(xt) >= kt ? exp2_hw(fmaf(xt, c, -Rt)) * it : 0.f;
   }
-  __device__ __forceinline__ float operator()(float xt, float xq) const {
+  // max(0, pt - q'(xq)), pt the entry's p' value
+  __device__ __forceinline__ float residual(float pt, float xq) const {
     const float pq = order_key(xq) >= kq ? exp2_hw(fmaf(xq, c, -Rq)) * iq : 0.f;
-    return fmaxf(target(xt) - pq, 0.f);
+    return fmaxf(pt - pq, 0.f);
+  }
+  __device__ __forceinline__ float operator()(float xt, float xq) const { return residual(target(xt), xq); }
+  // The kept target law p' alone (no draft side): the draw's weights when the
+  // residual has no mass, and those of the filtered bonus draw.
+  __device__ __forceinline__ ResidualF target_only() const {
+    ResidualF r = *this;
+    r.Rq = 0.f;
+    r.iq = 0.f;
+    r.kq = 0xFFFFFFFFu;
+    return r;
   }
 };
 
@@ -437,7 +448,9 @@ __device__ __forceinline__ void chunk_lane_weights(const T* tr, const T* dr, boo
 
 // The mass of scalar chunk c (the head or the tail, fewer than VEC elements),
 // computed by one wave; lane 0 stores (chunk max, chunk mass). Bonus chunks are
-// summed against fl(chunk max * c); residual chunks store max -inf.
+// summed against fl(chunk max * c); residual chunks store max -inf, except on the
+// filtered laws, whose residual chunks store the chunk's mass of p' in place of the
+// maximum (the draw's weights when the residual has no mass).
 template <typename T, typename Res>
 __device__ __forceinline__ void wave_scalar_chunk_mass(const SampleParams& P, const T* tr, const T* dr,
                                                        const Chunks& ch, int c, bool bonus, const Res& res,
@@ -452,6 +465,10 @@ __device__ __forceinline__ void wave_scalar_chunk_mass(const SampleParams& P, co
   if (bonus) {
     mx = wave_max(xt);
     a = (in && mx > -INFINITY) ? exp2_hw(fmaf(xt, P.c, -(mx * P.c))) : 0.f;
+  } else if constexpr (std::is_same<Res, ResidualF>::value) {
+    const float pt = in ? res.target(xt) : 0.f;
+    a = in ? res.residual(pt, Elem<T>::get(dr, e)) : 0.f;
+    mx = wave_sumf(pt);
   } else {
     a = in ? res(xt, Elem<T>::get(dr, e)) : 0.f;
   }
@@ -465,7 +482,8 @@ __device__ __forceinline__ void wave_scalar_chunk_mass(const SampleParams& P, co
 // The masses of vector chunks c, c + cstride, ..., (CU of them, below cend),
 // computed by one wave: the loads of all of them are issued before any is
 // reduced (kept as raw 16-byte vectors, so 2*CU loads per lane cost 8*CU
-// registers), and lane 63 stores (chunk max, chunk mass). Two chunks per wave
+// registers), and lane 63 stores (chunk max, chunk mass); on the filtered laws a
+// residual chunk stores its mass of p' in place of the maximum, as above. Two chunks per wave
 // measured best on gfx950 (two rounds of loads per wave at the 64 x 128k shape;
 // one, three or four chunks per round were 0.3-0.5 us slower per verify round).
 #ifndef SV_CHUNKS_PER_WAVE
@@ -525,8 +543,19 @@ __device__ __forceinline__ void wave_vector_chunks_mass(const SampleParams& P, c
 #pragma unroll
         for (int e = 0; e < VEC; ++e) xq[e] = -INFINITY;
       }
+      if constexpr (std::is_same<Res, ResidualF>::value) {
+        float ap = 0.f;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) a += res(xt[e], xq[e]);
+        for (int e = 0; e < VEC; ++e) {
+          const float pt = res.target(xt[e]);
+          ap += pt;
+          a += res.residual(pt, xq[e]);
+        }
+        mx = wave_scan_addf(ap);  // lane 63: the chunk's mass of p'
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) a += res(xt[e], xq[e]);
+      }
     }
     const float sum = wave_scan_addf(a);  // lane 63 holds the chunk's total
     if (lane == 63) {
@@ -779,32 +808,50 @@ __device__ __forceinline__ void draw_core(const SampleParams& P, const int b, co
   auto factor = [&](float cmj) -> float {
     return exp2_hw(static_cast<float>(static_cast<double>(cmj * P.c) - static_cast<double>(RMf)));
   };
+  // usep (filtered laws, wave-uniform): the residual has no mass, so the draw takes
+  // p'_n, whose chunk masses pass 2 left in place of the chunk maxima
+  bool usep = false;
   auto mass_of = [&](float cmj, double csj) -> double {
+    if (FILT && usep) return cmj > 0.f ? static_cast<double>(cmj) : 0.0;
     if (!bonus) return csj;
     return csj > 0.0 ? csj * static_cast<double>(factor(cmj)) : 0.0;
   };
-  double mine = 0.0;
-  int last_pos = -1;
-  float cm_last = 0.f;
-  if (cached) {
+  double mine, incl, Z;
+  int last_pos;
+  float cm_last;
+  auto totals = [&]() {
+    mine = 0.0;
+    last_pos = -1;
+    cm_last = 0.f;
+    if (cached) {
 #pragma unroll
-    for (int i = 0; i < kDrawRegChunks; ++i) {
-      const double mj = mass_of(cmr[i], csr[i]);  // 0 past the run
-      mine += mj;
-      if (mj > 0.0) {
-        last_pos = j0 + i;
-        cm_last = cmr[i];
+      for (int i = 0; i < kDrawRegChunks; ++i) {
+        const double mj = mass_of(cmr[i], csr[i]);  // 0 past the run
+        mine += mj;
+        if (mj > 0.0) {
+          last_pos = j0 + i;
+          cm_last = cmr[i];
+        }
+      }
+    } else {
+      for (int j = j0; j < j1; ++j) {
+        const double mj = mass_of(cm[j], cs[j]);
+        mine += mj;
+        if (mj > 0.0) last_pos = j;
       }
     }
-  } else {
-    for (int j = j0; j < j1; ++j) {
-      const double mj = mass_of(cm[j], cs[j]);
-      mine += mj;
-      if (mj > 0.0) last_pos = j;
+    incl = wave_scan_add(mine);  // chunk order, fp64
+    Z = lane_d(incl, 63);
+  };
+  totals();
+  ResOf<FILT> rw = res;  // the in-chunk weights
+  if constexpr (FILT) {
+    if (!is_bonus && !(Z > 0.0 && isfinite(Z))) {
+      usep = true;
+      rw = res.target_only();
+      totals();
     }
   }
-  const double incl = wave_scan_add(mine);  // chunk order, fp64
-  const double Z = lane_d(incl, 63);
   int32_t* ot = P.out_tokens + static_cast<int64_t>(b) * (K + 1);
   if (is_bonus && !(Z > 0.0 && isfinite(Z))) {  // a bonus row with no mass: fault
     for (int i = lane; i <= K; i += 64) ot[i] = -1;
@@ -812,7 +859,8 @@ __device__ __forceinline__ void draw_core(const SampleParams& P, const int b, co
     return;
   }
   if (!is_bonus && !(Z > 0.0 && isfinite(Z))) {
-    // zero residual mass: draw from p_n (p'_n when filtered) over the whole row
+    // zero residual mass: draw from p_n over the whole row (filtered laws reach this
+    // only when p'_n's chunk masses hold none either)
     auto pw = [&](int64_t e) { return res.target(Elem<T>::get(tr, e)); };
     float a = 0.f;
     for (int64_t e = lane; e < P.V; e += 64) a += pw(e);
@@ -888,7 +936,7 @@ __device__ __forceinline__ void draw_core(const SampleParams& P, const int b, co
     int64_t kf = -1, kl = -1;
     for (int64_t e = lo; e < hi; ++e) {
       const float xt = Elem<T>::get(tr, e);
-      const float wv = bonus ? exp2_hw(fmaf(xt, P.c, -R)) : res(xt, Elem<T>::get(dr, e));
+      const float wv = bonus ? exp2_hw(fmaf(xt, P.c, -R)) : rw(xt, Elem<T>::get(dr, e));
       run += wv;
       if (wv > 0.f) kl = e;
       if (kf < 0 && static_cast<double>(run) > tau) kf = e;
@@ -897,7 +945,7 @@ __device__ __forceinline__ void draw_core(const SampleParams& P, const int b, co
   } else {
     const bool paired = is_bonus || head_elems(dr, P.V) == ch.h;
     float w[VEC];
-    chunk_lane_weights<T>(tr, dr, paired, ch, jstar, bonus, res, P.c, R, w);
+    chunk_lane_weights<T>(tr, dr, paired, ch, jstar, bonus, rw, P.c, R, w);
     float ls = 0.f;
     int kl = -1;
 #pragma unroll

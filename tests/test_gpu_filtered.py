@@ -285,3 +285,43 @@ def test_one_read_top_p_and_large_top_k(dtype, V):
     assert np.array_equal(kept[sure], kept2[sure]), (kept, kept2)
     same_rows = (res.min_margin() >= 1e-6)
     assert np.array_equal(tok[same_rows], tok2[same_rows]) and np.array_equal(n[same_rows], n2[same_rows])
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 50021), ("bf16", 50021), ("f32", 152064)])
+def test_filtered_residual_without_mass_draws_from_the_kept_target(dtype, V):
+    """Draft rows equal to the target rows: the same filter keeps the same law on both
+    sides (p' = q'), and a draft token outside the kept set is rejected (q'(x) = 0 and
+    p'(x) = 0), leaving a residual with no mass, so the token is drawn from p'_n. The
+    kept set spans many chunks of the row; the draws are compared with the oracle."""
+    log(f"filtered zero residual {dtype} V={V}")
+    rng = np.random.default_rng(23)
+    B, K = 16, 2
+    tgt = rng.normal(0, 1, (B, K + 1, V)).astype(np.float32)
+    for b in range(B):
+        for i in range(K + 1):
+            hot = rng.choice(V, 40, replace=False)
+            tgt[b, i, hot] = rng.uniform(7.0, 9.0, 40).astype(np.float32)
+    drf = tgt[:, :K].copy()
+    toks = np.zeros((B, K), dtype=np.int64)
+    for b in range(B):
+        for i in range(K):
+            toks[b, i] = int(np.argmin(tgt[b, i]))  # never kept by top-p 0.9
+    uni = rng.random((B, K + 1, 2)).astype(np.float32)
+    ks = np.zeros(B, dtype=np.int32)
+    ps = np.full(B, 0.9, dtype=np.float32)
+    ps[::4] = 0.5
+    if dtype == "f32":
+        t, tg, dr = _f32_tensors(tgt, drf, toks, uni), tgt, drf
+    else:
+        t, tg, dr = _bf16_tensors(tgt, drf, toks, uni)
+    tok, n, probs, kept = run_gpu(t, ks, ps)
+    res = oracle.oracle_sample_filtered(tg, dr, toks, uni, 1.0, ks, ps)
+    assert np.all(res.n_accepted == 0) and np.all(n == 0), (n, res.n_accepted)
+    assert np.all(res.fallback), res.fallback  # the residual held no mass in every row
+    rep = compare_filtered(tg, dr, toks, uni, 1.0, ks, ps, res, tok, n, probs, kept)
+    log(f"  {rep.summary()}")
+    rep.check_accounting()
+    # every draw lands on a token the target's filter keeps at position 0
+    for b in range(B):
+        x0 = tg[b, 0]
+        assert tok[b, 0] >= 0 and x0[tok[b, 0]] >= np.sort(x0)[-int(kept[b, 0])], (b, tok[b, 0])
