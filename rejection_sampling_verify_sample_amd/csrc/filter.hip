@@ -37,7 +37,7 @@
 namespace sv {
 
 constexpr int kFiltBlock = 256;
-constexpr int kFiltUnroll = 2;
+constexpr int kFiltUnroll = 4;
 constexpr int kHistBins = 2048;
 constexpr int kFixBits = 40;
 constexpr int kFiltCap = 2048;   // candidate buffer of the one-pass top-k path (a power of two)
@@ -1649,7 +1649,7 @@ union FiltLds {
 };
 
 #ifndef SV_FILT_ROWS_GRID
-#define SV_FILT_ROWS_GRID 256  // workgroups of the multi-pass kernel
+#define SV_FILT_ROWS_GRID 512  // workgroups of the multi-pass kernel
 #endif
 #ifndef SV_FILT_MINB
 #define SV_FILT_MINB 5  // workgroups per CU the one-read kernel is compiled for (its LDS allows five)
