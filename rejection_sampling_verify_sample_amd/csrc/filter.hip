@@ -1128,9 +1128,12 @@ __device__ void scan_wide(WideBuf& wb, uint64_t r, double P, uint64_t A0) {
 // then top-p on the top-k law, or on the whole row when top-k is off (the row's mass
 // outside the buffer is Zrest). False (nothing written) when the buffer does not
 // hold the cut. Results as in the multi-pass select.
+// With Aabove > 0 (top-p alone), the buffer holds a band of keys and Nabove entries of
+// mass Aabove lie above it: the cut runs from that mass on, and those entries are kept.
 template <typename T>
 __device__ bool wide_cut(WideBuf& wb, int n, int kk, bool k_on, float pp, bool p_on, float c, float Rf,
-                         uint64_t Zrest, uint32_t& thr_out, uint64_t& kept_n, uint64_t& kept_m) {
+                         uint64_t Zrest, uint32_t& thr_out, uint64_t& kept_n, uint64_t& kept_m,
+                         uint64_t Aabove = 0, uint64_t Nabove = 0) {
   using WK = WideKey<T>;
   const int w = threadIdx.x >> 6;
   auto mass = [&](uint32_t k) { return to_fixed(fminf(exp2_hw(fmaf(key_value(WK::full(k)), c, -Rf)), 1.f)); };
@@ -1183,10 +1186,11 @@ __device__ bool wide_cut(WideBuf& wb, int n, int kk, bool k_on, float pp, bool p
       if (k >= lo) zc += mass(k);
     }
     const uint64_t Zc = block_sum_u64(zc);
-    const double Pm = static_cast<double>(pp) * static_cast<double>(Zc + Zrest);
-    if (static_cast<double>(Zc) < Pm) return false;  // the cut lies below the bound
+    const double Pm = static_cast<double>(pp) * static_cast<double>(Zc + Zrest + Aabove);
+    if (static_cast<double>(Zc + Aabove) < Pm) return false;  // the cut lies below the bound
+    if (Aabove > 0 && static_cast<double>(Aabove) >= Pm) return false;  // above the band
     uint32_t prefix = 0;
-    uint64_t A0 = 0;
+    uint64_t A0 = Aabove;
     for (int lev = 0; lev < levels; ++lev) {
       hist_wide<T, true>(wb, n, kmin, 8 * (levels - 1 - lev), lev == 0, prefix, lo, mass);
       scan_wide<true>(wb, 0, Pm, A0);
@@ -1206,8 +1210,8 @@ __device__ bool wide_cut(WideBuf& wb, int n, int kk, bool k_on, float pp, bool p
       ms += mass(k);
     }
   }
-  kept_n = block_sum_u64(cn);
-  kept_m = block_sum_u64(ms);
+  kept_n = block_sum_u64(cn) + Nabove;
+  kept_m = block_sum_u64(ms) + Aabove;
   thr_out = WK::thr(thr);
   return true;
 }
@@ -1553,6 +1557,290 @@ __device__ __forceinline__ bool hist16_row(const SampleParams& P, const FiltRow&
   return ok;
 }
 
+// ---------------------------------------------------------------- long fp32 rows with top-p alone: counts, then a band
+//
+// An fp32 row whose nucleus is larger than the buffer (a flat row with top-p alone)
+// is read twice instead of going to the multi-pass select. The first read counts its
+// entries in 4096 bins of 1/128 of a doubling of mass each (32 doublings), from one
+// doubling above the first step's maximum down (entries above kept as keys, those below summed as the
+// rest), and finds the row maximum. A bin's entries take masses between those of its
+// edges, so the counts bound the mass above every bin, and the bins where the cut can
+// lie form a band. The second read sums every entry's fixed-point mass exactly, the
+// whole row and the part above the band, and keeps the band's entries as keys; the cut
+// then runs on them from the mass above the band. The masses and the reference are the
+// multi-pass select's, so are the results. A bin index is a monotone function of the
+// value computed the same way in both reads, so the band holds whole ties.
+
+constexpr int kMassBins = 4096;       // bins of the first read (the bf16 route's key counts' memory)
+#ifndef SV_F32_BINS_PER_DOUBLING
+#define SV_F32_BINS_PER_DOUBLING 128
+#endif
+constexpr float kBinsPerDoubling = SV_F32_BINS_PER_DOUBLING;
+constexpr double kRestSlack = 1e-5;   // relative bound on the rounding of the first read's rest sum
+static_assert(kMassBins <= kHistKeys, "the bins use the key counts' memory");
+
+// Bin of x: -1 above mref (the high list), kMassBins below the counted bins (or NaN).
+__device__ __forceinline__ int mass_bin(float x, float mref, float s) {
+  if (x > mref) return -1;
+  const float d = (mref - x) * s;
+  return d < static_cast<float>(kMassBins) ? static_cast<int>(d) : kMassBins;
+}
+
+// The entries of 16-byte vector v of an fp32 row (those whose bit is set in `valid`)
+// in the first read: the maximum, the bin counts, the high list, the rest.
+__device__ __forceinline__ void f32_count_vec(WideBuf& wb, const u32x4& v, uint32_t valid, float mref, float s,
+                                              float c, float Lc, float& m, float& rs) {
+  const float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+  float vmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (!((valid >> e) & 1u)) continue;
+    vmax = fmaxf(vmax, x[e]);
+    const float d = (mref - x[e]) * s;  // NaN for a NaN entry: no bin, no rest
+    if (d >= 0.f && d < static_cast<float>(kMassBins)) atomicAdd(&wb.h.cnt[static_cast<int>(d)], 1u);
+    rs += (d >= static_cast<float>(kMassBins)) ? exp2_hw(fmaf(x[e], c, -Lc)) : 0.f;
+  }
+  m = fmaxf(m, vmax);
+  if (__ballot(vmax > mref)) {  // rare: entries above the counted bins, kept as full keys
+    uint32_t take = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) take |= (((valid >> e) & 1u) && x[e] > mref ? 1u : 0u) << e;
+    uint32_t pos = reserve_slots(wb.nbuf, static_cast<uint32_t>(__popc(take)));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((take >> e) & 1u) {
+        if (pos < static_cast<uint32_t>(kHighCap)) wb.h.high[pos] = order_key(x[e]);
+        ++pos;
+      }
+  }
+}
+
+// Visit every entry of a long fp32 row with 16-byte loads, kWideUnroll per thread per
+// step: f(vector, valid mask) for the whole vectors, then the scalar head (lanes 0-3 of
+// wave 0) and tail (lanes 4-7) as vectors with one valid entry; every lane of each
+// wave takes part in every call.
+template <typename F>
+__device__ __forceinline__ void f32_visit(const float* row, int64_t V, F&& f) {
+  constexpr int VEC = 4, BS = kFiltBlock, U = kWideUnroll;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t h = head_elems(row, V);
+  const int64_t nvec = (V - h) / VEC;
+  const u32x4* vb = reinterpret_cast<const u32x4*>(row + h);
+  const int64_t nsteps = nvec / (U * BS);
+  for (int64_t st = 0; st < nsteps; ++st) {
+    u32x4 cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = load_stream(vb + st * (U * BS) + threadIdx.x + u * BS);
+#pragma unroll
+    for (int u = 0; u < U; ++u) f(cur[u], 0xFu);
+  }
+  for (int64_t base = nsteps * (U * BS); base < nvec; base += BS) {
+    const int64_t vr = base + threadIdx.x;
+    const bool in = vr < nvec;
+    f(in ? load_stream(vb + vr) : u32x4{0u, 0u, 0u, 0u}, in ? 0xFu : 0u);
+  }
+  if (w == 0) {
+    const int64_t tail_lo = h + nvec * VEC;
+    const int64_t e = lane < 4 ? lane : tail_lo + (lane - 4);
+    const bool in = lane < 4 ? lane < h : (lane < 8 && e < V);
+    f(u32x4{in ? __float_as_uint(row[e]) : 0u, 0u, 0u, 0u}, in ? 1u : 0u);
+  }
+}
+
+// The first read of a long fp32 row (V > the buffer): bin counts in wb.h.cnt, the
+// entries above mref as keys in wb.h.high (wb.nbuf of them), each thread's rest sum
+// 2^(x*c - fl(loV*c)) over the entries below the bins, and the row maximum. False
+// when the row needs the multi-pass select (a first step with no finite logit).
+__device__ bool f32_count(const float* row, int64_t V, WideBuf& wb, float c, float& rowmax, float& mref_out,
+                          float& s_out, float& loV_out, double& rest_out) {
+  constexpr int BS = kFiltBlock, U = kWideUnroll, W = kFiltBlock / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) wb.nbuf = 0;
+  for (int i = threadIdx.x; i < kMassBins; i += BS) wb.h.cnt[i] = 0;
+  // the first step's maximum places the bins
+  const u32x4* vb = reinterpret_cast<const u32x4*>(row + head_elems(row, V));
+  float sm = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const u32x4 v = load_stream(vb + threadIdx.x + u * BS);  // V > the buffer: a whole first step
+    sm = fmaxf(sm, fmaxf(fmaxf(__uint_as_float(v.x), __uint_as_float(v.y)),
+                         fmaxf(__uint_as_float(v.z), __uint_as_float(v.w))));
+  }
+  sm = wave_max(sm);
+  if (lane == 0) wb.wmax[w] = sm;
+  __syncthreads();
+  float Ms = wb.wmax[0];
+#pragma unroll
+  for (int o = 1; o < W; ++o) Ms = fmaxf(Ms, wb.wmax[o]);
+  __syncthreads();  // wmax is written again at the end
+  if (!(Ms > -INFINITY) || !(Ms < INFINITY)) return false;  // uniform
+  const float s = c * kBinsPerDoubling;                        // bins per unit of logit
+  const float mref = Ms + 1.f / c;                             // one doubling of mass above
+  const float loV = mref - static_cast<float>(kMassBins) / s;  // about where the bins end
+  if (!(mref < INFINITY) || !(loV > -INFINITY)) return false;
+  const float Lc = loV * c;
+  float m = -INFINITY, rs = 0.f;
+  double rest = 0.0;
+  int k = 0;
+  f32_visit(row, V, [&](u32x4 v, uint32_t valid) {
+    f32_count_vec(wb, v, valid, mref, s, c, Lc, m, rs);
+    if (++k == 8) {  // the rest into double every few vectors
+      rest += static_cast<double>(rs);
+      rs = 0.f;
+      k = 0;
+    }
+  });
+  rest += static_cast<double>(rs);
+  __syncthreads();
+  const float wm = wave_max(m);
+  if (lane == 0) wb.wmax[w] = wm;
+  __syncthreads();
+  float M = wb.wmax[0];
+#pragma unroll
+  for (int o = 1; o < W; ++o) M = fmaxf(M, wb.wmax[o]);
+  rowmax = M;
+  mref_out = mref;
+  s_out = s;
+  loV_out = loV;
+  rest_out = rest;
+  return true;
+}
+
+// Top-p alone on a long fp32 row in two reads (see above). False (nothing written)
+// when the counts cannot place the cut in a band that fits the buffer: the row then
+// takes the multi-pass select.
+__device__ __forceinline__ bool f32_topp_row(const SampleParams& P, const FiltRow& r, WideBuf& wb, float pp, float xl) {
+  const float c = P.c;
+  const float* row = static_cast<const float*>(r.row);
+  const int64_t V = P.V;
+  if (!(pp > 0.f)) return false;  // uniform: p <= 0 keeps the largest logit's entries (the multi-pass select)
+  float M, mref, s, loV;
+  double rest;
+  if (!f32_count(row, V, wb, c, M, mref, s, loV, rest)) {
+    __syncthreads();
+    return false;
+  }
+  const uint32_t nh = wb.nbuf;
+  if (nh > static_cast<uint32_t>(kHighCap) || !(M > -INFINITY)) {
+    __syncthreads();
+    return false;
+  }
+  const float Rf = M * c + 1.f;  // as in the multi-pass select
+  auto fmv = [&](float x) -> uint64_t { return to_fixed(fminf(exp2_hw(fmaf(x, c, -Rf)), 1.f)); };
+  const int t = threadIdx.x;
+  // exact masses of the high list; the rest approximately, with its bounds
+  const uint64_t Hm = block_sum_u64(t < static_cast<int>(nh) ? fmv(key_value(wb.h.high[t])) : 0u);
+  const uint64_t Zr = rest_fixed(wb, rest, loV, c, Rf);
+  const double rlo = fmax(0.0, static_cast<double>(Zr) * (1.0 - kRestSlack) - static_cast<double>(V));
+  const double rhi = static_cast<double>(Zr) * (1.0 + kRestSlack) + static_cast<double>(V);
+  // bounds of a bin's entry masses: its edges, widened past the rounding of the bin
+  // index and of the edges (a few units in the last place of mref, in bins) and of the
+  // hardware exponential (relative 1e-6)
+  const float slack = 1e-3f + fabsf(mref) * s * 4e-7f;
+  auto bin_lo = [&](int j) -> uint64_t {
+    const uint64_t f = fmv(mref - (static_cast<float>(j) + 1.f + slack) / s);
+    return f > f / 1000000u + 1u ? f - f / 1000000u - 1u : 0u;
+  };
+  auto bin_hi = [&](int j) -> uint64_t {
+    const uint64_t f = fmv(mref - (static_cast<float>(j) - slack) / s);
+    return f + f / 1000000u + 1u;
+  };
+  // thread t holds bins 16t .. 16t + 15 (j grows as the value falls)
+  constexpr int per = kMassBins / kFiltBlock;
+  const int j0 = per * t;
+  uint64_t tl = 0, tu = 0;
+#pragma unroll 1
+  for (int i = 0; i < per; ++i) {
+    const uint64_t n = wb.h.cnt[j0 + i];
+    if (n) {
+      tl += n * bin_lo(j0 + i);
+      tu += n * bin_hi(j0 + i);
+    }
+  }
+  uint64_t Ltot, Utot;
+  const uint64_t le = block_excl_u64(tl, Ltot);  // the bins above thread t's (threads before t)
+  const uint64_t ue = block_excl_u64(tu, Utot);
+  const double Plo = static_cast<double>(pp) * (static_cast<double>(Hm + Ltot) + rlo);
+  const double Phi = static_cast<double>(pp) * (static_cast<double>(Hm + Utot) + rhi);
+  // the band [ja, jb]: the cut's bin j* is the first whose mass from the top reaches
+  // p * Z, so ja <= j* with ja the first bin whose upper bound reaches Plo, and j* <= jb
+  // with jb the first bin whose lower bound reaches Phi; bin -1 is the high list
+  int ja = kMassBins, jb = kMassBins;
+  {
+    uint64_t cu = Hm + ue, cl = Hm + le;
+#pragma unroll 1
+    for (int i = 0; i < per; ++i) {
+      const uint64_t n = wb.h.cnt[j0 + i];
+      if (n) {
+        cu += n * bin_hi(j0 + i);
+        cl += n * bin_lo(j0 + i);
+      }
+      if (ja == kMassBins && static_cast<double>(cu) >= Plo) ja = j0 + i;
+      if (jb == kMassBins && static_cast<double>(cl) >= Phi) jb = j0 + i;
+    }
+  }
+  ja = block_min_i32(wb.wmin, ja);
+  jb = block_min_i32(wb.wmin, jb);
+  if (static_cast<double>(Hm) >= Plo) ja = -1;  // the cut may lie in the high list
+  if (static_cast<double>(Hm) >= Phi) jb = -1;  // it does
+  if (jb >= kMassBins || ja > jb) {  // the cut may lie below the counted bins
+    __syncthreads();
+    return false;
+  }
+  uint64_t nbt = (t == 0 && ja < 0) ? nh : 0u;
+#pragma unroll 1
+  for (int i = 0; i < per; ++i)
+    if (j0 + i >= ja && j0 + i <= jb) nbt += wb.h.cnt[j0 + i];
+  const uint64_t nband = block_sum_u64(nbt);
+  if (nband == 0 || nband > static_cast<uint64_t>(WideKey<float>::kCap)) {
+    __syncthreads();
+    return false;
+  }
+  __syncthreads();  // every count has been read: the buffer reuses their memory
+  if (t == 0) wb.nbuf = 0;
+  __syncthreads();
+  // second read: exact masses, the band's entries as keys
+  uint64_t zt = 0, za = 0, zb = 0, na = 0;
+  f32_visit(row, V, [&](u32x4 v, uint32_t valid) {
+    const float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+    uint32_t take = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!((valid >> e) & 1u)) continue;
+      const uint64_t fm = fmv(x[e]);
+      const int j = mass_bin(x[e], mref, s);
+      const bool above = j < ja, in_band = j >= ja && j <= jb;  // selects, not branches
+      zt += fm;
+      za += above ? fm : 0u;
+      na += above ? 1u : 0u;
+      zb += in_band ? fm : 0u;
+      take |= (in_band ? 1u : 0u) << e;
+    }
+    if (__ballot(take != 0u)) {
+      uint32_t pos = reserve_slots(wb.nbuf, static_cast<uint32_t>(__popc(take)));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((take >> e) & 1u) {
+          if (pos < static_cast<uint32_t>(WideKey<float>::kCap)) wb.key[pos] = order_key(x[e]);
+          ++pos;
+        }
+    }
+  });
+  __syncthreads();
+  const uint32_t nb = wb.nbuf;
+  const uint64_t Zt = block_sum_u64(zt), A = block_sum_u64(za), Zb = block_sum_u64(zb), Na = block_sum_u64(na);
+  if (nb != nband) {  // uniform; the two reads see the same row, so this does not happen
+    __syncthreads();
+    return false;
+  }
+  uint32_t thr;
+  uint64_t kn, km;
+  const bool ok = wide_cut<float>(wb, static_cast<int>(nb), 0, false, pp, true, c, Rf, Zt - A - Zb, thr, kn, km, A, Na);
+  if (ok) filt_write(P, r, Rf, static_cast<double>(km) * 0x1p-40, thr, kn, xl);
+  __syncthreads();  // shared memory is reused by the next row
+  return ok;
+}
+
 // The one-read path of a row with top-p on, or with top-k and k > 64: top-p alone on
 // a long bf16 row goes through the key counts, every other row through the buffer.
 // False (nothing written) when the row needs the multi-pass select.
@@ -1562,7 +1850,12 @@ __device__ __forceinline__ bool filter_row_wide(const SampleParams& P, const Fil
   if constexpr (sizeof(T) == 2) {
     if (!k_on && P.V > WideKey<T>::kCap) return hist16_row(P, r, wb, pp, xl);
   }
-  return buffer_row<T>(P, r, wb, kk, k_on, pp, p_on, xl);
+  if (buffer_row<T>(P, r, wb, kk, k_on, pp, p_on, xl)) return true;
+  if constexpr (sizeof(T) == 4) {
+    // a long fp32 row whose nucleus the buffer cannot hold: two reads
+    if (!k_on && p_on && P.V > WideKey<T>::kCap) return f32_topp_row(P, r, wb, pp, xl);
+  }
+  return false;
 }
 
 // The multi-pass select of a row (any filter setting): a radix select over the

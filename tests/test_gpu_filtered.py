@@ -325,3 +325,35 @@ def test_filtered_residual_without_mass_draws_from_the_kept_target(dtype, V):
     for b in range(B):
         x0 = tg[b, 0]
         assert tok[b, 0] >= 0 and x0[tok[b, 0]] >= np.sort(x0)[-int(kept[b, 0])], (b, tok[b, 0])
+
+
+@pytest.mark.parametrize("V", [152064, 40003, 6145])
+def test_two_read_top_p_on_long_fp32_rows(V):
+    """Top-p alone on fp32 rows whose nucleus is larger than the candidate buffer (flat
+    rows) takes two reads: counts per key half bound the cut to a band of keys, and the
+    second read cuts there with exact masses. The kept counts, thresholds and the whole
+    round equal the multi-pass select's bit for bit, and agree with the oracle."""
+    log(f"two-read top-p fp32 V={V}")
+    rng = np.random.default_rng(31)
+    B, K = 8, 2
+    tgt = rng.normal(0, 0.5, (B, K + 1, V)).astype(np.float32)    # flat: most of the row is kept
+    tgt[1] = rng.normal(0, 1.0, (K + 1, V))
+    tgt[2] = np.round(tgt[2] * 8) / 8                              # ties across the band
+    tgt[3, :, : V // 3] = -np.inf                                  # masked third
+    tgt[4] = -np.abs(tgt[4]) - 3.0                                 # every logit negative
+    tgt[5, :, rng.choice(V, 3, replace=False)] = 6.0               # a few raised tokens on a flat row
+    tgt[6] = rng.uniform(-1, 1, (K + 1, V))
+    drf = (tgt[:, :K] + rng.normal(0, 0.3, (B, K, V))).astype(np.float32)
+    toks = rng.integers(0, V, (B, K))
+    uni = rng.random((B, K + 1, 2)).astype(np.float32)
+    ks = np.zeros(B, dtype=np.int32)
+    ps = np.array([0.9, 0.5, 0.9, 0.95, 0.99, 0.9, 0.999, 0.7], dtype=np.float32)
+    t = _f32_tensors(tgt, drf, toks, uni, T=0.8)
+    tok, n, probs, kept = run_gpu(t, ks, ps)
+    tok2, n2, probs2, kept2 = _run_multi_pass(t, ks, ps)
+    assert np.array_equal(kept, kept2), (kept, kept2)
+    assert np.array_equal(tok, tok2) and np.array_equal(n, n2)
+    res = oracle.oracle_sample_filtered(tgt, drf, toks, uni, 0.8, ks, ps)
+    rep = compare_filtered(tgt, drf, toks, uni, 0.8, ks, ps, res, tok, n, probs, kept)
+    log(f"  {rep.summary()}")
+    rep.check_accounting()
