@@ -661,33 +661,38 @@ def main() -> int:
 
     # ---------------------------------------------------------------- the other sampling workloads
     def filtered_leg_f32(leg):
-        """Top-k 50 + top-p 0.9 on every row of the B=256 K=4 V=152064 fp32 workload (its peaked half keeps
-        the peak on both sides, so rejected tokens outside the draft's kept set leave an empty residual)."""
+        """The B=256 K=4 V=152064 fp32 workload with top-k 50 + top-p 0.9 on every row (its peaked half keeps
+        the peak on both sides, so rejected tokens outside the draft's kept set leave an empty residual), then
+        with top-p 0.9 alone (its flat half's nuclei outgrow the candidate buffer: the two-read route)."""
         from workloads import make_filter_params
         B4, K4, V4 = leg.B, leg.K, leg.V
         fws4 = torch.zeros(rsv.sample_filtered_workspace_size(B4, K4, V4), dtype=torch.uint8, device=dev)
-        fk, fp = make_filter_params(B4, top_k=FILTER_K, top_p=FILTER_P)
-        topk, topp = torch.from_numpy(fk).to(dev), torch.from_numpy(fp).to(dev)
+        recs = []
+        for top_k, top_p in ((FILTER_K, FILTER_P), (0, FILTER_P)):
+            fk, fp = make_filter_params(B4, top_k=top_k, top_p=top_p)
+            topk, topp = torch.from_numpy(fk).to(dev), torch.from_numpy(fp).to(dev)
 
-        def fcall(st, phases=rsv.PHASE_ALL):
-            rsv.verify_sample_filtered(st["target"], st["draft"], st["draft_tokens"], st["uniforms"],
-                                       leg.inputs.temperature, topk, topp, out_tokens=st["out_tokens"],
-                                       out_num_accepted=st["out_n"], workspace=fws4, phases=phases)
+            def fcall(st, phases=rsv.PHASE_ALL, topk=topk, topp=topp):
+                rsv.verify_sample_filtered(st["target"], st["draft"], st["draft_tokens"], st["uniforms"],
+                                           leg.inputs.temperature, topk, topp, out_tokens=st["out_tokens"],
+                                           out_num_accepted=st["out_n"], workspace=fws4, phases=phases)
 
-        fsteps = GraphSteps(torch, lambda i, ph: fcall(leg.sets[i % leg.M], ph), leg.M, args.eager)
-        fn = max(leg.M, args.steps // 8)
-        tf = rep_stats(fsteps.reps(rsv.PHASE_ALL, fn, fn))
-        tff = rep_stats(fsteps.reps(rsv.PHASE_ROW_STATS, fn, fn))
-        del fsteps, fws4
-        rows = B4 * (2 * K4 + 1)
-        one_read = rows * V4 * leg.esz
-        rec = {"workload": f"{WORKLOAD_NAMES[4]}; top-k {FILTER_K} and top-p {FILTER_P} on every row",
-               "round": tf, "us_per_round": tf["us_median"], "rounds_per_s": round(1e6 / tf["us_median"], 1),
-               "filter_kernels": tff, "filter_kernel_us": tff["us_median"],
-               "filter_gbps_one_read": round(one_read / tff["us_median"] / 1e3, 1)}
-        log(f"filtered fp32 (workload 4, top-k {FILTER_K} + top-p {FILTER_P}): {tf['us_median']:.1f} us per round, "
-            f"filter kernels {tff['us_median']:.1f} us")
-        return rec
+            fsteps = GraphSteps(torch, lambda i, ph, f=fcall: f(leg.sets[i % leg.M], ph), leg.M, args.eager)
+            fn = max(leg.M, args.steps // 8)
+            tf = rep_stats(fsteps.reps(rsv.PHASE_ALL, fn, fn))
+            tff = rep_stats(fsteps.reps(rsv.PHASE_ROW_STATS, fn, fn))
+            del fsteps
+            rows = B4 * (2 * K4 + 1)
+            one_read = rows * V4 * leg.esz
+            what = (f"top-k {top_k} and top-p {top_p}" if top_k else f"top-p {top_p} alone") + " on every row"
+            recs.append({"workload": f"{WORKLOAD_NAMES[4]}; {what}", "top_k": top_k, "top_p": top_p,
+                         "round": tf, "us_per_round": tf["us_median"], "rounds_per_s": round(1e6 / tf["us_median"], 1),
+                         "filter_kernels": tff, "filter_kernel_us": tff["us_median"],
+                         "filter_gbps_one_read": round(one_read / tff["us_median"] / 1e3, 1)})
+            log(f"filtered fp32 (workload 4, {what}): {tf['us_median']:.1f} us per round, "
+                f"filter kernels {tff['us_median']:.1f} us")
+        del fws4
+        return recs
 
     filtered_f32 = None
     workloads = {}
