@@ -32,6 +32,7 @@ import json
 import math
 import os
 import platform
+import re
 import statistics
 import sys
 import time
@@ -212,8 +213,8 @@ def ingest_counters(fetch_csv: str, write_csv: str) -> int:
     out = {
         "about": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over "
                  "the dispatches of bench.py --counters), scaled by the factors a 256 MiB device copy gives "
-                 "(copy bytes / counter bytes). source_sha: the kernel sources the counters were taken on "
-                 "(bench.py reports null once they change).",
+                 "(copy bytes / counter bytes). source_sha: the code of the kernel sources the counters were "
+                 "taken on, comments and layout aside (bench.py reports null once it changes).",
         "fetch_scale": fs, "write_scale": ws,
         "workloads": {"k_sample_*": "B=64 K=8 V=128256 bf16", "k_sample_*_f32": "B=256 K=4 V=152064 fp32",
                       "k_greedy_*": "B=32 G=7 N=5 V=32000 bf16",
@@ -237,12 +238,21 @@ def kernel_sources() -> list:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")))
 
 
+def code_only(text: str) -> str:
+    """A source without its comments and with every run of whitespace made one space: what
+    the compiler builds from (no source here holds // or /* inside a string literal)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_sha() -> str:
+    """Hash of the code of every kernel source (comments and layout do not change it)."""
     h = hashlib.sha256()
     for path in kernel_sources():
         h.update(os.path.basename(path).encode())
-        with open(path, "rb") as fh:
-            h.update(fh.read())
+        with open(path, encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

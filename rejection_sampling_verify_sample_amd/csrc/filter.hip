@@ -21,16 +21,19 @@
 // Per row the kernel leaves the reference R, the kept mass against it, the key
 // threshold and the kept count; the accept, mass and draw kernels apply them.
 //
-// With top-k on and k <= 64 the row is read once instead (k_filter_fast): every
-// thread publishes its running maximum in LDS, and the k-th largest of those 256
-// maxima (each the maximum of a disjoint part of the row) is a lower bound of the
-// row's k-th largest logit. Entries at or above the bound (every entry top-k
-// keeps, plus a few hundred others) go to an LDS buffer. One wave then finds the
-// k-th largest key by a bitwise search and sorts the kept keys, and the top-p
-// group comes from an exact scan of the same fixed-point masses, so the results
-// are those of the multi-pass select. A row whose candidates overflow the buffer
-// (many entries tied at the top), and every other filtered row, take the
-// multi-pass select (k_filter_rows, which skips the rows finished before it).
+// k_filter reads most rows once instead, one workgroup per row, with the same
+// fixed-point masses against the same reference, so its results are the multi-pass
+// select's. With top-k on and k <= 64 every thread publishes its running maximum in
+// LDS, and the k-th largest of those 256 maxima (each the maximum of a disjoint part
+// of the row) is a lower bound of the row's k-th largest logit; entries at or above
+// it go to an LDS buffer, one wave finds the k-th largest key by a bitwise search and
+// sorts the kept keys, and the top-p group comes from an exact scan of their masses.
+// Rows with top-p on, or top-k > 64, take a bound from the first step of the read and
+// keep the entries above it in a buffer or, for long bf16 rows with top-p alone, count
+// entries per key; a long fp32 row with top-p alone whose nucleus outgrows the buffer
+// is read twice (bin counts bound the cut to a band, then exact masses and the band's
+// keys). Details stand above each route. A row none of them finishes is flagged for
+// the multi-pass select (k_filter_rows, which skips the rows finished before it).
 #include "common.hpp"
 #include "params.hpp"
 
@@ -1562,10 +1565,10 @@ __device__ __forceinline__ bool hist16_row(const SampleParams& P, const FiltRow&
 // An fp32 row whose nucleus is larger than the buffer (a flat row with top-p alone)
 // is read twice instead of going to the multi-pass select. The first read counts its
 // entries in 4096 bins of 1/128 of a doubling of mass each (32 doublings), from one
-// doubling above the first step's maximum down (entries above kept as keys, those below summed as the
-// rest), and finds the row maximum. A bin's entries take masses between those of its
-// edges, so the counts bound the mass above every bin, and the bins where the cut can
-// lie form a band. The second read sums every entry's fixed-point mass exactly, the
+// doubling above the first step's maximum down (entries above are kept as keys, those
+// below summed as the rest), and finds the row maximum. A bin's entries take masses
+// between those of its edges, so the counts bound the mass above every bin, and the
+// bins where the cut can lie form a band. The second read sums every entry's fixed-point mass exactly, the
 // whole row and the part above the band, and keeps the band's entries as keys; the cut
 // then runs on them from the mass above the band. The masses and the reference are the
 // multi-pass select's, so are the results. A bin index is a monotone function of the
@@ -1709,7 +1712,8 @@ __device__ bool f32_count(const float* row, int64_t V, WideBuf& wb, float c, flo
 // Top-p alone on a long fp32 row in two reads (see above). False (nothing written)
 // when the counts cannot place the cut in a band that fits the buffer: the row then
 // takes the multi-pass select.
-__device__ __forceinline__ bool f32_topp_row(const SampleParams& P, const FiltRow& r, WideBuf& wb, float pp, float xl) {
+__device__ __forceinline__ bool f32_topp_row(const SampleParams& P, const FiltRow& r, WideBuf& wb, float pp,
+                                             float xl) {
   const float c = P.c;
   const float* row = static_cast<const float*>(r.row);
   const int64_t V = P.V;
@@ -1835,7 +1839,8 @@ __device__ __forceinline__ bool f32_topp_row(const SampleParams& P, const FiltRo
   }
   uint32_t thr;
   uint64_t kn, km;
-  const bool ok = wide_cut<float>(wb, static_cast<int>(nb), 0, false, pp, true, c, Rf, Zt - A - Zb, thr, kn, km, A, Na);
+  const bool ok =
+      wide_cut<float>(wb, static_cast<int>(nb), 0, false, pp, true, c, Rf, Zt - A - Zb, thr, kn, km, A, Na);
   if (ok) filt_write(P, r, Rf, static_cast<double>(km) * 0x1p-40, thr, kn, xl);
   __syncthreads();  // shared memory is reused by the next row
   return ok;
