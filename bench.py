@@ -736,10 +736,10 @@ def main() -> int:
         grams = [torch.from_numpy(g).to(dev) for g in host]
         lasts = [torch.from_numpy(lookup_tokens(i, PB, PV, host)).to(dev) for i in range(16)]
 
-        def time_pool(pool):
-            skipped = torch.empty((PB,), dtype=torch.int32, device=dev)
-            pcand = torch.empty((PB, PG, PN - 1), dtype=torch.int32, device=dev)
-            pcount = torch.empty((PB,), dtype=torch.int32, device=dev)
+        def time_pool(pool, nb, grams, lasts):
+            skipped = torch.empty((nb,), dtype=torch.int32, device=dev)
+            pcand = torch.empty((nb, PG, PN - 1), dtype=torch.int32, device=dev)
+            pcount = torch.empty((nb,), dtype=torch.int32, device=dev)
 
             def pstep(i):
                 pool.insert(grams[i % 16], out_skipped=skipped)
@@ -763,19 +763,33 @@ def main() -> int:
 
         what = f"B={PB} V={PV} G={PG} N={PN}: insert W={PW} n-grams per sequence, then look up each sequence's last token"
         pool = rsv.NgramPool(PB, PV, PG, PN, dev)
-        tp, mean_c = time_pool(pool)
+        tp, mean_c = time_pool(pool, PB, grams, lasts)
         pool_leg = {"workload": f"n-gram pool {what}", "table_bytes": pool.nbytes,
                     "step": tp, "us_per_step": tp["us_median"], "steps_per_s": round(1e6 / tp["us_median"], 1),
                     "mean_candidates": mean_c}
         log(f"n-gram pool insert + lookup: {tp['us_median']:.2f} us per step ({pool.nbytes / 1e6:.1f} MB table)")
         del pool
         cache = rsv.NgramCache(PB, PV, PG, PN, CS, CW, dev)
-        tc, mean_c = time_pool(cache)
+        tc, mean_c = time_pool(cache, PB, grams, lasts)
         cache_leg = {"workload": f"hashed n-gram pool, {CS} sets x {CW} ways per sequence, {what}",
                      "table_bytes": cache.nbytes, "step": tc, "us_per_step": tc["us_median"],
                      "steps_per_s": round(1e6 / tc["us_median"], 1), "mean_candidates": mean_c}
         log(f"hashed n-gram pool insert + lookup: {tc['us_median']:.2f} us per step "
             f"({cache.nbytes / 1e6:.1f} MB table)")
+        del cache
+        # the sampling workloads' largest shape: B=256 V=152064 (the direct table would take 4.4 GB)
+        LB, LV = 256, 152064
+        host_l = ngram_steps(5, 16, LB, PW, PN, LV)
+        grams_l = [torch.from_numpy(g).to(dev) for g in host_l]
+        lasts_l = [torch.from_numpy(lookup_tokens(i, LB, LV, host_l)).to(dev) for i in range(16)]
+        cache = rsv.NgramCache(LB, LV, PG, PN, CS, CW, dev)
+        tl, mean_l = time_pool(cache, LB, grams_l, lasts_l)
+        cache_leg["large"] = {"workload": f"hashed n-gram pool, {CS} sets x {CW} ways per sequence, B={LB} V={LV} "
+                                          f"G={PG} N={PN}: insert W={PW} + lookup",
+                              "table_bytes": cache.nbytes, "direct_table_bytes": rsv.ngram_pool_bytes(LB, LV, PG, PN),
+                              "step": tl, "us_per_step": tl["us_median"], "mean_candidates": mean_l}
+        log(f"hashed n-gram pool B={LB} V={LV}: {tl['us_median']:.2f} us per step ({cache.nbytes / 1e6:.1f} MB table, "
+            f"direct {rsv.ngram_pool_bytes(LB, LV, PG, PN) / 1e9:.2f} GB)")
         del cache
 
     # ---------------------------------------------------------------- greedy verify, B=32 G=7 N=5 V=32000 bf16
