@@ -9,8 +9,8 @@
 //     strictly-larger kept entries hold mass < p, and always the row's largest.
 // The verify then runs unchanged on the renormalised kept laws p', q'.
 //
-// k_filter_rows: one 256-thread workgroup per logit row (target rows 0..K and
-// draft rows 0..K-1 of every batch row) finds the threshold exactly by a radix
+// The multi-pass select: one 256-thread workgroup per logit row (target rows 0..K
+// and draft rows 0..K-1 of every batch row) finds the threshold exactly by a radix
 // select on the 32-bit order key of the logits (digits of 11, 11 and 10 bits;
 // bf16 keys are resolved after two digits). Each digit is one pass over the row
 // that builds an LDS histogram of the digit over the entries still in play: the
@@ -18,8 +18,8 @@
 // in 64-bit integers), so every sum is exact and independent of the order the
 // atomics land in. Pass one also keeps the online maximum, which fixes R. The
 // row is re-read from cache by the later passes (plain loads, not streaming).
-// Per row the kernel leaves the reference R, the kept mass against it, the key
-// threshold and the kept count; the accept, mass and draw kernels apply them.
+// Per row it leaves the reference R, the kept mass against it, the key threshold
+// and the kept count; the accept, mass and draw kernels apply them.
 //
 // k_filter reads most rows once instead, one workgroup per row, with the same
 // fixed-point masses against the same reference, so its results are the multi-pass
@@ -32,8 +32,9 @@
 // keep the entries above it in a buffer or, for long bf16 rows with top-p alone, count
 // entries per key; a long fp32 row with top-p alone whose nucleus outgrows the buffer
 // is read twice (bin counts bound the cut to a band, then exact masses and the band's
-// keys). Details stand above each route. A row none of them finishes is flagged for
-// the multi-pass select (k_filter_rows, which skips the rows finished before it).
+// keys). Details stand above each route. A bf16 row none of them finishes takes the
+// multi-pass select in the same workgroup; an fp32 row is flagged for it and
+// k_filter_rows, launched after k_filter, runs it (it skips the rows finished before).
 #include "common.hpp"
 #include "params.hpp"
 
@@ -1940,22 +1941,24 @@ __device__ __forceinline__ void filter_row_plain(const SampleParams& P, const Fi
   __syncthreads();
 }
 
-// Shared memory of the one-read paths (a workgroup runs one at a time).
+// Shared memory of the row paths (a workgroup runs one at a time).
 union FiltLds {
   FastBuf fast;
   WideBuf wide;
+  FiltShared multi;  // the multi-pass select of a bf16 row the one-read paths leave
 };
 
 #ifndef SV_FILT_ROWS_GRID
-#define SV_FILT_ROWS_GRID 512  // workgroups of the multi-pass kernel
+#define SV_FILT_ROWS_GRID 512  // workgroups of the multi-pass kernel (fp32 rows)
 #endif
 #ifndef SV_FILT_MINB
 #define SV_FILT_MINB 5  // workgroups per CU the one-read kernel is compiled for (its LDS allows five)
 #endif
 
 // One workgroup per logit row, read once: no filter, top-k with k <= 64, or top-p /
-// larger top-k. A row these paths do not finish is flagged (f_flag = 1) for the
-// multi-pass select; every row's flag is written.
+// larger top-k. A bf16 row these paths do not finish takes the multi-pass select in
+// the same workgroup; an fp32 row is flagged (f_flag = 1) for k_filter_rows. Every
+// row's flag is written.
 // The grid is two-dimensional, one workgroup per row (no loop over rows: values
 // derived from the thread index are not kept live across rows).
 template <typename T>
@@ -1971,8 +1974,8 @@ __global__ __launch_bounds__(kFiltBlock, SV_FILT_MINB) void k_filter(SampleParam
     const bool k_on = kk > 0 && kk < P.V;
     const bool p_on = pp < 1.f;  // false for NaN
     bool done = false;
+    const float xl = filt_token_logit<T>(P, r);
     if (!P.filt_multi) {
-      const float xl = filt_token_logit<T>(P, r);
       if (k_on && kk <= kFiltFastK) {
         done = filter_row_fast<T>(P, r, lds.fast, kk, pp, xl);
       } else if (k_on || p_on) {
@@ -1982,11 +1985,20 @@ __global__ __launch_bounds__(kFiltBlock, SV_FILT_MINB) void k_filter(SampleParam
         done = true;
       }
     }
+    if constexpr (sizeof(T) == 2) {
+      // bf16 rows save the second launch; fp32 rows keep it (with this call inlined, the
+      // fp32 kernel's one-read paths measured slower)
+      if (!done) {
+        __syncthreads();  // the one-read path's shared memory is reused
+        filter_row_task<T>(P, r, lds.multi, kk, pp, xl);
+        done = true;
+      }
+    }
     if (threadIdx.x == 0) P.f_flag[r.fr] = done ? 0u : 1u;
   }
 }
 
-// The multi-pass select of the flagged rows. Workgroup w takes rows w, w + G, ...;
+// The multi-pass select of the flagged fp32 rows. Workgroup w takes rows w, w + G, ...;
 // each batch of 256 of its rows reads their flags at once.
 template <typename T>
 __global__ __launch_bounds__(kFiltBlock) void k_filter_rows(SampleParams P) {
@@ -2028,12 +2040,11 @@ static dim3 filt_grid_2d(int64_t tasks) {
 
 hipError_t launch_filter_rows(const SampleParams& P, bool bf16, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(P.B) * (2 * P.K + 1);
-  // the multi-pass kernel: every row when the one-read paths are off, else a few
-  // workgroups, since flagged rows are rare
+  // the multi-pass kernel of fp32 rows: every row when the one-read paths are off,
+  // else a few workgroups, since flagged rows are rare
   const int64_t g2 = P.filt_multi ? rows : (SV_FILT_ROWS_GRID);
   if (bf16) {
     hipLaunchKernelGGL(k_filter<bf16_t>, filt_grid_2d(rows), dim3(kFiltBlock), 0, stream, P);
-    hipLaunchKernelGGL(k_filter_rows<bf16_t>, filt_grid(rows, g2), dim3(kFiltBlock), 0, stream, P);
   } else {
     hipLaunchKernelGGL(k_filter<float>, filt_grid_2d(rows), dim3(kFiltBlock), 0, stream, P);
     hipLaunchKernelGGL(k_filter_rows<float>, filt_grid(rows, g2), dim3(kFiltBlock), 0, stream, P);

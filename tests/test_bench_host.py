@@ -24,7 +24,7 @@ MASS_F = "void sv::k_sample_mass<sv::bf16_t, true, true>(sv::SampleParams)"
 DRAW = "void sv::k_sample_draw<sv::bf16_t, false>(sv::SampleParams)"
 DRAW_F = "void sv::k_sample_draw<sv::bf16_t, true>(sv::SampleParams)"
 FILT = "void sv::k_filter<sv::bf16_t>(sv::SampleParams)"
-FROWS = "void sv::k_filter_rows<sv::bf16_t>(sv::SampleParams)"
+FROWS = "void sv::k_filter_rows<float>(sv::SampleParams)"
 
 
 def test_counter_means_split_filtered_variants_and_keep_three_calibration_copies(tmp_path):
