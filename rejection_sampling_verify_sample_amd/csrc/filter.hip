@@ -1710,6 +1710,158 @@ __device__ bool f32_count(const float* row, int64_t V, WideBuf& wb, float c, flo
   return true;
 }
 
+// The largest value x with mass_bin(x) >= J (+inf for J <= -1). The bin index falls
+// as the value rises, so mass_bin(x) < J exactly when x > this value (x not NaN); a
+// bisection over the order keys from -inf (bin kMassBins >= J) finds it.
+__device__ __forceinline__ float bin_floor_value(int J, float mref, float s) {
+  if (J <= -1) return INFINITY;
+  uint32_t lo = order_key(-INFINITY), hi = order_key(INFINITY);
+  while (lo < hi) {
+    const uint32_t mid = lo + (hi - lo + 1u) / 2u;
+    if (mass_bin(key_value(mid), mref, s) >= J) {
+      lo = mid;
+    } else {
+      hi = mid - 1u;
+    }
+  }
+  return key_value(lo);
+}
+
+// One thread's fixed-point sums of the second read: the whole row, above the band, in
+// the band (from the kept entries, after the read), and the count above it.
+struct F32Sums {
+  uint64_t zt = 0, za = 0, zb = 0, na = 0;
+  double dt = 0.0, da = 0.0;  // whole numbers below 2^53, moved to zt/za
+  __device__ __forceinline__ void flush() {
+    zt += static_cast<uint64_t>(dt);
+    za += static_cast<uint64_t>(da);
+    dt = da = 0.0;
+  }
+};
+
+// The fixed-point mass of x, round(m * 2^40) with m = min(2^(x*c - Rf), 1) rounded
+// half up as to_fixed does, as a double: m * 2^40 is exact in fp32, and adding 1/2 to
+// it is exact in fp64 (at most 24 significant bits, none below 2^-45).
+__device__ __forceinline__ double fixed_mass_f64(float x, float c, float Rf) {
+  const float m = fminf(exp2_hw(fmaf(x, c, -Rf)), 1.f);
+  return floor(static_cast<double>(m * 0x1p40f) + 0.5);
+}
+
+// The second read keeps the band's entries in four parts of the buffer, one per wave,
+// each wave counting its own entries in a register: a position of a step where some
+// lane holds a band entry costs one ballot, a lane count and a store, no atomic.
+constexpr int kBandWaves = kFiltBlock / 64;
+constexpr uint32_t kBandPart = WideKey<float>::kCap / kBandWaves;  // entries per wave
+
+// The entries of a 16-byte vector of the second read (those whose bit is set in
+// `valid`; the same mask on every lane except at the row's ends): their sums, and the
+// band's entries as raw bits in the wave's part `part`, n counting them (uniform; past
+// kBandPart they are counted, not stored).
+__device__ __forceinline__ void f32_band_vec(const u32x4& v, uint32_t valid, float c, float Rf, float Xa, float Xb,
+                                             F32Sums& sm, uint32_t* part, uint32_t& n) {
+  const float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bool ok = (valid >> e) & 1u;
+    const double q = ok ? fixed_mass_f64(x[e], c, Rf) : 0.0;
+    const bool above = ok && x[e] > Xa, in_band = ok && x[e] > Xb && x[e] <= Xa;  // NaN: neither
+    sm.dt += q;
+    sm.da += above ? q : 0.0;
+    sm.na += above ? 1u : 0u;
+    const uint64_t bm = __ballot(in_band);
+    if (bm != 0ull) {  // uniform
+      if (in_band) {
+        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bm >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bm), 0u));
+        if (n + rank < kBandPart) part[n + rank] = __float_as_uint(x[e]);
+      }
+      n += static_cast<uint32_t>(__popcll(bm));
+    }
+  }
+}
+
+// The second read of a long fp32 row: every entry's fixed-point mass summed (the row,
+// above the band) and the band's entries kept, then gathered to wb.key[0..nb) as keys
+// in wave order, their masses summed on the way. Whole steps of kWideUnroll vectors per thread, then the last
+// vectors, the scalar head (lanes 0-3 of wave 0) and tail (lanes 4-7); every lane of
+// each wave takes part in each vector. False (uniform) when a wave's part overflowed.
+__device__ bool f32_band_read(const float* row, int64_t V, WideBuf& wb, float c, float Rf, float Xa, float Xb,
+                              F32Sums& sm, uint32_t& nb) {
+  constexpr int BS = kFiltBlock, U = kWideUnroll;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t h = head_elems(row, V);
+  const int64_t nvec = (V - h) / 4;
+  const u32x4* vb = reinterpret_cast<const u32x4*>(row + h);
+  const int64_t nsteps = nvec / (U * BS);
+  uint32_t* part = wb.key + w * kBandPart;
+  uint32_t n = 0;
+  int k = 0;
+  for (int64_t st = 0; st < nsteps; ++st) {
+    u32x4 cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = load_stream(vb + st * (U * BS) + threadIdx.x + u * BS);
+#pragma unroll
+    for (int u = 0; u < U; ++u) f32_band_vec(cur[u], 0xFu, c, Rf, Xa, Xb, sm, part, n);
+    if (++k == 256) {  // 3072 entries of at most 2^40 each: the sums stay whole below 2^53
+      sm.flush();
+      k = 0;
+    }
+  }
+  for (int64_t base = nsteps * (U * BS); base < nvec; base += BS) {
+    const int64_t vr = base + threadIdx.x;
+    const bool in = vr < nvec;
+    f32_band_vec(in ? load_stream(vb + vr) : u32x4{0u, 0u, 0u, 0u}, in ? 0xFu : 0u, c, Rf, Xa, Xb, sm, part, n);
+  }
+  if (w == 0) {
+    const int64_t tail_lo = h + nvec * 4;
+    const int64_t e = lane < 4 ? lane : tail_lo + (lane - 4);
+    const bool in = lane < 4 ? lane < h : (lane < 8 && e < V);
+    f32_band_vec(u32x4{in ? __float_as_uint(row[e]) : 0u, 0u, 0u, 0u}, in ? 1u : 0u, c, Rf, Xa, Xb, sm, part, n);
+  }
+  sm.flush();
+  // gather the parts: wave o's entries go to [off[o], off[o] + cnt[o])
+  if (lane == 0) wb.wkey[0][w] = n;
+  __syncthreads();
+  uint32_t cnt[kBandWaves], off[kBandWaves];
+  uint32_t total = 0;
+  bool over = false;
+#pragma unroll
+  for (int o = 0; o < kBandWaves; ++o) {
+    cnt[o] = wb.wkey[0][o];
+    over = over || cnt[o] > kBandPart;
+    off[o] = total;
+    total += cnt[o];
+  }
+  nb = total;
+  if (over) return false;  // uniform
+  constexpr int kPer = WideKey<float>::kCap / kFiltBlock;
+  uint32_t tmp[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t i = threadIdx.x + static_cast<uint32_t>(j * kFiltBlock);
+    tmp[j] = 0u;
+    if (i < total) {
+      int o = 0;
+#pragma unroll
+      for (int q = 1; q < kBandWaves; ++q) o += (i >= off[q]) ? 1 : 0;
+      uint32_t base_o = off[0];
+#pragma unroll
+      for (int q = 1; q < kBandWaves; ++q) base_o = (o == q) ? off[q] : base_o;
+      const float x = __uint_as_float(wb.key[o * kBandPart + (i - base_o)]);
+      tmp[j] = order_key(x);
+      sm.zb += static_cast<uint64_t>(fixed_mass_f64(x, c, Rf));
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t i = threadIdx.x + static_cast<uint32_t>(j * kFiltBlock);
+    if (i < total) wb.key[i] = tmp[j];
+  }
+  __syncthreads();
+  return true;
+}
+
 // Top-p alone on a long fp32 row in two reads (see above). False (nothing written)
 // when the counts cannot place the cut in a band that fits the buffer: the row then
 // takes the multi-pass select.
@@ -1805,35 +1957,16 @@ __device__ __forceinline__ bool f32_topp_row(const SampleParams& P, const FiltRo
   if (t == 0) wb.nbuf = 0;
   __syncthreads();
   // second read: exact masses, the band's entries as keys
-  uint64_t zt = 0, za = 0, zb = 0, na = 0;
-  f32_visit(row, V, [&](u32x4 v, uint32_t valid) {
-    const float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
-    uint32_t take = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (!((valid >> e) & 1u)) continue;
-      const uint64_t fm = fmv(x[e]);
-      const int j = mass_bin(x[e], mref, s);
-      const bool above = j < ja, in_band = j >= ja && j <= jb;  // selects, not branches
-      zt += fm;
-      za += above ? fm : 0u;
-      na += above ? 1u : 0u;
-      zb += in_band ? fm : 0u;
-      take |= (in_band ? 1u : 0u) << e;
-    }
-    if (__ballot(take != 0u)) {
-      uint32_t pos = reserve_slots(wb.nbuf, static_cast<uint32_t>(__popc(take)));
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((take >> e) & 1u) {
-          if (pos < static_cast<uint32_t>(WideKey<float>::kCap)) wb.key[pos] = order_key(x[e]);
-          ++pos;
-        }
-    }
-  });
-  __syncthreads();
-  const uint32_t nb = wb.nbuf;
-  const uint64_t Zt = block_sum_u64(zt), A = block_sum_u64(za), Zb = block_sum_u64(zb), Na = block_sum_u64(na);
+  const float Xa = bin_floor_value(ja, mref, s);      // above the band: x > Xa
+  const float Xb = bin_floor_value(jb + 1, mref, s);  // in the band: Xb < x <= Xa
+  F32Sums sums;
+  uint32_t nb = 0;
+  if (!f32_band_read(row, V, wb, c, Rf, Xa, Xb, sums, nb)) {
+    __syncthreads();
+    return false;
+  }
+  const uint64_t Zt = block_sum_u64(sums.zt), A = block_sum_u64(sums.za), Zb = block_sum_u64(sums.zb);
+  const uint64_t Na = block_sum_u64(sums.na);
   if (nb != nband) {  // uniform; the two reads see the same row, so this does not happen
     __syncthreads();
     return false;

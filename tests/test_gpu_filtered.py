@@ -327,6 +327,58 @@ def test_filtered_residual_without_mass_draws_from_the_kept_target(dtype, V):
         assert tok[b, 0] >= 0 and x0[tok[b, 0]] >= np.sort(x0)[-int(kept[b, 0])], (b, tok[b, 0])
 
 
+def _crowd_ties_into_wave0(x, p, T, n_tie, rng):
+    """A flat fp32 row whose top-p cut falls inside a block of n_tie equal entries, all
+    placed where the second read hands them to wave 0 (16-byte vectors 0-63 of every
+    256: entries whose index mod 1024 is below 256)."""
+    V = x.size
+    order = np.argsort(-x.astype(np.float64), kind="stable")
+    m = np.exp((x[order].astype(np.float64) - x.max()) / T)
+    kstar = int(np.searchsorted(np.cumsum(m) / m.sum(), p))
+    lo = max(kstar - n_tie // 2, 0)
+    vals = x[order].copy()
+    vals[lo:lo + n_tie] = vals[kstar]                      # the block of ties around the cut
+    wave0 = np.nonzero((np.arange(V) % 1024) < 256)[0]
+    rest = np.setdiff1d(np.arange(V), wave0[:n_tie])
+    out = np.empty_like(x)
+    out[wave0[:n_tie]] = vals[lo:lo + n_tie]
+    others = np.concatenate([vals[:lo], vals[lo + n_tie:]])
+    out[rest] = others[rng.permutation(others.size)]
+    return out, vals[kstar]
+
+
+def test_two_read_band_held_by_one_wave():
+    """The second read keeps the band's entries in four parts of the buffer, one per
+    wave. Rows whose band (a block of 2500 ties at the cut) all falls to wave 0 overflow
+    its part of 1536; they take the multi-pass select, so the round equals it, and the
+    oracle's."""
+    log("two-read band in one wave")
+    rng = np.random.default_rng(37)
+    B, K, V, T, p = 2, 1, 152064, 0.8, 0.9
+    tgt = rng.normal(0, 0.5, (B, K + 1, V)).astype(np.float32)
+    for b in range(B):
+        for i in range(K + 1):
+            tgt[b, i], tv = _crowd_ties_into_wave0(tgt[b, i], p, T, 2500, rng)
+            m = np.exp((tgt[b, i].astype(np.float64) - tgt[b, i].max()) / T)
+            above, at = m[tgt[b, i] > tv].sum(), m[tgt[b, i] == tv].sum()
+            assert above < p * m.sum() <= above + at, "the cut must fall inside the block of ties"
+    drf = tgt[:, :K].copy()
+    drf[1] = tgt[1, :K] + rng.normal(0, 0.3, (K, V)).astype(np.float32)  # row 1: the draft side is not crowded
+    toks = rng.integers(0, V, (B, K))
+    uni = rng.random((B, K + 1, 2)).astype(np.float32)
+    ks = np.zeros(B, dtype=np.int32)
+    ps = np.full(B, p, dtype=np.float32)
+    t = _f32_tensors(tgt, drf, toks, uni, T=T)
+    tok, n, probs, kept = run_gpu(t, ks, ps)
+    tok2, n2, probs2, kept2 = _run_multi_pass(t, ks, ps)
+    assert np.array_equal(kept, kept2), (kept, kept2)
+    assert np.array_equal(tok, tok2) and np.array_equal(n, n2)
+    res = oracle.oracle_sample_filtered(tgt, drf, toks, uni, T, ks, ps)
+    rep = compare_filtered(tgt, drf, toks, uni, T, ks, ps, res, tok, n, probs, kept)
+    log(f"  {rep.summary()}")
+    rep.check_accounting()
+
+
 @pytest.mark.parametrize("V", [152064, 40003, 6145])
 def test_two_read_top_p_on_long_fp32_rows(V):
     """Top-p alone on fp32 rows whose nucleus is larger than the candidate buffer (flat
