@@ -15,7 +15,10 @@ the kernels run on -- and the median is reported with the spread.
 Prints ONE JSON line. Also reported: the pass-1 kernel alone (the dominant
 kernel, for the roofline); the other three sampling workloads (B=1 K=4 V=32000
 fp32, B=8 K=5 V=32000 bf16, B=256 K=4 V=152064 fp32) measured the same way;
-the headline round with early exit (pass 1 in stages, spec_verify_sample_staged);
+the headline round with two and with three independent batches in flight on as
+many streams (one batch's pass 2 and draw overlap another's pass 1; the value
+stays the one-batch round); the headline round with early exit (pass 1 in stages,
+spec_verify_sample_staged);
 the same round verified on top-k 50 / top-p 0.9 and on top-p 0.9 alone
 (spec_verify_sample_filtered); the n-gram pool (insert + lookup); the greedy
 verify and the sampling verify of greedy-drafted n-grams on their own workload
@@ -518,6 +521,70 @@ def workload_record(leg: SampleLeg, m: dict, n: int, kernel_key: str) -> dict:
             "mean_accepted": round(m["mean_accepted"], 4)}
 
 
+def in_flight(leg: SampleLeg, S: int, n: int, warmup: int) -> dict:
+    """The leg's round with S independent batches in flight: step j runs on stream j % S
+    (each stream with its own workspace and outputs) over input copy j % M, so one
+    batch's pass 2 and draw overlap another's pass 1. Every step is a whole round on
+    its own batch. Steps are captured in one graph per CHUNK_STEPS (forked from the
+    capture stream and joined at its end)."""
+    import numpy as np
+    torch, rsv = leg.torch, leg.rsv
+    dev = leg.ws.device
+    B, K, V = leg.B, leg.K, leg.V
+    base = torch.cuda.current_stream()
+    side = [torch.cuda.Stream() for _ in range(S - 1)]
+    wss = [torch.zeros(leg.ws.numel(), dtype=torch.uint8, device=dev) for _ in range(S)]
+    outs = [(torch.empty((B, K + 1), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev))
+            for _ in range(S)]
+
+    def step(j, streams):
+        k = j % S
+        st = leg.sets[j % leg.M]
+        with torch.cuda.stream(streams[k]):
+            rsv.verify_sample(st["target"], st["draft"], st["draft_tokens"], st["uniforms"], leg.inputs.temperature,
+                              out_tokens=outs[k][0], out_num_accepted=outs[k][1], workspace=wss[k])
+
+    chunk = S * max(1, CHUNK_STEPS // S)
+    for j in range(chunk):
+        step(j, [base] + side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream()
+        for sd in side:
+            sd.wait_stream(cs)
+        for j in range(chunk):
+            step(j, [cs] + side)
+        for sd in side:
+            cs.wait_stream(sd)
+    reps_n = max(1, n // chunk)
+    g.replay()
+    torch.cuda.synchronize()
+    same = all(np.array_equal(o[0].cpu().numpy(), leg.tokens) and np.array_equal(o[1].cpu().numpy(), leg.n_acc)
+               for o in outs)
+    for _ in range(max(1, warmup // chunk)):
+        g.replay()
+    per = []
+    for _ in range(REPS):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()  # lead: queued before the timed region
+        a.record()
+        for _ in range(reps_n):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / 1e3 / (reps_n * chunk))
+    stats = rep_stats(per)
+    t = stats["us_median"] / 1e6
+    by = sample_bytes(B, K, V, leg.esz, leg.n_acc)["step"]
+    del g
+    return {"batches_in_flight": S, "round": stats, "us_per_round": stats["us_median"],
+            "rounds_per_s": round(1.0 / t, 1), "draft_tokens_per_s": round(B * K / t, 1),
+            "achieved_gbps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBPS, 4),
+            "same_outputs": bool(same)}
+
+
 def oracle_parity(leg: SampleLeg) -> dict:
     """The oracle on every batch row of the leg's round, compared with the GPU outputs under the parity rule.
 
@@ -581,6 +648,16 @@ def main() -> int:
            "round": t_hot, "us_per_round": t_hot["us_median"], "rounds_per_s": round(1e6 / t_hot["us_median"], 1)}
     log(f"hot (one copy): {t_hot['us_median']:.2f} us per round")
     del hsteps
+    # independent batches in flight on separate streams (a serving loop verifying several
+    # micro-batches at once); reported beside the one-batch round, which stays the value
+    in_flight_legs = {}
+    if not args.eager:
+        for S in (2, 3):
+            r = in_flight(head, S, args.steps, args.warmup)
+            r["workload"] = f"{WORKLOAD_NAMES[3]}; {S} independent batches in flight on {S} streams"
+            in_flight_legs[str(S)] = r
+            log(f"{S} batches in flight: {r['us_per_round']:.2f} us per round ({r['achieved_gbps']:.0f} GB/s, "
+                f"{r['frac_of_hbm_peak']:.3f} of peak); outputs {'equal' if r['same_outputs'] else 'DIFFER'}")
 
     # ---------------------------------------------------------------- the same round with early exit (pass 1 in stages)
     staged = None
@@ -937,6 +1014,7 @@ def main() -> int:
         "parity": parity,
         "workloads": workloads,
         "hot_single_copy": hot,
+        "in_flight": in_flight_legs,
         "staged": staged,
         "filtered": filtered,
         "filtered_f32": filtered_f32,

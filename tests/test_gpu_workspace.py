@@ -77,3 +77,30 @@ def test_alternating_inputs_on_one_workspace():
         for t, r in ((ta, ra), (tb, rb)):
             got = _run(t, workspace=ws)
             assert np.array_equal(got[0], r[0]) and np.array_equal(got[1], r[1])
+
+
+def test_batches_in_flight_on_streams():
+    """Independent rounds in flight at once, one stream and one workspace each (the way a
+    serving loop overlaps one batch's pass 2 and draw with another's pass 1): queued
+    several times over without waiting, every stream's outputs equal the round's own
+    outputs run alone."""
+    specs = [make_sample_inputs(3, 20 + i, B=16, V=20000) for i in range(3)]
+    ts = [sample_tensors(s, DEV) for s in specs]
+    refs = [_run(t) for t in ts]
+    streams = [torch.cuda.Stream() for _ in ts]
+    wss = [torch.zeros(rsv.sample_workspace_size(16, 8, 20000), dtype=torch.uint8, device=DEV) for _ in ts]
+    outs = [(torch.empty((16, 9), dtype=torch.int32, device=DEV), torch.empty((16,), dtype=torch.int32, device=DEV))
+            for _ in ts]
+    log("3 streams")
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    got = []
+    for rep in range(6):
+        for i, (t, st) in enumerate(zip(ts, streams)):
+            with torch.cuda.stream(st):
+                o = rsv.verify_sample(t["target"], t["draft"], t["draft_tokens"], t["uniforms"], t["temperature"],
+                                      out_tokens=outs[i][0], out_num_accepted=outs[i][1], workspace=wss[i])
+                got.append((i, o.tokens.clone(), o.num_accepted.clone()))  # copies queued on the same stream
+    torch.cuda.synchronize()
+    for i, tok, n in got:
+        assert np.array_equal(tok.cpu().numpy(), refs[i][0]) and np.array_equal(n.cpu().numpy(), refs[i][1]), i
