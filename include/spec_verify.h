@@ -261,6 +261,9 @@ size_t spec_verify_sample_filtered_workspace_size(int32_t B, int32_t K, int32_t 
  * the read sets a bound meant to lie below the cut; the entries above it are kept
  * on chip (long bf16 rows with top-p alone: a count per bf16 value instead) and the
  * mass below it is summed, and the cut is taken there when they provably hold it.
+ * A long fp32 row with top-p alone whose kept set outgrows the on-chip buffer (a flat
+ * row) is read twice: counts in bins of mass bound the cut to a band of values, then
+ * the second read sums every entry's exact mass and keeps the band's entries.
  * A row none of these finishes (the kept entries overflow, or do not hold the
  * cut) takes an exact radix select, which reads the row once for its maximum and
  * once per radix digit of each active filter (bf16: 2 digits, fp32: 3). Results
