@@ -521,47 +521,33 @@ def workload_record(leg: SampleLeg, m: dict, n: int, kernel_key: str) -> dict:
             "mean_accepted": round(m["mean_accepted"], 4)}
 
 
-def in_flight(leg: SampleLeg, S: int, n: int, warmup: int) -> dict:
-    """The leg's round with S independent batches in flight: step j runs on stream j % S
-    (each stream with its own workspace and outputs) over input copy j % M, so one
-    batch's pass 2 and draw overlap another's pass 1. Every step is a whole round on
-    its own batch. Steps are captured in one graph per CHUNK_STEPS (forked from the
-    capture stream and joined at its end)."""
-    import numpy as np
-    torch, rsv = leg.torch, leg.rsv
-    dev = leg.ws.device
-    B, K, V = leg.B, leg.K, leg.V
+def in_flight_steps(torch, S: int, n: int, warmup: int, step) -> dict:
+    """Per-step time of step(j, k) with S independent batches in flight: step j runs on
+    stream k = j % S (the caller gives each stream its own workspace and outputs), all
+    captured in one graph per CHUNK_STEPS steps (forked from the capture stream and
+    joined at its end). REPS measurements of about n steps, each led by one untimed graph."""
     base = torch.cuda.current_stream()
     side = [torch.cuda.Stream() for _ in range(S - 1)]
-    wss = [torch.zeros(leg.ws.numel(), dtype=torch.uint8, device=dev) for _ in range(S)]
-    outs = [(torch.empty((B, K + 1), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev))
-            for _ in range(S)]
-
-    def step(j, streams):
-        k = j % S
-        st = leg.sets[j % leg.M]
-        with torch.cuda.stream(streams[k]):
-            rsv.verify_sample(st["target"], st["draft"], st["draft_tokens"], st["uniforms"], leg.inputs.temperature,
-                              out_tokens=outs[k][0], out_num_accepted=outs[k][1], workspace=wss[k])
-
     chunk = S * max(1, CHUNK_STEPS // S)
-    for j in range(chunk):
-        step(j, [base] + side)
+
+    def run(streams):
+        for j in range(chunk):
+            with torch.cuda.stream(streams[j % S]):
+                step(j, j % S)
+
+    for sd in side:
+        sd.wait_stream(base)
+    run([base] + side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         cs = torch.cuda.current_stream()
         for sd in side:
             sd.wait_stream(cs)
-        for j in range(chunk):
-            step(j, [cs] + side)
+        run([cs] + side)
         for sd in side:
             cs.wait_stream(sd)
     reps_n = max(1, n // chunk)
-    g.replay()
-    torch.cuda.synchronize()
-    same = all(np.array_equal(o[0].cpu().numpy(), leg.tokens) and np.array_equal(o[1].cpu().numpy(), leg.n_acc)
-               for o in outs)
     for _ in range(max(1, warmup // chunk)):
         g.replay()
     per = []
@@ -575,10 +561,32 @@ def in_flight(leg: SampleLeg, S: int, n: int, warmup: int) -> dict:
         b.record()
         torch.cuda.synchronize()
         per.append(a.elapsed_time(b) / 1e3 / (reps_n * chunk))
-    stats = rep_stats(per)
+    del g
+    return rep_stats(per)
+
+
+def in_flight(leg: SampleLeg, S: int, n: int, warmup: int) -> dict:
+    """The leg's round with S independent batches in flight (in_flight_steps): one
+    batch's pass 2 and draw overlap another's pass 1. Every step is a whole round on its
+    own batch (input copy j % M)."""
+    import numpy as np
+    torch, rsv = leg.torch, leg.rsv
+    dev = leg.ws.device
+    B, K, V = leg.B, leg.K, leg.V
+    wss = [torch.zeros(leg.ws.numel(), dtype=torch.uint8, device=dev) for _ in range(S)]
+    outs = [(torch.empty((B, K + 1), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev))
+            for _ in range(S)]
+
+    def step(j, k):
+        st = leg.sets[j % leg.M]
+        rsv.verify_sample(st["target"], st["draft"], st["draft_tokens"], st["uniforms"], leg.inputs.temperature,
+                          out_tokens=outs[k][0], out_num_accepted=outs[k][1], workspace=wss[k])
+
+    stats = in_flight_steps(torch, S, n, warmup, step)
+    same = all(np.array_equal(o[0].cpu().numpy(), leg.tokens) and np.array_equal(o[1].cpu().numpy(), leg.n_acc)
+               for o in outs)
     t = stats["us_median"] / 1e6
     by = sample_bytes(B, K, V, leg.esz, leg.n_acc)["step"]
-    del g
     return {"batches_in_flight": S, "round": stats, "us_per_round": stats["us_median"],
             "rounds_per_s": round(1.0 / t, 1), "draft_tokens_per_s": round(B * K / t, 1),
             "achieved_gbps": round(by / t / 1e9, 1), "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBPS, 4),
@@ -910,6 +918,26 @@ def main() -> int:
                   "frac_of_hbm_peak": round(gal / per / 1e9 / HBM_PEAK_GBPS, 4), "rotate": M5,
                   "algorithmic_bytes": gal, "argmax_traffic": measured_traffic("k_greedy_argmax")}
         log(f"greedy {per * 1e6:.2f} us/round ({gal / per / 1e9:.0f} GB/s)")
+        if not args.eager:
+            # two independent batches in flight, one stream, workspace and outputs each
+            gref = (gsets[0]["ot"].cpu().numpy(), gsets[0]["ol"].cpu().numpy(), gsets[0]["ob"].cpu().numpy())
+            gwss = [torch.zeros_like(gws) for _ in range(2)]
+            gouts = [(torch.empty_like(gsets[0]["ot"]), torch.empty_like(gsets[0]["ol"]), torch.empty_like(gsets[0]["ob"]))
+                     for _ in range(2)]
+
+            def gstep2(j, k):
+                st = gsets[j % M5]
+                rsv.verify_greedy(st["logits"], st["cand"], out_tokens=gouts[k][0], out_accept_len=gouts[k][1],
+                                  out_best=gouts[k][2], workspace=gwss[k])
+
+            tg2 = in_flight_steps(torch, 2, args.steps, args.warmup, gstep2)
+            same = all(np.array_equal(o.cpu().numpy(), r) for oo in gouts for o, r in zip(oo, gref))
+            p2 = tg2["us_median"] / 1e6
+            greedy["in_flight_2"] = {"batches_in_flight": 2, "round": tg2, "us_per_round": tg2["us_median"],
+                                     "rounds_per_s": round(1.0 / p2, 1), "achieved_gbps": round(gal / p2 / 1e9, 1),
+                                     "frac_of_hbm_peak": round(gal / p2 / 1e9 / HBM_PEAK_GBPS, 4),
+                                     "same_outputs": bool(same)}
+            log(f"greedy, 2 batches in flight: {p2 * 1e6:.2f} us/round ({gal / p2 / 1e9:.0f} GB/s)")
         del gsets
 
     # ---------------------------------------------------------------- sampling verify of one-hot n-grams, same shape
@@ -957,6 +985,26 @@ def main() -> int:
                "algorithmic_bytes": nalg, "mean_accepted": round(float(nL.mean()), 4), "rotate": MN,
                "pass1_traffic": measured_traffic("k_ngs_rowstats")}
         log(f"n-gram sampling verify {tn * 1e6:.2f} us/round ({nalg / tn / 1e9:.0f} GB/s), mean accepted {nL.mean():.3f}")
+        if not args.eager:
+            # two independent batches in flight, one stream, workspace and outputs each
+            nref = (nsets[0]["ot"].cpu().numpy(), nL, nsets[0]["orow"].cpu().numpy())
+            nwss = [torch.zeros_like(nws) for _ in range(2)]
+            nouts = [(torch.empty_like(nsets[0]["ot"]), torch.empty_like(nsets[0]["ol"]),
+                      torch.empty_like(nsets[0]["orow"])) for _ in range(2)]
+
+            def nstep2(j, k):
+                st = nsets[j % MN]
+                rsv.verify_ngram_sample(st["lg"], st["cand"], st["uni"], ns.temperature, out_tokens=nouts[k][0],
+                                        out_accept_len=nouts[k][1], out_rows=nouts[k][2], workspace=nwss[k])
+
+            tn2 = in_flight_steps(torch, 2, args.steps, args.warmup, nstep2)
+            same = all(np.array_equal(o.cpu().numpy(), r) for oo in nouts for o, r in zip(oo, nref))
+            q2 = tn2["us_median"] / 1e6
+            ngs["in_flight_2"] = {"batches_in_flight": 2, "round": tn2, "us_per_round": tn2["us_median"],
+                                  "rounds_per_s": round(1.0 / q2, 1), "achieved_gbps": round(nalg / q2 / 1e9, 1),
+                                  "frac_of_hbm_peak": round(nalg / q2 / 1e9 / HBM_PEAK_GBPS, 4),
+                                  "same_outputs": bool(same)}
+            log(f"n-gram sampling verify, 2 batches in flight: {q2 * 1e6:.2f} us/round ({nalg / q2 / 1e9:.0f} GB/s)")
         del nsets
 
     # ---------------------------------------------------------------- CPU oracle: baseline timing and parity accounting
