@@ -73,6 +73,8 @@ def parse_args():
     ap.add_argument("--no-greedy", action="store_true")
     ap.add_argument("--no-filtered", action="store_true", help="skip the top-k / top-p filtered legs")
     ap.add_argument("--no-staged", action="store_true", help="skip the early-exit (staged pass 1) leg")
+    ap.add_argument("--no-in-flight", action="store_true",
+                    help="skip the legs with several batches in flight (a kernel trace then holds one launch at a time)")
     ap.add_argument("--no-pool", action="store_true", help="skip the n-gram pool legs (direct and hashed)")
     ap.add_argument("--no-ngram-sample", action="store_true", help="skip the one-hot n-gram sampling verify leg")
     ap.add_argument("--eager", action="store_true", help="launch through the Python binding instead of graphs")
@@ -659,7 +661,7 @@ def main() -> int:
     # independent batches in flight on separate streams (a serving loop verifying several
     # micro-batches at once); reported beside the one-batch round, which stays the value
     in_flight_legs = {}
-    if not args.eager:
+    if not args.eager and not args.no_in_flight:
         for S in (2, 3):
             r = in_flight(head, S, args.steps, args.warmup)
             r["workload"] = f"{WORKLOAD_NAMES[3]}; {S} independent batches in flight on {S} streams"
@@ -918,7 +920,7 @@ def main() -> int:
                   "frac_of_hbm_peak": round(gal / per / 1e9 / HBM_PEAK_GBPS, 4), "rotate": M5,
                   "algorithmic_bytes": gal, "argmax_traffic": measured_traffic("k_greedy_argmax")}
         log(f"greedy {per * 1e6:.2f} us/round ({gal / per / 1e9:.0f} GB/s)")
-        if not args.eager:
+        if not args.eager and not args.no_in_flight:
             # two independent batches in flight, one stream, workspace and outputs each
             gref = (gsets[0]["ot"].cpu().numpy(), gsets[0]["ol"].cpu().numpy(), gsets[0]["ob"].cpu().numpy())
             gwss = [torch.zeros_like(gws) for _ in range(2)]
@@ -985,7 +987,7 @@ def main() -> int:
                "algorithmic_bytes": nalg, "mean_accepted": round(float(nL.mean()), 4), "rotate": MN,
                "pass1_traffic": measured_traffic("k_ngs_rowstats")}
         log(f"n-gram sampling verify {tn * 1e6:.2f} us/round ({nalg / tn / 1e9:.0f} GB/s), mean accepted {nL.mean():.3f}")
-        if not args.eager:
+        if not args.eager and not args.no_in_flight:
             # two independent batches in flight, one stream, workspace and outputs each
             nref = (nsets[0]["ot"].cpu().numpy(), nL, nsets[0]["orow"].cpu().numpy())
             nwss = [torch.zeros_like(nws) for _ in range(2)]
