@@ -1782,9 +1782,10 @@ __device__ __forceinline__ void f32_band_vec(const u32x4& v, uint32_t valid, flo
 
 // The second read of a long fp32 row: every entry's fixed-point mass summed (the row,
 // above the band) and the band's entries kept, then gathered to wb.key[0..nb) as keys
-// in wave order, their masses summed on the way. Whole steps of kWideUnroll vectors per thread, then the last
-// vectors, the scalar head (lanes 0-3 of wave 0) and tail (lanes 4-7); every lane of
-// each wave takes part in each vector. False (uniform) when a wave's part overflowed.
+// in wave order, their masses summed on the way. Whole steps of kWideUnroll vectors
+// per thread, then the last vectors, the scalar head (lanes 0-3 of wave 0) and tail
+// (lanes 4-7); every lane of each wave takes part in each vector. False (uniform)
+// when a wave's part overflowed.
 __device__ bool f32_band_read(const float* row, int64_t V, WideBuf& wb, float c, float Rf, float Xa, float Xb,
                               F32Sums& sm, uint32_t& nb) {
   constexpr int BS = kFiltBlock, U = kWideUnroll;
