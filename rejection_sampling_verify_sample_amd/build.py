@@ -1,6 +1,7 @@
 """Build libspecverify.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m rejection_sampling_verify_sample_amd.build [--check]
+Usage: python -m rejection_sampling_verify_sample_amd.build [-v]
+       python -m rejection_sampling_verify_sample_amd.build --asan-host OUT.so   (host code under AddressSanitizer)
 """
 from __future__ import annotations
 
@@ -59,5 +60,40 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+# The host code (argument checks, workspace layout, launches) instrumented with
+# AddressSanitizer; the device code is built as usual. Load it with the sanitizer's
+# runtime preloaded (asan_runtime()) and ASAN_OPTIONS=detect_leaks=0 (the Python
+# interpreter's own allocations are not this library's).
+ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libasan"]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime ('' when absent)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = shutil.which("clang") or ""
+    if not clang:
+        return ""
+    out = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = out.stdout.strip()
+    return path if os.path.isabs(path) and os.path.exists(path) else ""
+
+
+def build_asan_host(out_path: str, verbose: bool = False) -> str:
+    """Compile every HIP source into out_path with the host code under AddressSanitizer."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    flags = HIPCC_FLAGS + ["-Xarch_host", "-g"] + ASAN_HOST_FLAGS
+    cmd = [hipcc(), *flags, "-o", out_path, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr}")
+    return out_path
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--asan-host" in sys.argv:
+        print(build_asan_host(sys.argv[sys.argv.index("--asan-host") + 1], verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))
