@@ -61,10 +61,13 @@ def build(verbose: bool = False) -> str:
 
 
 # The host code (argument checks, workspace layout, launches) instrumented with
-# AddressSanitizer; the device code is built as usual. Load it with the sanitizer's
-# runtime preloaded (asan_runtime()) and ASAN_OPTIONS=detect_leaks=0 (the Python
-# interpreter's own allocations are not this library's).
-ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libasan"]
+# AddressSanitizer and UndefinedBehaviorSanitizer (any finding aborts); the device code
+# is built as usual. Load it with the sanitizer's runtime preloaded (asan_runtime())
+# and ASAN_OPTIONS=detect_leaks=0 (the Python interpreter's own allocations are not
+# this library's).
+ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                   "-shared-libasan"]
 
 
 def asan_runtime() -> str:

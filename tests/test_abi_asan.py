@@ -1,10 +1,11 @@
-"""The library's host code under AddressSanitizer (CPU only, no GPU).
+"""The library's host code under AddressSanitizer and UBSan (CPU only, no GPU).
 
 The C ABI's argument checks, workspace-size arithmetic and table geometry run on the
 host before any HIP call. The library is built once more with that host code
 instrumented (the device code as usual), and the ABI tests (tests/test_abi.py) run
-against it in a child process with the sanitizer's runtime preloaded; any invalid
-host memory access would abort the run with a report.
+against it in a child process with the sanitizer's runtime preloaded; an invalid
+host memory access or undefined behaviour (a signed overflow in a size, a shift past
+the width) would abort the run with a report.
 """
 import os
 import subprocess
@@ -28,7 +29,7 @@ sys.exit(pytest.main(["-q", "-p", "no:cacheprovider", {tests!r}]))
 """
 
 
-def test_abi_checks_are_clean_under_address_sanitizer(tmp_path):
+def test_abi_checks_are_clean_under_sanitizers(tmp_path):
     try:
         runtime = build.asan_runtime()
     except RuntimeError as e:  # no hipcc
@@ -40,6 +41,6 @@ def test_abi_checks_are_clean_under_address_sanitizer(tmp_path):
     code = RUNNER.format(root=ROOT, lib=lib, tests=os.path.join(HERE, "test_abi.py"))
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600)
     out = r.stdout + r.stderr
-    assert "AddressSanitizer" not in out, out[-4000:]
+    assert "AddressSanitizer" not in out and "runtime error" not in out, out[-4000:]
     assert r.returncode == 0, out[-4000:]
     assert " passed" in out
