@@ -327,6 +327,42 @@ def test_filtered_residual_without_mass_draws_from_the_kept_target(dtype, V):
         assert tok[b, 0] >= 0 and x0[tok[b, 0]] >= np.sort(x0)[-int(kept[b, 0])], (b, tok[b, 0])
 
 
+def _million_entry_row(rng, V, T, n_top=20000):
+    """A row of V entries whose nucleus is about n_top entries spread over 8 doublings of
+    mass (more than the candidate buffer holds), above a tail of V - n_top entries that
+    holds about 5% of the mass: the cut's band is narrow, the row long."""
+    x = (T * np.log(0.0485) + rng.normal(0, 0.05, V)).astype(np.float32)
+    top = rng.choice(V, n_top, replace=False)
+    x[top] = rng.uniform(0.0, 8 * T * np.log(2.0), n_top).astype(np.float32)
+    return x
+
+
+def test_two_read_top_p_on_a_million_entry_fp32_row():
+    """Top-p alone on fp32 rows of 2^20 entries whose nucleus outgrows the buffer but
+    whose band fits it: the two-read route, whose second read moves its per-thread
+    fp64 sums to 64-bit integers every 3,072 entries (more than 256 steps per thread
+    here). Equal to the multi-pass select, and the oracle's round."""
+    log("two-read top-p fp32 V=2^20")
+    rng = np.random.default_rng(41)
+    B, K, V, T = 2, 1, 1 << 20, 0.8
+    tgt = np.stack([np.stack([_million_entry_row(rng, V, T) for _ in range(K + 1)]) for _ in range(B)])
+    drf = (tgt[:, :K] + rng.normal(0, 0.05, (B, K, V))).astype(np.float32)
+    toks = rng.integers(0, V, (B, K))
+    uni = rng.random((B, K + 1, 2)).astype(np.float32)
+    ks = np.zeros(B, dtype=np.int32)
+    ps = np.array([0.9, 0.8], dtype=np.float32)
+    t = _f32_tensors(tgt, drf, toks, uni, T=T)
+    tok, n, probs, kept = run_gpu(t, ks, ps)
+    tok2, n2, probs2, kept2 = _run_multi_pass(t, ks, ps)
+    assert np.array_equal(kept, kept2), (kept, kept2)
+    assert np.array_equal(tok, tok2) and np.array_equal(n, n2)
+    assert np.all(kept > 6144)  # every nucleus outgrows the buffer
+    res = oracle.oracle_sample_filtered(tgt, drf, toks, uni, T, ks, ps)
+    rep = compare_filtered(tgt, drf, toks, uni, T, ks, ps, res, tok, n, probs, kept)
+    log(f"  {rep.summary()}")
+    rep.check_accounting()
+
+
 def _crowd_ties_into_wave0(x, p, T, n_tie, rng):
     """A flat fp32 row whose top-p cut falls inside a block of n_tie equal entries, all
     placed where the second read hands them to wave 0 (16-byte vectors 0-63 of every
