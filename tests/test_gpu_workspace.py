@@ -104,3 +104,42 @@ def test_batches_in_flight_on_streams():
     torch.cuda.synchronize()
     for i, tok, n in got:
         assert np.array_equal(tok.cpu().numpy(), refs[i][0]) and np.array_equal(n.cpu().numpy(), refs[i][1]), i
+
+
+def test_host_threads_each_on_their_stream():
+    """Four host threads, each with its own stream and round, call the verify at once
+    (ctypes releases the interpreter lock during the calls) with the binding's own
+    per-stream workspaces: every call's outputs equal the round's outputs run alone."""
+    import threading
+
+    specs = [make_sample_inputs(3, 30 + i, B=8, V=20000) for i in range(4)]
+    ts = [sample_tensors(s, DEV) for s in specs]
+    refs = [_run(t) for t in ts]
+    errors, done = [], []
+    log("4 threads")
+
+    def work(i):
+        try:
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.default_stream())
+            t = ts[i]
+            with torch.cuda.stream(st):
+                outs = [rsv.verify_sample(t["target"], t["draft"], t["draft_tokens"], t["uniforms"], t["temperature"])
+                        for _ in range(5)]
+            st.synchronize()
+            for o in outs:
+                if not (np.array_equal(o.tokens.cpu().numpy(), refs[i][0])
+                        and np.array_equal(o.num_accepted.cpu().numpy(), refs[i][1])):
+                    errors.append(i)
+            done.append(i)
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append((i, repr(e)))
+
+    torch.cuda.synchronize()
+    th = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for x in th:
+        x.start()
+    for x in th:
+        x.join(timeout=120)
+    assert not errors, errors
+    assert sorted(done) == [0, 1, 2, 3]
