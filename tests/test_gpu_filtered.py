@@ -113,6 +113,43 @@ def test_filtered_parity_full_size_k50_p09():
     rep.check_accounting()
 
 
+def test_filtered_parity_full_size_p09():
+    """The full B=64 K=8 V=128256 bf16 round with top-p 0.9 alone on every row (long bf16
+    rows: the key-count route), all rows compared."""
+    s = make_sample_inputs(3, 0)
+    k, p = make_filter_params(64, top_k=0, top_p=0.9)
+    rep = check(s, k, p, "p0.9")
+    save_report("cfg3 full p0.9", rep)
+    rep.check_accounting()
+
+
+@pytest.fixture(scope="module")
+def cfg4_full():
+    return make_sample_inputs(4, 0)
+
+
+@pytest.mark.parametrize("top_k,top_p", [(50, 0.9), (0, 0.9)])
+def test_filtered_parity_full_size_fp32_sampled(cfg4_full, top_k, top_p):
+    """The full B=256 K=4 V=152064 fp32 round (rows b < 128 peaked, the rest flat; flat
+    rows with top-p alone take the two-read route) launched whole, as timed; 32 batch
+    rows, 16 peaked and 16 flat, compared with the oracle run on those rows alone (a
+    batch row's outputs depend only on its own rows)."""
+    s = cfg4_full
+    B = s.shape[0]
+    k, p = make_filter_params(B, top_k=top_k, top_p=top_p)
+    log(f"cfg4 full k={top_k} p={top_p}")
+    tok, n, probs, kept = run_gpu(sample_tensors(s, DEV), k, p)
+    idx = np.r_[0:8, 120:128, 128:136, B - 8:B]
+    tgt, drf = s.target_f32()[idx], s.draft_f32()[idx]
+    toks, uni = s.draft_tokens[idx], s.uniforms[idx]
+    res = oracle.oracle_sample_filtered(tgt, drf, toks, uni, s.temperature, k[idx], p[idx])
+    rep = compare_filtered(tgt, drf, toks, uni, s.temperature, k[idx], p[idx], res, tok[idx], n[idx], probs[idx],
+                           kept[idx])
+    log(f"  {rep.summary()}")
+    save_report(f"cfg4 full sampled k{top_k} p{top_p}", rep)
+    rep.check_accounting()
+
+
 @pytest.mark.parametrize("k,p", [(None, None), (0, 1.0), (1, 1.0), (0, 1e-30), (0, float("nan")), (2000, 0.999),
                                  (7, 0.3), (0, 0.95)], ids=lambda x: str(x))
 def test_filter_settings(k, p):
