@@ -71,6 +71,7 @@ CASES = [
     (3, 33, 6, 40, 5, 8, 1, 6, 0.3, 0.3),            # direct-mapped: evictions inside every call
     (2, 40, 3, 1000, 3, 1, 64, 8, 0.2, 0.05),        # fully associative over 64 ways, evictions among them
     (4, 20, 4, 152064, 7, 1 << 16, 4, 3, 0.5, 0.02), # a 152064-token vocabulary over 65536 sets
+    (256, 15, 5, 152064, 7, 512, 8, 3, 0.5, 0.02),   # the bench's large leg: B=256 V=152064, 512 sets x 8 ways
 ]
 
 
