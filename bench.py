@@ -805,6 +805,11 @@ def main() -> int:
             log(f"workload {cfg}: {m['t_step'] * 1e6:.2f} us per round ({m['rounds_per_s']:.0f} rounds/s, "
                 f"{m['gbps']:.0f} GB/s = {m['gbps'] / HBM_PEAK_GBPS:.3f} of peak); pass 1 {m['t_pass1'] * 1e6:.2f} us "
                 f"({m['pass1_gbps'] / HBM_PEAK_GBPS:.3f} of peak)")
+            if cfg == 4 and not args.eager and not args.no_in_flight:
+                r4 = in_flight(leg, 2, max(CHUNK_STEPS, args.steps // 4), args.warmup // 4)
+                workloads["4"]["in_flight_2"] = r4
+                log(f"workload 4, 2 batches in flight: {r4['us_per_round']:.2f} us per round "
+                    f"({r4['frac_of_hbm_peak']:.3f} of peak); outputs {'equal' if r4['same_outputs'] else 'DIFFER'}")
             if cfg == 4 and not args.no_filtered:
                 filtered_f32 = filtered_leg_f32(leg)
             for st in leg.sets[1:]:
