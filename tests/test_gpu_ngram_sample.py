@@ -59,6 +59,8 @@ CASES = [
     (dict(B=16, G=3, N=2, V=500, peak=3.0), 3),               # the shortest n-grams: one try position + bonus
     (dict(B=4, G=2, N=65, V=300, peak=12.0, match_prob=0.97), 1),  # the longest n-grams, deep walks
     (dict(B=24, G=5, N=4, V=7, dtype="f32", peak=1.0), 3),    # V below one 16-byte vector
+    (dict(B=6, G=4, N=4, V=152064, peak=10.0), 1),           # rows past 16 blocks: read block after block
+    (dict(B=6, G=3, N=3, V=50021, dtype="f32", peak=8.0), 1),  # the same in fp32, odd V
 ]
 
 
