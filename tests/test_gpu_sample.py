@@ -88,6 +88,8 @@ PARITY_CASES = [
     (1, dict(B=5, K=1, V=7), 4),       # V smaller than one 16-byte vector
     (2, dict(B=4, K=64, V=3000), 1),   # the largest K: the ballot spans a whole wave
     (3, dict(B=7, K=0, V=1000), 2),    # K = 0: one draw from the bonus row
+    (1, dict(B=1, K=1, V=300001), 2),  # two rows of 300k: 36 pass-1 segments each, merged in a loop
+    (3, dict(B=2, K=2, V=1 << 20), 1), # rows of 2^20 bf16 entries over many segments and chunks
 ]
 
 
