@@ -89,6 +89,7 @@ CASES = [
     (3, dict(B=5, K=0, V=1000)),          # K = 0: the bonus row only
     (2, dict(B=3, K=64, V=3000)),         # the largest K
     (1, dict(B=4, K=2, V=7)),             # V smaller than a vector
+    (3, dict(B=3, K=2, V=1 << 20)),       # rows of 2^20 bf16 entries under every filter route
 ]
 
 
